@@ -1,0 +1,143 @@
+"""Python access to the float64 parity oracle -- TEST INFRASTRUCTURE ONLY.
+
+The oracle is a plain sequential per-token implementation of the gated delta
+rule in C (``gdn_oracle.c``), built into ``liboracle.so`` next to this file.
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use it;
+the HIP library and its binding never import this package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "gdn_oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, strict IEEE double: no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-std=c11",
+           "-Wall", "-Wextra", *extra_flags, "-o", output, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+_P = ctypes.c_void_p
+_F = ctypes.c_float
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_D = ctypes.c_double
+
+
+class Oracle:
+    """ctypes wrapper of one built oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"oracle library {path} is not built; run oracle.build()")
+        self.path = path
+        self._lib = ctypes.CDLL(path)
+        self._lib.gdn_oracle_prefill.restype = _I
+        self._lib.gdn_oracle_prefill.argtypes = [_I, _I, _I, _I, _I, _I, _I, _D,
+                                                 _P, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _I]
+        self._lib.gdn_oracle_decode.restype = _I
+        self._lib.gdn_oracle_decode.argtypes = [_I, _I, _I, _I, _I, _I, _D,
+                                                _P, _P, _P, _P, _P, _P, _I64, _P, _P, _I]
+        self._lib.gdn_oracle_max_threads.restype = _I
+        self._lib.gdn_oracle_max_threads.argtypes = []
+
+    def max_threads(self) -> int:
+        return int(self._lib.gdn_oracle_max_threads())
+
+    @staticmethod
+    def _f32(x):
+        return np.ascontiguousarray(x, dtype=np.float32)
+
+    @staticmethod
+    def _ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    def prefill(self, q, k, v, g, beta, s0=None, scale: float = 1.0, head_map: int = 0,
+                pairs: Optional[Sequence[int]] = None, threads: Optional[int] = None):
+        """Sequential float64 prefill.
+
+        q, k [B][Hk][T][dk]; v [B][Hv][T][dv]; g, beta [B][Hv][T]; s0 [B][Hv][dv][dk] or None.
+        Returns (o, s_final) as float64: o [B][Hv][T][dv] and s_final [B][Hv][dv][dk] when
+        pairs is None, else compact [npairs][T][dv] and [npairs][dv][dk] over the listed
+        flattened (b * Hv + h) pairs.
+        """
+        q, k, v, g, beta = (self._f32(x) for x in (q, k, v, g, beta))
+        B, Hk, T, dk = q.shape
+        Hv, dv = v.shape[1], v.shape[3]
+        if k.shape != q.shape or v.shape[:3] != (B, Hv, T) or g.shape != (B, Hv, T) \
+                or beta.shape != (B, Hv, T):
+            raise ValueError("inconsistent prefill input shapes")
+        s0c = None
+        if s0 is not None:
+            s0c = np.ascontiguousarray(s0, dtype=np.float64)
+            if s0c.shape != (B, Hv, dv, dk):
+                raise ValueError("s0 must be [B][Hv][dv][dk]")
+        if pairs is None:
+            n, pa = B * Hv, None
+        else:
+            pa = np.ascontiguousarray(pairs, dtype=np.int64)
+            n = len(pa)
+        o = np.empty((n, T, dv), dtype=np.float64)
+        s = np.empty((n, dv, dk), dtype=np.float64)
+        threads = threads or self.max_threads()
+        rc = self._lib.gdn_oracle_prefill(B, T, Hk, Hv, dk, dv, head_map, float(scale),
+                                          self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(g),
+                                          self._ptr(beta), self._ptr(s0c), self._ptr(pa), n,
+                                          self._ptr(o), self._ptr(s), int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle prefill rejected its arguments (code {rc})")
+        if pairs is None:
+            return o.reshape(B, Hv, T, dv), s.reshape(B, Hv, dv, dk)
+        return o, s
+
+    def decode_step(self, q, k, v, g, beta, state, scale: float = 1.0, head_map: int = 0,
+                    pairs: Optional[Sequence[int]] = None, threads: Optional[int] = None):
+        """One float64 decode step; updates ``state`` (float64, C-contiguous) in place.
+
+        q, k [B][Hk][dk]; v [B][Hv][dv]; g, beta [B][Hv]. state is [B][Hv][dv][dk] when pairs
+        is None, else [npairs][dv][dk]. Returns o ([B][Hv][dv] or [npairs][dv]).
+        """
+        q, k, v, g, beta = (self._f32(x) for x in (q, k, v, g, beta))
+        B, Hk, dk = q.shape
+        Hv, dv = v.shape[1], v.shape[2]
+        if state.dtype != np.float64 or not state.flags["C_CONTIGUOUS"]:
+            raise ValueError("state must be a C-contiguous float64 array")
+        if pairs is None:
+            n, pa = B * Hv, None
+        else:
+            pa = np.ascontiguousarray(pairs, dtype=np.int64)
+            n = len(pa)
+        if state.size != n * dv * dk:
+            raise ValueError("state has the wrong size")
+        o = np.empty((n, dv), dtype=np.float64)
+        threads = threads or self.max_threads()
+        rc = self._lib.gdn_oracle_decode(B, Hk, Hv, dk, dv, head_map, float(scale),
+                                         self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(g),
+                                         self._ptr(beta), self._ptr(pa), n, self._ptr(state),
+                                         self._ptr(o), int(threads))
+        if rc != 0:
+            raise ValueError(f"oracle decode rejected its arguments (code {rc})")
+        return o.reshape(B, Hv, dv) if pairs is None else o
+
+
+_default: Optional[Oracle] = None
+
+
+def load() -> Oracle:
+    """The oracle built next to this file (built on first use if missing)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default

@@ -1,0 +1,174 @@
+/*
+ * Parity oracle for the gated delta rule scan -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library. The product path (the HIP library and its
+ * Python binding) never calls it, and the two share no code.
+ *
+ * What it computes: the plain sequential definition of the gated delta rule,
+ * one token at a time, in float64. For every (sequence b, value head h):
+ *
+ *     S_t = exp(g_t) * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t (scale * q_t)
+ *
+ * S is dv x dk (row i = value dimension, column j = key dimension). That
+ * orientation is the one of the tinygrad gated-delta reference loops (the
+ * state is contracted with a key vector over its last index) on the
+ * "27b 935/47" compare page (tests of gated_delta_decode and
+ * gated_delta_prefill in test_llm_quant_cpu.py); the output is read from
+ * the updated state, as in the same tests, where the core output equals
+ * alpha*S*q + delta*(k.q) with S the state before the update.
+ *
+ * The decay enters as g (log-decay) and alpha = exp(g): a padded step with
+ * g = 0 and beta = 0 leaves S unchanged (the no-op rule in the commit log of
+ * the page "mergable fast RDNA3 Qwen 3.6", symbolic-length prefill entry).
+ *
+ * Key heads are shared by value heads: head_map 0 ("tiled") reads key head
+ * h % Hk, the repeat of key heads that gdn_qkv performs in the gdn_qkv test on
+ * the "27b 935/47" page; head_map 1 ("grouped") reads key head h / (Hv / Hk).
+ *
+ * Inputs are float32 (bfloat16 inputs arrive already widened exactly); every
+ * operation is done in double. Threads split the independent (b, h) pairs
+ * only, so results are bit-identical for any thread count.
+ *
+ * Parity pins (tests/test_oracle_pins.py): dense brute-force unrolling,
+ * exact rational arithmetic on tiny inputs, the pages' one-step formula,
+ * the padded no-op rule, continuation splits, the beta = 0 closed form,
+ * delta-rule recall with orthonormal keys, scale linearity, head-map
+ * permutation and thread-count invariance.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int key_head_of(int h, int Hk, int Hv, int head_map) {
+    if (head_map == 0) return h % Hk;
+    return h / (Hv / Hk);
+}
+
+/* One token of the recurrence on a dv x dk row-major state, then the output. */
+static void oracle_step(double *S, int dk, int dv, double alpha, double beta, double scale,
+                        const float *qq, const float *kk, const float *vv, double *u, double *out) {
+    /* u = S k */
+    for (int i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * (double)kk[j];
+        u[i] = acc;
+    }
+    /* S <- alpha * S (I - beta k k^T) + beta v k^T
+     *    = alpha * (S - beta (S k) k^T) + beta v k^T                    */
+    for (int i = 0; i < dv; ++i) {
+        for (int j = 0; j < dk; ++j) {
+            double kj = (double)kk[j];
+            double s = S[(int64_t)i * dk + j];
+            S[(int64_t)i * dk + j] = alpha * (s - beta * u[i] * kj) + beta * (double)vv[i] * kj;
+        }
+    }
+    /* o = S (scale q), from the updated state */
+    for (int i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * (scale * (double)qq[j]);
+        out[i] = acc;
+    }
+}
+
+static int check_shape(int B, int T, int Hk, int Hv, int dk, int dv, int head_map) {
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || dk < 1 || dv < 1) return 1;
+    if (Hv % Hk != 0) return 1;
+    if (head_map != 0 && head_map != 1) return 1;
+    return 0;
+}
+
+/*
+ * Prefill: q, k [B][Hk][T][dk]; v [B][Hv][T][dv]; g, beta [B][Hv][T];
+ * s0 [B][Hv][dv][dk] in double (a float32 initial state widens exactly) or NULL (zero state).
+ * pairs: list of flattened (b * Hv + h) indices to compute, or NULL for all
+ * B*Hv pairs in order. Outputs are compact over the list:
+ * o [npairs][T][dv], s_final [npairs][dv][dk] (either may be NULL).
+ * Returns 0, or 1 on invalid arguments.
+ */
+int gdn_oracle_prefill(int B, int T, int Hk, int Hv, int dk, int dv, int head_map, double scale,
+                       const float *q, const float *k, const float *v,
+                       const float *g, const float *beta, const double *s0,
+                       const int64_t *pairs, int64_t npairs,
+                       double *o, double *s_final, int nthreads) {
+    if (check_shape(B, T, Hk, Hv, dk, dv, head_map)) return 1;
+    if (!pairs) npairs = (int64_t)B * Hv;
+    for (int64_t p = 0; pairs && p < npairs; ++p)
+        if (pairs[p] < 0 || pairs[p] >= (int64_t)B * Hv) return 1;
+    if (nthreads < 1) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+    for (int64_t p = 0; p < npairs; ++p) {
+        int64_t pair = pairs ? pairs[p] : p;
+        int b = (int)(pair / Hv), h = (int)(pair % Hv);
+        int kh = key_head_of(h, Hk, Hv, head_map);
+        double *S = (double *)calloc((size_t)dv * dk, sizeof(double));
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *out = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !u || !out) { bad = 1; free(S); free(u); free(out); continue; }
+        if (s0) {
+            const double *src = s0 + ((int64_t)b * Hv + h) * dv * dk;
+            for (int64_t e = 0; e < (int64_t)dv * dk; ++e) S[e] = src[e];
+        }
+        for (int t = 0; t < T; ++t) {
+            const float *qq = q + (((int64_t)b * Hk + kh) * T + t) * dk;
+            const float *kk = k + (((int64_t)b * Hk + kh) * T + t) * dk;
+            const float *vv = v + (((int64_t)b * Hv + h) * T + t) * dv;
+            int64_t gi = ((int64_t)b * Hv + h) * T + t;
+            double alpha = exp((double)g[gi]);
+            oracle_step(S, dk, dv, alpha, (double)beta[gi], scale, qq, kk, vv, u, out);
+            if (o) memcpy(o + ((int64_t)p * T + t) * dv, out, sizeof(double) * (size_t)dv);
+        }
+        if (s_final) memcpy(s_final + (int64_t)p * dv * dk, S, sizeof(double) * (size_t)dv * dk);
+        free(S); free(u); free(out);
+    }
+    return bad ? 2 : 0;
+}
+
+/*
+ * One decode step for a batch: q, k [B][Hk][dk]; v [B][Hv][dv]; g, beta [B][Hv].
+ * state [npairs][dv][dk] (float64, updated in place) and o [npairs][dv] are
+ * compact over the pair list (NULL = all B*Hv pairs in order).
+ */
+int gdn_oracle_decode(int B, int Hk, int Hv, int dk, int dv, int head_map, double scale,
+                      const float *q, const float *k, const float *v,
+                      const float *g, const float *beta,
+                      const int64_t *pairs, int64_t npairs,
+                      double *state, double *o, int nthreads) {
+    if (check_shape(B, 1, Hk, Hv, dk, dv, head_map)) return 1;
+    if (!state || !o) return 1;
+    if (!pairs) npairs = (int64_t)B * Hv;
+    for (int64_t p = 0; pairs && p < npairs; ++p)
+        if (pairs[p] < 0 || pairs[p] >= (int64_t)B * Hv) return 1;
+    if (nthreads < 1) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : bad)
+    for (int64_t p = 0; p < npairs; ++p) {
+        int64_t pair = pairs ? pairs[p] : p;
+        int b = (int)(pair / Hv), h = (int)(pair % Hv);
+        int kh = key_head_of(h, Hk, Hv, head_map);
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!u) { bad = 1; continue; }
+        const float *qq = q + ((int64_t)b * Hk + kh) * dk;
+        const float *kk = k + ((int64_t)b * Hk + kh) * dk;
+        const float *vv = v + ((int64_t)b * Hv + h) * dv;
+        double alpha = exp((double)g[pair]);
+        oracle_step(state + (int64_t)p * dv * dk, dk, dv, alpha, (double)beta[pair], scale,
+                    qq, kk, vv, u, o + (int64_t)p * dv);
+        free(u);
+    }
+    return bad ? 2 : 0;
+}
+
+int gdn_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
