@@ -1,0 +1,184 @@
+"""Thin ctypes binding of libgdn.so: argument marshalling only.
+
+Every step of the scan runs in the HIP kernels behind the C ABI (include/gdn.h).
+PyTorch provides device memory and the current HIP stream; nothing here
+computes any part of the method, and there is no fallback: if libgdn.so is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
+GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
+
+EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_status_string",
+                    "gdn_last_error", "gdn_abi_version")
+
+
+class GdnShape(ctypes.Structure):
+    """Mirror of gdn_shape in include/gdn.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int),
+                ("head_map", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"gdn status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libgdn.so (torch is imported first so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m gated_delta_rule_56_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, SZ = ctypes.c_void_p, ctypes.c_size_t
+    lib.gdn_prefill_workspace_bytes.restype = SZ
+    lib.gdn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
+    lib.gdn_prefill.restype = ctypes.c_int
+    lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.gdn_decode.restype = ctypes.c_int
+    lib.gdn_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_abi_version.restype = ctypes.c_int
+    lib.gdn_abi_version.argtypes = []
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int) -> None:
+    if status != GDN_OK:
+        raise GdnError(status, lib.gdn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_handle(stream) -> Optional[int]:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, qkv_dtype, head_map, scale):
+    return GdnShape(batch, seq_len, num_k_heads, num_v_heads, head_dim, head_dim, chunk,
+                    qkv_dtype, head_map, float(scale))
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+            initial_state: Optional[torch.Tensor] = None, *, chunk: int = 64, head_map: int = GDN_HEADS_TILED,
+            scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+            final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gdn_prefill on torch tensors.
+
+    q, k [B][Hk][T][d] and v [B][Hv][T][d] (bfloat16 or float32); g, beta [B][Hv][T] float32;
+    initial_state [B][Hv][d][d] float32 or None. Returns (o, final_state). Pass
+    final_state=initial_state to update a state in place.
+    """
+    lib = load_library()
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, nm, dtype)
+    _dev_tensor(g, "g", torch.float32)
+    _dev_tensor(beta, "beta", torch.float32)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
+        raise ValueError("q, k must be [B][Hk][T][d] and v [B][Hv][T][d]")
+    B, Hk, T, d = q.shape
+    Hv = v.shape[1]
+    if v.shape != (B, Hv, T, d) or g.shape != (B, Hv, T) or beta.shape != (B, Hv, T):
+        raise ValueError("v must be [B][Hv][T][d] and g, beta [B][Hv][T]")
+    if initial_state is not None:
+        _dev_tensor(initial_state, "initial_state", torch.float32)
+        if initial_state.shape != (B, Hv, d, d):
+            raise ValueError("initial_state must be [B][Hv][d][d]")
+    if o is None:
+        o = torch.empty((B, Hv, T, d), dtype=torch.float32, device=q.device)
+    _dev_tensor(o, "o", torch.float32)
+    if o.shape != (B, Hv, T, d):
+        raise ValueError("o must be [B][Hv][T][d]")
+    if final_state is None and write_final_state:
+        final_state = torch.empty((B, Hv, d, d), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _dev_tensor(final_state, "final_state", torch.float32)
+        if final_state.shape != (B, Hv, d, d):
+            raise ValueError("final_state must be [B][Hv][d][d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shape = make_shape(B, T, Hk, Hv, d, chunk,
+                       GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, scale)
+    ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
+    workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    _check(lib, lib.gdn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), ws,
+                                _stream_handle(stream)))
+    return o, final_state
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+           state: torch.Tensor, *, head_map: int = GDN_HEADS_TILED, scale: Optional[float] = None,
+           o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """gdn_decode on torch tensors: q, k [B][Hk][d], v [B][Hv][d], g, beta [B][Hv],
+    state [B][Hv][d][d] float32 (updated in place). Returns o [B][Hv][d] float32."""
+    lib = load_library()
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, nm, dtype)
+    _dev_tensor(g, "g", torch.float32)
+    _dev_tensor(beta, "beta", torch.float32)
+    _dev_tensor(state, "state", torch.float32)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3:
+        raise ValueError("q, k must be [B][Hk][d] and v [B][Hv][d]")
+    B, Hk, d = q.shape
+    Hv = v.shape[1]
+    if v.shape != (B, Hv, d) or g.shape != (B, Hv) or beta.shape != (B, Hv) or state.shape != (B, Hv, d, d):
+        raise ValueError("v [B][Hv][d], g/beta [B][Hv], state [B][Hv][d][d] expected")
+    if o is None:
+        o = torch.empty((B, Hv, d), dtype=torch.float32, device=q.device)
+    _dev_tensor(o, "o", torch.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shape = make_shape(B, 1, Hk, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
+                       head_map, scale)
+    _check(lib, lib.gdn_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(state), _ptr(o), _stream_handle(stream)))
+    return o

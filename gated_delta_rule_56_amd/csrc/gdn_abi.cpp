@@ -1,0 +1,219 @@
+// C ABI of the gated delta rule library: argument validation (pure host code,
+// run before anything is enqueued), variant dispatch and error reporting.
+#include "gdn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdn_status fail(gdn_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(const Range &a, const Range &b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range range(const char *name, const void *p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks common to both calls. Element counts must stay far from int64 overflow.
+gdn_status check_common(const gdn_shape *s) {
+    if (!s) return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
+    if (s->batch < 1) return fail(GDN_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", s->batch);
+    if (s->num_k_heads < 1 || s->num_v_heads < 1)
+        return fail(GDN_ERR_INVALID_ARG, "head counts must be >= 1 (Hk=%d, Hv=%d)", s->num_k_heads, s->num_v_heads);
+    if (s->num_v_heads % s->num_k_heads != 0)
+        return fail(GDN_ERR_INVALID_ARG, "num_v_heads (%d) must be a multiple of num_k_heads (%d)",
+                    s->num_v_heads, s->num_k_heads);
+    if (s->head_dim_k < 1 || s->head_dim_v < 1)
+        return fail(GDN_ERR_INVALID_ARG, "head dims must be >= 1 (dk=%d, dv=%d)", s->head_dim_k, s->head_dim_v);
+    if (s->qkv_dtype != GDN_DTYPE_F32 && s->qkv_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_INVALID_ARG, "unknown qkv_dtype %d", (int)s->qkv_dtype);
+    if (s->head_map != GDN_HEADS_TILED && s->head_map != GDN_HEADS_GROUPED)
+        return fail(GDN_ERR_INVALID_ARG, "unknown head_map %d", (int)s->head_map);
+    if (!std::isfinite(s->scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
+    if (s->head_dim_k != s->head_dim_v)
+        return fail(GDN_ERR_UNSUPPORTED, "dk != dv (%d, %d) is not supported", s->head_dim_k, s->head_dim_v);
+    const double pairs = (double)s->batch * s->num_v_heads;
+    if (pairs * s->head_dim_v > 2147483647.0)
+        return fail(GDN_ERR_UNSUPPORTED, "batch * num_v_heads * head_dim is too large for one launch");
+    return GDN_OK;
+}
+
+gdn_status check_ptr(const void *p, const char *name, uintptr_t align) {
+    if (!p) return fail(GDN_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(GDN_ERR_INVALID_ARG, "%s is not %u-byte aligned", name, (unsigned)align);
+    return GDN_OK;
+}
+
+gdn_status check_no_overlap(const Range *outs, int nout, const Range *ins, int nin) {
+    for (int i = 0; i < nout; ++i)
+        for (int j = 0; j < nin; ++j)
+            if (overlaps(outs[i], ins[j]))
+                return fail(GDN_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, ins[j].name);
+    return GDN_OK;
+}
+
+#define GDN_TRY(expr)                      \
+    do {                                   \
+        gdn_status st_ = (expr);           \
+        if (st_ != GDN_OK) return st_;     \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_status_string(gdn_status st) {
+    switch (st) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARG: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case GDN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *gdn_last_error(void) { return g_last_error; }
+
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shape) {
+    (void)shape;
+    return 0;
+}
+
+gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *initial_state, float *o, float *final_state,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    GDN_TRY(check_common(s));
+    if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
+    if (s->chunk != 16 && s->chunk != 32 && s->chunk != 64)
+        return fail(GDN_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", s->chunk);
+    const int d = s->head_dim_k;
+    const bool bf16 = s->qkv_dtype == GDN_DTYPE_BF16;
+    if (bf16 && d != 128) return fail(GDN_ERR_UNSUPPORTED, "bfloat16 prefill supports head_dim 128 (got %d)", d);
+    if (!bf16 && d != 16 && d != 32 && d != 64 && d != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "float32 prefill supports head_dim 16, 32, 64 or 128 (got %d)", d);
+    const double tokens = (double)s->batch * s->num_v_heads * s->seq_len * d;
+    if (tokens > 4.0e15) return fail(GDN_ERR_UNSUPPORTED, "tensor sizes overflow");
+
+    const int64_t B = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
+    const int64_t esz = bf16 ? 2 : 4;
+    const int64_t qk_bytes = B * Hk * T * d * esz, v_bytes = B * Hv * T * d * esz;
+    const int64_t gb_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * 4, st_bytes = B * Hv * d * d * 4;
+    if (T > 0) {
+        GDN_TRY(check_ptr(q, "q", 16));
+        GDN_TRY(check_ptr(k, "k", 16));
+        GDN_TRY(check_ptr(v, "v", 16));
+        GDN_TRY(check_ptr(g, "g", 4));
+        GDN_TRY(check_ptr(beta, "beta", 4));
+        GDN_TRY(check_ptr(o, "o", 16));
+    }
+    if (initial_state) GDN_TRY(check_ptr(initial_state, "initial_state", 16));
+    if (final_state) GDN_TRY(check_ptr(final_state, "final_state", 16));
+
+    const Range ins[] = {range("q", q, T ? qk_bytes : 0), range("k", k, T ? qk_bytes : 0),
+                         range("v", v, T ? v_bytes : 0), range("g", g, T ? gb_bytes : 0),
+                         range("beta", beta, T ? gb_bytes : 0),
+                         range("initial_state", initial_state, initial_state ? st_bytes : 0)};
+    const Range out_o[] = {range("o", o, T ? o_bytes : 0)};
+    GDN_TRY(check_no_overlap(out_o, 1, ins, 6));
+    if (final_state) {
+        const Range out_s[] = {range("final_state", final_state, st_bytes)};
+        GDN_TRY(check_no_overlap(out_s, 1, ins, 5));  // q, k, v, g, beta
+        GDN_TRY(check_no_overlap(out_s, 1, out_o, 1));
+        if (initial_state && final_state != initial_state && overlaps(out_s[0], ins[5]))
+            return fail(GDN_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
+    }
+
+    gdn::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.init_state = initial_state;
+    p.o = o;
+    p.final_state = final_state;
+    p.B = s->batch;
+    p.T = s->seq_len;
+    p.Hk = s->num_k_heads;
+    p.Hv = s->num_v_heads;
+    p.D = d;
+    p.head_map = (int32_t)s->head_map;
+    p.scale = s->scale;
+    if (!final_state && T == 0) return GDN_OK;  // nothing to compute or write
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t err = bf16 ? gdn::launch_prefill_mfma(p, s->chunk, st) : gdn::launch_prefill_f32(p, s->chunk, st);
+    if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
+    return GDN_OK;
+}
+
+gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, float *state, float *o, void *stream) {
+    GDN_TRY(check_common(s));
+    if (s->seq_len != 1) return fail(GDN_ERR_INVALID_ARG, "decode needs seq_len == 1 (got %d)", s->seq_len);
+    const int d = s->head_dim_k;
+    if (d != 32 && d != 64 && d != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "decode supports head_dim 32, 64 or 128 (got %d)", d);
+    const bool bf16 = s->qkv_dtype == GDN_DTYPE_BF16;
+    const int64_t B = s->batch, Hk = s->num_k_heads, Hv = s->num_v_heads;
+    const int64_t esz = bf16 ? 2 : 4;
+    GDN_TRY(check_ptr(q, "q", 16));
+    GDN_TRY(check_ptr(k, "k", 16));
+    GDN_TRY(check_ptr(v, "v", 16));
+    GDN_TRY(check_ptr(g, "g", 4));
+    GDN_TRY(check_ptr(beta, "beta", 4));
+    GDN_TRY(check_ptr(state, "state", 16));
+    GDN_TRY(check_ptr(o, "o", 16));
+    const Range ins[] = {range("q", q, B * Hk * d * esz), range("k", k, B * Hk * d * esz),
+                         range("v", v, B * Hv * d * esz), range("g", g, B * Hv * 4),
+                         range("beta", beta, B * Hv * 4)};
+    const Range outs[] = {range("o", o, B * Hv * d * 4), range("state", state, B * Hv * d * d * 4)};
+    GDN_TRY(check_no_overlap(outs, 2, ins, 5));
+    if (overlaps(outs[0], outs[1])) return fail(GDN_ERR_INVALID_ARG, "o overlaps state");
+
+    gdn::DecodeParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.state = state;
+    p.o = o;
+    p.B = s->batch;
+    p.Hk = s->num_k_heads;
+    p.Hv = s->num_v_heads;
+    p.D = d;
+    p.head_map = (int32_t)s->head_map;
+    p.scale = s->scale;
+    const hipError_t err = gdn::launch_decode(p, bf16, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(GDN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
+    return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, element
+// conversions, MFMA wrappers and the value-head -> key-head mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Key head read by value head h (tiled: h % Hk; grouped: h / (Hv / Hk)).
+__device__ __forceinline__ int key_head(int h, int Hk, int Hv, int head_map) {
+    return head_map == 0 ? h % Hk : h / (Hv / Hk);
+}
+
+// D(16x16, f32) += A(16x32) * B(32x16), fp16 operands.
+// Lane l holds A[l % 16][kset(l / 16)], B[kset(l / 16)][l % 16] (8 k values each, in the
+// same order for A and B) and D[4 * (l / 16) + r][l % 16], r = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16, f32) += A(16x16) * B(16x16), fp16 operands; lane l holds 4 k values
+// k = 4 * (l / 16) + e of row / column l % 16, and D as above.
+__device__ __forceinline__ f32x4 mfma16x16x16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 cat(f16x4 lo, f16x4 hi) {
+    return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
+    return f16x4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+}
+
+}  // namespace gdn

@@ -1,0 +1,44 @@
+// Internal launch interface between the C ABI (gdn_abi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Arguments of one prefill launch, already validated by the ABI layer.
+struct PrefillParams {
+    const void *q;             // [B][Hk][T][D] bf16 or f32
+    const void *k;             // [B][Hk][T][D]
+    const void *v;             // [B][Hv][T][D]
+    const float *g;            // [B][Hv][T]
+    const float *beta;         // [B][Hv][T]
+    const float *init_state;   // [B][Hv][D][D] or nullptr (zero state)
+    float *o;                  // [B][Hv][T][D]
+    float *final_state;        // [B][Hv][D][D] or nullptr
+    int32_t B, T, Hk, Hv, D;
+    int32_t head_map;          // 0 tiled (h % Hk), 1 grouped (h / (Hv/Hk))
+    float scale;
+};
+
+struct DecodeParams {
+    const void *q;             // [B][Hk][D]
+    const void *k;             // [B][Hk][D]
+    const void *v;             // [B][Hv][D]
+    const float *g;            // [B][Hv]
+    const float *beta;         // [B][Hv]
+    float *state;              // [B][Hv][D][D], in place
+    float *o;                  // [B][Hv][D]
+    int32_t B, Hk, Hv, D;
+    int32_t head_map;
+    float scale;
+};
+
+// bf16 q/k/v, D = 128, chunk in {16, 32, 64}: fused chunked WY kernel on fp16 MFMA.
+hipError_t launch_prefill_mfma(const PrefillParams &p, int chunk, hipStream_t stream);
+// f32 q/k/v, D in {16, 32, 64, 128}, chunk in {16, 32, 64}: fp32 VALU chunked kernel.
+hipError_t launch_prefill_f32(const PrefillParams &p, int chunk, hipStream_t stream);
+// one decode step, D in {32, 64, 128}; bf16 selects bf16 q/k/v, else f32.
+hipError_t launch_decode(const DecodeParams &p, bool bf16, hipStream_t stream);
+
+}  // namespace gdn

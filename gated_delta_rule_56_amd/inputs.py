@@ -101,11 +101,18 @@ WORKLOADS = {
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (round-to-nearest-even); returns uint16 bit patterns."""
-    f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    """Round finite float32 values to bfloat16 (round-to-nearest-even); returns uint16 bit patterns."""
+    f = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    out = np.empty(f.shape, dtype=np.uint16)
+    step = 1 << 22
+    for s in range(0, f.size, step):
+        u = f[s:s + step].view(np.uint32).copy()
+        lsb = (u >> 16) & 1
+        u += 0x7FFF  # finite inputs cannot carry out of 32 bits
+        u += lsb
+        u >>= 16
+        out[s:s + step] = u
+    return out.reshape(np.shape(x))
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -114,7 +121,10 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def _l2_normalise(x: np.ndarray) -> np.ndarray:
-    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + QK_NORM_EPS)
+    """x / sqrt(sum(x*x) + eps) over the last axis, in place."""
+    norm = np.sqrt(np.einsum("...d,...d->...", x, x) + QK_NORM_EPS)
+    x /= norm[..., None]
+    return x
 
 
 def _softplus(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,144 @@
+/*
+ * gdn.h -- C ABI of the gated delta rule (GatedDeltaNet) scan for AMD MI355X (gfx950).
+ *
+ * The operation (one independent recurrence per sequence b and value head h):
+ *
+ *     S_t = exp(g_t) * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t (scale * q_t)
+ *
+ * with the state S a dv x dk matrix (row = value dimension, column = key
+ * dimension). Sources on the pages:
+ *   - state orientation, the one-step update and the output taken from the
+ *     updated state: tinygrad compare page "27b 935/47", the gated-delta
+ *     decode and prefill reference tests (test_llm_quant_cpu.py), where the
+ *     state is contracted with k and q over its last index and the core output
+ *     equals alpha*S*q + delta*(k.q) with delta = (v - alpha*S*k)*beta;
+ *   - prefill from a given state returning (outputs, next state), and a
+ *     one-token step as the decode call: the same tests' gated_delta_prefill
+ *     and gated_delta_decode signatures, and the commit log of page
+ *     "mergable fast RDNA3 Qwen 3.6" (a 1-token chunk is a decode step);
+ *   - padded steps with beta = 0 and g = 0 (alpha = exp(0) = 1) are exact
+ *     no-ops: commit log of page "mergable fast RDNA3 Qwen 3.6",
+ *     symbolic-length prefill entry;
+ *   - key heads shared by value heads: the gdn_qkv test on page "27b 935/47"
+ *     repeats (tiles) the key heads over the value heads (GDN_HEADS_TILED).
+ * The decay is passed as g (log-decay); the library forms alpha = exp(g).
+ * Callers pass q and k already L2-normalised and q without the scale.
+ *
+ * Memory: every tensor pointer is a DEVICE pointer to memory the caller owns
+ * (the library allocates nothing and keeps no state besides a thread-local
+ * error string). Tensors are dense, row-major, in the layouts given per call.
+ * q, k, v, o and the states must be 16-byte aligned; g and beta 4-byte aligned.
+ *
+ * Errors: arguments are validated synchronously on the host before anything
+ * is enqueued; on a non-OK status nothing was launched and gdn_last_error()
+ * describes the problem. Work is enqueued asynchronously on `stream` (a
+ * hipStream_t passed as void*; NULL = the null stream) and the caller
+ * synchronises. No C++ exception crosses this interface. Non-finite data is
+ * not detected: it propagates into the outputs.
+ *
+ * Precision: g, beta, the states and o are float32. q/k/v are float32 or
+ * bfloat16. The bfloat16 path runs its matrix products on fp16 MFMA operands
+ * with fp32 accumulation (bfloat16 inputs convert exactly while their
+ * magnitudes stay within fp16 range, about 6e-5 .. 6.5e4); the float32 path
+ * computes in fp32 throughout. Results depend on the chunk length through the
+ * order of reductions, so different chunk lengths agree within rounding, not
+ * bit for bit.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* malformed shape, NULL or misaligned pointer, overlapping output */
+    GDN_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported set below */
+    GDN_ERR_HIP = 3          /* the HIP runtime refused a launch; see gdn_last_error() */
+} gdn_status;
+
+typedef enum {
+    GDN_DTYPE_F32 = 0,  /* q, k, v are float32 */
+    GDN_DTYPE_BF16 = 1  /* q, k, v are bfloat16 */
+} gdn_dtype;
+
+typedef enum {
+    GDN_HEADS_TILED = 0,   /* value head h reads key head h % Hk (the pages' repeat of key heads) */
+    GDN_HEADS_GROUPED = 1  /* value head h reads key head h / (Hv / Hk) */
+} gdn_head_map;
+
+typedef struct {
+    int32_t batch;        /* B >= 1 */
+    int32_t seq_len;      /* T: prefill T >= 0 (need not be a multiple of chunk); decode: must be 1 */
+    int32_t num_k_heads;  /* Hk >= 1 */
+    int32_t num_v_heads;  /* Hv >= 1, a multiple of Hk */
+    int32_t head_dim_k;   /* dk */
+    int32_t head_dim_v;   /* dv */
+    int32_t chunk;        /* prefill chunk length C in {16, 32, 64}; ignored by decode */
+    gdn_dtype qkv_dtype;  /* element type of q, k, v */
+    gdn_head_map head_map;
+    float scale;          /* o_t = S_t (scale * q_t); must be finite */
+} gdn_shape;
+
+/*
+ * Supported set (GDN_ERR_UNSUPPORTED otherwise):
+ *   bfloat16: dk = dv = 128; C in {16, 32, 64}.
+ *   float32:  dk = dv in {16, 32, 64, 128}; C in {16, 32, 64}.
+ *   decode:   dk = dv in {32, 64, 128}, either dtype.
+ */
+
+/* Bytes of scratch memory gdn_prefill needs for this shape (0: pass NULL, 0). */
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
+
+/*
+ * Chunked prefill of T tokens from a given state; writes every output and the
+ * final state.
+ *   q, k           [B][Hk][T][dk]   qkv_dtype
+ *   v              [B][Hv][T][dv]   qkv_dtype
+ *   g, beta        [B][Hv][T]       float32 (log-decay and write strength)
+ *   initial_state  [B][Hv][dv][dk]  float32, or NULL for a zero state
+ *   o              [B][Hv][T][dv]   float32, output; must not overlap any input
+ *   final_state    [B][Hv][dv][dk]  float32, output, or NULL to skip; may be
+ *                                   the same pointer as initial_state (in place)
+ *   workspace      device scratch of gdn_prefill_workspace_bytes(shape) bytes
+ * A ragged batch passes every sequence padded to the common T with beta = 0,
+ * g = 0 (and zero q/k/v) on the padded steps, which leave the state unchanged.
+ */
+gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, const float *initial_state,
+                       float *o, float *final_state, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * One decode step for a batch of single tokens (shape->seq_len must be 1);
+ * updates the state in place and writes the output of the updated state.
+ *   q, k     [B][Hk][dk]       qkv_dtype
+ *   v        [B][Hv][dv]       qkv_dtype
+ *   g, beta  [B][Hv]           float32
+ *   state    [B][Hv][dv][dk]   float32, read and overwritten
+ *   o        [B][Hv][dv]       float32, output; must not overlap any input or the state
+ */
+gdn_status gdn_decode(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                      const float *g, const float *beta, float *state, float *o, void *stream);
+
+/* Static text for a status code. */
+const char *gdn_status_string(gdn_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,41 @@
+"""Helpers of the GPU parity tests: move seeded inputs to the device and compare."""
+from __future__ import annotations
+
+import numpy as np
+
+# Parity bars: max|got - ref| / max|ref| over all elements of a case.
+TOL_BF16 = 2e-3
+TOL_F32 = 1e-4
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    ref = np.asarray(ref, dtype=np.float64)
+    denom = float(np.max(np.abs(ref))) if ref.size else 0.0
+    if ref.size == 0:
+        return 0.0
+    err = float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref)))
+    return err / denom if denom > 0 else err
+
+
+def dev(arr: np.ndarray, torch_dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if torch_dtype is not None:
+        t = t.to(torch_dtype)
+    return t.cuda()
+
+
+def bf16_dev(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def qkv_dev(x):
+    """q, k, v of a ScanInputs as device tensors of its dtype (bf16 from the exact bits)."""
+    if x.qkv_dtype == "bf16":
+        return bf16_dev(x.q_bits), bf16_dev(x.k_bits), bf16_dev(x.v_bits)
+    return dev(x.q), dev(x.k), dev(x.v)
+
+
+def tol_for(x) -> float:
+    return TOL_BF16 if x.qkv_dtype == "bf16" else TOL_F32

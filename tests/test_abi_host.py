@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI (CPU only: no call here reaches a kernel launch).
+
+Every call below fails validation, which is pure host code that runs before
+anything touches the GPU, so fake device addresses are safe to pass.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_56_amd import binding
+    return binding.load_library()
+
+
+@pytest.fixture(scope="module")
+def bnd():
+    from gated_delta_rule_56_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib, bnd):
+    names = declared_functions()
+    assert names == sorted(bnd.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), f"libgdn.so does not export {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_status_string(0) == b"ok"
+    assert lib.gdn_status_string(1) == b"invalid argument"
+    assert lib.gdn_status_string(2) == b"unsupported configuration"
+    assert lib.gdn_status_string(3) == b"HIP runtime error"
+
+
+def _shape(bnd, **kw):
+    base = dict(batch=1, seq_len=64, num_k_heads=2, num_v_heads=4, head_dim=128, chunk=64,
+                qkv_dtype=bnd.GDN_DTYPE_BF16, head_map=0, scale=0.088)
+    base.update(kw)
+    return bnd.make_shape(**base)
+
+
+# Fake, well-aligned, non-overlapping device addresses (never dereferenced).
+GB = 1 << 30
+ADDR = dict(q=1 * GB, k=2 * GB, v=3 * GB, g=4 * GB, beta=5 * GB, s0=6 * GB, o=7 * GB, sf=8 * GB)
+
+
+def _prefill(lib, shape, **over):
+    a = dict(ADDR)
+    a.update(over)
+    return lib.gdn_prefill(ctypes.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
+                           a["o"], a["sf"], None, 0, None)
+
+
+def _decode(lib, shape, **over):
+    a = dict(ADDR)
+    a.update(over)
+    return lib.gdn_decode(ctypes.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
+                          a["o"], None)
+
+
+def _err(lib):
+    return lib.gdn_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,status,needle", [
+    ("batch", 0, 1, "batch"),
+    ("num_k_heads", 0, 1, "head counts"),
+    ("num_v_heads", 3, 1, "multiple"),
+    ("seq_len", -1, 1, "seq_len"),
+    ("chunk", 48, 2, "chunk"),
+    ("head_dim", 96, 2, "head_dim"),
+    ("qkv_dtype", 7, 1, "qkv_dtype"),
+    ("head_map", 2, 1, "head_map"),
+    ("scale", float("nan"), 1, "scale"),
+    ("scale", float("inf"), 1, "scale"),
+])
+def test_prefill_rejects_bad_shapes(lib, bnd, field, value, status, needle):
+    shape = _shape(bnd, **{field: value})
+    assert _prefill(lib, shape) == status
+    assert needle in _err(lib)
+
+
+def test_prefill_rejects_null_shape(lib):
+    assert lib.gdn_prefill(None, 1, 2, 3, 4, 5, 6, 7, 8, None, 0, None) == 1
+    assert "shape" in _err(lib)
+
+
+def test_prefill_f32_head_dims(lib, bnd):
+    shape = _shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32, head_dim=48)
+    assert _prefill(lib, shape) == 2
+    shape = _shape(bnd, qkv_dtype=bnd.GDN_DTYPE_BF16, head_dim=64)
+    assert _prefill(lib, shape) == 2 and "bfloat16" in _err(lib)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "o"])
+def test_prefill_rejects_null_pointers(lib, bnd, name):
+    assert _prefill(lib, _shape(bnd), **{name: None}) == 1
+    assert f"{name} is NULL" in _err(lib)
+
+
+@pytest.mark.parametrize("name,addr", [("q", 8), ("o", 4), ("s0", 2), ("sf", 12), ("g", 2)])
+def test_prefill_rejects_misaligned_pointers(lib, bnd, name, addr):
+    assert _prefill(lib, _shape(bnd), **{name: ADDR[name] + addr}) == 1
+    assert "aligned" in _err(lib)
+
+
+def test_prefill_rejects_overlaps(lib, bnd):
+    shape = _shape(bnd)
+    assert _prefill(lib, shape, o=ADDR["v"] + 256) == 1 and "o overlaps v" in _err(lib)
+    assert _prefill(lib, shape, sf=ADDR["q"]) == 1 and "final_state overlaps q" in _err(lib)
+    assert _prefill(lib, shape, sf=ADDR["o"] + 1024) == 1 and "final_state overlaps o" in _err(lib)
+    assert _prefill(lib, shape, sf=ADDR["s0"] + 4096) == 1 and "partially overlaps" in _err(lib)
+
+
+def test_decode_rejects(lib, bnd):
+    assert _decode(lib, _shape(bnd, seq_len=4)) == 1 and "seq_len" in _err(lib)
+    assert _decode(lib, _shape(bnd, seq_len=1, head_dim=16)) == 2
+    assert _decode(lib, _shape(bnd, seq_len=1), s0=None) == 1 and "state is NULL" in _err(lib)
+    assert _decode(lib, _shape(bnd, seq_len=1), o=ADDR["s0"] + 512) == 1 and "overlaps" in _err(lib)
+    assert _decode(lib, _shape(bnd, seq_len=1), s0=ADDR["k"]) == 1 and "state overlaps k" in _err(lib)
+
+
+def test_workspace_query(lib, bnd):
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd))) == 0
+
+
+def test_binding_rejects_cpu_tensors(bnd):
+    import torch
+    q = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        bnd.prefill(q, q, q, torch.zeros(1, 1, 4), torch.zeros(1, 1, 4))
