@@ -1,0 +1,249 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+One step = one gdn_prefill over the long-prefill workload (B=1, Hk=16, Hv=32,
+T=32768, d=128, bf16 q/k/v, chunk 64) followed by one gdn_decode step over the
+batched-decode workload (B=256, Hk=16, Hv=32, d=128, 537 MB fp32 state updated
+in place). Inputs are seeded synthetic data of exactly those shapes, resident in
+HBM before timing starts. Prints one JSON line; ``value`` is prefill tokens/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (a plain 1 GiB device copy, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 matrix peak
+PREFILL_WL = "long_prefill_32k"
+DECODE_WL = "batched_decode"
+
+
+def prefill_flops_per_token_head(C: int, d: int) -> float:
+    """Algorithmic FLOPs of the chunked WY form per (token, value head):
+    10*C*d (five C x C x d products per chunk) + 6*d^2 (three C x d x d products
+    per chunk) + 2*C^2/3 (the triangular solve)."""
+    return 10.0 * C * d + 6.0 * d * d + 2.0 * C * C / 3.0
+
+
+def prefill_bytes(B, T, Hk, Hv, d, qkv_bytes=2, init_state=False) -> int:
+    """Minimum HBM bytes of one prefill launch: q, k, v read once, g, beta read,
+    o written in fp32, final state written (and the initial state read if given)."""
+    qk = 2 * B * Hk * T * d * qkv_bytes
+    v = B * Hv * T * d * qkv_bytes
+    gb = 2 * B * Hv * T * 4
+    o = B * Hv * T * d * 4
+    st = B * Hv * d * d * 4 * (2 if init_state else 1)
+    return qk + v + gb + o + st
+
+
+def decode_bytes(B, Hk, Hv, d, qkv_bytes=2) -> int:
+    """Minimum HBM bytes of one decode step: the fp32 state read and written,
+    q, k, v, g, beta read, o written."""
+    return 2 * B * Hv * d * d * 4 + 2 * B * Hk * d * qkv_bytes + B * Hv * d * qkv_bytes + 2 * B * Hv * 4 \
+        + B * Hv * d * 4
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # 2^28 floats = 1 GiB read + 1 GiB written
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.add(x, 0.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 3}}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(every (sequence, head) chain is independent, so more GPUs would each run this same "
+              "single-GPU kernel on their own share)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    from gated_delta_rule_56_amd import binding, inputs
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t_gen = time.time()
+    pw = inputs.WORKLOADS[PREFILL_WL]
+    px = inputs.generate_workload(pw)
+    dw = inputs.WORKLOADS[DECODE_WL]
+    dx = inputs.generate_workload(dw)
+    t_gen = time.time() - t_gen
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- device-resident inputs
+    pq, pk, pv = bf(px.q_bits), bf(px.k_bits), bf(px.v_bits)
+    pg, pb = torch.from_numpy(px.g).to(dev), torch.from_numpy(px.beta).to(dev)
+    B, Hk, T, d = px.q.shape
+    Hv = px.v.shape[1]
+    po = torch.empty((B, Hv, T, d), dtype=torch.float32, device=dev)
+    psf = torch.empty((B, Hv, d, d), dtype=torch.float32, device=dev)
+    dq, dk, dv = bf(dx.q_bits), bf(dx.k_bits), bf(dx.v_bits)        # [steps][B][H][d]
+    dg, db = torch.from_numpy(dx.g).to(dev), torch.from_numpy(dx.beta).to(dev)
+    state = torch.from_numpy(dx.s0).to(dev)
+    dB, dHk, dHv, dd = dw.batch, dw.num_k_heads, dw.num_v_heads, dw.head_dim
+    do = torch.empty((dB, dHv, dd), dtype=torch.float32, device=dev)
+    nsteps_dec = dw.decode_steps
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        binding.prefill(pq, pk, pv, pg, pb, None, chunk=pw.chunk, scale=px.scale, o=po, final_state=psf)
+        if ev is not None:
+            ev[1].record(stream)
+        s = i % nsteps_dec
+        binding.decode(dq[s], dk[s], dv[s], dg[s], db[s], state, scale=dx.scale, o=do)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if not (torch.isfinite(po).all() and torch.isfinite(state).all()):
+        raise RuntimeError("non-finite outputs after warm-up")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prefill_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    ms_per_step = wall * 1e3 / args.steps
+    p_avg, d_avg = float(prefill_ms.mean()), float(decode_ms.mean())
+
+    tokens = B * T
+    value = tokens / (p_avg * 1e-3)
+    flops = prefill_flops_per_token_head(pw.chunk, d) * tokens * Hv
+    p_bytes = prefill_bytes(B, T, Hk, Hv, d)
+    d_bytes = decode_bytes(dB, dHk, dHv, dd)
+    p_gbps = p_bytes / (p_avg * 1e-3) / 1e9
+    d_gbps = d_bytes / (d_avg * 1e-3) / 1e9
+    p_tflops = flops / (p_avg * 1e-3) / 1e12
+
+    result = {
+        "metric": "GDN prefill tokens/s (Hv=32,d=128,T=32k) + MFMA util; decode HBM GB/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workloads)",
+        "config": {
+            "workload": f"{PREFILL_WL} prefill (B={B}, Hk={Hk}, Hv={Hv}, T={T}, d={d}, chunk={pw.chunk}) + "
+                        f"{DECODE_WL} step (B={dB}, Hk={dHk}, Hv={dHv}, d={dd}, fp32 state in place)",
+            "prefill": {"batch": B, "seq_len": T, "num_k_heads": Hk, "num_v_heads": Hv, "head_dim": d,
+                        "chunk": pw.chunk, "qkv_dtype": "bf16", "o_dtype": "f32"},
+            "decode": {"batch": dB, "num_k_heads": dHk, "num_v_heads": dHv, "head_dim": dd,
+                       "state_bytes": dB * dHv * dd * dd * 4},
+        },
+        "roofline": {
+            "kernel": "gdn_prefill_mfma_kernel<64>",
+            "bound": "hbm",
+            "achieved": p_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": p_gbps / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": p_bytes,
+            "avg_launch_ms": p_avg,
+        },
+        "mfma": {
+            "achieved": p_tflops,
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": p_tflops / MFMA_PEAK_TFLOPS,
+            "algorithmic_flops_per_launch": flops,
+        },
+        "decode": {
+            "kernel": "gdn_decode_kernel<128, bf16>",
+            "avg_launch_ms": d_avg,
+            "achieved": d_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": d_gbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": d_bytes,
+            "sequence_updates_per_s": dB / (d_avg * 1e-3),
+            "head_state_updates_per_s": dB * dHv / (d_avg * 1e-3),
+        },
+        "input_generation_s": t_gen,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(px, dx)
+    print(json.dumps(result))
+
+
+def cpu_baseline(px, dx):
+    """The float64 oracle on the host cores over the same prefill inputs."""
+    import oracle
+    orc = oracle.load()
+    threads = len(os.sched_getaffinity(0))
+    B, Hk, T, d = px.q.shape
+    Hv = px.v.shape[1]
+    # sample: every value head over the first T_s tokens (the oracle is sequential per head)
+    T_s = min(T, 8192)
+    q, k = px.q[:, :, :T_s], px.k[:, :, :T_s]
+    v, g, beta = px.v[:, :, :T_s], px.g[:, :, :T_s], px.beta[:, :, :T_s]
+    t = time.perf_counter()
+    orc.prefill(q, k, v, g, beta, None, scale=px.scale, threads=threads)
+    dt = time.perf_counter() - t
+    # decode: one step of all 8192 (b, h) pairs
+    st = np.ascontiguousarray(dx.s0.astype(np.float64))
+    t = time.perf_counter()
+    orc.decode_step(dx.q[0], dx.k[0], dx.v[0], dx.g[0], dx.beta[0], st, scale=dx.scale, threads=threads)
+    ddt = time.perf_counter() - t
+    return {
+        "value": B * T_s / dt,
+        "unit": "tokens/s",
+        "cores": min(threads, B * Hv),
+        "kind": "oracle",
+        "sample": f"prefill of all {B * Hv} value heads over the first {T_s} of {T} tokens "
+                  f"({dt:.2f} s); float64 sequential recurrence, OpenMP over (b, h) pairs",
+        "host_threads_available": threads,
+        "decode_sequence_updates_per_s": dx.s0.shape[0] / ddt,
+        "decode_sample": f"one step of all {dx.s0.shape[0] * dx.s0.shape[1]} (b, h) pairs ({ddt:.2f} s)",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_abi.cpp", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_prefill_mfma.hip"]
+SOURCES = ["gdn_abi.cpp", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_prefill_mfma.hip",
+           "gdn_prefill_chunk.hip", "gdn_prefill_scan.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

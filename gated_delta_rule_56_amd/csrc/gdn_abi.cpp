@@ -99,16 +99,15 @@ const char *gdn_status_string(gdn_status st) {
 
 const char *gdn_last_error(void) { return g_last_error; }
 
-size_t gdn_prefill_workspace_bytes(const gdn_shape *shape) {
-    (void)shape;
-    return 0;
+size_t gdn_prefill_workspace_bytes(const gdn_shape *s) {
+    if (check_common(s) != GDN_OK || s->seq_len < 0) return 0;
+    if (s->qkv_dtype != GDN_DTYPE_BF16 || (s->chunk != 32 && s->chunk != 64)) return 0;
+    return gdn::prefill_workspace_bytes(s->batch, s->num_v_heads, s->seq_len, s->chunk);
 }
 
 gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
                        const float *beta, const float *initial_state, float *o, float *final_state,
                        void *workspace, size_t workspace_bytes, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     GDN_TRY(check_common(s));
     if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
     if (s->chunk != 16 && s->chunk != 32 && s->chunk != 64)
@@ -166,9 +165,32 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     p.D = d;
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
+    const bool two_pass = bf16 && s->chunk != 16;
+    const size_t ws_need = two_pass ? gdn::prefill_workspace_bytes(B, Hv, T, s->chunk) : 0;
+    if (ws_need > 0) {
+        if (!workspace) return fail(GDN_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
+        if (workspace_bytes < ws_need)
+            return fail(GDN_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed", workspace_bytes, ws_need);
+        if (!aligned(workspace, 16)) return fail(GDN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+        const Range wsr[] = {range("workspace", workspace, (int64_t)ws_need)};
+        GDN_TRY(check_no_overlap(wsr, 1, ins, 6));
+        GDN_TRY(check_no_overlap(wsr, 1, out_o, 1));
+        if (final_state) {
+            const Range fs[] = {range("final_state", final_state, st_bytes)};
+            GDN_TRY(check_no_overlap(wsr, 1, fs, 1));
+        }
+    }
     if (!final_state && T == 0) return GDN_OK;  // nothing to compute or write
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t err = bf16 ? gdn::launch_prefill_mfma(p, s->chunk, st) : gdn::launch_prefill_f32(p, s->chunk, st);
+    hipError_t err = hipSuccess;
+    if (!bf16) {
+        err = gdn::launch_prefill_f32(p, s->chunk, st);
+    } else if (!two_pass) {
+        err = gdn::launch_prefill_mfma(p, s->chunk, st);
+    } else {
+        if (T > 0) err = gdn::launch_chunk_prep(p, s->chunk, workspace, st);
+        if (err == hipSuccess) err = gdn::launch_prefill_scan(p, s->chunk, workspace, st);
+    }
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
     return GDN_OK;
 }

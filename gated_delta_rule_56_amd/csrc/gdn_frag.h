@@ -1,0 +1,26 @@
+// Fragment order shared by the chunk kernel and the state kernel of the bf16
+// prefill path.
+//
+// A 16x16x32 MFMA contracts 32 values of k per step; lane group q = lane / 16
+// holds 8 of them. Any assignment works as long as the A and B operands use the
+// same one. We use, within k block kb (32 consecutive k):
+//   col(kb, q, e) = 32 kb + 16 (e / 4) + 4 q + (e % 4),   e = 0..7
+// because then the two 16x16 result tiles of an MFMA pair (rows 32 kb + 4 q + r
+// and 32 kb + 16 + 4 q + r held by lane group q) are directly the B operand of
+// the next contraction over that dimension, with no data movement.
+// Matrices read as A operands are stored "fragment-permuted": row-major, with
+// the value of column col(kb, q, e) at position 32 kb + 8 q + e, so that each
+// lane fetches its 8 values with one 16-byte load.
+#pragma once
+
+namespace gdn {
+
+// column held by lane group q, element e of k block kb
+__host__ __device__ constexpr int frag_col(int kb, int q, int e) { return 32 * kb + 16 * (e >> 2) + 4 * q + (e & 3); }
+
+// storage position of column c in a fragment-permuted row
+__host__ __device__ constexpr int frag_pos(int c) {
+    return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c & 31) >> 4) + (c & 3);
+}
+
+}  // namespace gdn

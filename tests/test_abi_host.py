@@ -135,7 +135,24 @@ def test_decode_rejects(lib, bnd):
 
 
 def test_workspace_query(lib, bnd):
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd))) == 0
+    # bf16 with chunk 32/64: fp16 T and A_qk per (b, value head, chunk)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd))) == 1 * 4 * 1 * 2 * 64 * 64 * 2
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, seq_len=100, chunk=32))) == 4 * 4 * 2 * 32 * 32 * 2
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, chunk=16))) == 0
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32))) == 0
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, batch=0))) == 0
+
+
+def test_prefill_checks_workspace(lib, bnd):
+    shape = _shape(bnd)
+    need = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
+    a = ADDR
+    call = lambda ws, n: lib.gdn_prefill(ctypes.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
+                                         a["o"], a["sf"], ws, n, None)
+    assert call(None, need) == 1 and "workspace is NULL" in _err(lib)
+    assert call(9 * GB, need - 1) == 1 and "needed" in _err(lib)
+    assert call(9 * GB + 8, need) == 1 and "aligned" in _err(lib)
+    assert call(a["v"], need) == 1 and "workspace overlaps v" in _err(lib)
 
 
 def test_binding_rejects_cpu_tensors(bnd):
