@@ -177,7 +177,7 @@ def main():
                        "state_bytes": dB * dHv * dd * dd * 4},
         },
         "roofline": {
-            "kernel": "gdn_prefill_mfma_kernel<64>",
+            "kernel": "gdn_prefill call: gdn_chunk_prep_kernel<64> + gdn_prefill_scan_kernel<64>",
             "bound": "hbm",
             "achieved": p_gbps,
             "peak": HBM_PEAK_GBPS,
