@@ -102,7 +102,7 @@ const char *gdn_last_error(void) { return g_last_error; }
 size_t gdn_prefill_workspace_bytes(const gdn_shape *s) {
     if (check_common(s) != GDN_OK || s->seq_len < 0) return 0;
     if (s->qkv_dtype != GDN_DTYPE_BF16 || (s->chunk != 32 && s->chunk != 64)) return 0;
-    return gdn::prefill_workspace_bytes(s->batch, s->num_v_heads, s->seq_len, s->chunk);
+    return gdn::prefill_workspace_bytes(s->batch, s->num_k_heads, s->num_v_heads, s->seq_len, s->chunk);
 }
 
 gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
@@ -166,7 +166,7 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
     const bool two_pass = bf16 && s->chunk != 16;
-    const size_t ws_need = two_pass ? gdn::prefill_workspace_bytes(B, Hv, T, s->chunk) : 0;
+    const size_t ws_need = two_pass ? gdn::prefill_workspace_bytes(B, Hk, Hv, T, s->chunk) : 0;
     if (ws_need > 0) {
         if (!workspace) return fail(GDN_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
         if (workspace_bytes < ws_need)

@@ -13,6 +13,9 @@
 // lane fetches its 8 values with one 16-byte load.
 #pragma once
 
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
 namespace gdn {
 
 // column held by lane group q, element e of k block kb
@@ -22,5 +25,22 @@ __host__ __device__ constexpr int frag_col(int kb, int q, int e) { return 32 * k
 __host__ __device__ constexpr int frag_pos(int c) {
     return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c & 31) >> 4) + (c & 3);
 }
+
+// Workspace of the bf16 prefill (offsets in fp16 elements):
+//   pair block  [B * Hv][NC]: T frags (C*C), A_qk frags (C*C), gamma, beta, exp(G_C - G) (3*C float)
+//   key block   [B * Hk][NC]: fp16 k tile (C * 128), row-swizzled
+template <int C>
+struct ChunkWs {
+    static constexpr int64_t kPairElems = 2 * C * C + 3 * C * 2;  // 3*C floats = 6*C halfs
+    static constexpr int64_t kKeyElems = (int64_t)C * 128;
+    int64_t npair_chunks, nkey_chunks, nc;
+    __host__ __device__ ChunkWs(int64_t B, int64_t Hk, int64_t Hv, int64_t NC)
+        : npair_chunks(B * Hv * NC), nkey_chunks(B * Hk * NC), nc(NC) {}
+    __host__ __device__ int64_t pair_chunk(int64_t pair, int64_t c) const { return (pair * nc + c) * kPairElems; }
+    __host__ __device__ int64_t key_chunk(int64_t bk, int64_t c) const {
+        return npair_chunks * kPairElems + (bk * nc + c) * kKeyElems;
+    }
+    __host__ __device__ int64_t bytes() const { return 2 * (npair_chunks * kPairElems + nkey_chunks * kKeyElems); }
+};
 
 }  // namespace gdn

@@ -38,7 +38,7 @@ struct DecodeParams {
 hipError_t launch_prefill_mfma(const PrefillParams &p, int chunk, hipStream_t stream);
 // bf16 q/k/v, D = 128, chunk in {32, 64}: chunk-parallel kernel (T and A_qk per
 // chunk into the workspace), then the sequential state pass reading them.
-size_t prefill_workspace_bytes(int64_t B, int64_t Hv, int64_t T, int chunk);
+size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk);
 hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStream_t stream);
 hipError_t launch_prefill_scan(const PrefillParams &p, int chunk, const void *ws, hipStream_t stream);
 // f32 q/k/v, D in {16, 32, 64, 128}, chunk in {16, 32, 64}: fp32 VALU chunked kernel.

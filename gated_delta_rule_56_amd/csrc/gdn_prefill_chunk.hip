@@ -7,8 +7,15 @@
 //   A     = strict_lower(diag(beta) (K K^T o Gamma))
 //   T     = (I + A)^{-1}                       (unit lower triangular)
 //   A_qk  = lower_incl(scale Q K^T o Gamma)
-// T and A_qk are written as fp16 C x C matrices in fragment-permuted row order
-// (gdn_frag.h) into the workspace: ws[((b * Hv + h) * NC + c) * 2 + {0: T, 1: A_qk}][C][C].
+// Outputs (the workspace, see chunk_ws_layout):
+//   per (b, h, chunk): T and A_qk as fp16 C x C matrices in per-lane MFMA fragment
+//     order (gdn_frag.h), so a lane fetches each operand fragment with one
+//     coalesced 16-byte load; then gamma_t = exp(G_t), beta_t and exp(G_C - G_t)
+//     as float[C] each (zero beta past the sequence end);
+//   per (b, key head, chunk): the k tile in fp16, rows of 16-byte column groups
+//     XOR-swizzled by row (group g of row t at g ^ (t % 16)), ready to be copied
+//     verbatim into LDS by the state-pass kernel. It is written by the first value
+//     head of each key head.
 // The state kernel then needs only T, A_qk and the chunk's q, k, v, g, beta.
 //
 // The inverse follows the forward substitution of the tinygrad helper
@@ -61,6 +68,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(PrefillParams 
     _Float16 *Tm = reinterpret_cast<_Float16 *>(smem + L::kTm);
 
     const int NC = (p.T + C - 1) / C;
+    const ChunkWs<C> wl(p.B, p.Hk, p.Hv, NC);
     const int c = blockIdx.x % NC;
     const int pair = blockIdx.x / NC;
     const int b = pair / p.Hv, h = pair % p.Hv;
@@ -100,8 +108,16 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(PrefillParams 
             if (lane >= m) x += y;
         }
         Gs[lane] = x;
+        const float gc = __shfl(x, C - 1, 64);
+        float *gates = reinterpret_cast<float *>(ws + wl.pair_chunk(pair, c) + 2 * C * C);
+        if (lane < C) {
+            gates[lane] = __expf(x);
+            gates[2 * C + lane] = __expf(gc - x);
+        }
     } else if (w == 1) {
-        Bs[lane] = (lane < n) ? p.beta[(int64_t)pair * p.T + t0 + lane] : 0.0f;
+        const float bt = (lane < n) ? p.beta[(int64_t)pair * p.T + t0 + lane] : 0.0f;
+        Bs[lane] = bt;
+        if (lane < C) reinterpret_cast<float *>(ws + wl.pair_chunk(pair, c) + 2 * C * C)[C + lane] = bt;
     }
     __syncthreads();
 
@@ -200,15 +216,26 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(PrefillParams 
     }
     __syncthreads();
 
-    // write T and A_qk, fragment-permuted: position 32 kb + 8 q + e <- column frag_col(kb, q, e)
-    _Float16 *wt = ws + ((int64_t)pair * NC + c) * 2 * C * C;
-    for (int idx = tid; idx < 2 * C * (C / 8); idx += kThreads) {
-        const int mat = idx / (C * (C / 8));
-        const int rem = idx % (C * (C / 8));
-        const int row = rem / (C / 8), g8 = rem % (C / 8);
-        const int kb = g8 >> 2, q = g8 & 3;
-        const _Float16 *src = (mat == 0 ? Tm : Aqk) + row * CP + 32 * kb + 4 * q;
-        *reinterpret_cast<f16x8 *>(wt + (int64_t)mat * C * C + row * C + 8 * g8) = cat(ld4(src), ld4(src + 16));
+    // write T and A_qk in per-lane fragment order: [mat][m][kb][lane][8], where lane l of
+    // token tile m, k block kb holds row 16 m + l % 16 at columns frag_col(kb, l / 16, 0..7)
+    constexpr int KBC = C / 32;
+    _Float16 *wt = ws + wl.pair_chunk(pair, c);
+    for (int idx = tid; idx < 2 * NT * KBC * 64; idx += kThreads) {
+        const int l = idx & 63;
+        const int f = idx >> 6;            // (mat * NT + m) * KBC + kb
+        const int kb = f % KBC, m = (f / KBC) % NT, mat = f / (KBC * NT);
+        const _Float16 *src = (mat == 0 ? Tm : Aqk) + (16 * m + (l & 15)) * CP + 32 * kb + 4 * (l >> 4);
+        *reinterpret_cast<f16x8 *>(wt + (int64_t)idx * 8) = cat(ld4(src), ld4(src + 16));
+    }
+    // the fp16 k tile, swizzled, once per key head
+    const int ratio = p.Hv / p.Hk;
+    const bool owner = p.head_map == 0 ? (h < p.Hk) : (h % ratio == 0);
+    if (owner) {
+        _Float16 *kw = ws + wl.key_chunk(b * p.Hk + kh, c);
+        for (int idx = tid; idx < C * 16; idx += kThreads) {
+            const int t = idx >> 4, pos = idx & 15, g = pos ^ (t & 15);
+            *reinterpret_cast<f16x8 *>(kw + (int64_t)idx * 8) = ld8(Ks + t * QP + 8 * g);
+        }
     }
 }
 
@@ -226,9 +253,11 @@ hipError_t launch_c(const PrefillParams &p, _Float16 *ws, hipStream_t stream) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int64_t B, int64_t Hv, int64_t T, int chunk) {
+size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
     const int64_t nc = (T + chunk - 1) / chunk;
-    return (size_t)(B * Hv * nc * 2 * chunk * chunk * 2);  // fp16 T and A_qk per chunk
+    if (chunk == 32) return ChunkWs<32>(B, Hk, Hv, nc).bytes();
+    if (chunk == 64) return ChunkWs<64>(B, Hk, Hv, nc).bytes();
+    return 0;
 }
 
 hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStream_t stream) {

@@ -10,16 +10,19 @@
 // beta_t v_t k_t^T, o_t = S_t scale q_t, with U solving (I + A) U = R).
 //
 // Roles inside the workgroup (4 waves, one per SIMD):
-//   wave 0 ("state") owns the 16 x 128 fp32 state block as MFMA accumulators
-//   and runs only the chain S -> X -> R -> U -> S: 38 MFMAs per 64-token
-//   chunk, all operands in registers or one LDS read away.
-//   waves 1-3 ("helpers") stage the next chunk (k in fragment order and
-//   transposed, v transposed, gates) into the other half of a double-buffered
-//   LDS area, and compute the outputs off the critical path: Q S^T of the
-//   current chunk from an fp16 copy of S, and O of the previous chunk from the
-//   fp16 copy of its U.
-// One workgroup barrier per chunk. Matrix operands are fp16 with fp32
-// accumulation; all k contractions use the fragment order of gdn_frag.h.
+//   wave 0, "state": owns the 16 x 128 fp32 state block as MFMA accumulators
+//     and runs only the chain S -> X -> R -> U -> S (38 MFMAs per 64-token
+//     chunk). K^T operands come straight from the row-major k tile through
+//     transposing LDS reads (ds_read_b64_tr_b16).
+//   wave 1, "loader": streams chunk c+2 into a 3-slot LDS ring with direct
+//     global->LDS loads (the fp16 k tile and T fragments and gates prepared by
+//     the chunk kernel, q and v as bf16) and waits for chunk c+1 with an exact
+//     vmcnt; nothing is converted in LDS.
+//   waves 2-3, "output": Y = Q S^T of chunk c from an fp16 copy of S, and
+//     O of chunk c-1 = gamma scale Y + A_qk U from an fp16 copy of U.
+// One workgroup barrier per chunk. The k and q tiles are stored with their 16-byte
+// column groups XOR-swizzled by row (group g of row t at g ^ (t % 16)) so that
+// MFMA fragment reads spread over the LDS banks.
 #include "gdn_device.h"
 #include "gdn_frag.h"
 #include "gdn_internal.h"
@@ -30,31 +33,33 @@ namespace {
 constexpr int kD = 128;
 constexpr int kRows = 16;
 constexpr int kThreads = 256;
-constexpr int kHelpers = 3;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int C>
 struct ScanSmem {
-    static constexpr int NT = C / 16;      // token tiles per chunk
-    static constexpr int KBC = C / 32;     // 32-wide k blocks over the chunk
-    static constexpr int KP = kD + 8;      // fp16 pitch of the fragment-permuted k rows
-    static constexpr int TP = C + 8;       // fp16 pitch of the transposed k rows
-    static constexpr int VP = C + 4;       // f32 pitch of the transposed v block
-    // one stage buffer
-    static constexpr size_t kKf = 0;                          // f16 [C][KP]
-    static constexpr size_t kKt = kKf + 2 * C * KP;           // f16 [128][TP]
-    static constexpr size_t kVt = kKt + 2 * kD * TP;          // f32 [16][VP]
-    static constexpr size_t kGam = kVt + 4 * kRows * VP;      // f32 [64] gamma_t
-    static constexpr size_t kBeta = kGam + 4 * 64;            // f32 [64]
-    static constexpr size_t kEg = kBeta + 4 * 64;             // f32 [64] exp(G_C - G_t)
-    static constexpr size_t kStage = kEg + 4 * 64;
-    // exchange buffers
-    static constexpr size_t kS16 = 2 * kStage;                // f16 [2][4][64][8]
-    static constexpr size_t kU16 = kS16 + 2 * 2 * 4 * 64 * 8;  // f16 [2][KBC][64][8]
-    static constexpr size_t kBytes = kU16 + 2 * 2 * KBC * 64 * 8;
-    static_assert(kKt % 16 == 0 && kVt % 16 == 0 && kGam % 16 == 0 && kStage % 16 == 0, "alignment");
+    static constexpr int NT = C / 16;     // token tiles per chunk
+    static constexpr int KBC = C / 32;    // 32-wide k blocks over the chunk
+    // one ring slot
+    static constexpr size_t sK = 0;                        // [C][128] fp16, swizzled
+    static constexpr size_t sQ = sK + 256 * C;             // [C][128] bf16, swizzled
+    static constexpr size_t sT = sQ + 256 * C;             // T fragments [NT][KBC][64][8] fp16
+    static constexpr size_t sV = sT + 2 * C * C;           // [C][16] bf16
+    static constexpr size_t sGate = sV + 32 * C;           // gamma [C], beta [C], exp(G_C - G) [C] f32
+    static constexpr size_t kSlot = sGate + 12 * C;
+    static constexpr int kDmaPerChunk = C / 4 + C / 4 + NT * KBC + C / 32 + 1;
+    // offsets
+    static constexpr size_t kRing = 0;
+    static constexpr size_t kS16 = 3 * kSlot;              // f16 [2][4][64][8]
+    static constexpr size_t kU16 = kS16 + 2 * 4 * 64 * 16; // f16 [2][KBC][64][8]
+    static constexpr size_t kBytes = kU16 + 2 * KBC * 64 * 16;
+    static_assert(sT % 16 == 0 && sV % 16 == 0 && sGate % 16 == 0 && kSlot % 16 == 0, "alignment");
+    static_assert(kDmaPerChunk <= 63, "vmcnt range");
 };
 
-__device__ __forceinline__ f16x8 ld8(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+__device__ __forceinline__ f16x8 ld8(const unsigned char *p) { return *reinterpret_cast<const f16x8 *>(p); }
+__device__ __forceinline__ f16x4 ld4h(const unsigned char *p) { return *reinterpret_cast<const f16x4 *>(p); }
 
 __device__ __forceinline__ f16x8 pack8(f32x4 lo, f32x4 hi) {
     return f16x8{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
@@ -66,10 +71,42 @@ __device__ __forceinline__ f16x4 bf16x4_to_f16(u16x4 u) {
                  (_Float16)bf16_bits_to_f32(u[2]), (_Float16)bf16_bits_to_f32(u[3])};
 }
 
+// byte offset of the 8-byte run of row t starting at column col (col % 4 == 0) in a swizzled tile
+__device__ __forceinline__ int swz(int t, int col) {
+    return t * 256 + ((((col >> 3) ^ (t & 15)) << 4) | ((col & 4) << 1));
+}
+
+// transposing LDS read: with source lane 4e + a (within 16) pointing at row r0 + e, column c0 + 4a,
+// lane a' receives rows r0 .. r0 + 3 of column c0 + a'
+__device__ __forceinline__ f16x4 ld_tr(const unsigned char *p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(f16x4, v);
+}
+
+__device__ __forceinline__ void dma16(const void *g, unsigned char *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, unsigned char *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS reads and
+// writes, not for its outstanding global loads, so the loader's direct-to-LDS
+// prefetches stay in flight across it (their completion is tracked with exact
+// vmcnt waits by the loader itself before any other wave reads that data).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int C>
 __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParams p, const _Float16 *ws) {
     using L = ScanSmem<C>;
-    constexpr int NT = L::NT, KBC = L::KBC, KP = L::KP, TP = L::TP, VP = L::VP;
+    constexpr int NT = L::NT, KBC = L::KBC;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     // ---- workgroup -> (b, key head, value head, row block); the row blocks and
@@ -91,15 +128,11 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
     const int li = lane & 15, q4 = lane >> 4;
     const int T = p.T;
     const int NC = (T + C - 1) / C;
-    const uint16_t *qg = static_cast<const uint16_t *>(p.q) + ((int64_t)b * p.Hk + kh) * T * kD;
-    const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hk + kh) * T * kD;
-    const uint16_t *vg = static_cast<const uint16_t *>(p.v) + (int64_t)pair * T * kD + kRows * dvb;
-    const float *gg = p.g + (int64_t)pair * T;
-    const float *bg = p.beta + (int64_t)pair * T;
-    const _Float16 *wsp = ws + (int64_t)pair * NC * 2 * C * C;   // [NC][2][C][C]
+    const ChunkWs<C> wl(p.B, p.Hk, p.Hv, NC);
 
-    _Float16 *S16 = reinterpret_cast<_Float16 *>(smem + L::kS16);  // [2][4][64][8]
-    _Float16 *U16 = reinterpret_cast<_Float16 *>(smem + L::kU16);  // [2][KBC][64][8]
+    unsigned char *S16 = smem + L::kS16;  // [2][4][64] x 16 B
+    unsigned char *U16 = smem + L::kU16;  // [2][KBC][64] x 16 B
+    auto slot = [&](int c) { return smem + L::kRing + (c % 3) * L::kSlot; };
 
     if (w == 0) {
         // ================================================================ state wave
@@ -110,72 +143,70 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         for (int jt = 0; jt < 8; ++jt)
             S[jt] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + srow + 16 * jt)
                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-        // T fragments of the current chunk: Tf[m][kb] = T[16 m + li][frag_col(kb, q4, .)]
-        f16x8 Tf[NT][KBC], Tn[NT][KBC];
-        auto load_T = [&](int c, f16x8 (&dst)[NT][KBC]) {
-            const _Float16 *src = wsp + (int64_t)c * 2 * C * C;
-#pragma unroll
-            for (int m = 0; m < NT; ++m)
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    if (kb <= m / 2) dst[m][kb] = ld8(src + (16 * m + li) * C + 32 * kb + 8 * q4);
-        };
         auto write_S16 = [&](int buf) {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
-                *reinterpret_cast<f16x8 *>(S16 + ((buf * 4 + kb) * 64 + lane) * 8) = pack8(S[2 * kb], S[2 * kb + 1]);
+                *reinterpret_cast<f16x8 *>(S16 + ((buf * 4 + kb) * 64 + lane) * 16) = pack8(S[2 * kb], S[2 * kb + 1]);
         };
-        if (NC > 0) load_T(0, Tf);
         write_S16(0);
-        __syncthreads();
+        lds_barrier();
 
         for (int c = 0; c < NC; ++c) {
-            const unsigned char *stage = smem + (c & 1) * L::kStage;
-            const _Float16 *Kf = reinterpret_cast<const _Float16 *>(stage + L::kKf);
-            const _Float16 *Kt = reinterpret_cast<const _Float16 *>(stage + L::kKt);
-            const float *Vt = reinterpret_cast<const float *>(stage + L::kVt);
-            const float *gam = reinterpret_cast<const float *>(stage + L::kGam);
-            const float *bet = reinterpret_cast<const float *>(stage + L::kBeta);
-            const float *eg = reinterpret_cast<const float *>(stage + L::kEg);
-            if (c + 1 < NC) load_T(c + 1, Tn);
+            const unsigned char *sl = slot(c);
+            const unsigned char *kt = sl + L::sK;
+            const uint16_t *vr = reinterpret_cast<const uint16_t *>(sl + L::sV);
+            const float *gam = reinterpret_cast<const float *>(sl + L::sGate);
+            const float *bet = gam + C;
+            const float *eg = gam + 2 * C;
 
-            // operands from the stage buffer
-            f16x8 ka[NT][4];
-#pragma unroll
-            for (int m = 0; m < NT; ++m)
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) ka[m][kb] = ld8(Kf + (16 * m + li) * KP + 32 * kb + 8 * q4);
-            f16x8 kt[8][KBC];
-#pragma unroll
-            for (int jt = 0; jt < 8; ++jt)
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) kt[jt][kb] = ld8(Kt + (16 * jt + li) * TP + 32 * kb + 8 * q4);
-            f32x4 vv[NT], gm[NT], bt[NT], ge[NT];
-#pragma unroll
-            for (int m = 0; m < NT; ++m) {
-                vv[m] = *reinterpret_cast<const f32x4 *>(Vt + li * VP + 16 * m + 4 * q4);
-                gm[m] = *reinterpret_cast<const f32x4 *>(gam + 16 * m + 4 * q4);
-                bt[m] = *reinterpret_cast<const f32x4 *>(bet + 16 * m + 4 * q4);
-                ge[m] = *reinterpret_cast<const f32x4 *>(eg + 16 * m + 4 * q4);
-            }
-            const float gC = gam[C - 1];
-
-            // X = K S^T
+            // X = K S^T; A operand: row 16 m + li, columns frag_col(kb, q4, .) (two 8-byte runs)
             f16x8 sb[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
             f32x4 X[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
+                const int t = 16 * m + li;
                 X[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) X[m] = mfma16x16x32(ka[m][kb], sb[kb], X[m]);
+                for (int kb = 0; kb < 4; ++kb) {
+                    const f16x8 a = cat(ld4h(kt + swz(t, 32 * kb + 4 * q4)), ld4h(kt + swz(t, 32 * kb + 16 + 4 * q4)));
+                    X[m] = mfma16x16x32(a, sb[kb], X[m]);
+                }
             }
-            // R = diag(beta) (V - diag(gamma) X)
+            // K^T fragments for the update: rows frag_col(kb, q4, .) of column 16 jt + li
+            f16x8 ktf[8][KBC];
+            {
+                const int e = li >> 2, a4 = (li & 3) * 4;
+#pragma unroll
+                for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+                    for (int kb = 0; kb < KBC; ++kb) {
+                        const int r0 = 32 * kb + 4 * q4 + e;
+                        ktf[jt][kb] = cat(ld_tr(kt + swz(r0, 16 * jt + a4)), ld_tr(kt + swz(r0 + 16, 16 * jt + a4)));
+                    }
+            }
+            f16x8 Tf[NT][KBC];
+#pragma unroll
+            for (int m = 0; m < NT; ++m)
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb)
+                    if (kb <= m / 2) Tf[m][kb] = ld8(sl + L::sT + ((m * KBC + kb) * 64 + lane) * 16);
+            f32x4 vv[NT], gm[NT], bt[NT], ge[NT];
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vv[m][r] = bf16_bits_to_f32(vr[(16 * m + 4 * q4 + r) * kRows + li]);
+                gm[m] = *reinterpret_cast<const f32x4 *>(gam + 16 * m + 4 * q4);
+                bt[m] = *reinterpret_cast<const f32x4 *>(bet + 16 * m + 4 * q4);
+                ge[m] = *reinterpret_cast<const f32x4 *>(eg + 16 * m + 4 * q4);
+            }
+            const float gC = gam[C - 1];
+
+            // R = diag(beta) (V - diag(gamma) X);  U = T R
             f32x4 R[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) R[m] = bt[m] * (vv[m] - gm[m] * X[m]);
-            // U = T R
             f16x8 rb[KBC];
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) rb[kb] = pack8(R[2 * kb], R[2 * kb + 1]);
@@ -187,10 +218,9 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
                 for (int kb = 0; kb < KBC; ++kb)
                     if (kb <= m / 2) U[m] = mfma16x16x32(Tf[m][kb], rb[kb], U[m]);
             }
-            // hand U (fp16, fragment order) to the helpers for the output
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb)
-                *reinterpret_cast<f16x8 *>(U16 + (((c & 1) * KBC + kb) * 64 + lane) * 8) = pack8(U[2 * kb], U[2 * kb + 1]);
+                *reinterpret_cast<f16x8 *>(U16 + (((c & 1) * KBC + kb) * 64 + lane) * 16) = pack8(U[2 * kb], U[2 * kb + 1]);
             // S <- gamma_C S + K^T (diag(exp(G_C - G)) U)
             f16x8 ub[KBC];
 #pragma unroll
@@ -199,155 +229,91 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             for (int jt = 0; jt < 8; ++jt) {
                 S[jt] *= gC;
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) S[jt] = mfma16x16x32(kt[jt][kb], ub[kb], S[jt]);
+                for (int kb = 0; kb < KBC; ++kb) S[jt] = mfma16x16x32(ktf[jt][kb], ub[kb], S[jt]);
             }
             write_S16((c + 1) & 1);
-            if (c + 1 < NC) {
-#pragma unroll
-                for (int m = 0; m < NT; ++m)
-#pragma unroll
-                    for (int kb = 0; kb < KBC; ++kb) Tf[m][kb] = Tn[m][kb];
-            }
-            __syncthreads();
+            lds_barrier();
         }
         if (p.final_state) {
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) *reinterpret_cast<f32x4 *>(p.final_state + srow + 16 * jt) = S[jt];
         }
-    } else {
-        // ================================================================ helper waves
-        const int hw = w - 1;              // 0..2
-        const int hl = hw * 64 + lane;     // 0..191
-        // token tiles whose outputs this helper computes
-        constexpr int MAXT = (NT + kHelpers - 1) / kHelpers;
-        // staging registers for the next chunk
-        constexpr int KV = (C * 16 + kHelpers * 64 - 1) / (kHelpers * 64);  // k vectors per lane
-        constexpr int VV = (C * 2 + kHelpers * 64 - 1) / (kHelpers * 64);   // v vectors per lane
-        u16x8 kreg[KV], vreg[VV];
-        float greg = 0.f, breg = 0.f;
-        u16x4 qreg[MAXT][4][2];            // q fragments of the next chunk, per tile and k block
-        f16x8 aqk[MAXT][KBC], aqk_n[MAXT][KBC];
-        f32x4 Y[MAXT], gmy[MAXT];
+    } else if (w == 1) {
+        // ================================================================ loader wave
+        const uint16_t *qg = static_cast<const uint16_t *>(p.q) + ((int64_t)b * p.Hk + kh) * T * kD;
+        const uint16_t *vg = static_cast<const uint16_t *>(p.v) + (int64_t)pair * T * kD + kRows * dvb;
+        // issue every direct-to-LDS load of chunk c (exactly L::kDmaPerChunk instructions)
+        auto issue = [&](int c) {
+            unsigned char *sl = slot(c);
+            const int t0 = c * C, last = min(C, T - t0) - 1;
+            const _Float16 *kw = ws + wl.key_chunk((int64_t)b * p.Hk + kh, c);
+            const _Float16 *pw = ws + wl.pair_chunk(pair, c);
+#pragma unroll
+            for (int i = 0; i < C / 4; ++i) {
+                // k: prepared fp16 tile, copied verbatim; q: bf16 rows, swizzled on the way in
+                dma16(kw + (i * 64 + lane) * 8, sl + L::sK + i * 1024);
+                const int pidx = i * 64 + lane, t = pidx >> 4, g = (pidx & 15) ^ (t & 15);
+                dma16(qg + (int64_t)(t0 + min(t, last)) * kD + 8 * g, sl + L::sQ + i * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < NT * KBC; ++i) dma16(pw + (i * 64 + lane) * 8, sl + L::sT + i * 1024);
+#pragma unroll
+            for (int i = 0; i < C / 32; ++i) {
+                const int t = 32 * i + (lane >> 1);
+                dma16(vg + (int64_t)(t0 + min(t, last)) * kD + 8 * (lane & 1), sl + L::sV + i * 1024);
+            }
+            if (lane < 3 * C / 4) dma16(pw + 2 * C * C + lane * 8, sl + L::sGate);
+        };
 
-        auto issue_stage_loads = [&](int c) {
-            const int t0 = c * C, n = min(C, T - t0);
-#pragma unroll
-            for (int i = 0; i < KV; ++i) {
-                const int v = hl + i * kHelpers * 64;
-                const int t = v % C, j0 = 8 * (v / C);
-                kreg[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                if (v < C * 16 && t < n) kreg[i] = *reinterpret_cast<const u16x8 *>(kg + (int64_t)(t0 + t) * kD + j0);
+        if (NC > 0) issue(0);
+        if (NC > 1) {
+            issue(1);
+            wait_vmcnt<L::kDmaPerChunk>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+        for (int c = 0; c < NC; ++c) {
+            if (c + 2 < NC) {
+                issue(c + 2);
+                wait_vmcnt<L::kDmaPerChunk>();
+            } else {
+                wait_vmcnt<0>();
             }
-#pragma unroll
-            for (int i = 0; i < VV; ++i) {
-                const int v = hl + i * kHelpers * 64;
-                const int t = v % C, i0 = 8 * (v / C);
-                vreg[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                if (v < C * 2 && t < n) vreg[i] = *reinterpret_cast<const u16x8 *>(vg + (int64_t)(t0 + t) * kD + i0);
-            }
-            if (hw == 0) {
-                greg = (lane < n) ? gg[t0 + lane] : 0.f;
-                breg = (lane < n) ? bg[t0 + lane] : 0.f;
-            }
-        };
-        auto write_stage = [&](int c) {
-            unsigned char *stage = smem + (c & 1) * L::kStage;
-            _Float16 *Kf = reinterpret_cast<_Float16 *>(stage + L::kKf);
-            _Float16 *Kt = reinterpret_cast<_Float16 *>(stage + L::kKt);
-            float *Vt = reinterpret_cast<float *>(stage + L::kVt);
-#pragma unroll
-            for (int i = 0; i < KV; ++i) {
-                const int v = hl + i * kHelpers * 64;
-                if (v < C * 16) {
-                    const int t = v % C, j0 = 8 * (v / C);
-                    f16x8 kh8;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) kh8[e] = (_Float16)bf16_bits_to_f32(kreg[i][e]);
-                    // fragment-permuted row: columns j0..j0+3 and j0+4..j0+7 are 4-runs
-                    *reinterpret_cast<f16x4 *>(Kf + t * KP + frag_pos(j0)) = f16x4{kh8[0], kh8[1], kh8[2], kh8[3]};
-                    *reinterpret_cast<f16x4 *>(Kf + t * KP + frag_pos(j0 + 4)) = f16x4{kh8[4], kh8[5], kh8[6], kh8[7]};
-                    const int tp = frag_pos(t);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) Kt[(j0 + e) * TP + tp] = kh8[e];
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < VV; ++i) {
-                const int v = hl + i * kHelpers * 64;
-                if (v < C * 2) {
-                    const int t = v % C, i0 = 8 * (v / C);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) Vt[(i0 + e) * VP + t] = bf16_bits_to_f32(vreg[i][e]);
-                }
-            }
-            if (hw == 0) {
-                float x = greg;
-#pragma unroll
-                for (int m = 1; m < 64; m <<= 1) {
-                    const float y = __shfl_up(x, m, 64);
-                    if (lane >= m) x += y;
-                }
-                const float gc = __shfl(x, C - 1, 64);
-                if (lane < C) {
-                    reinterpret_cast<float *>(stage + L::kGam)[lane] = __expf(x);
-                    reinterpret_cast<float *>(stage + L::kBeta)[lane] = breg;
-                    reinterpret_cast<float *>(stage + L::kEg)[lane] = __expf(gc - x);
-                }
-            }
-        };
-        auto load_q = [&](int c) {
-            const int t0 = c * C, n = min(C, T - t0);
-#pragma unroll
-            for (int s = 0; s < MAXT; ++s) {
-                const int m = hw + kHelpers * s;
-                const int t = 16 * m + li;
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        qreg[s][kb][hh] = u16x4{0, 0, 0, 0};
-                        if (m < NT && t < n)
-                            qreg[s][kb][hh] = *reinterpret_cast<const u16x4 *>(
-                                qg + (int64_t)(t0 + t) * kD + 32 * kb + 16 * hh + 4 * q4);
-                    }
-            }
-        };
+            lds_barrier();
+        }
+    } else {
+        // ================================================================ output waves
+        const int ow = w - 2;  // 0, 1: token tiles ow, ow + 2
+        constexpr int MAXT = (NT + 1) / 2;
+        f32x4 Y[MAXT], gmy[MAXT];
+        f16x8 aqk[MAXT][KBC];
         auto load_aqk = [&](int c) {
-            const _Float16 *src = wsp + ((int64_t)c * 2 + 1) * C * C;
+            const _Float16 *src = ws + wl.pair_chunk(pair, c) + C * C;
 #pragma unroll
             for (int s = 0; s < MAXT; ++s) {
-                const int m = hw + kHelpers * s;
+                const int m = ow + 2 * s;
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb)
-                    if (m < NT && kb <= m / 2) aqk_n[s][kb] = ld8(src + (16 * m + li) * C + 32 * kb + 8 * q4);
+                    if (m < NT && kb <= m / 2)
+                        aqk[s][kb] = *reinterpret_cast<const f16x8 *>(src + ((m * KBC + kb) * 64 + lane) * 8);
             }
         };
-
-        if (NC > 0) {
-            issue_stage_loads(0);
-            load_q(0);
-            write_stage(0);
-        }
-        __syncthreads();
-
+        lds_barrier();
         for (int c = 0; c <= NC; ++c) {
-            const bool has_next = c + 1 < NC;
-            if (has_next) issue_stage_loads(c + 1);
-            if (c < NC) load_aqk(c);
-            // O of the previous chunk
             if (c > 0) {
+                // O of the previous chunk
                 const int tp0 = (c - 1) * C, np = min(C, T - tp0);
                 float *og = p.o + ((int64_t)pair * T + tp0) * kD + kRows * dvb + li;
 #pragma unroll
                 for (int s = 0; s < MAXT; ++s) {
-                    const int m = hw + kHelpers * s;
+                    const int m = ow + 2 * s;
                     if (m < NT) {
                         f32x4 acc = gmy[s] * (p.scale * Y[s]);
 #pragma unroll
                         for (int kb = 0; kb < KBC; ++kb)
                             if (kb <= m / 2)
-                                acc = mfma16x16x32(aqk[s][kb],
-                                                   ld8(U16 + ((((c - 1) & 1) * KBC + kb) * 64 + lane) * 8), acc);
+                                acc = mfma16x16x32(aqk[s][kb], ld8(U16 + ((((c - 1) & 1) * KBC + kb) * 64 + lane) * 16), acc);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int t = 16 * m + 4 * q4 + r;
@@ -357,30 +323,31 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
                 }
             }
             if (c < NC) {
+                load_aqk(c);
                 // Y = Q S^T of this chunk, with S the state at the chunk start
-                const float *gam = reinterpret_cast<const float *>(smem + (c & 1) * L::kStage + L::kGam);
+                const unsigned char *qt = slot(c) + L::sQ;
+                const float *gam = reinterpret_cast<const float *>(slot(c) + L::sGate);
                 f16x8 sbf[4];
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) sbf[kb] = ld8(S16 + (((c & 1) * 4 + kb) * 64 + lane) * 8);
+                for (int kb = 0; kb < 4; ++kb) sbf[kb] = ld8(S16 + (((c & 1) * 4 + kb) * 64 + lane) * 16);
 #pragma unroll
                 for (int s = 0; s < MAXT; ++s) {
-                    const int m = hw + kHelpers * s;
+                    const int m = ow + 2 * s;
                     if (m < NT) {
+                        const int t = 16 * m + li;
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int kb = 0; kb < 4; ++kb)
-                            acc = mfma16x16x32(cat(bf16x4_to_f16(qreg[s][kb][0]), bf16x4_to_f16(qreg[s][kb][1])),
-                                               sbf[kb], acc);
+                        for (int kb = 0; kb < 4; ++kb) {
+                            const u16x4 lo = *reinterpret_cast<const u16x4 *>(qt + swz(t, 32 * kb + 4 * q4));
+                            const u16x4 hi = *reinterpret_cast<const u16x4 *>(qt + swz(t, 32 * kb + 16 + 4 * q4));
+                            acc = mfma16x16x32(cat(bf16x4_to_f16(lo), bf16x4_to_f16(hi)), sbf[kb], acc);
+                        }
                         Y[s] = acc;
                         gmy[s] = *reinterpret_cast<const f32x4 *>(gam + 16 * m + 4 * q4);
-#pragma unroll
-                        for (int kb = 0; kb < KBC; ++kb) aqk[s][kb] = aqk_n[s][kb];
                     }
                 }
-                if (has_next) load_q(c + 1);
+                lds_barrier();
             }
-            if (has_next) write_stage(c + 1);
-            if (c < NC) __syncthreads();
         }
     }
 }

@@ -134,10 +134,17 @@ def test_decode_rejects(lib, bnd):
     assert _decode(lib, _shape(bnd, seq_len=1), s0=ADDR["k"]) == 1 and "state overlaps k" in _err(lib)
 
 
+def _ws_bytes(B, Hk, Hv, T, C):
+    """fp16 T and A_qk plus three float gate vectors per (b, value head, chunk),
+    and the fp16 k tile per (b, key head, chunk)."""
+    nc = -(-T // C)
+    return 2 * (B * Hv * nc * (2 * C * C + 6 * C) + B * Hk * nc * C * 128)
+
+
 def test_workspace_query(lib, bnd):
-    # bf16 with chunk 32/64: fp16 T and A_qk per (b, value head, chunk)
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd))) == 1 * 4 * 1 * 2 * 64 * 64 * 2
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, seq_len=100, chunk=32))) == 4 * 4 * 2 * 32 * 32 * 2
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd))) == _ws_bytes(1, 2, 4, 64, 64)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, seq_len=100, chunk=32))) == \
+        _ws_bytes(1, 2, 4, 100, 32)
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, chunk=16))) == 0
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32))) == 0
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, batch=0))) == 0
