@@ -26,6 +26,8 @@ HIPCC_FLAGS = [
     "-mcode-object-version=5",
     # packed fp32 ops stay off on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no accvgpr copies around VALU work)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

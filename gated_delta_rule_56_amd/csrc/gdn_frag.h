@@ -26,13 +26,21 @@ __host__ __device__ constexpr int frag_pos(int c) {
     return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c & 31) >> 4) + (c & 3);
 }
 
+// Row swizzle of the 16-byte column groups of a 256-byte tile row: group G of row t
+// is stored at G ^ ksw(t % 16). ksw is a bijection on 0..15, so the 16 rows read
+// by one MFMA operand fetch land in 16 different bank groups, and
+// ksw(r) = r ^ ((r & 3) << 2) also keeps the transposing fetches of the k tile
+// (4 rows x 4 column runs per 16 lanes) conflict-free.
+__host__ __device__ constexpr int ksw(int r) { return r ^ ((r & 3) << 2); }
+
 // Workspace of the bf16 prefill (offsets in fp16 elements):
 //   pair block  [B * Hv][NC]: T frags (C*C), A_qk frags (C*C), gamma, beta, exp(G_C - G) (3*C float)
-//   key block   [B * Hk][NC]: fp16 k tile (C * 128), row-swizzled
+//   key block   [B * Hk][NC]: fp16 k tile (C * 128; each 32-column block in fragment
+//               order, then row-swizzled), then q in per-lane fragment order (C * 128)
 template <int C>
 struct ChunkWs {
     static constexpr int64_t kPairElems = 2 * C * C + 3 * C * 2;  // 3*C floats = 6*C halfs
-    static constexpr int64_t kKeyElems = (int64_t)C * 128;
+    static constexpr int64_t kKeyElems = 2 * (int64_t)C * 128;
     int64_t npair_chunks, nkey_chunks, nc;
     __host__ __device__ ChunkWs(int64_t B, int64_t Hk, int64_t Hv, int64_t NC)
         : npair_chunks(B * Hv * NC), nkey_chunks(B * Hk * NC), nc(NC) {}

@@ -12,10 +12,10 @@
 //     order (gdn_frag.h), so a lane fetches each operand fragment with one
 //     coalesced 16-byte load; then gamma_t = exp(G_t), beta_t and exp(G_C - G_t)
 //     as float[C] each (zero beta past the sequence end);
-//   per (b, key head, chunk): the k tile in fp16, rows of 16-byte column groups
-//     XOR-swizzled by row (group g of row t at g ^ (t % 16)), ready to be copied
-//     verbatim into LDS by the state-pass kernel. It is written by the first value
-//     head of each key head.
+//   per (b, key head, chunk): the k tile in fp16 (each 32-column block in fragment
+//     order, 16-byte groups swizzled by row, see ksw), ready to be copied verbatim
+//     into LDS by the state-pass kernel, and q in per-lane fragment order. Both are
+//     written by the first value head of each key head.
 // The state kernel then needs only T, A_qk and the chunk's q, k, v, g, beta.
 //
 // The inverse follows the forward substitution of the tinygrad helper
@@ -227,14 +227,23 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_prep_kernel(PrefillParams 
         const _Float16 *src = (mat == 0 ? Tm : Aqk) + (16 * m + (l & 15)) * CP + 32 * kb + 4 * (l >> 4);
         *reinterpret_cast<f16x8 *>(wt + (int64_t)idx * 8) = cat(ld4(src), ld4(src + 16));
     }
-    // the fp16 k tile, swizzled, once per key head
+    // the fp16 k tile and the q fragments, once per key head
     const int ratio = p.Hv / p.Hk;
     const bool owner = p.head_map == 0 ? (h < p.Hk) : (h % ratio == 0);
     if (owner) {
         _Float16 *kw = ws + wl.key_chunk(b * p.Hk + kh, c);
+        // k: group g of row t holds columns frag_col(g / 4, g % 4, 0..7) and sits at g ^ ksw(t % 16)
         for (int idx = tid; idx < C * 16; idx += kThreads) {
-            const int t = idx >> 4, pos = idx & 15, g = pos ^ (t & 15);
-            *reinterpret_cast<f16x8 *>(kw + (int64_t)idx * 8) = ld8(Ks + t * QP + 8 * g);
+            const int t = idx >> 4, g = idx & 15;
+            const _Float16 *src = Ks + t * QP + 32 * (g >> 2) + 4 * (g & 3);
+            *reinterpret_cast<f16x8 *>(kw + ((int64_t)t * 16 + (g ^ ksw(t & 15))) * 8) = cat(ld4(src), ld4(src + 16));
+        }
+        // q: per-lane fragments [m][kb][lane][8] for the A operand of Q S^T
+        _Float16 *qw = kw + C * 128;
+        for (int idx = tid; idx < NT * 4 * 64; idx += kThreads) {
+            const int l = idx & 63, kb = (idx >> 6) & 3, m = idx >> 8;
+            const _Float16 *src = Qs + (16 * m + (l & 15)) * QP + 32 * kb + 4 * (l >> 4);
+            *reinterpret_cast<f16x8 *>(qw + (int64_t)idx * 8) = cat(ld4(src), ld4(src + 16));
         }
     }
 }

@@ -1,9 +1,9 @@
 // Sequential half of the bf16 prefill: the pass over the chunks of one
 // (b, h, block of 16 state rows), with the fp32 state resident in registers.
 //
-// Per chunk c with start state S (rows i of this block), T and A_qk from the
-// chunk kernel (gdn_prefill_chunk.hip):
-//   X = K S^T,  R = diag(beta) (V - diag(gamma) X),  U = T R
+// Per chunk c with start state S (rows i of this block), T, A_qk and the gate
+// vectors from the chunk kernel (gdn_prefill_chunk.hip):
+//   X = K S^T,  R = diag(beta) V - diag(beta gamma) X,  U = T R
 //   S <- gamma_C S + (diag(exp(G_C - G)) U)^T K
 //   O = diag(gamma) (scale Q S^T) + A_qk U
 // (the chunked WY form of S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) +
@@ -11,18 +11,25 @@
 //
 // Roles inside the workgroup (4 waves, one per SIMD):
 //   wave 0, "state": owns the 16 x 128 fp32 state block as MFMA accumulators
-//     and runs only the chain S -> X -> R -> U -> S (38 MFMAs per 64-token
-//     chunk). K^T operands come straight from the row-major k tile through
-//     transposing LDS reads (ds_read_b64_tr_b16).
-//   wave 1, "loader": streams chunk c+2 into a 3-slot LDS ring with direct
-//     global->LDS loads (the fp16 k tile and T fragments and gates prepared by
-//     the chunk kernel, q and v as bf16) and waits for chunk c+1 with an exact
-//     vmcnt; nothing is converted in LDS.
+//     and runs only the chain S -> X -> R -> U -> S: 38 MFMAs and about a
+//     hundred VALU operations per 64-token chunk. K^T operands come straight
+//     from the row-major k tile through transposing LDS reads
+//     (ds_read_b64_tr_b16); every LDS address is a per-lane register plus an
+//     immediate (the chunk loop is unrolled over the ring slots).
+//   wave 1, "loader": streams chunk c+3 into a 4-slot LDS ring with direct
+//     global->LDS loads (the fp16 k tile, T fragments and gate vectors prepared
+//     by the chunk kernel, and the bf16 v rows), waits for chunk c+1 with an
+//     exact vmcnt and forms beta*v (transposed, fp32) and beta*gamma for it.
 //   waves 2-3, "output": Y = Q S^T of chunk c from an fp16 copy of S, and
-//     O of chunk c-1 = gamma scale Y + A_qk U from an fp16 copy of U.
-// One workgroup barrier per chunk. The k and q tiles are stored with their 16-byte
-// column groups XOR-swizzled by row (group g of row t at g ^ (t % 16)) so that
-// MFMA fragment reads spread over the LDS banks.
+//     O of chunk c-1 = gamma scale Y + A_qk U from an fp16 copy of U; their q
+//     and A_qk fragments (prepared by the chunk kernel in per-lane order) are
+//     prefetched two chunks ahead into registers, and o rows past the sequence
+//     end are dropped by a bounded buffer store rather than a branch.
+// One workgroup barrier per chunk. The k tile is stored with its 16-byte column
+// groups XOR-swizzled by row (group g of row t at g ^ (t % 16)) so that MFMA
+// fragment reads spread over the LDS banks.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_frag.h"
 #include "gdn_internal.h"
@@ -33,6 +40,10 @@ namespace {
 constexpr int kD = 128;
 constexpr int kRows = 16;
 constexpr int kThreads = 256;
+constexpr int kSlots = 4;
+// word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format, so that
+// out-of-range accesses (offset >= num_records bytes) are dropped by the hardware
+constexpr int kBufferFlags = 0x00020000;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -41,39 +52,31 @@ template <int C>
 struct ScanSmem {
     static constexpr int NT = C / 16;     // token tiles per chunk
     static constexpr int KBC = C / 32;    // 32-wide k blocks over the chunk
-    // one ring slot
-    static constexpr size_t sK = 0;                        // [C][128] fp16, swizzled
-    static constexpr size_t sQ = sK + 256 * C;             // [C][128] bf16, swizzled
-    static constexpr size_t sT = sQ + 256 * C;             // T fragments [NT][KBC][64][8] fp16
-    static constexpr size_t sV = sT + 2 * C * C;           // [C][16] bf16
-    static constexpr size_t sGate = sV + 32 * C;           // gamma [C], beta [C], exp(G_C - G) [C] f32
-    static constexpr size_t kSlot = sGate + 12 * C;
-    static constexpr int kDmaPerChunk = C / 4 + C / 4 + NT * KBC + C / 32 + 1;
-    // offsets
-    static constexpr size_t kRing = 0;
-    static constexpr size_t kS16 = 3 * kSlot;              // f16 [2][4][64][8]
-    static constexpr size_t kU16 = kS16 + 2 * 4 * 64 * 16; // f16 [2][KBC][64][8]
+    static constexpr int VP = C + 4;      // f32 pitch of the transposed beta*v block
+    // ring, grouped by tensor so that slot offsets are immediates
+    static constexpr size_t rK = 0;                             // [4][C][128] fp16, swizzled
+    static constexpr size_t rT = rK + kSlots * 256 * C;         // [4] T fragments [NT][KBC][64][8] fp16
+    static constexpr size_t rV = rT + kSlots * 2 * C * C;       // [4][C][16] bf16
+    static constexpr size_t rG = rV + kSlots * 32 * C;          // [4] gamma[C], beta[C], exp(G_C - G)[C] f32
+    // loader output, double-buffered
+    static constexpr size_t gBV = rG + kSlots * 12 * C;         // [2][16][VP] f32: beta_t v[t][i]
+    static constexpr size_t gBG = gBV + 2 * 4 * kRows * VP;     // [2][64] f32: beta_t gamma_t
+    // exchange
+    static constexpr size_t kS16 = gBG + 2 * 256;               // [2][4][64] x 16 B
+    static constexpr size_t kU16 = kS16 + 2 * 4 * 64 * 16;      // [2][KBC][64] x 16 B
     static constexpr size_t kBytes = kU16 + 2 * KBC * 64 * 16;
-    static_assert(sT % 16 == 0 && sV % 16 == 0 && sGate % 16 == 0 && kSlot % 16 == 0, "alignment");
-    static_assert(kDmaPerChunk <= 63, "vmcnt range");
+    static constexpr int kDma = C / 4 + NT * KBC + C / 32 + 1;  // DMA instructions per chunk
+    static_assert(rT % 16 == 0 && rV % 16 == 0 && rG % 16 == 0 && gBV % 16 == 0 && kS16 % 16 == 0, "alignment");
+    static_assert(kSlots * 256 * C <= 65536, "k-tile immediates");
+    static_assert(2 * kDma <= 63, "vmcnt range");
 };
 
 __device__ __forceinline__ f16x8 ld8(const unsigned char *p) { return *reinterpret_cast<const f16x8 *>(p); }
-__device__ __forceinline__ f16x4 ld4h(const unsigned char *p) { return *reinterpret_cast<const f16x4 *>(p); }
+__device__ __forceinline__ f32x4 ldf4(const unsigned char *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 __device__ __forceinline__ f16x8 pack8(f32x4 lo, f32x4 hi) {
     return f16x8{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
                  (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
-}
-
-__device__ __forceinline__ f16x4 bf16x4_to_f16(u16x4 u) {
-    return f16x4{(_Float16)bf16_bits_to_f32(u[0]), (_Float16)bf16_bits_to_f32(u[1]),
-                 (_Float16)bf16_bits_to_f32(u[2]), (_Float16)bf16_bits_to_f32(u[3])};
-}
-
-// byte offset of the 8-byte run of row t starting at column col (col % 4 == 0) in a swizzled tile
-__device__ __forceinline__ int swz(int t, int col) {
-    return t * 256 + ((((col >> 3) ^ (t & 15)) << 4) | ((col & 4) << 1));
 }
 
 // transposing LDS read: with source lane 4e + a (within 16) pointing at row r0 + e, column c0 + 4a,
@@ -85,9 +88,6 @@ __device__ __forceinline__ f16x4 ld_tr(const unsigned char *p) {
 
 __device__ __forceinline__ void dma16(const void *g, unsigned char *lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void *g, unsigned char *lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
 }
 
 template <int N>
@@ -103,10 +103,24 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Calls f(IC<c % 4>, c) for c = 0 .. n-1 with a compile-time ring slot.
+template <typename F>
+__device__ __forceinline__ void for_chunks(int n, F &&f) {
+    for (int c0 = 0; c0 < n; c0 += kSlots) {
+        f(IC<0>{}, c0);
+        if (c0 + 1 < n) f(IC<1>{}, c0 + 1);
+        if (c0 + 2 < n) f(IC<2>{}, c0 + 2);
+        if (c0 + 3 < n) f(IC<3>{}, c0 + 3);
+    }
+}
+
 template <int C>
 __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParams p, const _Float16 *ws) {
     using L = ScanSmem<C>;
-    constexpr int NT = L::NT, KBC = L::KBC;
+    constexpr int NT = L::NT, KBC = L::KBC, VP = L::VP;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     // ---- workgroup -> (b, key head, value head, row block); the row blocks and
@@ -130,10 +144,6 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
     const int NC = (T + C - 1) / C;
     const ChunkWs<C> wl(p.B, p.Hk, p.Hv, NC);
 
-    unsigned char *S16 = smem + L::kS16;  // [2][4][64] x 16 B
-    unsigned char *U16 = smem + L::kU16;  // [2][KBC][64] x 16 B
-    auto slot = [&](int c) { return smem + L::kRing + (c % 3) * L::kSlot; };
-
     if (w == 0) {
         // ================================================================ state wave
         // S[jt][r] = state[16 dvb + li][16 jt + 4 q4 + r]
@@ -143,73 +153,79 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         for (int jt = 0; jt < 8; ++jt)
             S[jt] = p.init_state ? *reinterpret_cast<const f32x4 *>(p.init_state + srow + 16 * jt)
                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-        auto write_S16 = [&](int buf) {
+        // fp16 copy of S in fragment order: B operand of X = K S^T, and the helpers' copy
+        f16x8 sb[4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                *reinterpret_cast<f16x8 *>(S16 + ((buf * 4 + kb) * 64 + lane) * 16) = pack8(S[2 * kb], S[2 * kb + 1]);
-        };
-        write_S16(0);
+        for (int kb = 0; kb < 4; ++kb) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+        unsigned char *s16 = smem + L::kS16 + lane * 16;
+        unsigned char *u16 = smem + L::kU16 + lane * 16;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<f16x8 *>(s16 + kb * 1024) = sb[kb];
+
+        // per-lane LDS addresses (slot, tile and block offsets are immediates). In the k tile,
+        // group g of row t holds columns frag_col(g / 4, g % 4, 0..7) at position g ^ ksw(t % 16).
+        // X operand, k block kb: row 16 m + li, group 4 kb + q4 (one 16-byte read)
+        const unsigned char *xa[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) xa[kb] = smem + L::rK + li * 256 + (((4 * kb + q4) ^ ksw(li)) << 4);
+        // K^T operand of the update, column tile jt: source row 4 q4 + (li >> 2) (+32 kb + 16 hh)
+        // holds columns 16 jt + 4 (li & 3) .. +3 in group 4 (jt / 2) + (li & 3), half jt % 2
+        const unsigned char *ta[8];
+        {
+            const int rt = 4 * q4 + (li >> 2);
+#pragma unroll
+            for (int jt = 0; jt < 8; ++jt) {
+                const int g = 4 * (jt >> 1) + (li & 3);
+                ta[jt] = smem + L::rK + rt * 256 + ((g ^ ksw(rt)) << 4) + (jt & 1) * 8;
+            }
+        }
+        const unsigned char *tfa = smem + L::rT + lane * 16;
+        const unsigned char *bva = smem + L::gBV + li * VP * 4 + 16 * q4;
+        const unsigned char *bga = smem + L::gBG + 16 * q4;
+        const unsigned char *ega = smem + L::rG + 8 * C + 16 * q4;
         lds_barrier();
 
-        for (int c = 0; c < NC; ++c) {
-            const unsigned char *sl = slot(c);
-            const unsigned char *kt = sl + L::sK;
-            const uint16_t *vr = reinterpret_cast<const uint16_t *>(sl + L::sV);
-            const float *gam = reinterpret_cast<const float *>(sl + L::sGate);
-            const float *bet = gam + C;
-            const float *eg = gam + 2 * C;
-
-            // X = K S^T; A operand: row 16 m + li, columns frag_col(kb, q4, .) (two 8-byte runs)
-            f16x8 sb[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+        for_chunks(NC, [&](auto sl, int c) {
+            constexpr int s = decltype(sl)::value;
+            constexpr int par = s & 1;
+            // X = K S^T
             f32x4 X[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-                const int t = 16 * m + li;
                 X[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const f16x8 a = cat(ld4h(kt + swz(t, 32 * kb + 4 * q4)), ld4h(kt + swz(t, 32 * kb + 16 + 4 * q4)));
-                    X[m] = mfma16x16x32(a, sb[kb], X[m]);
+                    X[m] = mfma16x16x32(ld8(xa[kb] + s * 256 * C + m * 4096), sb[kb], X[m]);
                 }
             }
-            // K^T fragments for the update: rows frag_col(kb, q4, .) of column 16 jt + li
+            // operands of the rest of the chain
             f16x8 ktf[8][KBC];
-            {
-                const int e = li >> 2, a4 = (li & 3) * 4;
 #pragma unroll
-                for (int jt = 0; jt < 8; ++jt)
+            for (int jt = 0; jt < 8; ++jt)
 #pragma unroll
-                    for (int kb = 0; kb < KBC; ++kb) {
-                        const int r0 = 32 * kb + 4 * q4 + e;
-                        ktf[jt][kb] = cat(ld_tr(kt + swz(r0, 16 * jt + a4)), ld_tr(kt + swz(r0 + 16, 16 * jt + a4)));
-                    }
-            }
+                for (int kb = 0; kb < KBC; ++kb)
+                    ktf[jt][kb] = cat(ld_tr(ta[jt] + s * 256 * C + kb * 8192),
+                                      ld_tr(ta[jt] + s * 256 * C + kb * 8192 + 4096));
             f16x8 Tf[NT][KBC];
 #pragma unroll
             for (int m = 0; m < NT; ++m)
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb)
-                    if (kb <= m / 2) Tf[m][kb] = ld8(sl + L::sT + ((m * KBC + kb) * 64 + lane) * 16);
-            f32x4 vv[NT], gm[NT], bt[NT], ge[NT];
+                    if (kb <= m / 2) Tf[m][kb] = ld8(tfa + s * 2 * C * C + (m * KBC + kb) * 1024);
+            f32x4 bv[NT], bg[NT], ge[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) vv[m][r] = bf16_bits_to_f32(vr[(16 * m + 4 * q4 + r) * kRows + li]);
-                gm[m] = *reinterpret_cast<const f32x4 *>(gam + 16 * m + 4 * q4);
-                bt[m] = *reinterpret_cast<const f32x4 *>(bet + 16 * m + 4 * q4);
-                ge[m] = *reinterpret_cast<const f32x4 *>(eg + 16 * m + 4 * q4);
+                bv[m] = ldf4(bva + par * 4 * kRows * VP + 64 * m);
+                bg[m] = ldf4(bga + par * 256 + 64 * m);
+                ge[m] = ldf4(ega + s * 12 * C + 64 * m);
             }
-            const float gC = gam[C - 1];
+            const float gC = *reinterpret_cast<const float *>(smem + L::rG + s * 12 * C + 4 * (C - 1));
 
-            // R = diag(beta) (V - diag(gamma) X);  U = T R
-            f32x4 R[NT];
-#pragma unroll
-            for (int m = 0; m < NT; ++m) R[m] = bt[m] * (vv[m] - gm[m] * X[m]);
+            // R = beta V - beta gamma X;  U = T R
             f16x8 rb[KBC];
 #pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) rb[kb] = pack8(R[2 * kb], R[2 * kb + 1]);
+            for (int kb = 0; kb < KBC; ++kb)
+                rb[kb] = pack8(bv[2 * kb] - bg[2 * kb] * X[2 * kb], bv[2 * kb + 1] - bg[2 * kb + 1] * X[2 * kb + 1]);
             f32x4 U[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
@@ -220,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             }
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb)
-                *reinterpret_cast<f16x8 *>(U16 + (((c & 1) * KBC + kb) * 64 + lane) * 16) = pack8(U[2 * kb], U[2 * kb + 1]);
+                *reinterpret_cast<f16x8 *>(u16 + (par * KBC + kb) * 1024) = pack8(U[2 * kb], U[2 * kb + 1]);
             // S <- gamma_C S + K^T (diag(exp(G_C - G)) U)
             f16x8 ub[KBC];
 #pragma unroll
@@ -231,123 +247,185 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb) S[jt] = mfma16x16x32(ktf[jt][kb], ub[kb], S[jt]);
             }
-            write_S16((c + 1) & 1);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+                *reinterpret_cast<f16x8 *>(s16 + ((1 - par) * 4 + kb) * 1024) = sb[kb];
+            }
             lds_barrier();
-        }
+        });
         if (p.final_state) {
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) *reinterpret_cast<f32x4 *>(p.final_state + srow + 16 * jt) = S[jt];
         }
     } else if (w == 1) {
         // ================================================================ loader wave
-        const uint16_t *qg = static_cast<const uint16_t *>(p.q) + ((int64_t)b * p.Hk + kh) * T * kD;
         const uint16_t *vg = static_cast<const uint16_t *>(p.v) + (int64_t)pair * T * kD + kRows * dvb;
-        // issue every direct-to-LDS load of chunk c (exactly L::kDmaPerChunk instructions)
+        // every direct-to-LDS load of chunk c (exactly L::kDma instructions)
         auto issue = [&](int c) {
-            unsigned char *sl = slot(c);
+            const int s = c % kSlots;
             const int t0 = c * C, last = min(C, T - t0) - 1;
             const _Float16 *kw = ws + wl.key_chunk((int64_t)b * p.Hk + kh, c);
             const _Float16 *pw = ws + wl.pair_chunk(pair, c);
+            unsigned char *kb_ = smem + L::rK + s * 256 * C;
 #pragma unroll
-            for (int i = 0; i < C / 4; ++i) {
-                // k: prepared fp16 tile, copied verbatim; q: bf16 rows, swizzled on the way in
-                dma16(kw + (i * 64 + lane) * 8, sl + L::sK + i * 1024);
-                const int pidx = i * 64 + lane, t = pidx >> 4, g = (pidx & 15) ^ (t & 15);
-                dma16(qg + (int64_t)(t0 + min(t, last)) * kD + 8 * g, sl + L::sQ + i * 1024);
-            }
+            for (int i = 0; i < C / 4; ++i) dma16(kw + (i * 64 + lane) * 8, kb_ + i * 1024);
+            unsigned char *tb = smem + L::rT + s * 2 * C * C;
 #pragma unroll
-            for (int i = 0; i < NT * KBC; ++i) dma16(pw + (i * 64 + lane) * 8, sl + L::sT + i * 1024);
+            for (int i = 0; i < NT * KBC; ++i) dma16(pw + (i * 64 + lane) * 8, tb + i * 1024);
+            unsigned char *vb = smem + L::rV + s * 32 * C;
 #pragma unroll
             for (int i = 0; i < C / 32; ++i) {
                 const int t = 32 * i + (lane >> 1);
-                dma16(vg + (int64_t)(t0 + min(t, last)) * kD + 8 * (lane & 1), sl + L::sV + i * 1024);
+                dma16(vg + (int64_t)(t0 + min(t, last)) * kD + 8 * (lane & 1), vb + i * 1024);
             }
-            if (lane < 3 * C / 4) dma16(pw + 2 * C * C + lane * 8, sl + L::sGate);
+            if (lane < 3 * C / 4) dma16(pw + 2 * C * C + lane * 8, smem + L::rG + s * 12 * C);
+        };
+        // beta * v (transposed, fp32) and beta * gamma of chunk c, into buffer c & 1
+        auto prepare = [&](int c) {
+            const int s = c % kSlots, par = c & 1;
+            if (lane < C) {
+                const float *gt = reinterpret_cast<const float *>(smem + L::rG + s * 12 * C);
+                const float bt = gt[C + lane];
+                const uint16_t *vr = reinterpret_cast<const uint16_t *>(smem + L::rV + s * 32 * C) + lane * kRows;
+                const u16x8 v0 = *reinterpret_cast<const u16x8 *>(vr);
+                const u16x8 v1 = *reinterpret_cast<const u16x8 *>(vr + 8);
+                float *bv = reinterpret_cast<float *>(smem + L::gBV + par * 4 * kRows * VP) + lane;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bv[e * VP] = bt * bf16_bits_to_f32(v0[e]);
+                    bv[(8 + e) * VP] = bt * bf16_bits_to_f32(v1[e]);
+                }
+                reinterpret_cast<float *>(smem + L::gBG + par * 256)[lane] = bt * gt[lane];
+            }
+        };
+        // wait until chunk c's loads have landed, given how many chunks were issued after it
+        auto wait_for = [&](int c) {
+            const int after = min(NC - 1, c + 2) - c;
+            if (after >= 2) wait_vmcnt<2 * L::kDma>();
+            else if (after == 1) wait_vmcnt<L::kDma>();
+            else wait_vmcnt<0>();
         };
 
-        if (NC > 0) issue(0);
-        if (NC > 1) {
-            issue(1);
-            wait_vmcnt<L::kDmaPerChunk>();
-        } else {
-            wait_vmcnt<0>();
+        for (int c = 0; c < min(NC, 3); ++c) issue(c);
+        if (NC > 0) {
+            wait_for(0);
+            prepare(0);
         }
         lds_barrier();
         for (int c = 0; c < NC; ++c) {
-            if (c + 2 < NC) {
-                issue(c + 2);
-                wait_vmcnt<L::kDmaPerChunk>();
-            } else {
-                wait_vmcnt<0>();
+            if (c + 3 < NC) issue(c + 3);
+            if (c + 1 < NC) {
+                wait_for(c + 1);
+                prepare(c + 1);
             }
             lds_barrier();
         }
     } else {
         // ================================================================ output waves
-        const int ow = w - 2;  // 0, 1: token tiles ow, ow + 2
-        constexpr int MAXT = (NT + 1) / 2;
+        // Wave ow owns token tiles ow and ow + 2 (NT is even). The steady-state loop below is
+        // branch-free: prefetches past the last chunk re-read the last chunk (never used) and o
+        // rows past the sequence end fall outside the store's buffer range, so every trip issues
+        // the same memory operations and the compiler's vmcnt waits stay exact instead of
+        // draining the prefetch queue.
+        static_assert(NT % 2 == 0, "two token tiles per output wave");
+        constexpr int MAXT = NT / 2;
+        const int ow = (w - 2) & 1;
         f32x4 Y[MAXT], gmy[MAXT];
-        f16x8 aqk[MAXT][KBC];
-        auto load_aqk = [&](int c) {
-            const _Float16 *src = ws + wl.pair_chunk(pair, c) + C * C;
+        f16x8 qf[2][MAXT][4];         // q fragments, double-buffered by chunk parity
+        f16x8 aqk[2][MAXT][KBC];      // A_qk fragments, double-buffered by chunk parity
+        const _Float16 *qsrc0 = ws + wl.key_chunk((int64_t)b * p.Hk + kh, 0) + C * kD + lane * 8;
+        const _Float16 *asrc0 = ws + wl.pair_chunk(pair, 0) + C * C + lane * 8;
+        auto load_q = [&](auto parc, int c) {
+            constexpr int par = decltype(parc)::value;
+            const _Float16 *src = qsrc0 + min(c, NC - 1) * ChunkWs<C>::kKeyElems;
 #pragma unroll
-            for (int s = 0; s < MAXT; ++s) {
-                const int m = ow + 2 * s;
+            for (int s2 = 0; s2 < MAXT; ++s2)
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    if (m < NT && kb <= m / 2)
-                        aqk[s][kb] = *reinterpret_cast<const f16x8 *>(src + ((m * KBC + kb) * 64 + lane) * 8);
+                for (int kb = 0; kb < 4; ++kb)
+                    qf[par][s2][kb] = *reinterpret_cast<const f16x8 *>(src + ((ow + 2 * s2) * 4 + kb) * 512);
+        };
+        auto load_aqk = [&](auto parc, int c) {
+            constexpr int par = decltype(parc)::value;
+            const _Float16 *src = asrc0 + min(c, NC - 1) * ChunkWs<C>::kPairElems;
+#pragma unroll
+            for (int s2 = 0; s2 < MAXT; ++s2)
+#pragma unroll
+                for (int kb = 0; kb <= s2 && kb < KBC; ++kb)  // tile m = ow + 2 s2 needs k blocks kb <= m / 2 = s2
+                    aqk[par][s2][kb] = *reinterpret_cast<const f16x8 *>(src + ((ow + 2 * s2) * KBC + kb) * 512);
+        };
+        const unsigned char *s16 = smem + L::kS16 + lane * 16;
+        const unsigned char *u16 = smem + L::kU16 + lane * 16;
+        auto emit_o = [&](auto parc, int c) {  // O of chunk c from buffer parity par = c & 1
+            constexpr int par = decltype(parc)::value;
+            const int tp0 = c * C, np = min(C, T - tp0);
+            // buffer view of this chunk's rows of o: stores past row np fall outside it and are dropped
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                p.o + ((int64_t)pair * T + tp0) * kD, 0, np * kD * 4, kBufferFlags);
+            const int ocol = (4 * q4 * kD + kRows * dvb + li) * 4;
+#pragma unroll
+            for (int s2 = 0; s2 < MAXT; ++s2) {
+                const int m = ow + 2 * s2;
+                f32x4 acc = gmy[s2] * (p.scale * Y[s2]);
+#pragma unroll
+                for (int kb = 0; kb <= s2 && kb < KBC; ++kb)
+                    acc = mfma16x16x32(aqk[par][s2][kb], ld8(u16 + (par * KBC + kb) * 1024), acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // (bit-cast a scalar copy: a bit cast of the vector element itself reads element 0)
+                    const float x = acc[r];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), orsrc,
+                                                         ocol + (16 * m + r) * kD * 4, 0, 0);
+                }
             }
         };
-        lds_barrier();
-        for (int c = 0; c <= NC; ++c) {
-            if (c > 0) {
-                // O of the previous chunk
-                const int tp0 = (c - 1) * C, np = min(C, T - tp0);
-                float *og = p.o + ((int64_t)pair * T + tp0) * kD + kRows * dvb + li;
+        // Y = Q S^T of chunk c with S the state at the chunk start, and gamma of its rows
+        auto chunk_y = [&](auto parc, int c) {
+            constexpr int par = decltype(parc)::value;
+            const float *gam = reinterpret_cast<const float *>(smem + L::rG + (c % kSlots) * 12 * C) + 4 * q4;
+            f16x8 sbf[4];
 #pragma unroll
-                for (int s = 0; s < MAXT; ++s) {
-                    const int m = ow + 2 * s;
-                    if (m < NT) {
-                        f32x4 acc = gmy[s] * (p.scale * Y[s]);
+            for (int kb = 0; kb < 4; ++kb) sbf[kb] = ld8(s16 + (par * 4 + kb) * 1024);
 #pragma unroll
-                        for (int kb = 0; kb < KBC; ++kb)
-                            if (kb <= m / 2)
-                                acc = mfma16x16x32(aqk[s][kb], ld8(U16 + ((((c - 1) & 1) * KBC + kb) * 64 + lane) * 16), acc);
+            for (int s2 = 0; s2 < MAXT; ++s2) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 16 * m + 4 * q4 + r;
-                            if (t < np) og[(int64_t)t * kD] = acc[r];
-                        }
-                    }
-                }
+                for (int kb = 0; kb < 4; ++kb) acc = mfma16x16x32(qf[par][s2][kb], sbf[kb], acc);
+                Y[s2] = acc;
+                gmy[s2] = *reinterpret_cast<const f32x4 *>(gam + 16 * (ow + 2 * s2));
             }
-            if (c < NC) {
-                load_aqk(c);
-                // Y = Q S^T of this chunk, with S the state at the chunk start
-                const unsigned char *qt = slot(c) + L::sQ;
-                const float *gam = reinterpret_cast<const float *>(slot(c) + L::sGate);
-                f16x8 sbf[4];
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) sbf[kb] = ld8(S16 + (((c & 1) * 4 + kb) * 64 + lane) * 16);
-#pragma unroll
-                for (int s = 0; s < MAXT; ++s) {
-                    const int m = ow + 2 * s;
-                    if (m < NT) {
-                        const int t = 16 * m + li;
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kb = 0; kb < 4; ++kb) {
-                            const u16x4 lo = *reinterpret_cast<const u16x4 *>(qt + swz(t, 32 * kb + 4 * q4));
-                            const u16x4 hi = *reinterpret_cast<const u16x4 *>(qt + swz(t, 32 * kb + 16 + 4 * q4));
-                            acc = mfma16x16x32(cat(bf16x4_to_f16(lo), bf16x4_to_f16(hi)), sbf[kb], acc);
-                        }
-                        Y[s] = acc;
-                        gmy[s] = *reinterpret_cast<const f32x4 *>(gam + 16 * m + 4 * q4);
-                    }
-                }
-                lds_barrier();
+        };
+        // interval of chunk c >= 1: O of chunk c - 1, then Y of chunk c; prefetches run two
+        // chunks (q) and one chunk (A_qk) ahead of their use
+        auto interval = [&](auto parc, int c) {
+            constexpr int par = decltype(parc)::value;
+            emit_o(IC<1 - par>{}, c - 1);
+            load_aqk(IC<1 - par>{}, c + 1);
+            chunk_y(IC<par>{}, c);
+            load_q(IC<par>{}, c + 2);
+            lds_barrier();
+        };
+
+        if (NC == 0) {  // empty sequence: nothing to read (the workspace may be empty), one barrier
+            lds_barrier();
+        } else {
+            // same issue order as the steady state: A_qk of c - 1, q of c, A_qk of c, q of c + 1
+            load_q(IC<0>{}, 0);
+            load_aqk(IC<0>{}, 0);
+            load_q(IC<1>{}, 1);
+            lds_barrier();
+            load_aqk(IC<1>{}, 1);
+            chunk_y(IC<0>{}, 0);
+            load_q(IC<0>{}, 2);
+            lds_barrier();
+            int c = 1;
+            for (; c + 1 < NC; c += 2) {
+                interval(IC<1>{}, c);
+                interval(IC<0>{}, c + 1);
             }
+            if (c < NC) interval(IC<1>{}, c);
+            if ((NC - 1) & 1) emit_o(IC<1>{}, NC - 1);
+            else emit_o(IC<0>{}, NC - 1);
         }
     }
 }

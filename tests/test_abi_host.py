@@ -136,9 +136,9 @@ def test_decode_rejects(lib, bnd):
 
 def _ws_bytes(B, Hk, Hv, T, C):
     """fp16 T and A_qk plus three float gate vectors per (b, value head, chunk),
-    and the fp16 k tile per (b, key head, chunk)."""
+    and the fp16 k tile and q fragments per (b, key head, chunk)."""
     nc = -(-T // C)
-    return 2 * (B * Hv * nc * (2 * C * C + 6 * C) + B * Hk * nc * C * 128)
+    return 2 * (B * Hv * nc * (2 * C * C + 6 * C) + B * Hk * nc * C * 256)
 
 
 def test_workspace_query(lib, bnd):
