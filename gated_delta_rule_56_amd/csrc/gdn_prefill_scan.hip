@@ -9,24 +9,36 @@
 // (the chunked WY form of S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) +
 // beta_t v_t k_t^T, o_t = S_t scale q_t, with U solving (I + A) U = R).
 //
-// Roles inside the workgroup (4 waves, one per SIMD):
+// Roles inside the workgroup (6 waves; wave i runs on SIMD i % 4):
 //   wave 0, "state": owns the 16 x 128 fp32 state block as MFMA accumulators
 //     and runs only the chain S -> X -> R -> U -> S: 38 MFMAs and about a
 //     hundred VALU operations per 64-token chunk. K^T operands come straight
 //     from the row-major k tile through transposing LDS reads
 //     (ds_read_b64_tr_b16); every LDS address is a per-lane register plus an
 //     immediate (the chunk loop is unrolled over the ring slots).
-//   wave 1, "loader": streams chunk c+3 into a 4-slot LDS ring with direct
-//     global->LDS loads (the fp16 k tile, T fragments and gate vectors prepared
-//     by the chunk kernel, and the bf16 v rows), waits for chunk c+1 with an
-//     exact vmcnt and forms beta*v (transposed, fp32) and beta*gamma for it.
-//   waves 2-3, "output": Y = Q S^T of chunk c from an fp16 copy of S, and
-//     O of chunk c-1 = gamma scale Y + A_qk U from an fp16 copy of U; their q
-//     and A_qk fragments (prepared by the chunk kernel in per-lane order) are
+//   waves 1 and 5, "loaders": stream chunk c+3 into a 4-slot LDS ring with
+//     direct global->LDS loads and wait for chunk c+1 with an exact vmcnt.
+//     Wave 1 moves the fp16 k tile prepared by the chunk kernel; wave 5 the T
+//     fragments on or below the diagonal, and one chunk further ahead the gate
+//     vectors and the bf16 v rows. Two waves because one wave can keep at most
+//     63 vector loads in flight, which is less than three chunks' worth.
+//   wave 4, "prefetch": requests chunk c+8 into L2. The k, q, T, A_qk, gate
+//     and v lines of a chunk are each read by 8 or 16 workgroups at about the
+//     same time; without it all of them would wait for the same HBM miss. Each
+//     line is touched by exactly one of the workgroups that share it.
+//   waves 2-3, "output": O^T rather than O, so that a lane ends up with four
+//     consecutive o columns of one token and stores them with one 16-byte
+//     store: Y^T = S Q^T of chunk c from an fp16 copy of S, and O^T of chunk
+//     c-1 = scale Y^T diag(gamma) + U^T A_qk^T from an fp16 copy of U (in the
+//     fragment order the fp16 copies are the A operands of these products as
+//     they are, and the q and A_qk fragments the B operands). The q and A_qk
+//     fragments (prepared by the chunk kernel in per-lane order) are
 //     prefetched two chunks ahead into registers, and o rows past the sequence
-//     end are dropped by a bounded buffer store rather than a branch.
+//     end are dropped by a bounded buffer store rather than a branch. They also
+//     form the operands of the next chunk from its v rows and gates: beta*v
+//     (transposed, fp32), beta*gamma, exp(G_C - G) and gamma.
 // One workgroup barrier per chunk. The k tile is stored with its 16-byte column
-// groups XOR-swizzled by row (group g of row t at g ^ (t % 16)) so that MFMA
+// groups XOR-swizzled by row (group g of row t at g ^ ksw(t % 16)) so that MFMA
 // fragment reads spread over the LDS banks.
 #include <type_traits>
 
@@ -39,7 +51,8 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kRows = 16;
-constexpr int kThreads = 256;
+constexpr int kThreads = 384;
+constexpr int kPrefetchAhead = 8;  // chunks
 constexpr int kSlots = 4;
 // word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format, so that
 // out-of-range accesses (offset >= num_records bytes) are dropped by the hardware
@@ -47,6 +60,7 @@ constexpr int kBufferFlags = 0x00020000;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int C>
 struct ScanSmem {
@@ -58,17 +72,20 @@ struct ScanSmem {
     static constexpr size_t rT = rK + kSlots * 256 * C;         // [4] T fragments [NT][KBC][64][8] fp16
     static constexpr size_t rV = rT + kSlots * 2 * C * C;       // [4][C][16] bf16
     static constexpr size_t rG = rV + kSlots * 32 * C;          // [4] gamma[C], beta[C], exp(G_C - G)[C] f32
-    // loader output, double-buffered
+    // per-chunk operands formed from v and the gates, double-buffered by chunk parity
     static constexpr size_t gBV = rG + kSlots * 12 * C;         // [2][16][VP] f32: beta_t v[t][i]
-    static constexpr size_t gBG = gBV + 2 * 4 * kRows * VP;     // [2][64] f32: beta_t gamma_t
+    static constexpr size_t gGT = gBV + 2 * 4 * kRows * VP;     // [2][3][64] f32: beta_t gamma_t, exp(G_C - G_t), gamma_t
     // exchange
-    static constexpr size_t kS16 = gBG + 2 * 256;               // [2][4][64] x 16 B
+    static constexpr size_t kS16 = gGT + 2 * 768;               // [2][4][64] x 16 B
     static constexpr size_t kU16 = kS16 + 2 * 4 * 64 * 16;      // [2][KBC][64] x 16 B
-    static constexpr size_t kBytes = kU16 + 2 * KBC * 64 * 16;
-    static constexpr int kDma = C / 4 + NT * KBC + C / 32 + 1;  // DMA instructions per chunk
+    static constexpr size_t kJunk = kU16 + 2 * KBC * 64 * 16;     // [64] x 4 B: target of the L2 prefetches
+    static constexpr size_t kBytes = kJunk + 256;
+    static constexpr int kDmaK = C / 4;                         // k-tile loads per chunk (wave 1)
+    static constexpr int kTFrags = NT * KBC - (NT / 2) * (KBC - 1);  // T fragments with kb <= m / 2
+    static constexpr int kDmaT = kTFrags + C / 32 + 1;          // T of chunk c, v and gates of c + 1 (wave 5)
     static_assert(rT % 16 == 0 && rV % 16 == 0 && rG % 16 == 0 && gBV % 16 == 0 && kS16 % 16 == 0, "alignment");
     static_assert(kSlots * 256 * C <= 65536, "k-tile immediates");
-    static_assert(2 * kDma <= 63, "vmcnt range");
+    static_assert(2 * kDmaK <= 63 && 2 * kDmaT <= 63, "vmcnt range");
 };
 
 __device__ __forceinline__ f16x8 ld8(const unsigned char *p) { return *reinterpret_cast<const f16x8 *>(p); }
@@ -88,6 +105,10 @@ __device__ __forceinline__ f16x4 ld_tr(const unsigned char *p) {
 
 __device__ __forceinline__ void dma16(const void *g, unsigned char *lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(const void *g, unsigned char *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
 }
 
 template <int N>
@@ -114,6 +135,31 @@ __device__ __forceinline__ void for_chunks(int n, F &&f) {
         if (c0 + 1 < n) f(IC<1>{}, c0 + 1);
         if (c0 + 2 < n) f(IC<2>{}, c0 + 2);
         if (c0 + 3 < n) f(IC<3>{}, c0 + 3);
+    }
+}
+
+// Operands of chunk c formed from its v rows and gate vectors (ring slot c % 4), into the
+// buffers of parity c & 1: beta_t v[t][8 h + e] for e = 0..7 (transposed), and with
+// all = true also beta_t gamma_t, exp(G_C - G_t) and gamma_t. Lane t < C handles token t.
+template <int C>
+__device__ __forceinline__ void prepare_chunk_impl(unsigned char *smem, int c, int h, bool all, int lane) {
+    using L = ScanSmem<C>;
+    constexpr int VP = L::VP;
+    const int s = c % kSlots, par = c & 1;
+    if (lane < C) {
+        const float *gt = reinterpret_cast<const float *>(smem + L::rG + s * 12 * C);
+        const float bt = gt[C + lane];
+        const u16x8 v8 = *reinterpret_cast<const u16x8 *>(smem + L::rV + s * 32 * C + (lane * kRows + 8 * h) * 2);
+        float *bv = reinterpret_cast<float *>(smem + L::gBV + par * 4 * kRows * VP) + 8 * h * VP + lane;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e * VP] = bt * bf16_bits_to_f32(v8[e]);
+        if (all) {
+            float *gg = reinterpret_cast<float *>(smem + L::gGT + par * 768) + lane;
+            const float gam = gt[lane];
+            gg[0] = bt * gam;
+            gg[64] = gt[2 * C + lane];
+            gg[128] = gam;
+        }
     }
 }
 
@@ -181,8 +227,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         }
         const unsigned char *tfa = smem + L::rT + lane * 16;
         const unsigned char *bva = smem + L::gBV + li * VP * 4 + 16 * q4;
-        const unsigned char *bga = smem + L::gBG + 16 * q4;
-        const unsigned char *ega = smem + L::rG + 8 * C + 16 * q4;
+        const unsigned char *bga = smem + L::gGT + 16 * q4;
+        const unsigned char *ega = smem + L::gGT + 256 + 16 * q4;
         lds_barrier();
 
         for_chunks(NC, [&](auto sl, int c) {
@@ -216,10 +262,10 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
                 bv[m] = ldf4(bva + par * 4 * kRows * VP + 64 * m);
-                bg[m] = ldf4(bga + par * 256 + 64 * m);
-                ge[m] = ldf4(ega + s * 12 * C + 64 * m);
+                bg[m] = ldf4(bga + par * 768 + 64 * m);
+                ge[m] = ldf4(ega + par * 768 + 64 * m);
             }
-            const float gC = *reinterpret_cast<const float *>(smem + L::rG + s * 12 * C + 4 * (C - 1));
+            const float gC = *reinterpret_cast<const float *>(smem + L::gGT + par * 768 + 512 + 4 * (C - 1));
 
             // R = beta V - beta gamma X;  U = T R
             f16x8 rb[KBC];
@@ -258,67 +304,118 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) *reinterpret_cast<f32x4 *>(p.final_state + srow + 16 * jt) = S[jt];
         }
-    } else if (w == 1) {
-        // ================================================================ loader wave
+    } else if (w == 4) {
+        // ================================================================ prefetch wave
+        // Lines of chunk c: the key block (k tile and q fragments, 4 C lines) shared by the
+        // 8 * ratio workgroups of this key head; the pair block (T, A_qk, gates) and the v rows
+        // (2 lines per token) shared by the 8 row blocks of this value head. Sharer s touches
+        // lines s, s + S, s + 2 S, ... of each.
+        const int S = 8 * ratio, sk = jj * 8 + dvb;
+        constexpr int kKeyLines = 4 * C;
+        constexpr int kPairLines = (int)((ChunkWs<C>::kPairElems * 2 + 127) / 128);
+        const int nk = (kKeyLines + S - 1) / S;  // key lines per sharer
+        constexpr int np = (kPairLines + 7) / 8, nv = C / 4;
+        const int total = nk + np + nv;
+        const unsigned char *wsb = reinterpret_cast<const unsigned char *>(ws);
+        const unsigned char *vb = static_cast<const unsigned char *>(p.v) + (int64_t)pair * T * kD * 2;
+        unsigned char *junk = smem + L::kJunk;
+        auto touch = [&](int c) {
+            const int n = min(C, T - c * C);
+            for (int l0 = 0; l0 < total; l0 += 64) {
+                const int l = l0 + lane;
+                // lanes with nothing to touch repeat a line of the key block
+                const unsigned char *a = wsb + wl.key_chunk((int64_t)b * p.Hk + kh, c) * 2 + (sk % kKeyLines) * 128;
+                if (l < nk) {
+                    const int line = sk + S * l;
+                    if (line < kKeyLines) a = wsb + wl.key_chunk((int64_t)b * p.Hk + kh, c) * 2 + (int64_t)line * 128;
+                } else if (l < nk + np) {
+                    const int line = dvb + 8 * (l - nk);
+                    if (line < kPairLines) a = wsb + wl.pair_chunk(pair, c) * 2 + (int64_t)line * 128;
+                } else if (l < total) {
+                    const int line = dvb + 8 * (l - nk - np);
+                    a = vb + ((int64_t)c * C + min(line >> 1, n - 1)) * kD * 2 + (line & 1) * 128;
+                }
+                dma4(a, junk);
+            }
+        };
+        for (int c = 3; c < min(NC, kPrefetchAhead); ++c) {
+            touch(c);
+            wait_vmcnt<8>();
+        }
+        lds_barrier();
+        for (int c = 0; c < NC; ++c) {
+            if (c + kPrefetchAhead < NC) touch(c + kPrefetchAhead);
+            wait_vmcnt<8>();
+            lds_barrier();
+        }
+        wait_vmcnt<0>();  // the prefetches write into this workgroup's LDS
+    } else if (w == 1 || w == 5) {
+        // ================================================================ loader waves
+        // Direct-to-LDS loads of chunk c (wave 1: L::kDmaK instructions, wave 5: L::kDmaT)
+        const bool kload = w == 1;
         const uint16_t *vg = static_cast<const uint16_t *>(p.v) + (int64_t)pair * T * kD + kRows * dvb;
-        // every direct-to-LDS load of chunk c (exactly L::kDma instructions)
-        auto issue = [&](int c) {
+        // v rows and gate vectors of chunk c into ring slot c % 4 (C / 32 + 1 instructions)
+        auto issue_vg = [&](int c) {
             const int s = c % kSlots;
             const int t0 = c * C, last = min(C, T - t0) - 1;
-            const _Float16 *kw = ws + wl.key_chunk((int64_t)b * p.Hk + kh, c);
-            const _Float16 *pw = ws + wl.pair_chunk(pair, c);
-            unsigned char *kb_ = smem + L::rK + s * 256 * C;
-#pragma unroll
-            for (int i = 0; i < C / 4; ++i) dma16(kw + (i * 64 + lane) * 8, kb_ + i * 1024);
-            unsigned char *tb = smem + L::rT + s * 2 * C * C;
-#pragma unroll
-            for (int i = 0; i < NT * KBC; ++i) dma16(pw + (i * 64 + lane) * 8, tb + i * 1024);
             unsigned char *vb = smem + L::rV + s * 32 * C;
 #pragma unroll
             for (int i = 0; i < C / 32; ++i) {
                 const int t = 32 * i + (lane >> 1);
                 dma16(vg + (int64_t)(t0 + min(t, last)) * kD + 8 * (lane & 1), vb + i * 1024);
             }
-            if (lane < 3 * C / 4) dma16(pw + 2 * C * C + lane * 8, smem + L::rG + s * 12 * C);
+            if (lane < 3 * C / 4) dma16(ws + wl.pair_chunk(pair, c) + 2 * C * C + lane * 8, smem + L::rG + s * 12 * C);
         };
-        // beta * v (transposed, fp32) and beta * gamma of chunk c, into buffer c & 1
-        auto prepare = [&](int c) {
-            const int s = c % kSlots, par = c & 1;
-            if (lane < C) {
-                const float *gt = reinterpret_cast<const float *>(smem + L::rG + s * 12 * C);
-                const float bt = gt[C + lane];
-                const uint16_t *vr = reinterpret_cast<const uint16_t *>(smem + L::rV + s * 32 * C) + lane * kRows;
-                const u16x8 v0 = *reinterpret_cast<const u16x8 *>(vr);
-                const u16x8 v1 = *reinterpret_cast<const u16x8 *>(vr + 8);
-                float *bv = reinterpret_cast<float *>(smem + L::gBV + par * 4 * kRows * VP) + lane;
+        // load group c: wave 1 the k tile of chunk c; wave 5 the T fragments of chunk c and the
+        // v rows and gates of chunk c + 1 (one chunk earlier, because the output waves form the
+        // beta*v block of chunk c + 1 from them while the state wave works on chunk c)
+        auto issue = [&](int c) {
+            const int s = c % kSlots;
+            if (kload) {
+                const _Float16 *kw = ws + wl.key_chunk((int64_t)b * p.Hk + kh, c);
+                unsigned char *kb_ = smem + L::rK + s * 256 * C;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bv[e * VP] = bt * bf16_bits_to_f32(v0[e]);
-                    bv[(8 + e) * VP] = bt * bf16_bits_to_f32(v1[e]);
-                }
-                reinterpret_cast<float *>(smem + L::gBG + par * 256)[lane] = bt * gt[lane];
+                for (int i = 0; i < C / 4; ++i) dma16(kw + (i * 64 + lane) * 8, kb_ + i * 1024);
+            } else {
+                const _Float16 *pw = ws + wl.pair_chunk(pair, c);
+                unsigned char *tb = smem + L::rT + s * 2 * C * C;
+#pragma unroll
+                for (int m = 0; m < NT; ++m)
+#pragma unroll
+                    for (int kb = 0; kb <= m / 2 && kb < KBC; ++kb)
+                        dma16(pw + ((m * KBC + kb) * 64 + lane) * 8, tb + (m * KBC + kb) * 1024);
+                // past the last chunk the group repeats the last chunk's v and gates, which
+                // keeps the instruction count per group fixed; the slot written is free
+                issue_vg(min(c + 1, NC - 1));
             }
         };
         // wait until chunk c's loads have landed, given how many chunks were issued after it
         auto wait_for = [&](int c) {
             const int after = min(NC - 1, c + 2) - c;
-            if (after >= 2) wait_vmcnt<2 * L::kDma>();
-            else if (after == 1) wait_vmcnt<L::kDma>();
-            else wait_vmcnt<0>();
+            if (kload) {
+                if (after >= 2) wait_vmcnt<2 * L::kDmaK>();
+                else if (after == 1) wait_vmcnt<L::kDmaK>();
+                else wait_vmcnt<0>();
+            } else {
+                if (after >= 2) wait_vmcnt<2 * L::kDmaT>();
+                else if (after == 1) wait_vmcnt<L::kDmaT>();
+                else wait_vmcnt<0>();
+            }
         };
 
+        if (NC > 0 && !kload) issue_vg(0);
         for (int c = 0; c < min(NC, 3); ++c) issue(c);
         if (NC > 0) {
             wait_for(0);
-            prepare(0);
+            if (!kload) {  // chunk 0's operands; the output waves form those of the later chunks
+                prepare_chunk_impl<C>(smem, 0, 0, true, lane);
+                prepare_chunk_impl<C>(smem, 0, 1, false, lane);
+            }
         }
         lds_barrier();
         for (int c = 0; c < NC; ++c) {
             if (c + 3 < NC) issue(c + 3);
-            if (c + 1 < NC) {
-                wait_for(c + 1);
-                prepare(c + 1);
-            }
+            if (c + 1 < NC) wait_for(c + 1);
             lds_barrier();
         }
     } else {
@@ -330,8 +427,9 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         // draining the prefetch queue.
         static_assert(NT % 2 == 0, "two token tiles per output wave");
         constexpr int MAXT = NT / 2;
-        const int ow = (w - 2) & 1;
-        f32x4 Y[MAXT], gmy[MAXT];
+        const int ow = w - 2;  // 0 or 1 (waves 2 and 3)
+        f32x4 Y[MAXT];   // lane (q4, li): Y^T[state row 4 q4 + r][token 16 m + li]
+        float gmy[MAXT];  // gamma of token 16 m + li
         f16x8 qf[2][MAXT][4];         // q fragments, double-buffered by chunk parity
         f16x8 aqk[2][MAXT][KBC];      // A_qk fragments, double-buffered by chunk parity
         const _Float16 *qsrc0 = ws + wl.key_chunk((int64_t)b * p.Hk + kh, 0) + C * kD + lane * 8;
@@ -362,27 +460,22 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             // buffer view of this chunk's rows of o: stores past row np fall outside it and are dropped
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                 p.o + ((int64_t)pair * T + tp0) * kD, 0, np * kD * 4, kBufferFlags);
-            const int ocol = (4 * q4 * kD + kRows * dvb + li) * 4;
+            const int ocol = (li * kD + kRows * dvb + 4 * q4) * 4;
 #pragma unroll
             for (int s2 = 0; s2 < MAXT; ++s2) {
                 const int m = ow + 2 * s2;
-                f32x4 acc = gmy[s2] * (p.scale * Y[s2]);
+                f32x4 acc = (gmy[s2] * p.scale) * Y[s2];
 #pragma unroll
                 for (int kb = 0; kb <= s2 && kb < KBC; ++kb)
-                    acc = mfma16x16x32(aqk[par][s2][kb], ld8(u16 + (par * KBC + kb) * 1024), acc);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // (bit-cast a scalar copy: a bit cast of the vector element itself reads element 0)
-                    const float x = acc[r];
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), orsrc,
-                                                         ocol + (16 * m + r) * kD * 4, 0, 0);
-                }
+                    acc = mfma16x16x32(ld8(u16 + (par * KBC + kb) * 1024), aqk[par][s2][kb], acc);
+                // o[16 m + li][16 dvb + 4 q4 + r], r = 0..3
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), orsrc, ocol + 16 * m * kD * 4, 0, 0);
             }
         };
-        // Y = Q S^T of chunk c with S the state at the chunk start, and gamma of its rows
+        // Y^T = S Q^T of chunk c with S the state at the chunk start, and gamma of its tokens
         auto chunk_y = [&](auto parc, int c) {
             constexpr int par = decltype(parc)::value;
-            const float *gam = reinterpret_cast<const float *>(smem + L::rG + (c % kSlots) * 12 * C) + 4 * q4;
+            const float *gam = reinterpret_cast<const float *>(smem + L::gGT + par * 768 + 512) + li;
             f16x8 sbf[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) sbf[kb] = ld8(s16 + (par * 4 + kb) * 1024);
@@ -390,19 +483,22 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             for (int s2 = 0; s2 < MAXT; ++s2) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) acc = mfma16x16x32(qf[par][s2][kb], sbf[kb], acc);
+                for (int kb = 0; kb < 4; ++kb) acc = mfma16x16x32(sbf[kb], qf[par][s2][kb], acc);
                 Y[s2] = acc;
-                gmy[s2] = *reinterpret_cast<const f32x4 *>(gam + 16 * (ow + 2 * s2));
+                gmy[s2] = gam[16 * (ow + 2 * s2)];
             }
         };
         // interval of chunk c >= 1: O of chunk c - 1, then Y of chunk c; prefetches run two
-        // chunks (q) and one chunk (A_qk) ahead of their use
+        // chunks (q) and one chunk (A_qk) ahead of their use. Then the beta*v block and gate
+        // operands of chunk c + 1 (its v rows and gates landed before this interval): wave ow
+        // forms columns 8 ow .. 8 ow + 7, wave 0 also the gate operands.
         auto interval = [&](auto parc, int c) {
             constexpr int par = decltype(parc)::value;
             emit_o(IC<1 - par>{}, c - 1);
             load_aqk(IC<1 - par>{}, c + 1);
             chunk_y(IC<par>{}, c);
             load_q(IC<par>{}, c + 2);
+            if (c + 1 < NC) prepare_chunk_impl<C>(smem, c + 1, ow, ow == 0, lane);
             lds_barrier();
         };
 
@@ -417,6 +513,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             load_aqk(IC<1>{}, 1);
             chunk_y(IC<0>{}, 0);
             load_q(IC<0>{}, 2);
+            if (1 < NC) prepare_chunk_impl<C>(smem, 1, ow, ow == 0, lane);
             lds_barrier();
             int c = 1;
             for (; c + 1 < NC; c += 2) {
