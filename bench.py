@@ -12,9 +12,11 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -53,6 +55,28 @@ def decode_bytes(B, Hk, Hv, d, qkv_bytes=2) -> int:
     q, k, v, g, beta read, o written."""
     return 2 * B * Hv * d * d * 4 + 2 * B * Hk * d * qkv_bytes + B * Hv * d * qkv_bytes + 2 * B * Hv * 4 \
         + B * Hv * d * 4
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_long32k_decode_b256_hbm_traffic.md")
+PREFILL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_56_amd", "csrc", f)
+                   for f in ("gdn_prefill_chunk.hip", "gdn_prefill_scan.hip", "gdn_frag.h", "gdn_device.h")]
+
+
+def measured_prefill_traffic():
+    """HBM bytes per gdn_prefill launch from the committed FETCH_SIZE / WRITE_SIZE summary,
+    or None when the kernel sources have changed since those counters were taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        h = hashlib.sha256()
+        for f in PREFILL_SOURCES:
+            h.update(open(f, "rb").read())
+    except OSError:
+        return None
+    m_bytes = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_sha = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not (m_bytes and m_sha) or h.hexdigest()[:len(m_sha.group(1))] != m_sha.group(1):
+        return None
+    return int(m_bytes.group(1))
 
 
 def copy_calibration():
@@ -183,7 +207,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": p_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": measured_prefill_traffic(),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": p_bytes,
             "avg_launch_ms": p_avg,
         },
@@ -220,8 +245,9 @@ def cpu_baseline(px, dx):
     threads = len(os.sched_getaffinity(0))
     B, Hk, T, d = px.q.shape
     Hv = px.v.shape[1]
-    # sample: every value head over the first T_s tokens (the oracle is sequential per head)
-    T_s = min(T, 8192)
+    # sample: the whole prefill workload, every value head over all T tokens (the oracle is
+    # sequential per head, parallel over the B * Hv heads)
+    T_s = T
     q, k = px.q[:, :, :T_s], px.k[:, :, :T_s]
     v, g, beta = px.v[:, :, :T_s], px.g[:, :, :T_s], px.beta[:, :, :T_s]
     t = time.perf_counter()
@@ -237,7 +263,7 @@ def cpu_baseline(px, dx):
         "unit": "tokens/s",
         "cores": min(threads, B * Hv),
         "kind": "oracle",
-        "sample": f"prefill of all {B * Hv} value heads over the first {T_s} of {T} tokens "
+        "sample": f"the whole prefill workload: all {B * Hv} value heads over {T_s} of {T} tokens "
                   f"({dt:.2f} s); float64 sequential recurrence, OpenMP over (b, h) pairs",
         "host_threads_available": threads,
         "decode_sequence_updates_per_s": dx.s0.shape[0] / ddt,
