@@ -2,6 +2,7 @@
 // run before anything is enqueued), variant dispatch and error reporting.
 #include "gdn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -160,6 +161,7 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     p.final_state = final_state;
     p.B = s->batch;
     p.T = s->seq_len;
+    p.Ts = s->seq_len;
     p.Hk = s->num_k_heads;
     p.Hv = s->num_v_heads;
     p.D = d;
@@ -187,9 +189,29 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
         err = gdn::launch_prefill_f32(p, s->chunk, st);
     } else if (!two_pass) {
         err = gdn::launch_prefill_mfma(p, s->chunk, st);
+    } else if (T == 0) {
+        err = gdn::launch_prefill_scan(p, s->chunk, workspace, st);  // copies or zeroes the state
     } else {
-        if (T > 0) err = gdn::launch_chunk_prep(p, s->chunk, workspace, st);
-        if (err == hipSuccess) err = gdn::launch_prefill_scan(p, s->chunk, workspace, st);
+        // consecutive token segments; the state is carried through final_state (in place per
+        // workgroup), or through the workspace when the caller wants no final state
+        const gdn::PrefillSegments sg = gdn::prefill_segments(B, Hk, Hv, T, s->chunk);
+        float *carry = final_state ? final_state
+                                   : reinterpret_cast<float *>(static_cast<char *>(workspace) + sg.state_offset);
+        for (int64_t i = 0; i < sg.count && err == hipSuccess; ++i) {
+            const int64_t t0 = i * sg.chunks * s->chunk;
+            gdn::PrefillParams ps = p;
+            ps.T = (int32_t)std::min<int64_t>(T - t0, sg.chunks * s->chunk);
+            ps.q = static_cast<const char *>(q) + t0 * d * esz;
+            ps.k = static_cast<const char *>(k) + t0 * d * esz;
+            ps.v = static_cast<const char *>(v) + t0 * d * esz;
+            ps.g = g + t0;
+            ps.beta = beta + t0;
+            ps.o = o + t0 * d;
+            ps.init_state = i == 0 ? initial_state : carry;
+            ps.final_state = i == sg.count - 1 ? final_state : carry;
+            err = gdn::launch_chunk_prep(ps, s->chunk, workspace, st);
+            if (err == hipSuccess) err = gdn::launch_prefill_scan(ps, s->chunk, workspace, st);
+        }
     }
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
     return GDN_OK;

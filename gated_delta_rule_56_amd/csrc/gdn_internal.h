@@ -16,7 +16,10 @@ struct PrefillParams {
     const float *init_state;   // [B][Hv][D][D] or nullptr (zero state)
     float *o;                  // [B][Hv][T][D]
     float *final_state;        // [B][Hv][D][D] or nullptr
-    int32_t B, T, Hk, Hv, D;
+    int32_t B, T, Hk, Hv, D;   // T: tokens processed by this launch
+    int32_t Ts;                // tokens between consecutive (b, head) sequences in q, k, v, g, beta
+                               // and o (T, or more when the launch covers a window of a longer
+                               // sequence and the pointers are offset to the window's start)
     int32_t head_map;          // 0 tiled (h % Hk), 1 grouped (h / (Hv/Hk))
     float scale;
 };
@@ -40,6 +43,14 @@ hipError_t launch_prefill_mfma(const PrefillParams &p, int chunk, hipStream_t st
 // chunk into the workspace), then the sequential state pass reading them.
 size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk);
 hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStream_t stream);
+
+// Token segments of a bf16 prefill with chunk 32 or 64: `count` segments of `chunks` chunks
+// (the last may be shorter); the workspace holds one segment's chunk data and, at byte
+// `state_offset`, room for the state carried between segments (`bytes` in all).
+struct PrefillSegments {
+    int64_t count, chunks, state_offset, bytes;
+};
+PrefillSegments prefill_segments(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk);
 hipError_t launch_prefill_scan(const PrefillParams &p, int chunk, const void *ws, hipStream_t stream);
 // f32 q/k/v, D in {16, 32, 64, 128}, chunk in {16, 32, 64}: fp32 VALU chunked kernel.
 hipError_t launch_prefill_f32(const PrefillParams &p, int chunk, hipStream_t stream);

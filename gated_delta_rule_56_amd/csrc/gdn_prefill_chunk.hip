@@ -30,6 +30,8 @@
 // 16 x 16 blocks: the diagonal blocks by substitution in fp32 (one wave each),
 // then the off-diagonal blocks by MFMA recursive doubling,
 //   T_ul = -T_uu A_ul T_ll  (16-blocks, then 32-blocks).
+#include <cstdlib>
+
 #include "gdn_device.h"
 #include "gdn_frag.h"
 #include "gdn_internal.h"
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(C * 4) void gdn_chunk_prep_kernel(PrefillParams p, 
     // frag_col(kb, q4, 0..7)), and g, beta of the first value head
     u16x8 qf[4], kf[4];
     {
-        const int64_t row = ((int64_t)bk * p.T + t0 + min(t, n - 1)) * kD + 4 * q4;
+        const int64_t row = ((int64_t)bk * p.Ts + t0 + min(t, n - 1)) * kD + 4 * q4;
         const uint16_t *qr = static_cast<const uint16_t *>(p.q) + row;
         const uint16_t *kr = static_cast<const uint16_t *>(p.k) + row;
 #pragma unroll
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(C * 4) void gdn_chunk_prep_kernel(PrefillParams p, 
     auto value_head = [&](int j) { return p.head_map == 0 ? kh + j * p.Hk : kh * ratio + j; };
     float g_next = 0.f, b_next = 0.f;
     auto load_gb = [&](int j) {
-        const int64_t base = ((int64_t)b * p.Hv + value_head(j)) * p.T + t0;
+        const int64_t base = ((int64_t)b * p.Hv + value_head(j)) * p.Ts + t0;
         g_next = lane < n ? p.g[base + lane] : 0.f;
         b_next = lane < n ? p.beta[base + lane] : 0.f;
     };
@@ -317,11 +319,46 @@ hipError_t launch_c(const PrefillParams &p, _Float16 *ws, hipStream_t stream) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
-    const int64_t nc = (T + chunk - 1) / chunk;
+namespace {
+int64_t chunk_ws_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t nc, int chunk) {
     if (chunk == 32) return ChunkWs<32>(B, Hk, Hv, nc).bytes();
     if (chunk == 64) return ChunkWs<64>(B, Hk, Hv, nc).bytes();
     return 0;
+}
+}  // namespace
+
+// A prefill runs as consecutive token segments (chunk prep, then the state pass, per segment)
+// so that the workspace stays bounded: a segment holds as many chunks as fit a budget of
+// workspace + v + o bytes (1.5 GiB, or GDN_PREFILL_SEGMENT_BYTES). Splitting costs a pipeline
+// start per segment, so the budget is large: smaller segments were measured slower.
+int64_t prefill_segment_budget() {
+    const char *e = std::getenv("GDN_PREFILL_SEGMENT_BYTES");
+    if (e && *e) {
+        const long long v = std::atoll(e);
+        if (v > 0) return v;
+    }
+    return 1536ll << 20;
+}
+
+PrefillSegments prefill_segments(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
+    PrefillSegments sg{0, 0, 0, 0};
+    if (T <= 0 || (chunk != 32 && chunk != 64)) return sg;
+    const int64_t nc = (T + chunk - 1) / chunk;
+    const int64_t per_chunk = chunk_ws_bytes(B, Hk, Hv, 1, chunk) + B * Hv * chunk * kD * (2 + 4);
+    const int64_t budget = prefill_segment_budget();
+    int64_t seg = budget / per_chunk;
+    if (seg < 1) seg = 1;
+    if (seg > nc) seg = nc;
+    sg.count = (nc + seg - 1) / seg;
+    sg.chunks = (nc + sg.count - 1) / sg.count;  // balanced: every segment but the last has this many
+    sg.state_offset = (chunk_ws_bytes(B, Hk, Hv, sg.chunks, chunk) + 255) / 256 * 256;
+    // a carried state between segments, when the caller passes no final_state
+    sg.bytes = sg.count > 1 ? sg.state_offset + B * Hv * kD * kD * 4 : chunk_ws_bytes(B, Hk, Hv, sg.chunks, chunk);
+    return sg;
+}
+
+size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
+    return (size_t)prefill_segments(B, Hk, Hv, T, chunk).bytes;
 }
 
 hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStream_t stream) {

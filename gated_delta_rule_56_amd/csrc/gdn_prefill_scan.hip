@@ -186,7 +186,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int li = lane & 15, q4 = lane >> 4;
-    const int T = p.T;
+    const int T = p.T;                 // tokens of this launch
+    const int64_t Ts = p.Ts;           // token stride between (b, h) sequences
     const int NC = (T + C - 1) / C;
     const ChunkWs<C> wl(p.B, p.Hk, p.Hv, NC);
 
@@ -234,24 +235,15 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         for_chunks(NC, [&](auto sl, int c) {
             constexpr int s = decltype(sl)::value;
             constexpr int par = s & 1;
-            // X = K S^T
-            f32x4 X[NT];
+            // The LDS operands of the chunk are requested in two batches, in the order of use, so
+            // that the MFMAs wait on in-order LDS returns rather than on one round trip each:
+            // X's k fragments, T, beta*v and beta*gamma now; the K^T fragments of the update
+            // once the X products are issued.
+            f16x8 xk[NT][4];
 #pragma unroll
-            for (int m = 0; m < NT; ++m) {
-                X[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < NT; ++m)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    X[m] = mfma16x16x32(ld8(xa[kb] + s * 256 * C + m * 4096), sb[kb], X[m]);
-                }
-            }
-            // operands of the rest of the chain
-            f16x8 ktf[8][KBC];
-#pragma unroll
-            for (int jt = 0; jt < 8; ++jt)
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    ktf[jt][kb] = cat(ld_tr(ta[jt] + s * 256 * C + kb * 8192),
-                                      ld_tr(ta[jt] + s * 256 * C + kb * 8192 + 4096));
+                for (int kb = 0; kb < 4; ++kb) xk[m][kb] = ld8(xa[kb] + s * 256 * C + m * 4096);
             f16x8 Tf[NT][KBC];
 #pragma unroll
             for (int m = 0; m < NT; ++m)
@@ -263,9 +255,29 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             for (int m = 0; m < NT; ++m) {
                 bv[m] = ldf4(bva + par * 4 * kRows * VP + 64 * m);
                 bg[m] = ldf4(bga + par * 768 + 64 * m);
-                ge[m] = ldf4(ega + par * 768 + 64 * m);
             }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // X = K S^T
+            f32x4 X[NT];
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+                X[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) X[m] = mfma16x16x32(xk[m][kb], sb[kb], X[m]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f16x8 ktf[8][KBC];
+#pragma unroll
+            for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+                for (int kb = 0; kb < KBC; ++kb)
+                    ktf[jt][kb] = cat(ld_tr(ta[jt] + s * 256 * C + kb * 8192),
+                                      ld_tr(ta[jt] + s * 256 * C + kb * 8192 + 4096));
+#pragma unroll
+            for (int m = 0; m < NT; ++m) ge[m] = ldf4(ega + par * 768 + 64 * m);
             const float gC = *reinterpret_cast<const float *>(smem + L::gGT + par * 768 + 512 + 4 * (C - 1));
+            __builtin_amdgcn_sched_barrier(0);
 
             // R = beta V - beta gamma X;  U = T R
             f16x8 rb[KBC];
@@ -317,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         constexpr int np = (kPairLines + 7) / 8, nv = C / 4;
         const int total = nk + np + nv;
         const unsigned char *wsb = reinterpret_cast<const unsigned char *>(ws);
-        const unsigned char *vb = static_cast<const unsigned char *>(p.v) + (int64_t)pair * T * kD * 2;
+        const unsigned char *vb = static_cast<const unsigned char *>(p.v) + pair * Ts * kD * 2;
         unsigned char *junk = smem + L::kJunk;
         auto touch = [&](int c) {
             const int n = min(C, T - c * C);
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         // ================================================================ loader waves
         // Direct-to-LDS loads of chunk c (wave 1: L::kDmaK instructions, wave 5: L::kDmaT)
         const bool kload = w == 1;
-        const uint16_t *vg = static_cast<const uint16_t *>(p.v) + (int64_t)pair * T * kD + kRows * dvb;
+        const uint16_t *vg = static_cast<const uint16_t *>(p.v) + pair * Ts * kD + kRows * dvb;
         // v rows and gate vectors of chunk c into ring slot c % 4 (C / 32 + 1 instructions)
         auto issue_vg = [&](int c) {
             const int s = c % kSlots;
@@ -459,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             const int tp0 = c * C, np = min(C, T - tp0);
             // buffer view of this chunk's rows of o: stores past row np fall outside it and are dropped
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                p.o + ((int64_t)pair * T + tp0) * kD, 0, np * kD * 4, kBufferFlags);
+                p.o + (pair * Ts + tp0) * kD, 0, np * kD * 4, kBufferFlags);
             const int ocol = (li * kD + kRows * dvb + 4 * q4) * 4;
 #pragma unroll
             for (int s2 = 0; s2 < MAXT; ++s2) {

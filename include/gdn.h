@@ -94,7 +94,16 @@ typedef struct {
  *   decode:   dk = dv in {32, 64, 128}, either dtype.
  */
 
-/* Bytes of scratch memory gdn_prefill needs for this shape (0: pass NULL, 0). */
+/*
+ * Bytes of scratch memory gdn_prefill needs for this shape (0: pass NULL, 0).
+ * The bfloat16 path with chunk 32 or 64 runs the sequence as consecutive token
+ * segments, each needing about 16.4 KB of workspace per token at B * Hv = 32 (it
+ * scales with B * Hv), so that the workspace stays bounded: a segment takes as many
+ * chunks as fit 1.5 GiB of workspace + v + o, or the byte count in the environment
+ * variable GDN_PREFILL_SEGMENT_BYTES when set (read by this call and by gdn_prefill,
+ * which must see the same value). With more than one segment the workspace also holds
+ * the state carried between segments.
+ */
 size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
 
 /*

@@ -134,17 +134,39 @@ def test_decode_rejects(lib, bnd):
     assert _decode(lib, _shape(bnd, seq_len=1), s0=ADDR["k"]) == 1 and "state overlaps k" in _err(lib)
 
 
-def _ws_bytes(B, Hk, Hv, T, C):
-    """fp16 T and A_qk plus three float gate vectors per (b, value head, chunk),
-    and the fp16 k tile and q fragments per (b, key head, chunk)."""
+def _ws_bytes(B, Hk, Hv, T, C, budget=1536 << 20):
+    """One token segment's chunk data: fp16 T and A_qk plus three float gate vectors per
+    (b, value head, chunk), and the fp16 k tile and q fragments per (b, key head, chunk);
+    plus, when the sequence takes several segments, the fp32 state carried between them.
+    Segments hold as many chunks as fit `budget` bytes of workspace, v and o, balanced."""
     nc = -(-T // C)
-    return 2 * (B * Hv * nc * (2 * C * C + 6 * C) + B * Hk * nc * C * 256)
+    chunk_bytes = lambda n: 2 * (B * Hv * n * (2 * C * C + 6 * C) + B * Hk * n * C * 256)
+    per_chunk = chunk_bytes(1) + B * Hv * C * 128 * 6
+    seg = min(max(budget // per_chunk, 1), nc)
+    count = -(-nc // seg)
+    chunks = -(-nc // count)
+    if count == 1:
+        return chunk_bytes(chunks)
+    return -(-chunk_bytes(chunks) // 256) * 256 + B * Hv * 128 * 128 * 4
 
 
 def test_workspace_query(lib, bnd):
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd))) == _ws_bytes(1, 2, 4, 64, 64)
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, seq_len=100, chunk=32))) == \
         _ws_bytes(1, 2, 4, 100, 32)
+    # the long workload (T = 32768, 16 key / 32 value heads) is one segment by default
+    big = _shape(bnd, seq_len=32768, num_k_heads=16, num_v_heads=32)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(big)) == _ws_bytes(1, 16, 32, 32768, 64)
+    assert _ws_bytes(1, 16, 32, 32768, 64) == 2 * 512 * (32 * (2 * 64 * 64 + 6 * 64) + 16 * 64 * 256)
+
+
+def test_workspace_segments(lib, bnd, monkeypatch):
+    """A smaller segment budget splits the sequence: 9 segments of 57 chunks at 160 MiB."""
+    monkeypatch.setenv("GDN_PREFILL_SEGMENT_BYTES", str(160 << 20))
+    big = _shape(bnd, seq_len=32768, num_k_heads=16, num_v_heads=32)
+    got = lib.gdn_prefill_workspace_bytes(ctypes.byref(big))
+    assert got == _ws_bytes(1, 16, 32, 32768, 64, budget=160 << 20)
+    assert got < 80 << 20
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, chunk=16))) == 0
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32))) == 0
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, batch=0))) == 0
