@@ -22,10 +22,12 @@
 //     fragments on or below the diagonal, and one chunk further ahead the gate
 //     vectors and the bf16 v rows. Two waves because one wave can keep at most
 //     63 vector loads in flight, which is less than three chunks' worth.
-//   wave 4, "prefetch": requests chunk c+8 into L2. The k, q, T, A_qk, gate
-//     and v lines of a chunk are each read by 8 or 16 workgroups at about the
-//     same time; without it all of them would wait for the same HBM miss. Each
-//     line is touched by exactly one of the workgroups that share it.
+//   wave 4, "prefetch and store": requests chunk c+8 into L2. The k, q, T, A_qk,
+//     gate and v lines of a chunk are each read by 8 or 16 workgroups at about
+//     the same time; without it all of them would wait for the same HBM miss.
+//     Each line is touched by exactly one of the workgroups that share it. It
+//     also writes the o rows of chunk c-2 to memory from LDS, so that the
+//     output waves, which wait on their own loads, never wait on stores.
 //   waves 2-3, "output": O^T rather than O, so that a lane ends up with four
 //     consecutive o columns of one token and stores them with one 16-byte
 //     store: Y^T = S Q^T of chunk c from an fp16 copy of S, and O^T of chunk
@@ -37,7 +39,7 @@
 //     end are dropped by a bounded buffer store rather than a branch. They also
 //     form the operands of the next chunk from its v rows and gates: beta*v
 //     (transposed, fp32), beta*gamma, exp(G_C - G) and gamma.
-// One workgroup barrier per chunk. The k tile is stored with its 16-byte column
+// One workgroup barrier per chunk, and one more at the end for the last o rows. The k tile is stored with its 16-byte column
 // groups XOR-swizzled by row (group g of row t at g ^ ksw(t % 16)) so that MFMA
 // fragment reads spread over the LDS banks.
 #include <type_traits>
@@ -57,6 +59,7 @@ constexpr int kSlots = 4;
 // word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format, so that
 // out-of-range accesses (offset >= num_records bytes) are dropped by the hardware
 constexpr int kBufferFlags = 0x00020000;
+
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -78,7 +81,8 @@ struct ScanSmem {
     // exchange
     static constexpr size_t kS16 = gGT + 2 * 768;               // [2][4][64] x 16 B
     static constexpr size_t kU16 = kS16 + 2 * 4 * 64 * 16;      // [2][KBC][64] x 16 B
-    static constexpr size_t kJunk = kU16 + 2 * KBC * 64 * 16;     // [64] x 4 B: target of the L2 prefetches
+    static constexpr size_t kOst = kU16 + 2 * KBC * 64 * 16;      // [2][C][16] f32: o rows of a chunk, to store
+    static constexpr size_t kJunk = kOst + 2 * C * kRows * 4;     // [64] x 4 B: target of the L2 prefetches
     static constexpr size_t kBytes = kJunk + 256;
     static constexpr int kDmaK = C / 4;                         // k-tile loads per chunk (wave 1)
     static constexpr int kTFrags = NT * KBC - (NT / 2) * (KBC - 1);  // T fragments with kb <= m / 2
@@ -316,6 +320,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) *reinterpret_cast<f32x4 *>(p.final_state + srow + 16 * jt) = S[jt];
         }
+        lds_barrier();
     } else if (w == 4) {
         // ================================================================ prefetch wave
         // Lines of chunk c: the key block (k tile and q fragments, 4 C lines) shared by the
@@ -350,6 +355,22 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
                 dma4(a, junk);
             }
         };
+        // o rows of chunk c (staged in LDS buffer c & 1 by the output waves): lane l stores row
+        // 16 i + l / 4, columns 4 (l % 4) .. + 3 of this block; rows past the end fall outside
+        // the buffer range and are dropped
+        auto store_o = [&](int c) {
+            const int tp0 = c * C, np = min(C, T - tp0);
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                p.o + (pair * Ts + tp0) * kD, 0, np * kD * 4, kBufferFlags);
+            const float *src = reinterpret_cast<const float *>(smem + L::kOst + (c & 1) * C * kRows * 4);
+#pragma unroll
+            for (int i = 0; i < C / 16; ++i) {
+                const int row = 16 * i + (lane >> 2), col = 4 * (lane & 3);
+                const f32x4 v4 = *reinterpret_cast<const f32x4 *>(src + row * kRows + col);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), orsrc,
+                                                      (row * kD + kRows * dvb + col) * 4, 0, 0);
+            }
+        };
         for (int c = 3; c < min(NC, kPrefetchAhead); ++c) {
             touch(c);
             wait_vmcnt<8>();
@@ -357,9 +378,13 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         lds_barrier();
         for (int c = 0; c < NC; ++c) {
             if (c + kPrefetchAhead < NC) touch(c + kPrefetchAhead);
-            wait_vmcnt<8>();
+            if (c >= 2) store_o(c - 2);  // staged in the interval before the last barrier
+            wait_vmcnt<16>();
             lds_barrier();
         }
+        if (NC >= 2) store_o(NC - 2);
+        lds_barrier();
+        if (NC >= 1) store_o(NC - 1);
         wait_vmcnt<0>();  // the prefetches write into this workgroup's LDS
     } else if (w == 1 || w == 5) {
         // ================================================================ loader waves
@@ -430,6 +455,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             if (c + 1 < NC) wait_for(c + 1);
             lds_barrier();
         }
+        lds_barrier();
     } else {
         // ================================================================ output waves
         // Wave ow owns token tiles ow and ow + 2 (NT is even). The steady-state loop below is
@@ -466,13 +492,9 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         };
         const unsigned char *s16 = smem + L::kS16 + lane * 16;
         const unsigned char *u16 = smem + L::kU16 + lane * 16;
-        auto emit_o = [&](auto parc, int c) {  // O of chunk c from buffer parity par = c & 1
+        auto emit_o = [&](auto parc, int c) {  // O of chunk c from buffer parity par = c & 1, into LDS
             constexpr int par = decltype(parc)::value;
-            const int tp0 = c * C, np = min(C, T - tp0);
-            // buffer view of this chunk's rows of o: stores past row np fall outside it and are dropped
-            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                p.o + (pair * Ts + tp0) * kD, 0, np * kD * 4, kBufferFlags);
-            const int ocol = (li * kD + kRows * dvb + 4 * q4) * 4;
+            float *ost = reinterpret_cast<float *>(smem + L::kOst + par * C * kRows * 4) + li * kRows + 4 * q4;
 #pragma unroll
             for (int s2 = 0; s2 < MAXT; ++s2) {
                 const int m = ow + 2 * s2;
@@ -481,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
                 for (int kb = 0; kb <= s2 && kb < KBC; ++kb)
                     acc = mfma16x16x32(ld8(u16 + (par * KBC + kb) * 1024), aqk[par][s2][kb], acc);
                 // o[16 m + li][16 dvb + 4 q4 + r], r = 0..3
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), orsrc, ocol + 16 * m * kD * 4, 0, 0);
+                *reinterpret_cast<f32x4 *>(ost + 16 * m * kRows) = acc;
             }
         };
         // Y^T = S Q^T of chunk c with S the state at the chunk start, and gamma of its tokens
@@ -514,7 +536,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             lds_barrier();
         };
 
-        if (NC == 0) {  // empty sequence: nothing to read (the workspace may be empty), one barrier
+        if (NC == 0) {  // empty sequence: nothing to read (the workspace may be empty)
+            lds_barrier();
             lds_barrier();
         } else {
             // same issue order as the steady state: A_qk of c - 1, q of c, A_qk of c, q of c + 1
@@ -535,6 +558,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             if (c < NC) interval(IC<1>{}, c);
             if ((NC - 1) & 1) emit_o(IC<1>{}, NC - 1);
             else emit_o(IC<0>{}, NC - 1);
+            lds_barrier();
         }
     }
 }
