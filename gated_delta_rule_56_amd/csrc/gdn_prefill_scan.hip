@@ -235,19 +235,21 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         const unsigned char *bga = smem + L::gGT + 16 * q4;
         const unsigned char *ega = smem + L::gGT + 256 + 16 * q4;
         lds_barrier();
+        // X's k fragments are read one chunk ahead: the k tile of chunk c + 1 is in LDS during
+        // chunk c, so its reads overlap the end of chunk c instead of starting chunk c + 1
+        f16x8 xk[NT][4];
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) xk[m][kb] = ld8(xa[kb] + m * 4096);
 
         for_chunks(NC, [&](auto sl, int c) {
             constexpr int s = decltype(sl)::value;
             constexpr int par = s & 1;
-            // The LDS operands of the chunk are requested in two batches, in the order of use, so
-            // that the MFMAs wait on in-order LDS returns rather than on one round trip each:
-            // X's k fragments, T, beta*v and beta*gamma now; the K^T fragments of the update
-            // once the X products are issued.
-            f16x8 xk[NT][4];
-#pragma unroll
-            for (int m = 0; m < NT; ++m)
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) xk[m][kb] = ld8(xa[kb] + s * 256 * C + m * 4096);
+            // The remaining LDS operands of the chunk are requested in two batches, in the order
+            // of use, so that the MFMAs wait on in-order LDS returns rather than on one round
+            // trip each: T, beta*v and beta*gamma now; the K^T fragments of the update once the
+            // X products are issued.
             f16x8 Tf[NT][KBC];
 #pragma unroll
             for (int m = 0; m < NT; ++m)
@@ -309,6 +311,12 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb) S[jt] = mfma16x16x32(ktf[jt][kb], ub[kb], S[jt]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            // X's k fragments of chunk c + 1 (after the last chunk this reads a stale slot, unused)
+#pragma unroll
+            for (int m = 0; m < NT; ++m)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) xk[m][kb] = ld8(xa[kb] + ((s + 1) % kSlots) * 256 * C + m * 4096);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
@@ -427,13 +435,14 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
             }
         };
         // wait until chunk c's loads have landed, given how many chunks were issued after it
+        // (the k tile is waited for one chunk earlier than the rest: see the state wave)
         auto wait_for = [&](int c) {
-            const int after = min(NC - 1, c + 2) - c;
             if (kload) {
-                if (after >= 2) wait_vmcnt<2 * L::kDmaK>();
-                else if (after == 1) wait_vmcnt<L::kDmaK>();
+                const int after = min(NC - 1, c + 1) - c;
+                if (after >= 1) wait_vmcnt<L::kDmaK>();
                 else wait_vmcnt<0>();
             } else {
+                const int after = min(NC - 1, c + 2) - c;
                 if (after >= 2) wait_vmcnt<2 * L::kDmaT>();
                 else if (after == 1) wait_vmcnt<L::kDmaT>();
                 else wait_vmcnt<0>();
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         if (NC > 0 && !kload) issue_vg(0);
         for (int c = 0; c < min(NC, 3); ++c) issue(c);
         if (NC > 0) {
-            wait_for(0);
+            wait_for(kload ? min(1, NC - 1) : 0);
             if (!kload) {  // chunk 0's operands; the output waves form those of the later chunks
                 prepare_chunk_impl<C>(smem, 0, 0, true, lane);
                 prepare_chunk_impl<C>(smem, 0, 1, false, lane);
@@ -452,7 +461,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         lds_barrier();
         for (int c = 0; c < NC; ++c) {
             if (c + 3 < NC) issue(c + 3);
-            if (c + 1 < NC) wait_for(c + 1);
+            const int next = kload ? c + 2 : c + 1;
+            if (next < NC) wait_for(next);
             lds_barrier();
         }
         lds_barrier();
