@@ -48,6 +48,8 @@ class Oracle:
         self._lib.gdn_oracle_decode.restype = _I
         self._lib.gdn_oracle_decode.argtypes = [_I, _I, _I, _I, _I, _I, _D,
                                                 _P, _P, _P, _P, _P, _P, _I64, _P, _P, _I]
+        self._lib.gdn_oracle_gated_rmsnorm.restype = _I
+        self._lib.gdn_oracle_gated_rmsnorm.argtypes = [_I64, _I, _P, _P, _P, _D, _P, _I]
         self._lib.gdn_oracle_max_threads.restype = _I
         self._lib.gdn_oracle_max_threads.argtypes = []
 
@@ -128,6 +130,28 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle decode rejected its arguments (code {rc})")
         return o.reshape(B, Hv, dv) if pairs is None else o
+
+
+    def gated_rmsnorm(self, x, weight, gate=None, eps: float = 1e-6, threads: Optional[int] = None):
+        """Gated RMSNorm over the last axis in float64: x / sqrt(mean(x^2) + eps) * weight *
+        silu(gate) (gate None: no gate factor). x is widened to float64, weight and gate to
+        float32 then float64; returns a new float64 array of x's shape."""
+        xc = np.ascontiguousarray(x, dtype=np.float64)
+        n = xc.shape[-1]
+        w = self._f32(weight)
+        if w.shape != (n,):
+            raise ValueError("weight must have the last-axis length of x")
+        gc = None
+        if gate is not None:
+            gc = self._f32(gate)
+            if gc.shape != xc.shape:
+                raise ValueError("gate must have the shape of x")
+        y = np.empty_like(xc)
+        rc = self._lib.gdn_oracle_gated_rmsnorm(xc.size // n, n, self._ptr(xc), self._ptr(gc), self._ptr(w),
+                                                float(eps), self._ptr(y), int(threads or self.max_threads()))
+        if rc != 0:
+            raise ValueError(f"oracle gated_rmsnorm rejected its arguments (code {rc})")
+        return y
 
 
 _default: Optional[Oracle] = None

@@ -35,7 +35,9 @@
  * exact rational arithmetic on tiny inputs, the pages' one-step formula,
  * the padded no-op rule, continuation splits, the beta = 0 closed form,
  * delta-rule recall with orthonormal keys, scale linearity, head-map
- * permutation and thread-count invariance.
+ * permutation and thread-count invariance; for the gated RMSNorm epilogue
+ * (gdn_oracle_gated_rmsnorm, at the end), unit root-mean-square rows, the eps
+ * closed form, quoted sigmoid values and per-column weights.
  */
 #include <math.h>
 #include <stdint.h>
@@ -171,4 +173,41 @@ int gdn_oracle_max_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/*
+ * Gated RMSNorm of output rows: the output epilogue of the gated delta kernels
+ * on the "27b 935/47" page (the q8_gated_rmsnorm test, and the norm_weight /
+ * norm_eps arguments of gated_delta, whose result is checked against an
+ * RMSNorm of the core output). For each row x of n values:
+ *
+ *     y = x / sqrt(mean(x^2) + eps) * weight * silu(gate),  silu(z) = z / (1 + exp(-z))
+ *
+ * with the gate factor left out when gate is NULL. weight has n values shared
+ * by every row (the page applies weight[:128] to both heads of its core
+ * output). Rows are independent; x and y may be the same array.
+ */
+int gdn_oracle_gated_rmsnorm(int64_t rows, int n, const double *x, const float *gate, const float *weight,
+                             double eps, double *y, int nthreads) {
+    if (rows < 0 || n <= 0 || !x || !weight || !y || !(eps >= 0.0)) return 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * n;
+        double ss = 0.0;
+        for (int i = 0; i < n; ++i) ss += xr[i] * xr[i];
+        const double inv = 1.0 / sqrt(ss / n + eps);
+        double *yr = y + r * n;
+        for (int i = 0; i < n; ++i) {
+            double v = xr[i] * inv * (double)weight[i];
+            if (gate) {
+                const double z = (double)gate[r * n + i];
+                v *= z / (1.0 + exp(-z));
+            }
+            yr[i] = v;
+        }
+    }
+    return 0;
 }

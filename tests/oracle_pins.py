@@ -17,7 +17,9 @@ The independent references used here:
 * closed forms: beta = 0 (pure decay), delta-rule recall with orthonormal keys;
 * exact invariants: padded steps (beta = 0, g = 0, q = k = v = 0) are no-ops
   (page "mergable fast RDNA3 Qwen 3.6", symbolic-length prefill entry),
-  continuation splits, scale linearity, head-map relabelling, thread count.
+  continuation splits, scale linearity, head-map relabelling, thread count;
+* for the gated RMSNorm epilogue: unit root-mean-square rows, the eps closed
+  form, quoted sigmoid values, per-column weights and row independence.
 """
 from __future__ import annotations
 
@@ -284,6 +286,68 @@ def pin_pair_subset(orc, seed=22):
             ("pair subset", p)
 
 
+# ---------------------------------------------------------------- gated RMSNorm epilogue
+# The output epilogue of the gated delta kernels ("27b 935/47" page): y = x / sqrt(mean(x^2) +
+# eps) * weight * silu(gate). Pinned by closed forms and exact invariants, and by sigmoid
+# values quoted as constants (sigmoid(1) = 1 / (1 + 1/e) etc.).
+_SIGMOID = {0.0: 0.5, 1.0: 0.7310585786300049, -1.0: 0.2689414213699951, 2.0: 0.8807970779778823,
+            -3.0: 0.04742587317756678}
+
+
+def pin_rmsnorm_unit_rms(orc, seed=23):
+    """eps = 0, weight = 1, no gate: every output row has root-mean-square exactly 1, and
+    doubling a row leaves its output unchanged bit for bit (powers of two scale exactly)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((5, 128)) * rng.uniform(0.1, 10.0, (5, 1))
+    w = np.ones(128, np.float32)
+    y = orc.gated_rmsnorm(x, w, eps=0.0)
+    rms = np.sqrt(np.mean(y * y, axis=-1))
+    assert np.max(np.abs(rms - 1.0)) < 1e-14, ("unit rms", rms)
+    assert np.array_equal(orc.gated_rmsnorm(2.0 * x, w, eps=0.0), y), "scale invariance"
+    assert np.all(np.sign(y) == np.sign(x)), "sign"
+
+
+def pin_rmsnorm_eps(orc, seed=24):
+    """weight = 1, no gate: mean(y^2) = m / (m + eps) with m = mean(x^2), for several eps."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((4, 64)) * 0.01
+    m = np.mean(x * x, axis=-1)
+    for eps in (1e-6, 1e-4, 3e-3):
+        y = orc.gated_rmsnorm(x, np.ones(64, np.float32), eps=eps)
+        got = np.mean(y * y, axis=-1)
+        assert np.max(np.abs(got - m / (m + eps))) < 1e-13, ("eps", eps)
+
+
+def pin_rmsnorm_gate_and_weight(orc, seed=25):
+    """A constant row c (so the normalised value is c / sqrt(c^2 + eps)) times weight times
+    silu(gate) = gate * sigmoid(gate), against quoted sigmoid values; weight acts per column,
+    the same for every row, and rows are independent."""
+    eps = 1e-6
+    gates = np.array(sorted(_SIGMOID), dtype=np.float32)
+    n = len(gates)
+    c = np.array([0.5, -2.0, 3.0])
+    x = np.repeat(c[:, None], n, axis=1)
+    w = np.array([1.0, 2.0, -0.5, 4.0, 0.25][:n], np.float32)
+    gate = np.tile(gates, (3, 1))
+    y = orc.gated_rmsnorm(x, w, gate=gate, eps=eps)
+    for r in range(3):
+        for i, z in enumerate(gates):
+            want = c[r] / math.sqrt(c[r] * c[r] + eps) * float(w[i]) * float(z) * _SIGMOID[float(z)]
+            assert abs(y[r, i] - want) <= 1e-15 * max(1.0, abs(want)), ("gated value", r, i, y[r, i], want)
+    rng = np.random.default_rng(seed)
+    x2 = rng.standard_normal((6, 32))
+    g2 = rng.standard_normal((6, 32)).astype(np.float32)
+    w2 = rng.standard_normal(32).astype(np.float32)
+    y2 = orc.gated_rmsnorm(x2, w2, gate=g2)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    assert np.array_equal(orc.gated_rmsnorm(x2[perm], w2, gate=g2[perm]), y2[perm]), "rows independent"
+    w3 = np.full(32, 2.0, np.float32)
+    y3 = orc.gated_rmsnorm(x2, w3, gate=g2)
+    y1 = orc.gated_rmsnorm(x2, np.ones(32, np.float32), gate=g2)
+    assert np.array_equal(y3, 2.0 * y1), "weight scales its column"
+
+
 ALL_PINS = [pin_bruteforce_unroll, pin_exact_rational, pin_pages_one_step, pin_padded_noop,
             pin_continuation, pin_beta_zero, pin_recall, pin_scale_linear, pin_head_map,
-            pin_threads, pin_decode_matches_prefill, pin_pair_subset]
+            pin_threads, pin_decode_matches_prefill, pin_pair_subset,
+            pin_rmsnorm_unit_rms, pin_rmsnorm_eps, pin_rmsnorm_gate_and_weight]

@@ -48,6 +48,12 @@ MUTANTS = {
          "    /* S <- alpha * S (I - beta k k^T) + beta v k^T"),
         ("        out[i] = acc;\n    }\n}", "    }\n}"),
     ],
+    "rmsnorm_sum_not_mean": ("const double inv = 1.0 / sqrt(ss / n + eps);", "const double inv = 1.0 / sqrt(ss + eps);"),
+    "rmsnorm_eps_outside": ("const double inv = 1.0 / sqrt(ss / n + eps);", "const double inv = 1.0 / (sqrt(ss / n) + eps);"),
+    "rmsnorm_no_sqrt": ("const double inv = 1.0 / sqrt(ss / n + eps);", "const double inv = 1.0 / (ss / n + eps);"),
+    "silu_is_sigmoid": ("v *= z / (1.0 + exp(-z));", "v *= 1.0 / (1.0 + exp(-z));"),
+    "silu_sign": ("v *= z / (1.0 + exp(-z));", "v *= z / (1.0 + exp(z));"),
+    "weight_by_row": ("double v = xr[i] * inv * (double)weight[i];", "double v = xr[i] * inv * (double)weight[r % n];"),
     "output_step_off_by_one": ("if (o) memcpy(o + ((int64_t)p * T + t) * dv, out,",
                                "if (o) memcpy(o + ((int64_t)p * T + (t + 1) % T) * dv, out,"),
 }
