@@ -20,8 +20,8 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
 
-EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_status_string",
-                    "gdn_last_error", "gdn_abi_version")
+EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_gated_rmsnorm",
+                    "gdn_status_string", "gdn_last_error", "gdn_abi_version")
 
 
 class GdnShape(ctypes.Structure):
@@ -58,6 +58,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, SZ, P]
     lib.gdn_decode.restype = ctypes.c_int
     lib.gdn_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
+    lib.gdn_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_gated_rmsnorm.argtypes = [ctypes.POINTER(GdnShape), P, P, P, ctypes.c_float, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_last_error.restype = ctypes.c_char_p
@@ -181,4 +183,37 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
                        head_map, scale)
     _check(lib, lib.gdn_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state), _ptr(o), _stream_handle(stream)))
+    return o
+
+
+def gated_rmsnorm(o: torch.Tensor, weight: torch.Tensor, gate: Optional[torch.Tensor] = None, *,
+                  eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """gdn_gated_rmsnorm on torch tensors, in place: every row of the last axis of o
+    ([B][Hv][T][dv] from prefill or [B][Hv][dv] from decode, float32) becomes
+    o / sqrt(mean(o^2) + eps) * weight * silu(gate); weight [dv] float32; gate of o's shape in
+    bfloat16 or float32, or None for no gate factor. Returns o."""
+    lib = load_library()
+    _dev_tensor(o, "o", torch.float32)
+    if o.dim() == 3:
+        B, Hv, d = o.shape
+        T = 1
+    elif o.dim() == 4:
+        B, Hv, T, d = o.shape
+    else:
+        raise ValueError("o must be [B][Hv][T][dv] or [B][Hv][dv]")
+    _dev_tensor(weight, "weight", torch.float32)
+    if weight.shape != (d,):
+        raise ValueError("weight must be [dv]")
+    dtype = torch.float32
+    if gate is not None:
+        dtype = gate.dtype
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("gate must be bfloat16 or float32")
+        _dev_tensor(gate, "gate", dtype)
+        if gate.shape != o.shape:
+            raise ValueError("gate must have the shape of o")
+    shape = make_shape(B, T, Hv, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
+                       GDN_HEADS_TILED, 1.0)
+    _check(lib, lib.gdn_gated_rmsnorm(ctypes.byref(shape), _ptr(o), _ptr(gate), _ptr(weight), float(eps),
+                                      _stream_handle(stream)))
     return o

@@ -217,6 +217,36 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     return GDN_OK;
 }
 
+gdn_status gdn_gated_rmsnorm(const gdn_shape *s, float *o, const void *gate, const float *weight, float eps,
+                             void *stream) {
+    GDN_TRY(check_common(s));
+    if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
+    const int d = s->head_dim_v;
+    if (d != 16 && d != 32 && d != 64 && d != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "gated_rmsnorm supports head_dim_v 16, 32, 64 or 128 (got %d)", d);
+    if (!std::isfinite(eps) || eps < 0.0f) return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const int64_t rows = (int64_t)s->batch * s->num_v_heads * s->seq_len;
+    if (rows == 0) return GDN_OK;
+    const bool bf16 = s->qkv_dtype == GDN_DTYPE_BF16;
+    GDN_TRY(check_ptr(o, "o", 16));
+    GDN_TRY(check_ptr(weight, "weight", 16));
+    if (gate) GDN_TRY(check_ptr(gate, "gate", bf16 ? 8 : 16));
+    const Range ins[] = {range("gate", gate, gate ? rows * d * (bf16 ? 2 : 4) : 0), range("weight", weight, d * 4)};
+    const Range outs[] = {range("o", o, rows * d * 4)};
+    GDN_TRY(check_no_overlap(outs, 1, ins, 2));
+    gdn::NormParams p;
+    p.o = o;
+    p.gate = gate;
+    p.weight = weight;
+    p.rows = rows;
+    p.D = d;
+    p.gate_bf16 = bf16;
+    p.eps = eps;
+    const hipError_t err = gdn::launch_gated_rmsnorm(p, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(GDN_ERR_HIP, "gated_rmsnorm launch failed: %s", hipGetErrorString(err));
+    return GDN_OK;
+}
+
 gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
                       const float *beta, float *state, float *o, void *stream) {
     GDN_TRY(check_common(s));

@@ -44,6 +44,18 @@ hipError_t launch_prefill_mfma(const PrefillParams &p, int chunk, hipStream_t st
 size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk);
 hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStream_t stream);
 
+// Gated RMSNorm of `rows` output rows of D floats, in place.
+struct NormParams {
+    float *o;               // [rows][D]
+    const void *gate;       // [rows][D] bf16 bits or float, or nullptr (no gate factor)
+    const float *weight;    // [D]
+    int64_t rows;
+    int32_t D;
+    bool gate_bf16;
+    float eps;
+};
+hipError_t launch_gated_rmsnorm(const NormParams &p, hipStream_t stream);
+
 // Token segments of a bf16 prefill with chunk 32 or 64: `count` segments of `chunks` chunks
 // (the last may be shorter); the workspace holds one segment's chunk data and, at byte
 // `state_offset`, room for the state carried between segments (`bytes` in all).

@@ -223,3 +223,23 @@ def generate_workload(wl: Workload) -> ScanInputs:
                     wl.qkv_dtype, wl.seed, decay_mult=wl.decay_mult, init_state=wl.init_state,
                     lengths=wl.lengths, decode_steps=wl.decode_steps)
 
+
+
+@dataclasses.dataclass
+class NormInputs:
+    """Inputs of the gated RMSNorm epilogue: gate (float32 values; bf16 bits when the workload
+    is bf16) of the output's shape, and weight [dv] float32."""
+    gate: np.ndarray
+    gate_bits: Optional[np.ndarray]
+    weight: np.ndarray
+
+
+def generate_norm(out_shape: Sequence[int], qkv_dtype: str, seed: int) -> NormInputs:
+    """Seeded gate ~ N(0, 1) of the output's shape, stored like q/k/v (bf16-rounded for a bf16
+    workload), and a weight ~ N(0, 1) over the head dimension, rounded to float16 values (the
+    pages draw their norm weights in float16)."""
+    rng = np.random.default_rng(seed)
+    gate = rng.standard_normal(tuple(out_shape))
+    weight = rng.standard_normal(out_shape[-1]).astype(np.float16).astype(np.float32)
+    gf, gb = _store(gate, qkv_dtype)
+    return NormInputs(gate=gf, gate_bits=gb, weight=weight)

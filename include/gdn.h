@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -142,6 +142,25 @@ const char *gdn_status_string(gdn_status status);
 
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */
 const char *gdn_last_error(void);
+
+/*
+ * Gated RMSNorm of the output, in place: the output epilogue that the gated
+ * delta kernels apply on the "27b 935/47" compare page (its q8_gated_rmsnorm
+ * test; the norm_weight and norm_eps arguments of gated_delta). For every row
+ * x of head_dim_v values of o:
+ *     x <- x / sqrt(mean(x^2) + eps) * weight * silu(gate),  silu(z) = z / (1 + exp(-z))
+ *   o       [B][Hv][T][dv] float32 with T = shape->seq_len (a gdn_decode output
+ *           [B][Hv][dv] is the case T = 1); read and overwritten
+ *   gate    [B][Hv][T][dv] in shape->qkv_dtype, or NULL for no gate factor
+ *   weight  [dv] float32, the same for every head and token
+ *   eps     finite, >= 0
+ * Supported: head_dim_v in {16, 32, 64, 128}. gate and weight must not overlap o.
+ * Not fused into gdn_prefill: there the dv values of one output row come from
+ * dv / 16 different workgroups, so the row's norm would need a reduction
+ * across workgroups; this call is one extra streaming pass over o.
+ */
+gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, float *o, const void *gate, const float *weight,
+                             float eps, void *stream);
 
 /* GDN_ABI_VERSION of the built library. */
 int gdn_abi_version(void);

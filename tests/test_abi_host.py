@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib, bnd):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(1) == b"invalid argument"
     assert lib.gdn_status_string(2) == b"unsupported configuration"
@@ -189,3 +189,22 @@ def test_binding_rejects_cpu_tensors(bnd):
     q = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         bnd.prefill(q, q, q, torch.zeros(1, 1, 4), torch.zeros(1, 1, 4))
+
+
+def _norm(lib, shape, o=7 * GB, gate=8 * GB, weight=9 * GB, eps=1e-6):
+    return lib.gdn_gated_rmsnorm(ctypes.byref(shape), o, gate, weight, ctypes.c_float(eps), None)
+
+
+def test_gated_rmsnorm_rejects(lib, bnd):
+    shape = _shape(bnd, seq_len=10)
+    assert _norm(lib, _shape(bnd, seq_len=10, head_dim=48)) == 2 and "head_dim_v" in _err(lib)
+    assert _norm(lib, shape, eps=float("nan")) == 1 and "eps" in _err(lib)
+    assert _norm(lib, shape, eps=-1.0) == 1 and "eps" in _err(lib)
+    assert _norm(lib, shape, o=None) == 1 and "o is NULL" in _err(lib)
+    assert _norm(lib, shape, weight=None) == 1 and "weight is NULL" in _err(lib)
+    assert _norm(lib, shape, o=7 * GB + 4) == 1 and "aligned" in _err(lib)
+    assert _norm(lib, shape, gate=8 * GB + 2) == 1 and "aligned" in _err(lib)  # bf16 gate: 8-byte aligned
+    assert _norm(lib, shape, gate=7 * GB + 4096) == 1 and "o overlaps gate" in _err(lib)
+    assert _norm(lib, shape, weight=7 * GB + 512) == 1 and "o overlaps weight" in _err(lib)
+    # no rows: nothing to check or launch
+    assert _norm(lib, _shape(bnd, seq_len=0), o=None) == 0
