@@ -50,6 +50,8 @@ class Oracle:
                                                 _P, _P, _P, _P, _P, _P, _I64, _P, _P, _I]
         self._lib.gdn_oracle_gated_rmsnorm.restype = _I
         self._lib.gdn_oracle_gated_rmsnorm.argtypes = [_I64, _I, _P, _P, _P, _D, _P, _I]
+        self._lib.gdn_oracle_qkv_prologue.restype = _I
+        self._lib.gdn_oracle_qkv_prologue.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _D, _I]
         self._lib.gdn_oracle_max_threads.restype = _I
         self._lib.gdn_oracle_max_threads.argtypes = []
 
@@ -152,6 +154,35 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle gated_rmsnorm rejected its arguments (code {rc})")
         return y
+
+
+    def qkv_prologue(self, x, w, Hk: int, Hv: int, d: int, state=None, eps: float = 1e-6,
+                     threads: Optional[int] = None):
+        """Causal depthwise conv (K = w.shape[1] taps) + SiLU, then the q | k | v split with
+        per-head L2 normalisation of q and k, in float64. x [B][T][(2 Hk + Hv) d] (float32
+        values), w [(2 Hk + Hv) d][K], state [B][K-1][channels] or None (zero rows). Returns
+        (q [B][Hk][T][d], k [B][Hk][T][d], v [B][Hv][T][d], new state [B][K-1][channels])."""
+        xc = self._f32(x)
+        B, T, C = xc.shape
+        wc = self._f32(w)
+        K = wc.shape[1]
+        if C != (2 * Hk + Hv) * d or wc.shape != (C, K):
+            raise ValueError("x must be [B][T][(2 Hk + Hv) d] and w [channels][K]")
+        sc = None
+        if state is not None:
+            sc = np.ascontiguousarray(state, dtype=np.float64)
+            if sc.shape != (B, K - 1, C):
+                raise ValueError("state must be [B][K-1][channels]")
+        q = np.empty((B, Hk, T, d))
+        k = np.empty((B, Hk, T, d))
+        v = np.empty((B, Hv, T, d))
+        st = np.empty((B, K - 1, C))
+        rc = self._lib.gdn_oracle_qkv_prologue(B, T, Hk, Hv, d, K, self._ptr(xc), self._ptr(wc), self._ptr(sc),
+                                               self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(st),
+                                               float(eps), int(threads or self.max_threads()))
+        if rc != 0:
+            raise ValueError(f"oracle qkv_prologue rejected its arguments (code {rc})")
+        return q, k, v, st
 
 
 _default: Optional[Oracle] = None

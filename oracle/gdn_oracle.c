@@ -211,3 +211,78 @@ int gdn_oracle_gated_rmsnorm(int64_t rows, int n, const double *x, const float *
     }
     return 0;
 }
+
+/*
+ * Input prologue of the scan: the causal depthwise convolution with SiLU and
+ * the gdn_qkv split of the "27b 935/47" page (its causal_conv_silu and
+ * gdn_qkv tests). x holds, per (b, t), Cch = (2 Hk + Hv) d channels; conv
+ * weight w is [Cch][K]; the convolution state holds the K - 1 rows before
+ * t = 0. With window = state rows followed by the rows of x:
+ *
+ *     y[b][t][c] = silu(sum_{i<K} window[b][t + i][c] * w[c][i])
+ *
+ * Channels [0, Hk d) are q, [Hk d, 2 Hk d) are k and the rest v, each split
+ * into heads of d channels. q and k heads are scaled by
+ * 1 / sqrt(sum of squares over the head + eps) (an L2 normalisation); v is
+ * left as is. Outputs are head-major: q, k [B][Hk][T][d], v [B][Hv][T][d].
+ * The value heads' sharing of key heads is left to the scan (no repeat), and
+ * so is the 1/sqrt(d) query scale. state_out (if not NULL) receives the last
+ * K - 1 window rows, the state that continues the sequence; it may be
+ * state_in. state_in NULL means zero rows.
+ */
+int gdn_oracle_qkv_prologue(int B, int T, int Hk, int Hv, int d, int K, const float *x, const float *w,
+                            const double *state_in, double *q, double *k, double *v, double *state_out,
+                            double eps, int nthreads) {
+    if (B <= 0 || T < 0 || Hk <= 0 || Hv <= 0 || d <= 0 || K <= 0 || !x || !w || !q || !k || !v) return 1;
+    if (d > 1024) return 3;
+    const int C = (2 * Hk + Hv) * d;
+    const int W = T + K - 1;
+    double *win = (double *)malloc(sizeof(double) * (size_t)W * C);
+    double *newst = state_out ? (double *)malloc(sizeof(double) * (size_t)B * (K - 1) * C) : NULL;
+    if (!win || (state_out && !newst)) {
+        free(win);
+        free(newst);
+        return 2;
+    }
+    for (int b = 0; b < B; ++b) {
+        for (int r = 0; r < K - 1; ++r)
+            for (int c = 0; c < C; ++c)
+                win[(size_t)r * C + c] = state_in ? state_in[((size_t)b * (K - 1) + r) * C + c] : 0.0;
+        for (int t = 0; t < T; ++t)
+            for (int c = 0; c < C; ++c) win[(size_t)(t + K - 1) * C + c] = (double)x[((size_t)b * T + t) * C + c];
+        if (newst)
+            for (int r = 0; r < K - 1; ++r)
+                for (int c = 0; c < C; ++c) newst[((size_t)b * (K - 1) + r) * C + c] = win[(size_t)(T + r) * C + c];
+#ifdef _OPENMP
+        if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+        for (int t = 0; t < T; ++t) {
+            double y[1024];  /* one head (d <= 1024) */
+            for (int hh = 0; hh < 2 * Hk + Hv; ++hh) {
+                for (int j = 0; j < d; ++j) {
+                    const int c = hh * d + j;
+                    double acc = 0.0;
+                    for (int i = 0; i < K; ++i) acc += win[(size_t)(t + i) * C + c] * (double)w[(size_t)c * K + i];
+                    y[j] = acc / (1.0 + exp(-acc));
+                }
+                double f = 1.0;
+                if (hh < 2 * Hk) {
+                    double ss = 0.0;
+                    for (int j = 0; j < d; ++j) ss += y[j] * y[j];
+                    f = 1.0 / sqrt(ss + eps);
+                }
+                double *dst = hh < Hk ? q + (((size_t)b * Hk + hh) * T + t) * d
+                            : hh < 2 * Hk ? k + (((size_t)b * Hk + (hh - Hk)) * T + t) * d
+                                          : v + (((size_t)b * Hv + (hh - 2 * Hk)) * T + t) * d;
+                for (int j = 0; j < d; ++j) dst[j] = y[j] * f;
+            }
+        }
+    }
+    if (newst) {
+        memcpy(state_out, newst, sizeof(double) * (size_t)B * (K - 1) * C);
+        free(newst);
+    }
+    free(win);
+    return 0;
+}

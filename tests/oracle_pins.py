@@ -19,7 +19,10 @@ The independent references used here:
   (page "mergable fast RDNA3 Qwen 3.6", symbolic-length prefill entry),
   continuation splits, scale linearity, head-map relabelling, thread count;
 * for the gated RMSNorm epilogue: unit root-mean-square rows, the eps closed
-  form, quoted sigmoid values, per-column weights and row independence.
+  form, quoted sigmoid values, per-column weights and row independence;
+* for the input prologue: single-tap convolutions against quoted SiLU values,
+  continuation splits, the q/k normalisation against the unnormalised v path,
+  and one-hot channels landing in their head-major slots.
 """
 from __future__ import annotations
 
@@ -347,7 +350,100 @@ def pin_rmsnorm_gate_and_weight(orc, seed=25):
     assert np.array_equal(y3, 2.0 * y1), "weight scales its column"
 
 
+# ---------------------------------------------------------------- input prologue
+# Causal depthwise convolution + SiLU and the q | k | v split with per-head L2 normalisation
+# ("27b 935/47" page: causal_conv_silu and gdn_qkv tests).
+def _silu_quoted(z):
+    return z * _SIGMOID[float(z)]
+
+
+def pin_prologue_taps(orc, seed=26):
+    """Only the last tap set: y = silu(x) channel by channel (quoted sigmoid values), v heads
+    unnormalised. Only the first tap set: y_t = silu(x_{t-3}), taking the state rows for t < 3."""
+    Hk, Hv, d, K = 1, 2, 4, 4
+    C = (2 * Hk + Hv) * d
+    vals = np.array(sorted(_SIGMOID), dtype=np.float32)
+    rng = np.random.default_rng(seed)
+    x = rng.choice(vals, size=(1, 6, C)).astype(np.float32)
+    w = np.zeros((C, K), np.float32)
+    w[:, K - 1] = 1.0
+    _, _, v, _ = orc.qkv_prologue(x, w, Hk, Hv, d, eps=0.0)
+    for h in range(Hv):
+        for t in range(6):
+            for j in range(d):
+                want = _silu_quoted(float(x[0, t, (2 * Hk + h) * d + j]))
+                assert abs(v[0, h, t, j] - want) <= 1e-15 * max(1.0, abs(want)), ("last tap", h, t, j)
+    w[:] = 0.0
+    w[:, 0] = 1.0
+    state = rng.choice(vals, size=(1, K - 1, C)).astype(np.float64)
+    _, _, v, _ = orc.qkv_prologue(x, w, Hk, Hv, d, state=state, eps=0.0)
+    for h in range(Hv):
+        for t in range(6):
+            for j in range(d):
+                c = (2 * Hk + h) * d + j
+                src = state[0, t, c] if t < K - 1 else x[0, t - (K - 1), c]
+                want = _silu_quoted(float(src))
+                assert abs(v[0, h, t, j] - want) <= 1e-15 * max(1.0, abs(want)), ("first tap", h, t, j)
+
+
+def pin_prologue_continuation(orc, seed=27):
+    """One call over T tokens equals a call over m tokens then one over T - m from the returned
+    state, bit for bit; the returned state is the last K - 1 input rows."""
+    rng = np.random.default_rng(seed)
+    B, T, Hk, Hv, d, K = 2, 9, 2, 4, 8, 4
+    C = (2 * Hk + Hv) * d
+    x = rng.standard_normal((B, T, C)).astype(np.float32)
+    w = rng.standard_normal((C, K)).astype(np.float32)
+    s0 = rng.standard_normal((B, K - 1, C))
+    q, k, v, st = orc.qkv_prologue(x, w, Hk, Hv, d, state=s0)
+    assert np.array_equal(st, x[:, T - (K - 1):].astype(np.float64)), "state = last rows"
+    for m in (1, 2, 5):
+        q1, k1, v1, st1 = orc.qkv_prologue(x[:, :m], w, Hk, Hv, d, state=s0)
+        q2, k2, v2, st2 = orc.qkv_prologue(x[:, m:], w, Hk, Hv, d, state=st1)
+        for a_, b1, b2 in ((q, q1, q2), (k, k1, k2), (v, v1, v2)):
+            assert np.array_equal(a_, np.concatenate([b1, b2], axis=2)), ("continuation", m)
+        assert np.array_equal(st, st2), ("continued state", m)
+
+
+def pin_prologue_norm_and_layout(orc, seed=28):
+    """q and k heads are the v-style activations divided by their L2 norm: the same channel data
+    placed in a q, a k and a v head gives q = k = v / |v| (eps = 0) and |q|^2 = s / (s + eps) with
+    s = |v|^2 in general. A single nonzero channel lands in exactly its (tensor, head, t, j)."""
+    rng = np.random.default_rng(seed)
+    Hk, Hv, d, K, T = 1, 1, 16, 4, 5
+    C = 3 * d
+    head = rng.standard_normal((1, T, d)).astype(np.float32)
+    x = np.concatenate([head, head, head], axis=-1)
+    w = np.tile(rng.standard_normal((d, K)).astype(np.float32), (3, 1))
+    q, k, v, _ = orc.qkv_prologue(x, w, Hk, Hv, d, eps=0.0)
+    n = np.linalg.norm(v, axis=-1, keepdims=True)
+    assert np.max(np.abs(q - v / n)) < 1e-15 and np.array_equal(q, k), "q, k = v / |v|"
+    eps = 0.3
+    q, _, v, _ = orc.qkv_prologue(x, w, Hk, Hv, d, eps=eps)
+    s_ = np.sum(v * v, axis=-1)
+    assert np.max(np.abs(np.sum(q * q, axis=-1) - s_ / (s_ + eps))) < 1e-14, "eps closed form"
+    Hk, Hv, d = 2, 4, 4
+    C = (2 * Hk + Hv) * d
+    w = np.zeros((C, K), np.float32)
+    w[:, K - 1] = 1.0
+    for c, t in ((0, 0), (5, 3), (2 * d + 1, 1), (3 * d + 3, 4), (4 * d + 2, 2), (7 * d + 3, 0)):
+        x = np.zeros((1, 5, C), np.float32)
+        x[0, t, c] = 1.0
+        q, k, v, _ = orc.qkv_prologue(x, w, Hk, Hv, d, eps=1e-300)  # eps > 0: all-zero heads stay 0
+        hh, j = divmod(c, d)
+        outs = {"q": q, "k": k, "v": v}
+        name, h = ("q", hh) if hh < Hk else ("k", hh - Hk) if hh < 2 * Hk else ("v", hh - 2 * Hk)
+        want = 1.0 if name != "v" else _SIGMOID[1.0]
+        for nm, arr in outs.items():
+            nz = np.argwhere(arr != 0.0)
+            if nm == name:
+                assert nz.tolist() == [[0, h, t, j]] and abs(arr[0, h, t, j] - want) < 1e-15, ("one-hot", c, t)
+            else:
+                assert nz.size == 0, ("leak", nm, c)
+
+
 ALL_PINS = [pin_bruteforce_unroll, pin_exact_rational, pin_pages_one_step, pin_padded_noop,
             pin_continuation, pin_beta_zero, pin_recall, pin_scale_linear, pin_head_map,
             pin_threads, pin_decode_matches_prefill, pin_pair_subset,
-            pin_rmsnorm_unit_rms, pin_rmsnorm_eps, pin_rmsnorm_gate_and_weight]
+            pin_rmsnorm_unit_rms, pin_rmsnorm_eps, pin_rmsnorm_gate_and_weight,
+            pin_prologue_taps, pin_prologue_continuation, pin_prologue_norm_and_layout]

@@ -54,6 +54,16 @@ MUTANTS = {
     "silu_is_sigmoid": ("v *= z / (1.0 + exp(-z));", "v *= 1.0 / (1.0 + exp(-z));"),
     "silu_sign": ("v *= z / (1.0 + exp(-z));", "v *= z / (1.0 + exp(z));"),
     "weight_by_row": ("double v = xr[i] * inv * (double)weight[i];", "double v = xr[i] * inv * (double)weight[r % n];"),
+    "conv_taps_reversed": ("acc += win[(size_t)(t + i) * C + c] * (double)w[(size_t)c * K + i];",
+                           "acc += win[(size_t)(t + i) * C + c] * (double)w[(size_t)c * K + (K - 1 - i)];"),
+    "conv_window_shifted": ("acc += win[(size_t)(t + i) * C + c] * (double)w[(size_t)c * K + i];",
+                            "acc += win[(size_t)(t + i + (i < K - 1)) * C + c] * (double)w[(size_t)c * K + i];"),
+    "conv_state_ignored": ("win[(size_t)r * C + c] = state_in ? state_in[((size_t)b * (K - 1) + r) * C + c] : 0.0;",
+                           "win[(size_t)r * C + c] = 0.0;"),
+    "prologue_silu_is_sigmoid": ("y[j] = acc / (1.0 + exp(-acc));", "y[j] = 1.0 / (1.0 + exp(-acc));"),
+    "prologue_v_normalised": ("if (hh < 2 * Hk) {", "if (hh < 2 * Hk + Hv) {"),
+    "prologue_mean_not_sum": ("f = 1.0 / sqrt(ss + eps);", "f = 1.0 / sqrt(ss / d + eps);"),
+    "prologue_k_reads_q": ("k + (((size_t)b * Hk + (hh - Hk)) * T + t) * d", "k + (((size_t)b * Hk + (hh - Hk + Hk - 1) % Hk) * T + t) * d"),
     "output_step_off_by_one": ("if (o) memcpy(o + ((int64_t)p * T + t) * dv, out,",
                                "if (o) memcpy(o + ((int64_t)p * T + (t + 1) % T) * dv, out,"),
 }
