@@ -12,6 +12,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -182,6 +183,35 @@ def main():
     if not torch.isfinite(po).all():
         raise RuntimeError("non-finite outputs after the gated RMSNorm")
 
+    # the input prologue (conv + SiLU, q/k/v split, q/k L2 norm) on the long workload's raw
+    # projections: x [1][32768][(2 Hk + Hv) d] bf16
+    prng = np.random.default_rng(pw.seed + 200)
+    Cx = (2 * Hk + Hv) * d
+    px_bits = inputs.bf16_round(prng.standard_normal((B, T, Cx), dtype=np.float32))
+    xr = bf(px_bits)
+    del px_bits
+    cw = torch.from_numpy((prng.standard_normal((Cx, 4)) * 0.5).astype(np.float32)).to(dev)
+    cst = torch.zeros((B, 3, Cx), dtype=torch.float32, device=dev)
+    for _ in range(max(1, args.warmup)):
+        pro = binding.qkv_prologue(xr, cw, cst, num_k_heads=Hk, num_v_heads=Hv, head_dim=d)
+    del pro
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    pqkv = [torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv)]
+    lib = binding.load_library()
+    pshape = binding.make_shape(B, T, Hk, Hv, d, 0, binding.GDN_DTYPE_BF16, 0, 1.0)
+    for e in pev:
+        e[0].record(stream)
+        rc = lib.gdn_qkv_prologue(ctypes.byref(pshape), xr.data_ptr(), cw.data_ptr(), cst.data_ptr(),
+                                  pqkv[0].data_ptr(), pqkv[1].data_ptr(), pqkv[2].data_ptr(),
+                                  ctypes.c_float(1e-6), stream.cuda_stream)
+        e[1].record(stream)
+        if rc != 0:
+            raise RuntimeError(lib.gdn_last_error().decode())
+    torch.cuda.synchronize()
+    pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+    pro_bytes = xr.numel() * 2 + sum(t.numel() for t in pqkv) * 2 + cw.numel() * 4 + 2 * cst.numel() * 4
+    del xr, pqkv
+
     prefill_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     decode_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     ms_per_step = wall * 1e3 / args.steps
@@ -256,6 +286,16 @@ def main():
             "frac": norm_bytes / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": norm_bytes,
             "rows": po.numel() // po.shape[-1],
+        },
+        "qkv_prologue": {
+            "kernel": "gdn_qkv_prologue_kernel<128, bf16> (conv + SiLU, q/k/v split, q/k L2 norm)",
+            "shape": f"x [{B}][{T}][{Cx}] bf16 -> q, k [{B}][{Hk}][{T}][{d}], v [{B}][{Hv}][{T}][{d}]",
+            "avg_launch_ms": pro_ms,
+            "achieved": pro_bytes / (pro_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": pro_bytes / (pro_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": pro_bytes,
         },
         "input_generation_s": t_gen,
     }

@@ -21,7 +21,7 @@ GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
 
 EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_gated_rmsnorm",
-                    "gdn_status_string", "gdn_last_error", "gdn_abi_version")
+                    "gdn_qkv_prologue", "gdn_status_string", "gdn_last_error", "gdn_abi_version")
 
 
 class GdnShape(ctypes.Structure):
@@ -60,6 +60,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [ctypes.POINTER(GdnShape), P, P, P, ctypes.c_float, P]
+    lib.gdn_qkv_prologue.restype = ctypes.c_int
+    lib.gdn_qkv_prologue.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, ctypes.c_float, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_last_error.restype = ctypes.c_char_p
@@ -217,3 +219,36 @@ def gated_rmsnorm(o: torch.Tensor, weight: torch.Tensor, gate: Optional[torch.Te
     _check(lib, lib.gdn_gated_rmsnorm(ctypes.byref(shape), _ptr(o), _ptr(gate), _ptr(weight), float(eps),
                                       _stream_handle(stream)))
     return o
+
+
+def qkv_prologue(x: torch.Tensor, conv_weight: torch.Tensor, conv_state: Optional[torch.Tensor] = None, *,
+                 num_k_heads: int, num_v_heads: int, head_dim: int, eps: float = 1e-6,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """gdn_qkv_prologue on torch tensors: x [B][T][(2 Hk + Hv) d] (bfloat16 or float32), conv_weight
+    [(2 Hk + Hv) d][4] float32, conv_state [B][3][(2 Hk + Hv) d] float32 (updated in place) or None.
+    Returns (q, k, v) in x's dtype: q, k [B][Hk][T][d], v [B][Hv][T][d]."""
+    lib = load_library()
+    dtype = x.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be bfloat16 or float32")
+    _dev_tensor(x, "x", dtype)
+    Hk, Hv, d = num_k_heads, num_v_heads, head_dim
+    C = (2 * Hk + Hv) * d
+    if x.dim() != 3 or x.shape[2] != C:
+        raise ValueError("x must be [B][T][(2 Hk + Hv) d]")
+    B, T, _ = x.shape
+    _dev_tensor(conv_weight, "conv_weight", torch.float32)
+    if conv_weight.shape != (C, 4):
+        raise ValueError("conv_weight must be [(2 Hk + Hv) d][4]")
+    if conv_state is not None:
+        _dev_tensor(conv_state, "conv_state", torch.float32)
+        if conv_state.shape != (B, 3, C):
+            raise ValueError("conv_state must be [B][3][(2 Hk + Hv) d]")
+    q = torch.empty((B, Hk, T, d), dtype=dtype, device=x.device)
+    k = torch.empty((B, Hk, T, d), dtype=dtype, device=x.device)
+    v = torch.empty((B, Hv, T, d), dtype=dtype, device=x.device)
+    shape = make_shape(B, T, Hk, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
+                       GDN_HEADS_TILED, 1.0)
+    _check(lib, lib.gdn_qkv_prologue(ctypes.byref(shape), _ptr(x), _ptr(conv_weight), _ptr(conv_state),
+                                     _ptr(q), _ptr(k), _ptr(v), float(eps), _stream_handle(stream)))
+    return q, k, v

@@ -19,7 +19,8 @@ LIBRARY = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
 
 SOURCES = ["gdn_abi.cpp", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_prefill_mfma.hip",
-           "gdn_prefill_chunk.hip", "gdn_prefill_scan.hip", "gdn_norm.hip"]
+           "gdn_prefill_chunk.hip", "gdn_prefill_scan.hip", "gdn_norm.hip",
+           "gdn_prologue.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -247,6 +247,53 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *s, float *o, const void *gate, con
     return GDN_OK;
 }
 
+gdn_status gdn_qkv_prologue(const gdn_shape *s, const void *x, const float *conv_weight, float *conv_state,
+                            void *q, void *k, void *v, float eps, void *stream) {
+    GDN_TRY(check_common(s));
+    if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
+    const int d = s->head_dim_k;
+    if (s->head_dim_v != d) return fail(GDN_ERR_UNSUPPORTED, "dk != dv (%d, %d) is not supported", d, s->head_dim_v);
+    if (d != 16 && d != 32 && d != 64 && d != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "qkv_prologue supports head_dim 16, 32, 64 or 128 (got %d)", d);
+    if (!std::isfinite(eps) || !(eps > 0.0f)) return fail(GDN_ERR_INVALID_ARG, "eps must be finite and > 0");
+    const int64_t B = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
+    if (T == 0) return GDN_OK;
+    const bool bf16 = s->qkv_dtype == GDN_DTYPE_BF16;
+    const int64_t esz = bf16 ? 2 : 4, C = (2 * Hk + Hv) * d;
+    GDN_TRY(check_ptr(x, "x", 16));
+    GDN_TRY(check_ptr(conv_weight, "conv_weight", 16));
+    if (conv_state) GDN_TRY(check_ptr(conv_state, "conv_state", 16));
+    GDN_TRY(check_ptr(q, "q", 16));
+    GDN_TRY(check_ptr(k, "k", 16));
+    GDN_TRY(check_ptr(v, "v", 16));
+    const Range ins[] = {range("x", x, B * T * C * esz), range("conv_weight", conv_weight, C * 4 * 4),
+                         range("conv_state", conv_state, conv_state ? B * 3 * C * 4 : 0)};
+    const Range outs[] = {range("q", q, B * Hk * T * d * esz), range("k", k, B * Hk * T * d * esz),
+                          range("v", v, B * Hv * T * d * esz)};
+    GDN_TRY(check_no_overlap(outs, 3, ins, 3));
+    GDN_TRY(check_no_overlap(outs, 1, outs + 1, 2));
+    GDN_TRY(check_no_overlap(outs + 1, 1, outs + 2, 1));
+    const Range st[] = {range("conv_state", conv_state, conv_state ? B * 3 * C * 4 : 0)};
+    GDN_TRY(check_no_overlap(st, 1, ins, 2));
+    gdn::PrologueParams p;
+    p.x = x;
+    p.conv_weight = conv_weight;
+    p.conv_state = conv_state;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.B = s->batch;
+    p.T = s->seq_len;
+    p.Hk = s->num_k_heads;
+    p.Hv = s->num_v_heads;
+    p.D = d;
+    p.bf16 = bf16;
+    p.eps = eps;
+    const hipError_t err = gdn::launch_qkv_prologue(p, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(GDN_ERR_HIP, "qkv_prologue launch failed: %s", hipGetErrorString(err));
+    return GDN_OK;
+}
+
 gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
                       const float *beta, float *state, float *o, void *stream) {
     GDN_TRY(check_common(s));

@@ -56,6 +56,18 @@ struct NormParams {
 };
 hipError_t launch_gated_rmsnorm(const NormParams &p, hipStream_t stream);
 
+// Causal conv + SiLU, q | k | v split and q/k L2 normalisation (4-tap kernel).
+struct PrologueParams {
+    const void *x;            // [B][T][(2 Hk + Hv) D] bf16 bits or float
+    const float *conv_weight; // [(2 Hk + Hv) D][4]
+    float *conv_state;        // [B][3][(2 Hk + Hv) D] in/out, or nullptr (zero rows, not written)
+    void *q, *k, *v;          // [B][Hk][T][D], [B][Hk][T][D], [B][Hv][T][D] in x's type
+    int32_t B, T, Hk, Hv, D;
+    bool bf16;
+    float eps;
+};
+hipError_t launch_qkv_prologue(const PrologueParams &p, hipStream_t stream);
+
 // Token segments of a bf16 prefill with chunk 32 or 64: `count` segments of `chunks` chunks
 // (the last may be shorter); the workspace holds one segment's chunk data and, at byte
 // `state_offset`, room for the state carried between segments (`bytes` in all).

@@ -162,6 +162,30 @@ const char *gdn_last_error(void);
 gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, float *o, const void *gate, const float *weight,
                              float eps, void *stream);
 
+/*
+ * Input prologue of the scan in one pass: the causal depthwise convolution
+ * with SiLU and the q | k | v split with per-head L2 normalisation (the
+ * causal_conv_silu and gdn_qkv tests on the "27b 935/47" compare page). With
+ * window = the 3 conv_state rows before t = 0 followed by the rows of x,
+ *     y[b][t][c] = silu(sum_{i<4} window[b][t + i][c] * conv_weight[c][i])
+ * channels [0, Hk d) of y are q, [Hk d, 2 Hk d) k and the rest v, in heads of
+ * d; each q and k head is scaled by 1 / sqrt(sum of its squares + eps). The
+ * outputs are in gdn_prefill's layouts (key heads are not repeated for the
+ * value heads and q is not scaled by 1/sqrt(d): gdn_prefill does both).
+ *   x            [B][T][(2 Hk + Hv) d]  qkv_dtype (shape->seq_len = T)
+ *   conv_weight  [(2 Hk + Hv) d][4]     float32
+ *   conv_state   [B][3][(2 Hk + Hv) d]  float32, read and replaced by the last
+ *                                       3 window rows (what continues the
+ *                                       sequence), or NULL: zero rows, not written
+ *   q, k         [B][Hk][T][d]          qkv_dtype, outputs
+ *   v            [B][Hv][T][d]          qkv_dtype, output
+ *   eps          finite, > 0 (the pages use 1e-6)
+ * Supported: d in {16, 32, 64, 128}. Outputs must not overlap each other or
+ * any input. With T = 0 nothing is read or written.
+ */
+gdn_status gdn_qkv_prologue(const gdn_shape *shape, const void *x, const float *conv_weight, float *conv_state,
+                            void *q, void *k, void *v, float eps, void *stream);
+
 /* GDN_ABI_VERSION of the built library. */
 int gdn_abi_version(void);
 

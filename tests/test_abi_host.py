@@ -208,3 +208,22 @@ def test_gated_rmsnorm_rejects(lib, bnd):
     assert _norm(lib, shape, weight=7 * GB + 512) == 1 and "o overlaps weight" in _err(lib)
     # no rows: nothing to check or launch
     assert _norm(lib, _shape(bnd, seq_len=0), o=None) == 0
+
+
+def _prologue(lib, shape, x=1 * GB, w=2 * GB, st=3 * GB, q=4 * GB, k=5 * GB, v=6 * GB, eps=1e-6):
+    return lib.gdn_qkv_prologue(ctypes.byref(shape), x, w, st, q, k, v, ctypes.c_float(eps), None)
+
+
+def test_qkv_prologue_rejects(lib, bnd):
+    shape = _shape(bnd, seq_len=10)
+    assert _prologue(lib, _shape(bnd, seq_len=10, head_dim=48)) == 2 and "head_dim" in _err(lib)
+    assert _prologue(lib, shape, eps=0.0) == 1 and "eps" in _err(lib)
+    assert _prologue(lib, shape, eps=float("inf")) == 1 and "eps" in _err(lib)
+    assert _prologue(lib, shape, x=None) == 1 and "x is NULL" in _err(lib)
+    assert _prologue(lib, shape, w=None) == 1 and "conv_weight is NULL" in _err(lib)
+    assert _prologue(lib, shape, v=None) == 1 and "v is NULL" in _err(lib)
+    assert _prologue(lib, shape, q=4 * GB + 8) == 1 and "aligned" in _err(lib)
+    assert _prologue(lib, shape, k=4 * GB + 512) == 1 and "overlaps" in _err(lib)
+    assert _prologue(lib, shape, q=1 * GB + 64) == 1 and "q overlaps x" in _err(lib)
+    assert _prologue(lib, shape, st=2 * GB + 16) == 1 and "conv_state overlaps conv_weight" in _err(lib)
+    assert _prologue(lib, _shape(bnd, seq_len=0), x=None) == 0  # nothing to do
