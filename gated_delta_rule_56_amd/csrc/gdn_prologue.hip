@@ -24,13 +24,11 @@ constexpr int kThreads = 256;
 constexpr int kTile = 64;  // tokens per workgroup
 constexpr int kTaps = 4;
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu with the hardware reciprocal (about 1 ulp): the exact division costs about ten
+// instructions, and this kernel evaluates one silu per channel and token
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
-// float -> bfloat16 bits, round to nearest even
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 template <bool kBf16>
 __device__ __forceinline__ void load8(const void *base, int64_t idx, float *out) {
@@ -52,10 +50,10 @@ __device__ __forceinline__ void load8(const void *base, int64_t idx, float *out)
 template <bool kBf16>
 __device__ __forceinline__ void store8(void *base, int64_t idx, const float *y) {
     if constexpr (kBf16) {
-        u16x8 u;
+        bf16x8 h;  // round to nearest even (gfx950 converts two values per instruction)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = f32_to_bf16_bits(y[e]);
-        *reinterpret_cast<u16x8 *>(static_cast<uint16_t *>(base) + idx) = u;
+        for (int e = 0; e < 8; ++e) h[e] = (__bf16)y[e];
+        *reinterpret_cast<u16x8 *>(static_cast<uint16_t *>(base) + idx) = __builtin_bit_cast(u16x8, h);
     } else {
         *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + idx) = f32x4{y[0], y[1], y[2], y[3]};
         *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + idx + 4) = f32x4{y[4], y[5], y[6], y[7]};
@@ -71,8 +69,9 @@ __global__ __launch_bounds__(kThreads) void gdn_qkv_prologue_kernel(ProloguePara
 
     const int H3 = 2 * p.Hk + p.Hv;
     const int ntile = (p.T + kTile - 1) / kTile;
-    const int tile = blockIdx.x % ntile;
-    const int hd = (blockIdx.x / ntile) % H3;
+    // heads vary fastest, so that the workgroups in flight together read whole token rows of x
+    const int hd = blockIdx.x % H3;
+    const int tile = (blockIdx.x / H3) % ntile;
     const int b = blockIdx.x / (ntile * H3);
     const int64_t C = (int64_t)H3 * D;
     const int t0 = tile * kTile;
@@ -125,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void gdn_qkv_prologue_kernel(ProloguePara
             for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
 #pragma unroll
             for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-            const float f = 1.0f / sqrtf(ss + p.eps);
+            const float f = __builtin_amdgcn_rsqf(ss + p.eps);
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] *= f;
         }
