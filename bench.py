@@ -166,6 +166,30 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the decode sequence (every pre-generated step, state in place) captured in one HIP graph
+    dstate_g = state.clone()
+    do_g = torch.empty((nsteps_dec,) + tuple(do.shape), dtype=torch.float32, device=dev)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for s in range(nsteps_dec):
+                binding.decode(dq[s], dk[s], dv[s], dg[s], db[s], dstate_g, scale=dx.scale, o=do_g[s])
+    stream.wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(1, args.steps // 10))]
+    for e in gev:
+        e[0].record(stream)
+        graph.replay()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    dgraph_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in gev])) / nsteps_dec
+    if not torch.isfinite(dstate_g).all():
+        raise RuntimeError("non-finite state after the captured decode sequence")
+    del graph, dstate_g, do_g
+
     # the gated RMSNorm epilogue on the prefill output (1M rows of 128 floats, bf16 gate)
     nrm = inputs.generate_norm(po.shape, "bf16", seed=pw.seed + 100)
     ngate = bf(nrm.gate_bits)
@@ -276,6 +300,13 @@ def main():
             "algorithmic_bytes_per_launch": d_bytes,
             "sequence_updates_per_s": dB / (d_avg * 1e-3),
             "head_state_updates_per_s": dB * dHv / (d_avg * 1e-3),
+            "graph": {
+                "what": f"{nsteps_dec} consecutive in-place steps captured in one HIP graph, per step",
+                "avg_step_ms": dgraph_ms,
+                "achieved": d_bytes / (dgraph_ms * 1e-3) / 1e9,
+                "frac": d_bytes / (dgraph_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "sequence_updates_per_s": dB / (dgraph_ms * 1e-3),
+            },
         },
         "gated_rmsnorm": {
             "kernel": "gdn_gated_rmsnorm_kernel<128, bf16 gate> on the prefill output (separate pass)",

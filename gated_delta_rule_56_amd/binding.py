@@ -104,16 +104,26 @@ def make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, qkv_dt
                     qkv_dtype, head_map, float(scale))
 
 
+def prefill_workspace_bytes(batch: int, seq_len: int, num_k_heads: int, num_v_heads: int, head_dim: int, *,
+                            chunk: int = 64, dtype: torch.dtype = torch.bfloat16,
+                            head_map: int = GDN_HEADS_TILED) -> int:
+    """gdn_prefill_workspace_bytes for a prefill of this shape (0 when none is needed)."""
+    shape = make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk,
+                       GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, 1.0)
+    return int(load_library().gdn_prefill_workspace_bytes(ctypes.byref(shape)))
+
+
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
             initial_state: Optional[torch.Tensor] = None, *, chunk: int = 64, head_map: int = GDN_HEADS_TILED,
             scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
-            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """gdn_prefill on torch tensors.
 
     q, k [B][Hk][T][d] and v [B][Hv][T][d] (bfloat16 or float32); g, beta [B][Hv][T] float32;
     initial_state [B][Hv][d][d] float32 or None. Returns (o, final_state). Pass
-    final_state=initial_state to update a state in place.
+    final_state=initial_state to update a state in place. workspace: a uint8 device tensor of at
+    least prefill_workspace_bytes(...) bytes, or None to allocate one for this call.
     """
     lib = load_library()
     dtype = q.dtype
@@ -149,7 +159,13 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     shape = make_shape(B, T, Hk, Hv, d, chunk,
                        GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, scale)
     ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
-    workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    if workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+    else:
+        _dev_tensor(workspace, "workspace", torch.uint8)
+        if workspace.numel() < ws:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes; {ws} needed")
+        ws = workspace.numel()
     _check(lib, lib.gdn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), ws,
                                 _stream_handle(stream)))
