@@ -51,10 +51,10 @@ def prefill_bytes(B, T, Hk, Hv, d, qkv_bytes=2, init_state=False) -> int:
     return qk + v + gb + o + st
 
 
-def decode_bytes(B, Hk, Hv, d, qkv_bytes=2) -> int:
-    """Minimum HBM bytes of one decode step: the fp32 state read and written,
-    q, k, v, g, beta read, o written."""
-    return 2 * B * Hv * d * d * 4 + 2 * B * Hk * d * qkv_bytes + B * Hv * d * qkv_bytes + 2 * B * Hv * 4 \
+def decode_bytes(B, Hk, Hv, d, qkv_bytes=2, state_bytes=4) -> int:
+    """Minimum HBM bytes of one decode step: the state read and written (fp32, or fp16
+    with state_bytes=2), q, k, v, g, beta read, o written."""
+    return 2 * B * Hv * d * d * state_bytes + 2 * B * Hk * d * qkv_bytes + B * Hv * d * qkv_bytes + 2 * B * Hv * 4 \
         + B * Hv * d * 4
 
 
@@ -190,6 +190,23 @@ def main():
         raise RuntimeError("non-finite state after the captured decode sequence")
     del graph, dstate_g, do_g
 
+    # decode on a float16 copy of the state (float32 arithmetic, the state stored in float16)
+    dstate16 = state.half()
+    for s in range(max(1, args.warmup)):
+        binding.decode(dq[s], dk[s], dv[s], dg[s], db[s], dstate16, scale=dx.scale, o=do)
+    hev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i, e in enumerate(hev):
+        s = i % nsteps_dec
+        e[0].record(stream)
+        binding.decode(dq[s], dk[s], dv[s], dg[s], db[s], dstate16, scale=dx.scale, o=do)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    d16_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in hev]))
+    d16_bytes = decode_bytes(dB, dHk, dHv, dd, state_bytes=2)
+    if not torch.isfinite(dstate16).all():
+        raise RuntimeError("non-finite float16 state")
+    del dstate16
+
     # the gated RMSNorm epilogue on the prefill output (1M rows of 128 floats, bf16 gate)
     nrm = inputs.generate_norm(po.shape, "bf16", seed=pw.seed + 100)
     ngate = bf(nrm.gate_bits)
@@ -300,6 +317,15 @@ def main():
             "algorithmic_bytes_per_launch": d_bytes,
             "sequence_updates_per_s": dB / (d_avg * 1e-3),
             "head_state_updates_per_s": dB * dHv / (d_avg * 1e-3),
+            "f16_state": {
+                "what": "the same step with the state stored in float16 (268 MB), float32 arithmetic",
+                "kernel": "gdn_decode_kernel<128, bf16, f16 state>",
+                "avg_launch_ms": d16_ms,
+                "achieved": d16_bytes / (d16_ms * 1e-3) / 1e9,
+                "frac": d16_bytes / (d16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "algorithmic_bytes_per_launch": d16_bytes,
+                "sequence_updates_per_s": dB / (d16_ms * 1e-3),
+            },
             "graph": {
                 "what": f"{nsteps_dec} consecutive in-place steps captured in one HIP graph, per step",
                 "avg_step_ms": dgraph_ms,

@@ -19,6 +19,9 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
+GDN_STATE_F32, GDN_STATE_F16 = 0, 1
+ABI_VERSION = 3
+_STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
 
 EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_gated_rmsnorm",
                     "gdn_qkv_prologue", "gdn_status_string", "gdn_last_error", "gdn_abi_version")
@@ -30,7 +33,7 @@ class GdnShape(ctypes.Structure):
                 ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int),
-                ("head_map", ctypes.c_int), ("scale", ctypes.c_float)]
+                ("head_map", ctypes.c_int), ("scale", ctypes.c_float), ("state_dtype", ctypes.c_int)]
 
 
 class GdnError(RuntimeError):
@@ -68,6 +71,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_last_error.argtypes = []
     lib.gdn_abi_version.restype = ctypes.c_int
     lib.gdn_abi_version.argtypes = []
+    if lib.gdn_abi_version() != ABI_VERSION:  # the structures above would not match the library's
+        raise ImportError(f"{path} has ABI version {lib.gdn_abi_version()}, this binding needs {ABI_VERSION}; "
+                          "rebuild it")
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -99,9 +105,16 @@ def _stream_handle(stream) -> Optional[int]:
     return s.cuda_stream
 
 
-def make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, qkv_dtype, head_map, scale):
+def make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, qkv_dtype, head_map, scale,
+               state_dtype=GDN_STATE_F32):
     return GdnShape(batch, seq_len, num_k_heads, num_v_heads, head_dim, head_dim, chunk,
-                    qkv_dtype, head_map, float(scale))
+                    qkv_dtype, head_map, float(scale), state_dtype)
+
+
+def _state_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.dtype not in _STATE_DTYPES:
+        raise TypeError(f"{name} must be a float32 or float16 tensor")
+    return _dev_tensor(t, name, t.dtype)
 
 
 def prefill_workspace_bytes(batch: int, seq_len: int, num_k_heads: int, num_v_heads: int, head_dim: int, *,
@@ -117,13 +130,16 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
             initial_state: Optional[torch.Tensor] = None, *, chunk: int = 64, head_map: int = GDN_HEADS_TILED,
             scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
-            workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """gdn_prefill on torch tensors.
 
     q, k [B][Hk][T][d] and v [B][Hv][T][d] (bfloat16 or float32); g, beta [B][Hv][T] float32;
-    initial_state [B][Hv][d][d] float32 or None. Returns (o, final_state). Pass
-    final_state=initial_state to update a state in place. workspace: a uint8 device tensor of at
-    least prefill_workspace_bytes(...) bytes, or None to allocate one for this call.
+    initial_state [B][Hv][d][d] float32 or float16, or None. Returns (o, final_state). Pass
+    final_state=initial_state to update a state in place. The states share one storage type:
+    that of the state tensors passed, else state_dtype (default float32). workspace: a uint8
+    device tensor of at least prefill_workspace_bytes(...) bytes, or None to allocate one for
+    this call.
     """
     lib = load_library()
     dtype = q.dtype
@@ -139,8 +155,14 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     Hv = v.shape[1]
     if v.shape != (B, Hv, T, d) or g.shape != (B, Hv, T) or beta.shape != (B, Hv, T):
         raise ValueError("v must be [B][Hv][T][d] and g, beta [B][Hv][T]")
+    given = [t.dtype for t in (initial_state, final_state) if t is not None]
+    if given and state_dtype is not None and state_dtype != given[0]:
+        raise TypeError(f"state_dtype {state_dtype} differs from the state tensors' {given[0]}")
+    sdt = given[0] if given else (state_dtype or torch.float32)
+    if sdt not in _STATE_DTYPES or any(t != sdt for t in given):
+        raise TypeError("the states must be float32 or float16, both of the same type")
     if initial_state is not None:
-        _dev_tensor(initial_state, "initial_state", torch.float32)
+        _state_tensor(initial_state, "initial_state")
         if initial_state.shape != (B, Hv, d, d):
             raise ValueError("initial_state must be [B][Hv][d][d]")
     if o is None:
@@ -149,15 +171,16 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     if o.shape != (B, Hv, T, d):
         raise ValueError("o must be [B][Hv][T][d]")
     if final_state is None and write_final_state:
-        final_state = torch.empty((B, Hv, d, d), dtype=torch.float32, device=q.device)
+        final_state = torch.empty((B, Hv, d, d), dtype=sdt, device=q.device)
     if final_state is not None:
-        _dev_tensor(final_state, "final_state", torch.float32)
+        _state_tensor(final_state, "final_state")
         if final_state.shape != (B, Hv, d, d):
             raise ValueError("final_state must be [B][Hv][d][d]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     shape = make_shape(B, T, Hk, Hv, d, chunk,
-                       GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, scale)
+                       GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, scale,
+                       _STATE_DTYPES[sdt])
     ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
     if workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
@@ -176,7 +199,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
            state: torch.Tensor, *, head_map: int = GDN_HEADS_TILED, scale: Optional[float] = None,
            o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """gdn_decode on torch tensors: q, k [B][Hk][d], v [B][Hv][d], g, beta [B][Hv],
-    state [B][Hv][d][d] float32 (updated in place). Returns o [B][Hv][d] float32."""
+    state [B][Hv][d][d] float32 or float16 (updated in place). Returns o [B][Hv][d] float32."""
     lib = load_library()
     dtype = q.dtype
     if dtype not in (torch.bfloat16, torch.float32):
@@ -185,7 +208,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
         _dev_tensor(t, nm, dtype)
     _dev_tensor(g, "g", torch.float32)
     _dev_tensor(beta, "beta", torch.float32)
-    _dev_tensor(state, "state", torch.float32)
+    _state_tensor(state, "state")
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3:
         raise ValueError("q, k must be [B][Hk][d] and v [B][Hv][d]")
     B, Hk, d = q.shape
@@ -198,7 +221,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     shape = make_shape(B, 1, Hk, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
-                       head_map, scale)
+                       head_map, scale, _STATE_DTYPES[state.dtype])
     _check(lib, lib.gdn_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state), _ptr(o), _stream_handle(stream)))
     return o

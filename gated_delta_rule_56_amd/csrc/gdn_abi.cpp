@@ -53,6 +53,8 @@ gdn_status check_common(const gdn_shape *s) {
         return fail(GDN_ERR_INVALID_ARG, "unknown qkv_dtype %d", (int)s->qkv_dtype);
     if (s->head_map != GDN_HEADS_TILED && s->head_map != GDN_HEADS_GROUPED)
         return fail(GDN_ERR_INVALID_ARG, "unknown head_map %d", (int)s->head_map);
+    if (s->state_dtype != GDN_STATE_F32 && s->state_dtype != GDN_STATE_F16)
+        return fail(GDN_ERR_INVALID_ARG, "unknown state_dtype %d", (int)s->state_dtype);
     if (!std::isfinite(s->scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
     if (s->head_dim_k != s->head_dim_v)
         return fail(GDN_ERR_UNSUPPORTED, "dk != dv (%d, %d) is not supported", s->head_dim_k, s->head_dim_v);
@@ -107,7 +109,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *s) {
 }
 
 gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
-                       const float *beta, const float *initial_state, float *o, float *final_state,
+                       const float *beta, const void *initial_state, float *o, void *final_state,
                        void *workspace, size_t workspace_bytes, void *stream) {
     GDN_TRY(check_common(s));
     if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
@@ -124,7 +126,9 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     const int64_t B = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
     const int64_t esz = bf16 ? 2 : 4;
     const int64_t qk_bytes = B * Hk * T * d * esz, v_bytes = B * Hv * T * d * esz;
-    const int64_t gb_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * 4, st_bytes = B * Hv * d * d * 4;
+    const bool st16 = s->state_dtype == GDN_STATE_F16;
+    const int64_t gb_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * 4;
+    const int64_t st_bytes = B * Hv * d * d * (st16 ? 2 : 4);
     if (T > 0) {
         GDN_TRY(check_ptr(q, "q", 16));
         GDN_TRY(check_ptr(k, "k", 16));
@@ -167,6 +171,7 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     p.D = d;
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
+    p.init_f16 = p.final_f16 = st16;
     const bool two_pass = bf16 && s->chunk != 16;
     const size_t ws_need = two_pass ? gdn::prefill_workspace_bytes(B, Hk, Hv, T, s->chunk) : 0;
     if (ws_need > 0) {
@@ -192,11 +197,11 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     } else if (T == 0) {
         err = gdn::launch_prefill_scan(p, s->chunk, workspace, st);  // copies or zeroes the state
     } else {
-        // consecutive token segments; the state is carried through final_state (in place per
-        // workgroup), or through the workspace when the caller wants no final state
+        // consecutive token segments; the state is carried through a float32 final_state (in
+        // place per workgroup), or through the workspace (float32) when the caller wants no final
+        // state or a float16 one
         const gdn::PrefillSegments sg = gdn::prefill_segments(B, Hk, Hv, T, s->chunk);
-        float *carry = final_state ? final_state
-                                   : reinterpret_cast<float *>(static_cast<char *>(workspace) + sg.state_offset);
+        void *carry = final_state && !st16 ? final_state : static_cast<char *>(workspace) + sg.state_offset;
         for (int64_t i = 0; i < sg.count && err == hipSuccess; ++i) {
             const int64_t t0 = i * sg.chunks * s->chunk;
             gdn::PrefillParams ps = p;
@@ -209,6 +214,8 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
             ps.o = o + t0 * d;
             ps.init_state = i == 0 ? initial_state : carry;
             ps.final_state = i == sg.count - 1 ? final_state : carry;
+            ps.init_f16 = i == 0 && st16;
+            ps.final_f16 = i == sg.count - 1 && st16;
             err = gdn::launch_chunk_prep(ps, s->chunk, workspace, st);
             if (err == hipSuccess) err = gdn::launch_prefill_scan(ps, s->chunk, workspace, st);
         }
@@ -295,7 +302,7 @@ gdn_status gdn_qkv_prologue(const gdn_shape *s, const void *x, const float *conv
 }
 
 gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
-                      const float *beta, float *state, float *o, void *stream) {
+                      const float *beta, void *state, float *o, void *stream) {
     GDN_TRY(check_common(s));
     if (s->seq_len != 1) return fail(GDN_ERR_INVALID_ARG, "decode needs seq_len == 1 (got %d)", s->seq_len);
     const int d = s->head_dim_k;
@@ -314,7 +321,8 @@ gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const vo
     const Range ins[] = {range("q", q, B * Hk * d * esz), range("k", k, B * Hk * d * esz),
                          range("v", v, B * Hv * d * esz), range("g", g, B * Hv * 4),
                          range("beta", beta, B * Hv * 4)};
-    const Range outs[] = {range("o", o, B * Hv * d * 4), range("state", state, B * Hv * d * d * 4)};
+    const bool st16 = s->state_dtype == GDN_STATE_F16;
+    const Range outs[] = {range("o", o, B * Hv * d * 4), range("state", state, B * Hv * d * d * (st16 ? 2 : 4))};
     GDN_TRY(check_no_overlap(outs, 2, ins, 5));
     if (overlaps(outs[0], outs[1])) return fail(GDN_ERR_INVALID_ARG, "o overlaps state");
 
@@ -332,6 +340,7 @@ gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const vo
     p.D = d;
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
+    p.state_f16 = st16;
     const hipError_t err = gdn::launch_decode(p, bf16, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
     return GDN_OK;

@@ -1,5 +1,5 @@
 // Batched single-token gated delta rule step: a streaming, in-place update of
-// fp32 states in HBM.
+// float32 or float16 states in HBM (float32 arithmetic either way).
 //
 // For each (b, h) and each state row i (value dimension), with alpha = exp(g):
 //   r_i = S[i,:] . k,  p_i = S[i,:] . q
@@ -11,9 +11,9 @@
 // reference test (compare page "27b 935/47", gated_delta_decode test), which
 // reads the output off the pre-update state as alpha S q + delta (k . q).
 //
-// Mapping: one workgroup (4 waves) per (b, h); a row of D floats is spread over
-// D/4 lanes holding 16 bytes each, so a wave covers 256 contiguous bytes per
-// access (fully coalesced 128-byte lines). Each lane first issues all of its
+// Mapping: one workgroup (4 waves) per (b, h); a state row is spread over
+// lanes holding 16 bytes each (4 float32 or 8 float16 values; 8 bytes for
+// float16 at D = 32), so each access of a wave covers whole 128-byte lines. Each lane first issues all of its
 // row loads (D/4 * 16 bytes per lane for D = 128) to keep HBM busy, then
 // reduces the two dot products across the row's lanes with xor shuffles and
 // streams the updated rows back with non-temporal stores.
@@ -34,18 +34,41 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t *p, int64_t 
     return bf16_bits_to_f32(p[i]);
 }
 
-template <typename T>
-__device__ __forceinline__ f32x4 load4(const T *p, int64_t i);
-template <>
-__device__ __forceinline__ f32x4 load4<float>(const float *p, int64_t i) {
-    return *reinterpret_cast<const f32x4 *>(p + i);
+// N consecutive q / k values (float32 or bfloat16 bits) as floats
+template <int N, typename T>
+__device__ __forceinline__ void load_vec(const T *p, int64_t i, float *out) {
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int j = 0; j < N; j += 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(p + i + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[j + e] = a[e];
+        }
+    } else if constexpr (N == 8) {
+        const u16x8 u = *reinterpret_cast<const u16x8 *>(p + i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = bf16_bits_to_f32(u[e]);
+    } else {
+        const u16x4 u = *reinterpret_cast<const u16x4 *>(p + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = bf16_bits_to_f32(u[e]);
+    }
 }
-template <>
-__device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t *p, int64_t i) {
-    u16x4 u = *reinterpret_cast<const u16x4 *>(p + i);
-    return f32x4{bf16_bits_to_f32(u[0]), bf16_bits_to_f32(u[1]), bf16_bits_to_f32(u[2]),
-                 bf16_bits_to_f32(u[3])};
-}
+
+// N consecutive state values (float32 or float16), loaded and stored non-temporally
+template <int N, typename SD>
+struct StateRow {
+    typedef SD vec __attribute__((ext_vector_type(N)));
+    vec x;
+    __device__ __forceinline__ void load(const SD *p) { x = __builtin_nontemporal_load(reinterpret_cast<const vec *>(p)); }
+    __device__ __forceinline__ float get(int e) const { return (float)x[e]; }
+    __device__ __forceinline__ static void store(SD *p, const float *y) {
+        vec v;
+#pragma unroll
+        for (int e = 0; e < N; ++e) v[e] = (SD)y[e];  // float16: round to nearest even
+        __builtin_nontemporal_store(v, reinterpret_cast<vec *>(p));
+    }
+};
 
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
@@ -54,9 +77,16 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
-template <int D, typename T>
+// columns per lane: 16 bytes of state, except where a wave would cover more rows than
+// it owns (float16 states at D = 32)
+template <int D, typename SD>
+constexpr int cols_per_lane() { return sizeof(SD) == 2 && D >= 64 ? 8 : 4; }
+
+// T: q/k/v element (float or bfloat16 bits); SD: state element (float or _Float16)
+template <int D, typename T, typename SD>
 __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams p) {
-    constexpr int LPR = D / 4;                      // lanes per state row
+    constexpr int CPL = cols_per_lane<D, SD>();
+    constexpr int LPR = D / CPL;                    // lanes per state row
     constexpr int RPA = 64 / LPR;                   // rows per wave per access
     constexpr int ROWS_PER_WAVE = D / (kDecodeThreads / 64);
     constexpr int ITERS = ROWS_PER_WAVE / RPA;
@@ -66,26 +96,28 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
     const int b = pair / p.Hv, h = pair % p.Hv;
     const int kh = key_head(h, p.Hk, p.Hv, p.head_map);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = (lane % LPR) * 4;
+    const int col = (lane % LPR) * CPL;
     const int sub = lane / LPR;
 
     const T *qp = static_cast<const T *>(p.q) + ((int64_t)b * p.Hk + kh) * D;
     const T *kp = static_cast<const T *>(p.k) + ((int64_t)b * p.Hk + kh) * D;
     const T *vp = static_cast<const T *>(p.v) + ((int64_t)b * p.Hv + h) * D;
-    float *S = p.state + (int64_t)pair * D * D;
+    SD *S = static_cast<SD *>(p.state) + (int64_t)pair * D * D;
 
     const int row0 = wave * ROWS_PER_WAVE + sub;
-    f32x4 s[ITERS];
+    StateRow<CPL, SD> s[ITERS];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it)
-        s[it] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4 *>(S + (int64_t)(row0 + it * RPA) * D + col));
+    for (int it = 0; it < ITERS; ++it) s[it].load(S + (int64_t)(row0 + it * RPA) * D + col);
 
-    const f32x4 kv = load4<T>(kp, col);
-    const f32x4 qv = load4<T>(qp, col);
+    float kv[CPL], qv[CPL];
+    load_vec<CPL>(kp, col, kv);
+    load_vec<CPL>(qp, col, qv);
     const float alpha = __expf(p.g[pair]);
     const float beta = p.beta[pair];
-    const float kq = row_sum<LPR>(kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3]);
+    float kq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) kq += kv[e] * qv[e];
+    kq = row_sum<LPR>(kq);
     const float kappa = p.scale * kq;
     const float as = alpha * p.scale;
 
@@ -95,28 +127,37 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
 
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-        const f32x4 x = s[it];
-        float rk = x[0] * kv[0] + x[1] * kv[1] + x[2] * kv[2] + x[3] * kv[3];
-        float rq = x[0] * qv[0] + x[1] * qv[1] + x[2] * qv[2] + x[3] * qv[3];
+        float rk = 0.0f, rq = 0.0f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            rk += s[it].get(e) * kv[e];
+            rq += s[it].get(e) * qv[e];
+        }
         rk = row_sum<LPR>(rk);
         rq = row_sum<LPR>(rq);
         const float delta = beta * (vrow[it] - alpha * rk);
-        const f32x4 y = f32x4{alpha * x[0] + delta * kv[0], alpha * x[1] + delta * kv[1],
-                              alpha * x[2] + delta * kv[2], alpha * x[3] + delta * kv[3]};
+        float y[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) y[e] = alpha * s[it].get(e) + delta * kv[e];
         const int row = row0 + it * RPA;
-        __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(S + (int64_t)row * D + col));
+        StateRow<CPL, SD>::store(S + (int64_t)row * D + col, y);
         if (col == 0) p.o[(int64_t)pair * D + row] = as * rq + delta * kappa;
     }
 }
 
+template <int D, typename T>
+hipError_t launch_dt(const DecodeParams &p, hipStream_t stream) {
+    dim3 grid((unsigned)(p.B * p.Hv)), block(kDecodeThreads);
+    if (p.state_f16)
+        hipLaunchKernelGGL((gdn_decode_kernel<D, T, _Float16>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gdn_decode_kernel<D, T, float>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const DecodeParams &p, bool bf16, hipStream_t stream) {
-    dim3 grid((unsigned)(p.B * p.Hv)), block(kDecodeThreads);
-    if (bf16)
-        hipLaunchKernelGGL((gdn_decode_kernel<D, uint16_t>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((gdn_decode_kernel<D, float>), grid, block, 0, stream, p);
-    return hipGetLastError();
+    return bf16 ? launch_dt<D, uint16_t>(p, stream) : launch_dt<D, float>(p, stream);
 }
 
 }  // namespace

@@ -43,4 +43,21 @@ __device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
     return f16x4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
 }
 
+// 4 consecutive state values at element index i of a float32 or float16 state.
+__device__ __forceinline__ f32x4 load_state4(const void *base, int64_t i, bool f16) {
+    if (f16) {
+        const f16x4 h = *reinterpret_cast<const f16x4 *>(static_cast<const _Float16 *>(base) + i);
+        return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    }
+    return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + i);
+}
+
+// ... and stored, float16 rounded to nearest even.
+__device__ __forceinline__ void store_state4(void *base, int64_t i, f32x4 v, bool f16) {
+    if (f16)
+        *reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(base) + i) = to_f16x4(v);
+    else
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + i) = v;
+}
+
 }  // namespace gdn

@@ -13,15 +13,16 @@ struct PrefillParams {
     const void *v;             // [B][Hv][T][D]
     const float *g;            // [B][Hv][T]
     const float *beta;         // [B][Hv][T]
-    const float *init_state;   // [B][Hv][D][D] or nullptr (zero state)
+    const void *init_state;    // [B][Hv][D][D] f32 (f16 when init_f16), or nullptr (zero state)
     float *o;                  // [B][Hv][T][D]
-    float *final_state;        // [B][Hv][D][D] or nullptr
+    void *final_state;         // [B][Hv][D][D] f32 (f16 when final_f16), or nullptr
     int32_t B, T, Hk, Hv, D;   // T: tokens processed by this launch
     int32_t Ts;                // tokens between consecutive (b, head) sequences in q, k, v, g, beta
                                // and o (T, or more when the launch covers a window of a longer
                                // sequence and the pointers are offset to the window's start)
     int32_t head_map;          // 0 tiled (h % Hk), 1 grouped (h / (Hv/Hk))
     float scale;
+    bool init_f16 = false, final_f16 = false;  // state storage types (the chunk-32/64 bf16 path only)
 };
 
 struct DecodeParams {
@@ -30,11 +31,12 @@ struct DecodeParams {
     const void *v;             // [B][Hv][D]
     const float *g;            // [B][Hv]
     const float *beta;         // [B][Hv]
-    float *state;              // [B][Hv][D][D], in place
+    void *state;               // [B][Hv][D][D] f32 (f16 when state_f16), in place
     float *o;                  // [B][Hv][D]
     int32_t B, Hk, Hv, D;
     int32_t head_map;
     float scale;
+    bool state_f16 = false;
 };
 
 // bf16 q/k/v, D = 128, chunk 16: single fused chunked WY kernel on fp16 MFMA.

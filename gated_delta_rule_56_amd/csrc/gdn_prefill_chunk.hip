@@ -352,7 +352,8 @@ PrefillSegments prefill_segments(int64_t B, int64_t Hk, int64_t Hv, int64_t T, i
     sg.count = (nc + seg - 1) / seg;
     sg.chunks = (nc + sg.count - 1) / sg.count;  // balanced: every segment but the last has this many
     sg.state_offset = (chunk_ws_bytes(B, Hk, Hv, sg.chunks, chunk) + 255) / 256 * 256;
-    // a carried state between segments, when the caller passes no final_state
+    // a float32 state carried between segments, for callers that pass no final_state or a
+    // float16 one
     sg.bytes = sg.count > 1 ? sg.state_offset + B * Hv * kD * kD * 4 : chunk_ws_bytes(B, Hk, Hv, sg.chunks, chunk);
     return sg;
 }

@@ -69,7 +69,10 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
 
     for (int e = tid; e < kRows * D; e += kF32Threads) {
         const int i = e / D, j = e % D;
-        S[i * L::QP + j] = p.init_state ? p.init_state[sbase + (int64_t)i * D + j] : 0.0f;
+        const int64_t si = sbase + (int64_t)i * D + j;
+        S[i * L::QP + j] = !p.init_state ? 0.0f
+                           : p.init_f16  ? (float)static_cast<const _Float16 *>(p.init_state)[si]
+                                         : static_cast<const float *>(p.init_state)[si];
     }
 
     for (int t0 = 0; t0 < T; t0 += C) {
@@ -185,7 +188,11 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
     if (p.final_state) {
         for (int e = tid; e < kRows * D; e += kF32Threads) {
             const int i = e / D, j = e % D;
-            p.final_state[sbase + (int64_t)i * D + j] = S[i * L::QP + j];
+            const int64_t si = sbase + (int64_t)i * D + j;
+            if (p.final_f16)
+                static_cast<_Float16 *>(p.final_state)[si] = (_Float16)S[i * L::QP + j];
+            else
+                static_cast<float *>(p.final_state)[si] = S[i * L::QP + j];
         }
     }
 }

@@ -37,8 +37,8 @@
  * synchronises. No C++ exception crosses this interface. Non-finite data is
  * not detected: it propagates into the outputs.
  *
- * Precision: g, beta, the states and o are float32. q/k/v are float32 or
- * bfloat16. The bfloat16 path runs its matrix products on fp16 MFMA operands
+ * Precision: g, beta and o are float32; the states are float32, or float16
+ * when shape->state_dtype says so (below). q/k/v are float32 or bfloat16. The bfloat16 path runs its matrix products on fp16 MFMA operands
  * with fp32 accumulation (bfloat16 inputs convert exactly while their
  * magnitudes stay within fp16 range, about 6e-5 .. 6.5e4); the float32 path
  * computes in fp32 throughout. Results depend on the chunk length through the
@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -68,6 +68,20 @@ typedef enum {
     GDN_DTYPE_F32 = 0,  /* q, k, v are float32 */
     GDN_DTYPE_BF16 = 1  /* q, k, v are bfloat16 */
 } gdn_dtype;
+
+/*
+ * Storage type of the states (prefill initial and final state, decode state). The
+ * recurrence always runs in float32; a float16 state is widened on load and rounded
+ * to nearest-even float16 when written, which halves the state traffic of decode.
+ * The gated delta decode and prefill tests on page "27b 935/47" hold the
+ * recurrent state in float16 (the decode test rounds its expected next state
+ * back to float16). float16 covers magnitudes up to 65504: a state beyond that
+ * becomes infinite.
+ */
+typedef enum {
+    GDN_STATE_F32 = 0,
+    GDN_STATE_F16 = 1
+} gdn_state_dtype;
 
 typedef enum {
     GDN_HEADS_TILED = 0,   /* value head h reads key head h % Hk (the pages' repeat of key heads) */
@@ -85,6 +99,7 @@ typedef struct {
     gdn_dtype qkv_dtype;  /* element type of q, k, v */
     gdn_head_map head_map;
     float scale;          /* o_t = S_t (scale * q_t); must be finite */
+    gdn_state_dtype state_dtype; /* element type of the states */
 } gdn_shape;
 
 /*
@@ -92,6 +107,8 @@ typedef struct {
  *   bfloat16: dk = dv = 128; C in {16, 32, 64}.
  *   float32:  dk = dv in {16, 32, 64, 128}; C in {16, 32, 64}.
  *   decode:   dk = dv in {32, 64, 128}, either dtype.
+ *   float16 states: decode (any of the above) and the bfloat16 prefill with
+ *   C in {32, 64}.
  */
 
 /*
@@ -112,17 +129,17 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
  *   q, k           [B][Hk][T][dk]   qkv_dtype
  *   v              [B][Hv][T][dv]   qkv_dtype
  *   g, beta        [B][Hv][T]       float32 (log-decay and write strength)
- *   initial_state  [B][Hv][dv][dk]  float32, or NULL for a zero state
+ *   initial_state  [B][Hv][dv][dk]  state_dtype, or NULL for a zero state
  *   o              [B][Hv][T][dv]   float32, output; must not overlap any input
- *   final_state    [B][Hv][dv][dk]  float32, output, or NULL to skip; may be
+ *   final_state    [B][Hv][dv][dk]  state_dtype, output, or NULL to skip; may be
  *                                   the same pointer as initial_state (in place)
  *   workspace      device scratch of gdn_prefill_workspace_bytes(shape) bytes
  * A ragged batch passes every sequence padded to the common T with beta = 0,
  * g = 0 (and zero q/k/v) on the padded steps, which leave the state unchanged.
  */
 gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, const void *v,
-                       const float *g, const float *beta, const float *initial_state,
-                       float *o, float *final_state, void *workspace, size_t workspace_bytes,
+                       const float *g, const float *beta, const void *initial_state,
+                       float *o, void *final_state, void *workspace, size_t workspace_bytes,
                        void *stream);
 
 /*
@@ -131,11 +148,11 @@ gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, con
  *   q, k     [B][Hk][dk]       qkv_dtype
  *   v        [B][Hv][dv]       qkv_dtype
  *   g, beta  [B][Hv]           float32
- *   state    [B][Hv][dv][dk]   float32, read and overwritten
+ *   state    [B][Hv][dv][dk]   state_dtype, read and overwritten
  *   o        [B][Hv][dv]       float32, output; must not overlap any input or the state
  */
 gdn_status gdn_decode(const gdn_shape *shape, const void *q, const void *k, const void *v,
-                      const float *g, const float *beta, float *state, float *o, void *stream);
+                      const float *g, const float *beta, void *state, float *o, void *stream);
 
 /* Static text for a status code. */
 const char *gdn_status_string(gdn_status status);

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib, bnd):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(1) == b"invalid argument"
     assert lib.gdn_status_string(2) == b"unsupported configuration"
@@ -85,6 +85,7 @@ def _err(lib):
     ("head_dim", 96, 2, "head_dim"),
     ("qkv_dtype", 7, 1, "qkv_dtype"),
     ("head_map", 2, 1, "head_map"),
+    ("state_dtype", 2, 1, "state_dtype"),
     ("scale", float("nan"), 1, "scale"),
     ("scale", float("inf"), 1, "scale"),
 ])
@@ -124,6 +125,19 @@ def test_prefill_rejects_overlaps(lib, bnd):
     assert _prefill(lib, shape, sf=ADDR["q"]) == 1 and "final_state overlaps q" in _err(lib)
     assert _prefill(lib, shape, sf=ADDR["o"] + 1024) == 1 and "final_state overlaps o" in _err(lib)
     assert _prefill(lib, shape, sf=ADDR["s0"] + 4096) == 1 and "partially overlaps" in _err(lib)
+
+
+def test_state_bytes_follow_state_dtype(lib, bnd):
+    """A float16 state occupies half the bytes: a final state right after a float16 initial
+    state passes the overlap checks (the call then stops at the missing workspace), the same
+    placement with float32 states overlaps."""
+    st16 = 1 * 4 * 128 * 128 * 2
+    f16 = _shape(bnd, state_dtype=bnd.GDN_STATE_F16)
+    assert _prefill(lib, f16, sf=ADDR["s0"] + st16) == 1 and "workspace is NULL" in _err(lib)
+    assert _prefill(lib, _shape(bnd), sf=ADDR["s0"] + st16) == 1 and "partially overlaps" in _err(lib)
+    assert _prefill(lib, f16, sf=ADDR["s0"] + st16 - 16) == 1 and "partially overlaps" in _err(lib)
+    assert _decode(lib, _shape(bnd, seq_len=1, state_dtype=bnd.GDN_STATE_F16), o=ADDR["s0"] + st16 - 16) == 1
+    assert "o overlaps state" in _err(lib)
 
 
 def test_decode_rejects(lib, bnd):
