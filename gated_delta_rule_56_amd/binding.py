@@ -23,8 +23,9 @@ GDN_STATE_F32, GDN_STATE_F16 = 0, 1
 ABI_VERSION = 3
 _STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
 
-EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_decode", "gdn_gated_rmsnorm",
-                    "gdn_qkv_prologue", "gdn_status_string", "gdn_last_error", "gdn_abi_version")
+EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_varlen_workspace_bytes",
+                    "gdn_prefill_varlen", "gdn_decode", "gdn_gated_rmsnorm", "gdn_qkv_prologue",
+                    "gdn_status_string", "gdn_last_error", "gdn_abi_version")
 
 
 class GdnShape(ctypes.Structure):
@@ -59,6 +60,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
     lib.gdn_prefill.restype = ctypes.c_int
     lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.gdn_prefill_varlen_workspace_bytes.restype = SZ
+    lib.gdn_prefill_varlen_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
+    lib.gdn_prefill_varlen.restype = ctypes.c_int
+    lib.gdn_prefill_varlen.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.gdn_decode.restype = ctypes.c_int
     lib.gdn_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
@@ -192,6 +197,66 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     _check(lib, lib.gdn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), ws,
                                 _stream_handle(stream)))
+    return o, final_state
+
+
+def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                   cu_seqlens: torch.Tensor, initial_state: Optional[torch.Tensor] = None, *, chunk: int = 64,
+                   head_map: int = GDN_HEADS_TILED, scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                   final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
+                   workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gdn_prefill_varlen on torch tensors: B sequences packed along one token axis.
+
+    q, k [Hk][T][d] and v [Hv][T][d] bfloat16; g, beta [Hv][T] float32; cu_seqlens [B + 1]
+    int32 on the GPU (0 = cu[0] <= ... <= cu[B] = T); initial_state [B][Hv][d][d] float32 or
+    float16, or None. Returns (o [Hv][T][d] float32, final_state [B][Hv][d][d]).
+    """
+    lib = load_library()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, nm, torch.bfloat16)
+    _dev_tensor(g, "g", torch.float32)
+    _dev_tensor(beta, "beta", torch.float32)
+    _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("q, k must be [Hk][T][d], v [Hv][T][d] and cu_seqlens [B + 1]")
+    Hk, T, d = q.shape
+    Hv = v.shape[0]
+    B = cu_seqlens.numel() - 1
+    if v.shape != (Hv, T, d) or g.shape != (Hv, T) or beta.shape != (Hv, T):
+        raise ValueError("v must be [Hv][T][d] and g, beta [Hv][T]")
+    given = [t.dtype for t in (initial_state, final_state) if t is not None]
+    if given and state_dtype is not None and state_dtype != given[0]:
+        raise TypeError(f"state_dtype {state_dtype} differs from the state tensors' {given[0]}")
+    sdt = given[0] if given else (state_dtype or torch.float32)
+    if sdt not in _STATE_DTYPES or any(t != sdt for t in given):
+        raise TypeError("the states must be float32 or float16, both of the same type")
+    if initial_state is not None:
+        _state_tensor(initial_state, "initial_state")
+        if initial_state.shape != (B, Hv, d, d):
+            raise ValueError("initial_state must be [B][Hv][d][d]")
+    if o is None:
+        o = torch.empty((Hv, T, d), dtype=torch.float32, device=q.device)
+    _dev_tensor(o, "o", torch.float32)
+    if o.shape != (Hv, T, d):
+        raise ValueError("o must be [Hv][T][d]")
+    if final_state is None and write_final_state:
+        final_state = torch.empty((B, Hv, d, d), dtype=sdt, device=q.device)
+    if final_state is not None:
+        _state_tensor(final_state, "final_state")
+        if final_state.shape != (B, Hv, d, d):
+            raise ValueError("final_state must be [B][Hv][d][d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shape = make_shape(B, T, Hk, Hv, d, chunk, GDN_DTYPE_BF16, head_map, scale, _STATE_DTYPES[sdt])
+    ws = lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(shape))
+    if workspace is None:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _dev_tensor(workspace, "workspace", torch.uint8)
+    _check(lib, lib.gdn_prefill_varlen(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                       _ptr(workspace), workspace.numel(), _stream_handle(stream)))
     return o, final_state
 
 

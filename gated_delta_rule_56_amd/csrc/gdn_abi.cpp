@@ -224,6 +224,95 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     return GDN_OK;
 }
 
+size_t gdn_prefill_varlen_workspace_bytes(const gdn_shape *s) {
+    if (check_common(s) != GDN_OK || s->seq_len < 0) return 0;
+    if (s->qkv_dtype != GDN_DTYPE_BF16 || s->head_dim_k != 128 || (s->chunk != 32 && s->chunk != 64)) return 0;
+    return (size_t)gdn::varlen_layout(s->batch, s->num_k_heads, s->num_v_heads, s->seq_len, s->chunk).bytes;
+}
+
+gdn_status gdn_prefill_varlen(const gdn_shape *s, const int32_t *cu_seqlens, const void *q, const void *k,
+                              const void *v, const float *g, const float *beta, const void *initial_state, float *o,
+                              void *final_state, void *workspace, size_t workspace_bytes, void *stream) {
+    GDN_TRY(check_common(s));
+    if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
+    if (s->qkv_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "packed sequences need bfloat16 q/k/v");
+    if (s->chunk != 32 && s->chunk != 64)
+        return fail(GDN_ERR_UNSUPPORTED, "packed sequences need chunk 32 or 64 (got %d)", s->chunk);
+    const int d = s->head_dim_k;
+    if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "packed sequences need head_dim 128 (got %d)", d);
+    const int64_t N = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
+    if ((double)Hv * T * d > 4.0e15 || N > (1 << 24)) return fail(GDN_ERR_UNSUPPORTED, "tensor sizes overflow");
+    const bool st16 = s->state_dtype == GDN_STATE_F16;
+    const int64_t qk_bytes = Hk * T * d * 2, v_bytes = Hv * T * d * 2, gb_bytes = Hv * T * 4, o_bytes = Hv * T * d * 4;
+    const int64_t st_bytes = N * Hv * d * d * (st16 ? 2 : 4);
+    GDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", 4));
+    if (T > 0) {
+        GDN_TRY(check_ptr(q, "q", 16));
+        GDN_TRY(check_ptr(k, "k", 16));
+        GDN_TRY(check_ptr(v, "v", 16));
+        GDN_TRY(check_ptr(g, "g", 4));
+        GDN_TRY(check_ptr(beta, "beta", 4));
+        GDN_TRY(check_ptr(o, "o", 16));
+    }
+    if (initial_state) GDN_TRY(check_ptr(initial_state, "initial_state", 16));
+    if (final_state) GDN_TRY(check_ptr(final_state, "final_state", 16));
+    const gdn::VarlenLayout vl = gdn::varlen_layout(N, Hk, Hv, T, s->chunk);
+    if (vl.nchunks > 0x7fffffff / (Hk > Hv ? Hk : Hv))
+        return fail(GDN_ERR_UNSUPPORTED, "too many chunks for one launch");
+    if (!workspace) return fail(GDN_ERR_INVALID_ARG, "workspace is NULL (%lld bytes needed)", (long long)vl.bytes);
+    if ((int64_t)workspace_bytes < vl.bytes)
+        return fail(GDN_ERR_INVALID_ARG, "workspace has %zu bytes, %lld needed", workspace_bytes, (long long)vl.bytes);
+    if (!aligned(workspace, 16)) return fail(GDN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+
+    const Range ins[] = {range("q", q, T ? qk_bytes : 0), range("k", k, T ? qk_bytes : 0),
+                         range("v", v, T ? v_bytes : 0), range("g", g, T ? gb_bytes : 0),
+                         range("beta", beta, T ? gb_bytes : 0), range("cu_seqlens", cu_seqlens, (N + 1) * 4),
+                         range("initial_state", initial_state, initial_state ? st_bytes : 0)};
+    const Range outs[] = {range("o", o, T ? o_bytes : 0), range("workspace", workspace, vl.bytes)};
+    GDN_TRY(check_no_overlap(outs, 2, ins, 7));
+    if (overlaps(outs[0], outs[1])) return fail(GDN_ERR_INVALID_ARG, "o overlaps workspace");
+    if (final_state) {
+        const Range out_s[] = {range("final_state", final_state, st_bytes)};
+        GDN_TRY(check_no_overlap(out_s, 1, ins, 6));  // all but initial_state
+        GDN_TRY(check_no_overlap(out_s, 1, outs, 2));
+        if (initial_state && final_state != initial_state && overlaps(out_s[0], ins[6]))
+            return fail(GDN_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
+    }
+
+    gdn::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.init_state = initial_state;
+    p.o = o;
+    p.final_state = final_state;
+    p.B = (int32_t)N;
+    p.T = (int32_t)T;
+    p.Ts = (int32_t)T;
+    p.Hk = s->num_k_heads;
+    p.Hv = s->num_v_heads;
+    p.D = d;
+    p.head_map = (int32_t)s->head_map;
+    p.scale = s->scale;
+    p.init_f16 = p.final_f16 = st16;
+    char *wsb = static_cast<char *>(workspace);
+    p.seqs = reinterpret_cast<const int32_t *>(wsb + vl.seq_offset);
+    p.chunks = reinterpret_cast<const int32_t *>(wsb + vl.chunk_offset);
+    p.nchunks = (int32_t)vl.nchunks;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t err = gdn::launch_varlen_tables(cu_seqlens, (int32_t)N, (int32_t)T, s->chunk,
+                                               reinterpret_cast<int32_t *>(wsb + vl.seq_offset),
+                                               reinterpret_cast<int32_t *>(wsb + vl.chunk_offset),
+                                               (int32_t)vl.nchunks, st);
+    if (err == hipSuccess && T > 0) err = gdn::launch_chunk_prep(p, s->chunk, workspace, st);
+    if (err == hipSuccess) err = gdn::launch_prefill_scan(p, s->chunk, workspace, st);
+    if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
+    return GDN_OK;
+}
+
 gdn_status gdn_gated_rmsnorm(const gdn_shape *s, float *o, const void *gate, const float *weight, float eps,
                              void *stream) {
     GDN_TRY(check_common(s));

@@ -22,7 +22,12 @@ struct PrefillParams {
                                // sequence and the pointers are offset to the window's start)
     int32_t head_map;          // 0 tiled (h % Hk), 1 grouped (h / (Hv/Hk))
     float scale;
-    bool init_f16 = false, final_f16 = false;  // state storage types (the chunk-32/64 bf16 path only)
+    bool init_f16 = false, final_f16 = false;  // state storage types
+    // packed sequences (chunk-32/64 bf16 path): B sequences laid end to end in one token axis
+    // of T tokens (q, k, v, g, beta, o as for one sequence); nullptr for the padded layout
+    const int32_t *seqs = nullptr;    // [B][4]: first token, tokens, first workspace chunk, 0
+    const int32_t *chunks = nullptr;  // [nchunks][2]: first token, tokens (0: unused slot)
+    int32_t nchunks = 0;              // workspace chunks of the packed layout
 };
 
 struct DecodeParams {
@@ -69,6 +74,15 @@ struct PrologueParams {
     float eps;
 };
 hipError_t launch_qkv_prologue(const PrologueParams &p, hipStream_t stream);
+
+// Packed sequences: the workspace of gdn_prefill_varlen (chunk data for `nchunks` chunks, then
+// the sequence and chunk tables), and the launch that fills the tables from cu_seqlens.
+struct VarlenLayout {
+    int64_t nchunks, seq_offset, chunk_offset, bytes;
+};
+VarlenLayout varlen_layout(int64_t nseq, int64_t Hk, int64_t Hv, int64_t T, int chunk);
+hipError_t launch_varlen_tables(const int32_t *cu_seqlens, int32_t nseq, int32_t T, int chunk, int32_t *seqs,
+                                int32_t *chunks, int32_t nchunks, hipStream_t stream);
 
 // Token segments of a bf16 prefill with chunk 32 or 64: `count` segments of `chunks` chunks
 // (the last may be shorter); the workspace holds one segment's chunk data and, at byte

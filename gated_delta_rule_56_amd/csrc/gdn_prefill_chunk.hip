@@ -81,8 +81,10 @@ __global__ __launch_bounds__(C * 4) void gdn_chunk_prep_kernel(PrefillParams p, 
     _Float16 *Ah = reinterpret_cast<_Float16 *>(smem + L::kAh);
     _Float16 *Tm = reinterpret_cast<_Float16 *>(smem + L::kTm);
 
-    const int NC = (p.T + C - 1) / C;
-    const ChunkWs<C> wl(p.B, p.Hk, p.Hv, NC);
+    // padded layout: chunk c of sequence b at token c C; packed sequences: workspace chunk c
+    // of the one token axis, at the token the chunk table gives (tokens 0: an unused slot)
+    const int NC = p.chunks ? p.nchunks : (p.T + C - 1) / C;
+    const ChunkWs<C> wl(p.chunks ? 1 : p.B, p.Hk, p.Hv, NC);
     const int c = blockIdx.x % NC;
     const int bk = blockIdx.x / NC;  // b * Hk + key head
     const int b = bk / p.Hk, kh = bk % p.Hk;
@@ -90,7 +92,12 @@ __global__ __launch_bounds__(C * 4) void gdn_chunk_prep_kernel(PrefillParams p, 
     const int tid = threadIdx.x, lane = tid & 63;
     const int m = __builtin_amdgcn_readfirstlane(tid >> 6);  // token tile of this wave
     const int li = lane & 15, q4 = lane >> 4;
-    const int t0 = c * C, n = min(C, p.T - t0);
+    int t0 = c * C, n = min(C, p.T - t0);
+    if (p.chunks) {
+        t0 = p.chunks[2 * c];
+        n = p.chunks[2 * c + 1];
+        if (n <= 0) return;  // the whole workgroup: no barrier has been reached yet
+    }
     const int t = 16 * m + li;  // token row of this lane in the fragments below
     const bool live = t < n;
 
@@ -311,8 +318,10 @@ hipError_t launch_c(const PrefillParams &p, _Float16 *ws, hipStream_t stream) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_chunk_prep_kernel<C>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (err != hipSuccess) return err;
-    const int NC = (p.T + C - 1) / C;
-    dim3 grid((unsigned)((int64_t)p.B * p.Hk * NC)), block(C * 4);
+    const int64_t NC = p.chunks ? p.nchunks : (p.T + C - 1) / C;
+    const int64_t nb = (p.chunks ? 1 : p.B) * p.Hk * NC;
+    if (nb > 0x7fffffff) return hipErrorInvalidValue;
+    dim3 grid((unsigned)nb), block(C * 4);
     hipLaunchKernelGGL((gdn_chunk_prep_kernel<C>), grid, block, bytes, stream, p, ws);
     return hipGetLastError();
 }
@@ -360,6 +369,17 @@ PrefillSegments prefill_segments(int64_t B, int64_t Hk, int64_t Hv, int64_t T, i
 
 size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
     return (size_t)prefill_segments(B, Hk, Hv, T, chunk).bytes;
+}
+
+VarlenLayout varlen_layout(int64_t nseq, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
+    VarlenLayout v{0, 0, 0, 0};
+    if (nseq < 1 || T < 0 || (chunk != 32 && chunk != 64)) return v;
+    // every sequence rounds up to whole chunks: at most one partial chunk per sequence
+    v.nchunks = (T + chunk - 1) / chunk + nseq;
+    v.seq_offset = (chunk_ws_bytes(1, Hk, Hv, v.nchunks, chunk) + 255) / 256 * 256;
+    v.chunk_offset = v.seq_offset + (nseq * 16 + 255) / 256 * 256;
+    v.bytes = v.chunk_offset + v.nchunks * 8;
+    return v;
 }
 
 hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStream_t stream) {

@@ -190,10 +190,23 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int li = lane & 15, q4 = lane >> 4;
-    const int T = p.T;                 // tokens of this launch
-    const int64_t Ts = p.Ts;           // token stride between (b, h) sequences
+    // tokens of this sequence and where they sit: padded layout, (b, h) at token pair * Ts and
+    // workspace chunks 0 .. NC - 1 of (b, key head) / (b, h); packed sequences, sequence b at
+    // the first token and workspace chunk the sequence table gives, in the one token axis
+    int T = p.T;
+    int64_t tok = (int64_t)pair * p.Ts;                       // first token in the token-major arrays
+    int64_t wkey = (int64_t)b * p.Hk + kh, wpair = pair;      // workspace rows
+    int c0 = 0;                                               // first workspace chunk
+    if (p.seqs) {
+        const int32_t *e = p.seqs + 4 * b;
+        T = e[1];
+        tok = (int64_t)h * p.Ts + e[0];
+        wkey = kh;
+        wpair = h;
+        c0 = e[2];
+    }
     const int NC = (T + C - 1) / C;
-    const ChunkWs<C> wl(p.B, p.Hk, p.Hv, NC);
+    const ChunkWs<C> wl(p.seqs ? 1 : p.B, p.Hk, p.Hv, p.seqs ? p.nchunks : NC);
 
     if (w == 0) {
         // ================================================================ state wave
@@ -341,20 +354,20 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         constexpr int np = (kPairLines + 7) / 8, nv = C / 4;
         const int total = nk + np + nv;
         const unsigned char *wsb = reinterpret_cast<const unsigned char *>(ws);
-        const unsigned char *vb = static_cast<const unsigned char *>(p.v) + pair * Ts * kD * 2;
+        const unsigned char *vb = static_cast<const unsigned char *>(p.v) + tok * kD * 2;
         unsigned char *junk = smem + L::kJunk;
         auto touch = [&](int c) {
             const int n = min(C, T - c * C);
             for (int l0 = 0; l0 < total; l0 += 64) {
                 const int l = l0 + lane;
                 // lanes with nothing to touch repeat a line of the key block
-                const unsigned char *a = wsb + wl.key_chunk((int64_t)b * p.Hk + kh, c) * 2 + (sk % kKeyLines) * 128;
+                const unsigned char *a = wsb + wl.key_chunk(wkey, c0 + c) * 2 + (sk % kKeyLines) * 128;
                 if (l < nk) {
                     const int line = sk + S * l;
-                    if (line < kKeyLines) a = wsb + wl.key_chunk((int64_t)b * p.Hk + kh, c) * 2 + (int64_t)line * 128;
+                    if (line < kKeyLines) a = wsb + wl.key_chunk(wkey, c0 + c) * 2 + (int64_t)line * 128;
                 } else if (l < nk + np) {
                     const int line = dvb + 8 * (l - nk);
-                    if (line < kPairLines) a = wsb + wl.pair_chunk(pair, c) * 2 + (int64_t)line * 128;
+                    if (line < kPairLines) a = wsb + wl.pair_chunk(wpair, c0 + c) * 2 + (int64_t)line * 128;
                 } else if (l < total) {
                     const int line = dvb + 8 * (l - nk - np);
                     a = vb + ((int64_t)c * C + min(line >> 1, n - 1)) * kD * 2 + (line & 1) * 128;
@@ -368,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         auto store_o = [&](int c) {
             const int tp0 = c * C, np = min(C, T - tp0);
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                p.o + (pair * Ts + tp0) * kD, 0, np * kD * 4, kBufferFlags);
+                p.o + (tok + tp0) * kD, 0, np * kD * 4, kBufferFlags);
             const float *src = reinterpret_cast<const float *>(smem + L::kOst + (c & 1) * C * kRows * 4);
 #pragma unroll
             for (int i = 0; i < C / 16; ++i) {
@@ -397,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         // ================================================================ loader waves
         // Direct-to-LDS loads of chunk c (wave 1: L::kDmaK instructions, wave 5: L::kDmaT)
         const bool kload = w == 1;
-        const uint16_t *vg = static_cast<const uint16_t *>(p.v) + pair * Ts * kD + kRows * dvb;
+        const uint16_t *vg = static_cast<const uint16_t *>(p.v) + tok * kD + kRows * dvb;
         // v rows and gate vectors of chunk c into ring slot c % 4 (C / 32 + 1 instructions)
         auto issue_vg = [&](int c) {
             const int s = c % kSlots;
@@ -408,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
                 const int t = 32 * i + (lane >> 1);
                 dma16(vg + (int64_t)(t0 + min(t, last)) * kD + 8 * (lane & 1), vb + i * 1024);
             }
-            if (lane < 3 * C / 4) dma16(ws + wl.pair_chunk(pair, c) + 2 * C * C + lane * 8, smem + L::rG + s * 12 * C);
+            if (lane < 3 * C / 4) dma16(ws + wl.pair_chunk(wpair, c0 + c) + 2 * C * C + lane * 8, smem + L::rG + s * 12 * C);
         };
         // load group c: wave 1 the k tile of chunk c; wave 5 the T fragments of chunk c and the
         // v rows and gates of chunk c + 1 (one chunk earlier, because the output waves form the
@@ -416,12 +429,12 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         auto issue = [&](int c) {
             const int s = c % kSlots;
             if (kload) {
-                const _Float16 *kw = ws + wl.key_chunk((int64_t)b * p.Hk + kh, c);
+                const _Float16 *kw = ws + wl.key_chunk(wkey, c0 + c);
                 unsigned char *kb_ = smem + L::rK + s * 256 * C;
 #pragma unroll
                 for (int i = 0; i < C / 4; ++i) dma16(kw + (i * 64 + lane) * 8, kb_ + i * 1024);
             } else {
-                const _Float16 *pw = ws + wl.pair_chunk(pair, c);
+                const _Float16 *pw = ws + wl.pair_chunk(wpair, c0 + c);
                 unsigned char *tb = smem + L::rT + s * 2 * C * C;
 #pragma unroll
                 for (int m = 0; m < NT; ++m)
@@ -479,8 +492,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         float gmy[MAXT];  // gamma of token 16 m + li
         f16x8 qf[2][MAXT][4];         // q fragments, double-buffered by chunk parity
         f16x8 aqk[2][MAXT][KBC];      // A_qk fragments, double-buffered by chunk parity
-        const _Float16 *qsrc0 = ws + wl.key_chunk((int64_t)b * p.Hk + kh, 0) + C * kD + lane * 8;
-        const _Float16 *asrc0 = ws + wl.pair_chunk(pair, 0) + C * C + lane * 8;
+        const _Float16 *qsrc0 = ws + wl.key_chunk(wkey, c0) + C * kD + lane * 8;
+        const _Float16 *asrc0 = ws + wl.pair_chunk(wpair, c0) + C * C + lane * 8;
         auto load_q = [&](auto parc, int c) {
             constexpr int par = decltype(parc)::value;
             const _Float16 *src = qsrc0 + min(c, NC - 1) * ChunkWs<C>::kKeyElems;

@@ -143,6 +143,36 @@ gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, con
                        void *stream);
 
 /*
+ * Prefill of B sequences of different lengths packed end to end along one token axis,
+ * without padding: sequence i holds tokens cu_seqlens[i] .. cu_seqlens[i + 1] - 1 and runs
+ * as its own recurrence from initial state i. The result equals gdn_prefill on each
+ * sequence alone, and equals the padded ragged batch (every sequence padded to a common
+ * length with beta = 0, g = 0 steps, which leave the state unchanged: the symbolic-length
+ * prefill entry in the commit log of page "mergable fast RDNA3 Qwen 3.6") on the real tokens.
+ * shape->batch = B (number of sequences), shape->seq_len = T (packed tokens, >= 0).
+ *   cu_seqlens     [B + 1]          int32, DEVICE memory: 0 = cu[0] <= cu[1] <= ... <= cu[B] = T
+ *   q, k           [Hk][T][dk]      qkv_dtype (bfloat16 only)
+ *   v              [Hv][T][dv]      qkv_dtype
+ *   g, beta        [Hv][T]          float32
+ *   initial_state  [B][Hv][dv][dk]  state_dtype, or NULL for zero states
+ *   o              [Hv][T][dv]      float32, output
+ *   final_state    [B][Hv][dv][dk]  state_dtype, output, or NULL; may equal initial_state
+ *   workspace      device scratch of gdn_prefill_varlen_workspace_bytes(shape) bytes; it
+ *                  grows with T (about 16.4 KB per token at Hv = 32) and is not split into
+ *                  token segments
+ * Supported: bfloat16 q/k/v, dk = dv = 128, chunk 32 or 64. cu_seqlens is read on the GPU
+ * only, so its values are not validated on the host: the kernels clamp every bound into
+ * [0, T] and every length to >= 0, which keeps all accesses inside the buffers for any
+ * contents, but only a valid array gives meaningful results (tokens outside every sequence
+ * leave their o rows unwritten; overlapping sequences write the same rows).
+ */
+size_t gdn_prefill_varlen_workspace_bytes(const gdn_shape *shape);
+gdn_status gdn_prefill_varlen(const gdn_shape *shape, const int32_t *cu_seqlens, const void *q,
+                              const void *k, const void *v, const float *g, const float *beta,
+                              const void *initial_state, float *o, void *final_state, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for a batch of single tokens (shape->seq_len must be 1);
  * updates the state in place and writes the output of the updated state.
  *   q, k     [B][Hk][dk]       qkv_dtype

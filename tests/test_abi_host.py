@@ -241,3 +241,43 @@ def test_qkv_prologue_rejects(lib, bnd):
     assert _prologue(lib, shape, q=1 * GB + 64) == 1 and "q overlaps x" in _err(lib)
     assert _prologue(lib, shape, st=2 * GB + 16) == 1 and "conv_state overlaps conv_weight" in _err(lib)
     assert _prologue(lib, _shape(bnd, seq_len=0), x=None) == 0  # nothing to do
+
+
+def _varlen(lib, shape, cu=10 * GB, ws=9 * GB, nbytes=None, **over):
+    a = dict(ADDR)
+    a.update(over)
+    if nbytes is None:
+        nbytes = lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(shape))
+    return lib.gdn_prefill_varlen(ctypes.byref(shape), cu, a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
+                                  a["o"], a["sf"], ws, nbytes, None)
+
+
+def test_varlen_workspace_query(lib, bnd):
+    """Chunk data for ceil(T / C) + B chunks (one partial chunk per sequence at most), then the
+    sequence table (16 bytes per sequence) and the chunk table (8 bytes per chunk)."""
+    shape = _shape(bnd, batch=4, seq_len=692, num_k_heads=16, num_v_heads=32)
+    nch = -(-692 // 64) + 4
+    data = 2 * nch * (32 * (2 * 64 * 64 + 6 * 64) + 16 * 64 * 256)
+    seq_off = -(-data // 256) * 256
+    chunk_off = seq_off + (-(-4 * 16 // 256) * 256)
+    assert lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(shape)) == chunk_off + nch * 8
+    assert lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(_shape(bnd, chunk=16))) == 0
+    assert lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(_shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32))) == 0
+    assert lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(_shape(bnd, seq_len=0))) > 0
+
+
+def test_varlen_rejects(lib, bnd):
+    shape = _shape(bnd, batch=3, seq_len=100)
+    assert _varlen(lib, _shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32)) == 2 and "bfloat16" in _err(lib)
+    assert _varlen(lib, _shape(bnd, chunk=16)) == 2 and "chunk" in _err(lib)
+    assert _varlen(lib, _shape(bnd, head_dim=64), nbytes=1 << 30) == 2 and "head_dim" in _err(lib)
+    assert _varlen(lib, shape, cu=None) == 1 and "cu_seqlens is NULL" in _err(lib)
+    assert _varlen(lib, shape, cu=10 * GB + 2) == 1 and "aligned" in _err(lib)
+    assert _varlen(lib, shape, ws=None) == 1 and "workspace is NULL" in _err(lib)
+    need = lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(shape))
+    assert _varlen(lib, shape, nbytes=need - 1) == 1 and "needed" in _err(lib)
+    assert _varlen(lib, shape, ws=9 * GB + 8) == 1 and "aligned" in _err(lib)
+    assert _varlen(lib, shape, o=ADDR["v"] + 256) == 1 and "o overlaps v" in _err(lib)
+    assert _varlen(lib, shape, cu=ADDR["o"] + 64) == 1 and "overlaps cu_seqlens" in _err(lib)
+    assert _varlen(lib, shape, ws=ADDR["q"]) == 1 and "workspace overlaps q" in _err(lib)
+    assert _varlen(lib, shape, sf=ADDR["s0"] + 4096) == 1 and "partially overlaps" in _err(lib)
