@@ -190,18 +190,25 @@ def main():
         raise RuntimeError("non-finite state after the captured decode sequence")
     del graph, dstate_g, do_g
 
+    def time_batch(fn, n):
+        """Mean duration of n back-to-back launches, from one pair of HIP events on the launch
+        stream around all of them (per-launch event pairs add their own overhead to kernels
+        of a fraction of a millisecond)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     # decode on a float16 copy of the state (float32 arithmetic, the state stored in float16)
     dstate16 = state.half()
     for s in range(max(1, args.warmup)):
         binding.decode(dq[s], dk[s], dv[s], dg[s], db[s], dstate16, scale=dx.scale, o=do)
-    hev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i, e in enumerate(hev):
-        s = i % nsteps_dec
-        e[0].record(stream)
-        binding.decode(dq[s], dk[s], dv[s], dg[s], db[s], dstate16, scale=dx.scale, o=do)
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    d16_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in hev]))
+    d16_ms = time_batch(lambda i: binding.decode(dq[i % nsteps_dec], dk[i % nsteps_dec], dv[i % nsteps_dec],
+                                                 dg[i % nsteps_dec], db[i % nsteps_dec], dstate16,
+                                                 scale=dx.scale, o=do), args.steps)
     d16_bytes = decode_bytes(dB, dHk, dHv, dd, state_bytes=2)
     if not torch.isfinite(dstate16).all():
         raise RuntimeError("non-finite float16 state")
@@ -213,13 +220,7 @@ def main():
     nweight = torch.from_numpy(nrm.weight).to(dev)
     for _ in range(max(1, args.warmup)):
         binding.gated_rmsnorm(po, nweight, ngate)
-    nev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in nev:
-        e[0].record(stream)
-        binding.gated_rmsnorm(po, nweight, ngate)
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    norm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in nev]))
+    norm_ms = time_batch(lambda i: binding.gated_rmsnorm(po, nweight, ngate), args.steps)
     norm_bytes = po.numel() * (4 + 4 + 2) + nweight.numel() * 4
     if not torch.isfinite(po).all():
         raise RuntimeError("non-finite outputs after the gated RMSNorm")
@@ -236,20 +237,17 @@ def main():
     for _ in range(max(1, args.warmup)):
         pro = binding.qkv_prologue(xr, cw, cst, num_k_heads=Hk, num_v_heads=Hv, head_dim=d)
     del pro
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     pqkv = [torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv)]
     lib = binding.load_library()
     pshape = binding.make_shape(B, T, Hk, Hv, d, 0, binding.GDN_DTYPE_BF16, 0, 1.0)
-    for e in pev:
-        e[0].record(stream)
+
+    def prologue_call(_):
         rc = lib.gdn_qkv_prologue(ctypes.byref(pshape), xr.data_ptr(), cw.data_ptr(), cst.data_ptr(),
                                   pqkv[0].data_ptr(), pqkv[1].data_ptr(), pqkv[2].data_ptr(),
                                   ctypes.c_float(1e-6), stream.cuda_stream)
-        e[1].record(stream)
         if rc != 0:
             raise RuntimeError(lib.gdn_last_error().decode())
-    torch.cuda.synchronize()
-    pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+    pro_ms = time_batch(prologue_call, args.steps)
     pro_bytes = xr.numel() * 2 + sum(t.numel() for t in pqkv) * 2 + cw.numel() * 4 + 2 * cst.numel() * 4
     del xr, pqkv
 
