@@ -40,13 +40,14 @@ def prefill_flops_per_token_head(C: int, d: int) -> float:
     return 10.0 * C * d + 6.0 * d * d + 2.0 * C * C / 3.0
 
 
-def prefill_bytes(B, T, Hk, Hv, d, qkv_bytes=2, init_state=False) -> int:
+def prefill_bytes(B, T, Hk, Hv, d, qkv_bytes=2, init_state=False, o_bytes=4) -> int:
     """Minimum HBM bytes of one prefill launch: q, k, v read once, g, beta read,
-    o written in fp32, final state written (and the initial state read if given)."""
+    o written (fp32, or fp16 with o_bytes=2), final state written (and the initial state
+    read if given)."""
     qk = 2 * B * Hk * T * d * qkv_bytes
     v = B * Hv * T * d * qkv_bytes
     gb = 2 * B * Hv * T * 4
-    o = B * Hv * T * d * 4
+    o = B * Hv * T * d * o_bytes
     st = B * Hv * d * d * 4 * (2 if init_state else 1)
     return qk + v + gb + o + st
 
@@ -214,6 +215,14 @@ def main():
         raise RuntimeError("non-finite float16 state")
     del dstate16
 
+    # the same prefill writing float16 o, and the epilogue on those rows (generated below)
+    po16 = torch.empty(po.shape, dtype=torch.float16, device=dev)
+    for _ in range(max(1, args.warmup)):
+        binding.prefill(pq, pk, pv, pg, pb, None, chunk=pw.chunk, scale=px.scale, o=po16, final_state=psf)
+    p16_ms = time_batch(lambda i: binding.prefill(pq, pk, pv, pg, pb, None, chunk=pw.chunk, scale=px.scale,
+                                                  o=po16, final_state=psf), args.steps)
+    p16_bytes = prefill_bytes(B, T, Hk, Hv, d, o_bytes=2)
+
     # the gated RMSNorm epilogue on the prefill output (1M rows of 128 floats, bf16 gate)
     nrm = inputs.generate_norm(po.shape, "bf16", seed=pw.seed + 100)
     ngate = bf(nrm.gate_bits)
@@ -222,6 +231,13 @@ def main():
         binding.gated_rmsnorm(po, nweight, ngate)
     norm_ms = time_batch(lambda i: binding.gated_rmsnorm(po, nweight, ngate), args.steps)
     norm_bytes = po.numel() * (4 + 4 + 2) + nweight.numel() * 4
+    for _ in range(max(1, args.warmup)):
+        binding.gated_rmsnorm(po16, nweight, ngate)
+    norm16_ms = time_batch(lambda i: binding.gated_rmsnorm(po16, nweight, ngate), args.steps)
+    norm16_bytes = po16.numel() * (2 + 2 + 2) + nweight.numel() * 4
+    if not torch.isfinite(po16).all():
+        raise RuntimeError("non-finite float16 outputs after the gated RMSNorm")
+    del po16
     if not torch.isfinite(po).all():
         raise RuntimeError("non-finite outputs after the gated RMSNorm")
 
@@ -332,6 +348,16 @@ def main():
                 "sequence_updates_per_s": dB / (dgraph_ms * 1e-3),
             },
         },
+        "prefill_f16_o": {
+            "what": "the same prefill call writing o in float16 (half the o bytes)",
+            "avg_launch_ms": p16_ms,
+            "tokens_per_s": tokens / (p16_ms * 1e-3),
+            "achieved": p16_bytes / (p16_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": p16_bytes / (p16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": p16_bytes,
+        },
         "gated_rmsnorm": {
             "kernel": "gdn_gated_rmsnorm_kernel<128, bf16 gate> on the prefill output (separate pass)",
             "avg_launch_ms": norm_ms,
@@ -341,6 +367,12 @@ def main():
             "frac": norm_bytes / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": norm_bytes,
             "rows": po.numel() // po.shape[-1],
+            "f16_o": {
+                "avg_launch_ms": norm16_ms,
+                "achieved": norm16_bytes / (norm16_ms * 1e-3) / 1e9,
+                "frac": norm16_bytes / (norm16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "algorithmic_bytes_per_launch": norm16_bytes,
+            },
         },
         "qkv_prologue": {
             "kernel": "gdn_qkv_prologue_kernel<128, bf16> (conv + SiLU, q/k/v split, q/k L2 norm)",

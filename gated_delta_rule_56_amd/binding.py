@@ -20,8 +20,10 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
 GDN_STATE_F32, GDN_STATE_F16 = 0, 1
-ABI_VERSION = 3
+GDN_OUT_F32, GDN_OUT_F16 = 0, 1
+ABI_VERSION = 4
 _STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
+_OUT_DTYPES = {torch.float32: GDN_OUT_F32, torch.float16: GDN_OUT_F16}
 
 EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_varlen_workspace_bytes",
                     "gdn_prefill_varlen", "gdn_decode", "gdn_gated_rmsnorm", "gdn_qkv_prologue",
@@ -34,7 +36,8 @@ class GdnShape(ctypes.Structure):
                 ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int),
-                ("head_map", ctypes.c_int), ("scale", ctypes.c_float), ("state_dtype", ctypes.c_int)]
+                ("head_map", ctypes.c_int), ("scale", ctypes.c_float), ("state_dtype", ctypes.c_int),
+                ("o_dtype", ctypes.c_int)]
 
 
 class GdnError(RuntimeError):
@@ -111,9 +114,23 @@ def _stream_handle(stream) -> Optional[int]:
 
 
 def make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, qkv_dtype, head_map, scale,
-               state_dtype=GDN_STATE_F32):
+               state_dtype=GDN_STATE_F32, o_dtype=GDN_OUT_F32):
     return GdnShape(batch, seq_len, num_k_heads, num_v_heads, head_dim, head_dim, chunk,
-                    qkv_dtype, head_map, float(scale), state_dtype)
+                    qkv_dtype, head_map, float(scale), state_dtype, o_dtype)
+
+
+def _out_tensor(o: Optional[torch.Tensor], shape, o_dtype: torch.dtype, device) -> torch.Tensor:
+    """The output tensor: o as passed (float32 or float16, of the given shape), else a new one."""
+    if o is None:
+        if o_dtype not in _OUT_DTYPES:
+            raise TypeError("o_dtype must be torch.float32 or torch.float16")
+        o = torch.empty(shape, dtype=o_dtype, device=device)
+    if not isinstance(o, torch.Tensor) or o.dtype not in _OUT_DTYPES:
+        raise TypeError("o must be a float32 or float16 tensor")
+    _dev_tensor(o, "o", o.dtype)
+    if tuple(o.shape) != tuple(shape):
+        raise ValueError(f"o must be {list(shape)}")
+    return o
 
 
 def _state_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -136,15 +153,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
             scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
             workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
-            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            o_dtype: torch.dtype = torch.float32, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """gdn_prefill on torch tensors.
 
     q, k [B][Hk][T][d] and v [B][Hv][T][d] (bfloat16 or float32); g, beta [B][Hv][T] float32;
     initial_state [B][Hv][d][d] float32 or float16, or None. Returns (o, final_state). Pass
     final_state=initial_state to update a state in place. The states share one storage type:
-    that of the state tensors passed, else state_dtype (default float32). workspace: a uint8
-    device tensor of at least prefill_workspace_bytes(...) bytes, or None to allocate one for
-    this call.
+    that of the state tensors passed, else state_dtype (default float32). o is float32, or
+    float16 (o_dtype, or the type of the o passed). workspace: a uint8 device tensor of at
+    least prefill_workspace_bytes(...) bytes, or None to allocate one for this call.
     """
     lib = load_library()
     dtype = q.dtype
@@ -170,11 +187,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
         _state_tensor(initial_state, "initial_state")
         if initial_state.shape != (B, Hv, d, d):
             raise ValueError("initial_state must be [B][Hv][d][d]")
-    if o is None:
-        o = torch.empty((B, Hv, T, d), dtype=torch.float32, device=q.device)
-    _dev_tensor(o, "o", torch.float32)
-    if o.shape != (B, Hv, T, d):
-        raise ValueError("o must be [B][Hv][T][d]")
+    o = _out_tensor(o, (B, Hv, T, d), o_dtype, q.device)
     if final_state is None and write_final_state:
         final_state = torch.empty((B, Hv, d, d), dtype=sdt, device=q.device)
     if final_state is not None:
@@ -185,7 +198,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
         scale = 1.0 / math.sqrt(d)
     shape = make_shape(B, T, Hk, Hv, d, chunk,
                        GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, scale,
-                       _STATE_DTYPES[sdt])
+                       _STATE_DTYPES[sdt], _OUT_DTYPES[o.dtype])
     ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
     if workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
@@ -205,12 +218,13 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                    head_map: int = GDN_HEADS_TILED, scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
                    final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
                    workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
-                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                   o_dtype: torch.dtype = torch.float32, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """gdn_prefill_varlen on torch tensors: B sequences packed along one token axis.
 
     q, k [Hk][T][d] and v [Hv][T][d] bfloat16; g, beta [Hv][T] float32; cu_seqlens [B + 1]
     int32 on the GPU (0 = cu[0] <= ... <= cu[B] = T); initial_state [B][Hv][d][d] float32 or
-    float16, or None. Returns (o [Hv][T][d] float32, final_state [B][Hv][d][d]).
+    float16, or None. Returns (o [Hv][T][d] float32 or float16 (o_dtype), final_state
+    [B][Hv][d][d]).
     """
     lib = load_library()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -235,11 +249,7 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
         _state_tensor(initial_state, "initial_state")
         if initial_state.shape != (B, Hv, d, d):
             raise ValueError("initial_state must be [B][Hv][d][d]")
-    if o is None:
-        o = torch.empty((Hv, T, d), dtype=torch.float32, device=q.device)
-    _dev_tensor(o, "o", torch.float32)
-    if o.shape != (Hv, T, d):
-        raise ValueError("o must be [Hv][T][d]")
+    o = _out_tensor(o, (Hv, T, d), o_dtype, q.device)
     if final_state is None and write_final_state:
         final_state = torch.empty((B, Hv, d, d), dtype=sdt, device=q.device)
     if final_state is not None:
@@ -248,7 +258,8 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
             raise ValueError("final_state must be [B][Hv][d][d]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    shape = make_shape(B, T, Hk, Hv, d, chunk, GDN_DTYPE_BF16, head_map, scale, _STATE_DTYPES[sdt])
+    shape = make_shape(B, T, Hk, Hv, d, chunk, GDN_DTYPE_BF16, head_map, scale, _STATE_DTYPES[sdt],
+                       _OUT_DTYPES[o.dtype])
     ws = lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(shape))
     if workspace is None:
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
@@ -262,9 +273,10 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
 
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
            state: torch.Tensor, *, head_map: int = GDN_HEADS_TILED, scale: Optional[float] = None,
-           o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+           o: Optional[torch.Tensor] = None, o_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
     """gdn_decode on torch tensors: q, k [B][Hk][d], v [B][Hv][d], g, beta [B][Hv],
-    state [B][Hv][d][d] float32 or float16 (updated in place). Returns o [B][Hv][d] float32."""
+    state [B][Hv][d][d] float32 or float16 (updated in place). Returns o [B][Hv][d] float32 or
+    float16 (o_dtype, or the type of the o passed)."""
     lib = load_library()
     dtype = q.dtype
     if dtype not in (torch.bfloat16, torch.float32):
@@ -280,13 +292,11 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
     Hv = v.shape[1]
     if v.shape != (B, Hv, d) or g.shape != (B, Hv) or beta.shape != (B, Hv) or state.shape != (B, Hv, d, d):
         raise ValueError("v [B][Hv][d], g/beta [B][Hv], state [B][Hv][d][d] expected")
-    if o is None:
-        o = torch.empty((B, Hv, d), dtype=torch.float32, device=q.device)
-    _dev_tensor(o, "o", torch.float32)
+    o = _out_tensor(o, (B, Hv, d), o_dtype, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     shape = make_shape(B, 1, Hk, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
-                       head_map, scale, _STATE_DTYPES[state.dtype])
+                       head_map, scale, _STATE_DTYPES[state.dtype], _OUT_DTYPES[o.dtype])
     _check(lib, lib.gdn_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state), _ptr(o), _stream_handle(stream)))
     return o
@@ -295,11 +305,13 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
 def gated_rmsnorm(o: torch.Tensor, weight: torch.Tensor, gate: Optional[torch.Tensor] = None, *,
                   eps: float = 1e-6, stream=None) -> torch.Tensor:
     """gdn_gated_rmsnorm on torch tensors, in place: every row of the last axis of o
-    ([B][Hv][T][dv] from prefill or [B][Hv][dv] from decode, float32) becomes
+    ([B][Hv][T][dv] from prefill or [B][Hv][dv] from decode, float32 or float16) becomes
     o / sqrt(mean(o^2) + eps) * weight * silu(gate); weight [dv] float32; gate of o's shape in
     bfloat16 or float32, or None for no gate factor. Returns o."""
     lib = load_library()
-    _dev_tensor(o, "o", torch.float32)
+    if not isinstance(o, torch.Tensor) or o.dtype not in _OUT_DTYPES:
+        raise TypeError("o must be a float32 or float16 tensor")
+    _dev_tensor(o, "o", o.dtype)
     if o.dim() == 3:
         B, Hv, d = o.shape
         T = 1
@@ -319,7 +331,7 @@ def gated_rmsnorm(o: torch.Tensor, weight: torch.Tensor, gate: Optional[torch.Te
         if gate.shape != o.shape:
             raise ValueError("gate must have the shape of o")
     shape = make_shape(B, T, Hv, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
-                       GDN_HEADS_TILED, 1.0)
+                       GDN_HEADS_TILED, 1.0, o_dtype=_OUT_DTYPES[o.dtype])
     _check(lib, lib.gdn_gated_rmsnorm(ctypes.byref(shape), _ptr(o), _ptr(gate), _ptr(weight), float(eps),
                                       _stream_handle(stream)))
     return o

@@ -55,6 +55,8 @@ gdn_status check_common(const gdn_shape *s) {
         return fail(GDN_ERR_INVALID_ARG, "unknown head_map %d", (int)s->head_map);
     if (s->state_dtype != GDN_STATE_F32 && s->state_dtype != GDN_STATE_F16)
         return fail(GDN_ERR_INVALID_ARG, "unknown state_dtype %d", (int)s->state_dtype);
+    if (s->o_dtype != GDN_OUT_F32 && s->o_dtype != GDN_OUT_F16)
+        return fail(GDN_ERR_INVALID_ARG, "unknown o_dtype %d", (int)s->o_dtype);
     if (!std::isfinite(s->scale)) return fail(GDN_ERR_INVALID_ARG, "scale must be finite");
     if (s->head_dim_k != s->head_dim_v)
         return fail(GDN_ERR_UNSUPPORTED, "dk != dv (%d, %d) is not supported", s->head_dim_k, s->head_dim_v);
@@ -109,7 +111,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *s) {
 }
 
 gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
-                       const float *beta, const void *initial_state, float *o, void *final_state,
+                       const float *beta, const void *initial_state, void *o, void *final_state,
                        void *workspace, size_t workspace_bytes, void *stream) {
     GDN_TRY(check_common(s));
     if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
@@ -126,8 +128,10 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     const int64_t B = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
     const int64_t esz = bf16 ? 2 : 4;
     const int64_t qk_bytes = B * Hk * T * d * esz, v_bytes = B * Hv * T * d * esz;
-    const bool st16 = s->state_dtype == GDN_STATE_F16;
-    const int64_t gb_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * 4;
+    const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
+    if (o16 && !(bf16 && s->chunk != 16))
+        return fail(GDN_ERR_UNSUPPORTED, "float16 o needs bfloat16 q/k/v and chunk 32 or 64");
+    const int64_t gb_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * (o16 ? 2 : 4);
     const int64_t st_bytes = B * Hv * d * d * (st16 ? 2 : 4);
     if (T > 0) {
         GDN_TRY(check_ptr(q, "q", 16));
@@ -172,6 +176,7 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
     p.init_f16 = p.final_f16 = st16;
+    p.o_f16 = o16;
     const bool two_pass = bf16 && s->chunk != 16;
     const size_t ws_need = two_pass ? gdn::prefill_workspace_bytes(B, Hk, Hv, T, s->chunk) : 0;
     if (ws_need > 0) {
@@ -211,7 +216,7 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
             ps.v = static_cast<const char *>(v) + t0 * d * esz;
             ps.g = g + t0;
             ps.beta = beta + t0;
-            ps.o = o + t0 * d;
+            ps.o = static_cast<char *>(o) + t0 * d * (o16 ? 2 : 4);
             ps.init_state = i == 0 ? initial_state : carry;
             ps.final_state = i == sg.count - 1 ? final_state : carry;
             ps.init_f16 = i == 0 && st16;
@@ -231,7 +236,7 @@ size_t gdn_prefill_varlen_workspace_bytes(const gdn_shape *s) {
 }
 
 gdn_status gdn_prefill_varlen(const gdn_shape *s, const int32_t *cu_seqlens, const void *q, const void *k,
-                              const void *v, const float *g, const float *beta, const void *initial_state, float *o,
+                              const void *v, const float *g, const float *beta, const void *initial_state, void *o,
                               void *final_state, void *workspace, size_t workspace_bytes, void *stream) {
     GDN_TRY(check_common(s));
     if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
@@ -243,8 +248,9 @@ gdn_status gdn_prefill_varlen(const gdn_shape *s, const int32_t *cu_seqlens, con
     if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "packed sequences need head_dim 128 (got %d)", d);
     const int64_t N = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
     if ((double)Hv * T * d > 4.0e15 || N > (1 << 24)) return fail(GDN_ERR_UNSUPPORTED, "tensor sizes overflow");
-    const bool st16 = s->state_dtype == GDN_STATE_F16;
-    const int64_t qk_bytes = Hk * T * d * 2, v_bytes = Hv * T * d * 2, gb_bytes = Hv * T * 4, o_bytes = Hv * T * d * 4;
+    const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
+    const int64_t qk_bytes = Hk * T * d * 2, v_bytes = Hv * T * d * 2, gb_bytes = Hv * T * 4;
+    const int64_t o_bytes = Hv * T * d * (o16 ? 2 : 4);
     const int64_t st_bytes = N * Hv * d * d * (st16 ? 2 : 4);
     GDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", 4));
     if (T > 0) {
@@ -298,6 +304,7 @@ gdn_status gdn_prefill_varlen(const gdn_shape *s, const int32_t *cu_seqlens, con
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
     p.init_f16 = p.final_f16 = st16;
+    p.o_f16 = o16;
     char *wsb = static_cast<char *>(workspace);
     p.seqs = reinterpret_cast<const int32_t *>(wsb + vl.seq_offset);
     p.chunks = reinterpret_cast<const int32_t *>(wsb + vl.chunk_offset);
@@ -313,7 +320,7 @@ gdn_status gdn_prefill_varlen(const gdn_shape *s, const int32_t *cu_seqlens, con
     return GDN_OK;
 }
 
-gdn_status gdn_gated_rmsnorm(const gdn_shape *s, float *o, const void *gate, const float *weight, float eps,
+gdn_status gdn_gated_rmsnorm(const gdn_shape *s, void *o, const void *gate, const float *weight, float eps,
                              void *stream) {
     GDN_TRY(check_common(s));
     if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
@@ -328,7 +335,8 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *s, float *o, const void *gate, con
     GDN_TRY(check_ptr(weight, "weight", 16));
     if (gate) GDN_TRY(check_ptr(gate, "gate", bf16 ? 8 : 16));
     const Range ins[] = {range("gate", gate, gate ? rows * d * (bf16 ? 2 : 4) : 0), range("weight", weight, d * 4)};
-    const Range outs[] = {range("o", o, rows * d * 4)};
+    const bool o16 = s->o_dtype == GDN_OUT_F16;
+    const Range outs[] = {range("o", o, rows * d * (o16 ? 2 : 4))};
     GDN_TRY(check_no_overlap(outs, 1, ins, 2));
     gdn::NormParams p;
     p.o = o;
@@ -338,6 +346,7 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *s, float *o, const void *gate, con
     p.D = d;
     p.gate_bf16 = bf16;
     p.eps = eps;
+    p.o_f16 = o16;
     const hipError_t err = gdn::launch_gated_rmsnorm(p, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "gated_rmsnorm launch failed: %s", hipGetErrorString(err));
     return GDN_OK;
@@ -391,7 +400,7 @@ gdn_status gdn_qkv_prologue(const gdn_shape *s, const void *x, const float *conv
 }
 
 gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
-                      const float *beta, void *state, float *o, void *stream) {
+                      const float *beta, void *state, void *o, void *stream) {
     GDN_TRY(check_common(s));
     if (s->seq_len != 1) return fail(GDN_ERR_INVALID_ARG, "decode needs seq_len == 1 (got %d)", s->seq_len);
     const int d = s->head_dim_k;
@@ -410,8 +419,9 @@ gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const vo
     const Range ins[] = {range("q", q, B * Hk * d * esz), range("k", k, B * Hk * d * esz),
                          range("v", v, B * Hv * d * esz), range("g", g, B * Hv * 4),
                          range("beta", beta, B * Hv * 4)};
-    const bool st16 = s->state_dtype == GDN_STATE_F16;
-    const Range outs[] = {range("o", o, B * Hv * d * 4), range("state", state, B * Hv * d * d * (st16 ? 2 : 4))};
+    const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
+    const Range outs[] = {range("o", o, B * Hv * d * (o16 ? 2 : 4)),
+                          range("state", state, B * Hv * d * d * (st16 ? 2 : 4))};
     GDN_TRY(check_no_overlap(outs, 2, ins, 5));
     if (overlaps(outs[0], outs[1])) return fail(GDN_ERR_INVALID_ARG, "o overlaps state");
 
@@ -430,6 +440,7 @@ gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const vo
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
     p.state_f16 = st16;
+    p.o_f16 = o16;
     const hipError_t err = gdn::launch_decode(p, bf16, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
     return GDN_OK;

@@ -141,7 +141,13 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
         for (int e = 0; e < CPL; ++e) y[e] = alpha * s[it].get(e) + delta * kv[e];
         const int row = row0 + it * RPA;
         StateRow<CPL, SD>::store(S + (int64_t)row * D + col, y);
-        if (col == 0) p.o[(int64_t)pair * D + row] = as * rq + delta * kappa;
+        if (col == 0) {
+            const float oi = as * rq + delta * kappa;
+            if (p.o_f16)
+                static_cast<_Float16 *>(p.o)[(int64_t)pair * D + row] = (_Float16)oi;
+            else
+                static_cast<float *>(p.o)[(int64_t)pair * D + row] = oi;
+        }
     }
 }
 

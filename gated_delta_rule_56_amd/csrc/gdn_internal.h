@@ -14,7 +14,7 @@ struct PrefillParams {
     const float *g;            // [B][Hv][T]
     const float *beta;         // [B][Hv][T]
     const void *init_state;    // [B][Hv][D][D] f32 (f16 when init_f16), or nullptr (zero state)
-    float *o;                  // [B][Hv][T][D]
+    void *o;                   // [B][Hv][T][D] f32 (f16 when o_f16)
     void *final_state;         // [B][Hv][D][D] f32 (f16 when final_f16), or nullptr
     int32_t B, T, Hk, Hv, D;   // T: tokens processed by this launch
     int32_t Ts;                // tokens between consecutive (b, head) sequences in q, k, v, g, beta
@@ -23,6 +23,7 @@ struct PrefillParams {
     int32_t head_map;          // 0 tiled (h % Hk), 1 grouped (h / (Hv/Hk))
     float scale;
     bool init_f16 = false, final_f16 = false;  // state storage types
+    bool o_f16 = false;                        // o stored as f16 (the chunk-32/64 bf16 path)
     // packed sequences (chunk-32/64 bf16 path): B sequences laid end to end in one token axis
     // of T tokens (q, k, v, g, beta, o as for one sequence); nullptr for the padded layout
     const int32_t *seqs = nullptr;    // [B][4]: first token, tokens, first workspace chunk, 0
@@ -37,11 +38,12 @@ struct DecodeParams {
     const float *g;            // [B][Hv]
     const float *beta;         // [B][Hv]
     void *state;               // [B][Hv][D][D] f32 (f16 when state_f16), in place
-    float *o;                  // [B][Hv][D]
+    void *o;                   // [B][Hv][D] f32 (f16 when o_f16)
     int32_t B, Hk, Hv, D;
     int32_t head_map;
     float scale;
     bool state_f16 = false;
+    bool o_f16 = false;
 };
 
 // bf16 q/k/v, D = 128, chunk 16: single fused chunked WY kernel on fp16 MFMA.
@@ -53,13 +55,14 @@ hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStr
 
 // Gated RMSNorm of `rows` output rows of D floats, in place.
 struct NormParams {
-    float *o;               // [rows][D]
+    void *o;                // [rows][D] f32 (f16 when o_f16), in place
     const void *gate;       // [rows][D] bf16 bits or float, or nullptr (no gate factor)
     const float *weight;    // [D]
     int64_t rows;
     int32_t D;
     bool gate_bf16;
     float eps;
+    bool o_f16 = false;
 };
 hipError_t launch_gated_rmsnorm(const NormParams &p, hipStream_t stream);
 

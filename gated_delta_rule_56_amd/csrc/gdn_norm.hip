@@ -1,4 +1,4 @@
-// Gated RMSNorm of output rows, in place: the output epilogue that the gated
+// Gated RMSNorm of output rows (float32 or float16), in place: the output epilogue that the gated
 // delta kernels on the "27b 935/47" page apply (the q8_gated_rmsnorm test, and
 // the norm_weight / norm_eps arguments of gated_delta). For every row x of D
 // values of o:
@@ -33,9 +33,24 @@ __device__ __forceinline__ f32x4 load_gate<float>(const float *g) {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(g));
 }
 
-// GT: uint16_t (bfloat16 bits) or float gate; kGate false: no gate factor
-template <int D, typename GT, bool kGate>
-__global__ __launch_bounds__(kThreads) void gdn_gated_rmsnorm_kernel(float *o, const GT *gate, const float *weight,
+// 4 consecutive o values, float32 or float16 (rounded to nearest even on store)
+__device__ __forceinline__ f32x4 load_o4(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+__device__ __forceinline__ f32x4 load_o4(const _Float16 *p) {
+    const f16x4 h = __builtin_nontemporal_load(reinterpret_cast<const f16x4 *>(p));
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+__device__ __forceinline__ void store_o4(float *p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ void store_o4(_Float16 *p, f32x4 v) {
+    __builtin_nontemporal_store(to_f16x4(v), reinterpret_cast<f16x4 *>(p));
+}
+
+// OT: float or _Float16 o; GT: uint16_t (bfloat16 bits) or float gate; kGate false: no gate factor
+template <int D, typename OT, typename GT, bool kGate>
+__global__ __launch_bounds__(kThreads) void gdn_gated_rmsnorm_kernel(OT *o, const GT *gate, const float *weight,
                                                                      float eps, int64_t rows) {
     constexpr int LPR = D / 4;     // lanes per row
     constexpr int RPW = 64 / LPR;  // rows per wave
@@ -43,8 +58,8 @@ __global__ __launch_bounds__(kThreads) void gdn_gated_rmsnorm_kernel(float *o, c
     const int li = lane % LPR;
     const int64_t row = ((int64_t)blockIdx.x * (kThreads / 64) + w) * RPW + lane / LPR;
     if (row >= rows) return;  // whole row groups: the shuffles below stay inside a group
-    float *px = o + row * D + 4 * li;
-    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(px));
+    OT *px = o + row * D + 4 * li;
+    const f32x4 x = load_o4(px);
     float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
@@ -55,26 +70,32 @@ __global__ __launch_bounds__(kThreads) void gdn_gated_rmsnorm_kernel(float *o, c
         const f32x4 g = load_gate<GT>(gate + row * D + 4 * li);
         y = y * f32x4{silu(g[0]), silu(g[1]), silu(g[2]), silu(g[3])};
     }
-    __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(px));
+    store_o4(px, y);
 }
 
-template <int D>
-hipError_t launch_d(const NormParams &p, hipStream_t stream) {
+template <int D, typename OT>
+hipError_t launch_do(const NormParams &p, hipStream_t stream) {
     constexpr int rows_per_block = (kThreads / 64) * (64 / (D / 4));
     const int64_t blocks = (p.rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(kThreads);
+    OT *o = static_cast<OT *>(p.o);
     if (!p.gate) {
-        hipLaunchKernelGGL((gdn_gated_rmsnorm_kernel<D, float, false>), grid, block, 0, stream, p.o,
+        hipLaunchKernelGGL((gdn_gated_rmsnorm_kernel<D, OT, float, false>), grid, block, 0, stream, o,
                            static_cast<const float *>(nullptr), p.weight, p.eps, p.rows);
     } else if (p.gate_bf16) {
-        hipLaunchKernelGGL((gdn_gated_rmsnorm_kernel<D, uint16_t, true>), grid, block, 0, stream, p.o,
+        hipLaunchKernelGGL((gdn_gated_rmsnorm_kernel<D, OT, uint16_t, true>), grid, block, 0, stream, o,
                            static_cast<const uint16_t *>(p.gate), p.weight, p.eps, p.rows);
     } else {
-        hipLaunchKernelGGL((gdn_gated_rmsnorm_kernel<D, float, true>), grid, block, 0, stream, p.o,
+        hipLaunchKernelGGL((gdn_gated_rmsnorm_kernel<D, OT, float, true>), grid, block, 0, stream, o,
                            static_cast<const float *>(p.gate), p.weight, p.eps, p.rows);
     }
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const NormParams &p, hipStream_t stream) {
+    return p.o_f16 ? launch_do<D, _Float16>(p, stream) : launch_do<D, float>(p, stream);
 }
 
 }  // namespace

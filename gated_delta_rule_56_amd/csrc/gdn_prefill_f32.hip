@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
     const float *vg = static_cast<const float *>(p.v) + ((int64_t)b * p.Hv + h) * T * D;
     const float *gg = p.g + ((int64_t)b * p.Hv + h) * T;
     const float *bg = p.beta + ((int64_t)b * p.Hv + h) * T;
-    float *og = p.o + ((int64_t)b * p.Hv + h) * T * D;
+    float *og = static_cast<float *>(p.o) + ((int64_t)b * p.Hv + h) * T * D;
     const int64_t sbase = ((int64_t)pair * D + blk * kRows) * D;
 
     for (int e = tid; e < kRows * D; e += kF32Threads) {

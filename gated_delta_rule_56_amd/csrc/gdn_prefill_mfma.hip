@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_mfma_kernel(PrefillParam
     const uint16_t *vg = static_cast<const uint16_t *>(p.v) + (int64_t)pair * T * kD;
     const float *gg = p.g + (int64_t)pair * T;
     const float *bg = p.beta + (int64_t)pair * T;
-    float *og = p.o + (int64_t)pair * T * kD;
+    float *og = static_cast<float *>(p.o) + (int64_t)pair * T * kD;
 
     // ---- state fragment: S[jl][r] = state[16 dvb + li][32 w + 16 jl + 4 q4 + r]
     const int64_t srow = ((int64_t)pair * kD + kRows * dvb + li) * kD + 32 * w + 4 * q4;

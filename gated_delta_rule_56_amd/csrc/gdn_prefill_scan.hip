@@ -64,6 +64,7 @@ constexpr int kBufferFlags = 0x00020000;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int C>
 struct ScanSmem {
@@ -378,17 +379,22 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         // o rows of chunk c (staged in LDS buffer c & 1 by the output waves): lane l stores row
         // 16 i + l / 4, columns 4 (l % 4) .. + 3 of this block; rows past the end fall outside
         // the buffer range and are dropped
+        // (float16 o: the same rows and columns, rounded to nearest even, 8 bytes per lane)
+        const int osz = p.o_f16 ? 2 : 4;
         auto store_o = [&](int c) {
             const int tp0 = c * C, np = min(C, T - tp0);
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                p.o + (tok + tp0) * kD, 0, np * kD * 4, kBufferFlags);
+                static_cast<char *>(p.o) + (tok + tp0) * kD * osz, 0, np * kD * osz, kBufferFlags);
             const float *src = reinterpret_cast<const float *>(smem + L::kOst + (c & 1) * C * kRows * 4);
 #pragma unroll
             for (int i = 0; i < C / 16; ++i) {
                 const int row = 16 * i + (lane >> 2), col = 4 * (lane & 3);
                 const f32x4 v4 = *reinterpret_cast<const f32x4 *>(src + row * kRows + col);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), orsrc,
-                                                      (row * kD + kRows * dvb + col) * 4, 0, 0);
+                const int off = (row * kD + kRows * dvb + col) * osz;
+                if (p.o_f16)
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, to_f16x4(v4)), orsrc, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), orsrc, off, 0, 0);
             }
         };
         for (int c = 3; c < min(NC, kPrefetchAhead); ++c) {

@@ -37,8 +37,9 @@
  * synchronises. No C++ exception crosses this interface. Non-finite data is
  * not detected: it propagates into the outputs.
  *
- * Precision: g, beta and o are float32; the states are float32, or float16
- * when shape->state_dtype says so (below). q/k/v are float32 or bfloat16. The bfloat16 path runs its matrix products on fp16 MFMA operands
+ * Precision: g and beta are float32; o is float32, or float16 when
+ * shape->o_dtype says so; the states are float32, or float16 when
+ * shape->state_dtype says so (below). q/k/v are float32 or bfloat16. The bfloat16 path runs its matrix products on fp16 MFMA operands
  * with fp32 accumulation (bfloat16 inputs convert exactly while their
  * magnitudes stay within fp16 range, about 6e-5 .. 6.5e4); the float32 path
  * computes in fp32 throughout. Results depend on the chunk length through the
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -83,6 +84,17 @@ typedef enum {
     GDN_STATE_F16 = 1
 } gdn_state_dtype;
 
+/*
+ * Storage type of the outputs o (prefill, decode, and the gated RMSNorm's in-place rows).
+ * float16 rounds each output to nearest even (at most 2^-11 of its value), which keeps the
+ * bfloat16 path inside its 2e-3 accuracy bar while halving the bytes of o, the largest
+ * tensor a long prefill writes; bfloat16 outputs (2^-8) would not.
+ */
+typedef enum {
+    GDN_OUT_F32 = 0,
+    GDN_OUT_F16 = 1
+} gdn_out_dtype;
+
 typedef enum {
     GDN_HEADS_TILED = 0,   /* value head h reads key head h % Hk (the pages' repeat of key heads) */
     GDN_HEADS_GROUPED = 1  /* value head h reads key head h / (Hv / Hk) */
@@ -100,6 +112,7 @@ typedef struct {
     gdn_head_map head_map;
     float scale;          /* o_t = S_t (scale * q_t); must be finite */
     gdn_state_dtype state_dtype; /* element type of the states */
+    gdn_out_dtype o_dtype;       /* element type of o */
 } gdn_shape;
 
 /*
@@ -107,8 +120,9 @@ typedef struct {
  *   bfloat16: dk = dv = 128; C in {16, 32, 64}.
  *   float32:  dk = dv in {16, 32, 64, 128}; C in {16, 32, 64}.
  *   decode:   dk = dv in {32, 64, 128}, either dtype.
- *   float16 states: decode (any of the above) and the bfloat16 prefill with
- *   C in {32, 64}.
+ *   float16 states: decode and every prefill path.
+ *   float16 o: decode, the gated RMSNorm, and the bfloat16 prefill with C in
+ *   {32, 64} (fixed-length and packed).
  */
 
 /*
@@ -130,7 +144,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
  *   v              [B][Hv][T][dv]   qkv_dtype
  *   g, beta        [B][Hv][T]       float32 (log-decay and write strength)
  *   initial_state  [B][Hv][dv][dk]  state_dtype, or NULL for a zero state
- *   o              [B][Hv][T][dv]   float32, output; must not overlap any input
+ *   o              [B][Hv][T][dv]   o_dtype, output; must not overlap any input
  *   final_state    [B][Hv][dv][dk]  state_dtype, output, or NULL to skip; may be
  *                                   the same pointer as initial_state (in place)
  *   workspace      device scratch of gdn_prefill_workspace_bytes(shape) bytes
@@ -139,7 +153,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
  */
 gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, const void *v,
                        const float *g, const float *beta, const void *initial_state,
-                       float *o, void *final_state, void *workspace, size_t workspace_bytes,
+                       void *o, void *final_state, void *workspace, size_t workspace_bytes,
                        void *stream);
 
 /*
@@ -155,7 +169,7 @@ gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, con
  *   v              [Hv][T][dv]      qkv_dtype
  *   g, beta        [Hv][T]          float32
  *   initial_state  [B][Hv][dv][dk]  state_dtype, or NULL for zero states
- *   o              [Hv][T][dv]      float32, output
+ *   o              [Hv][T][dv]      o_dtype, output
  *   final_state    [B][Hv][dv][dk]  state_dtype, output, or NULL; may equal initial_state
  *   workspace      device scratch of gdn_prefill_varlen_workspace_bytes(shape) bytes; it
  *                  grows with T (about 16.4 KB per token at Hv = 32) and is not split into
@@ -169,7 +183,7 @@ gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, con
 size_t gdn_prefill_varlen_workspace_bytes(const gdn_shape *shape);
 gdn_status gdn_prefill_varlen(const gdn_shape *shape, const int32_t *cu_seqlens, const void *q,
                               const void *k, const void *v, const float *g, const float *beta,
-                              const void *initial_state, float *o, void *final_state, void *workspace,
+                              const void *initial_state, void *o, void *final_state, void *workspace,
                               size_t workspace_bytes, void *stream);
 
 /*
@@ -179,10 +193,10 @@ gdn_status gdn_prefill_varlen(const gdn_shape *shape, const int32_t *cu_seqlens,
  *   v        [B][Hv][dv]       qkv_dtype
  *   g, beta  [B][Hv]           float32
  *   state    [B][Hv][dv][dk]   state_dtype, read and overwritten
- *   o        [B][Hv][dv]       float32, output; must not overlap any input or the state
+ *   o        [B][Hv][dv]       o_dtype, output; must not overlap any input or the state
  */
 gdn_status gdn_decode(const gdn_shape *shape, const void *q, const void *k, const void *v,
-                      const float *g, const float *beta, void *state, float *o, void *stream);
+                      const float *g, const float *beta, void *state, void *o, void *stream);
 
 /* Static text for a status code. */
 const char *gdn_status_string(gdn_status status);
@@ -196,7 +210,7 @@ const char *gdn_last_error(void);
  * test; the norm_weight and norm_eps arguments of gated_delta). For every row
  * x of head_dim_v values of o:
  *     x <- x / sqrt(mean(x^2) + eps) * weight * silu(gate),  silu(z) = z / (1 + exp(-z))
- *   o       [B][Hv][T][dv] float32 with T = shape->seq_len (a gdn_decode output
+ *   o       [B][Hv][T][dv] in shape->o_dtype with T = shape->seq_len (a gdn_decode output
  *           [B][Hv][dv] is the case T = 1); read and overwritten
  *   gate    [B][Hv][T][dv] in shape->qkv_dtype, or NULL for no gate factor
  *   weight  [dv] float32, the same for every head and token
@@ -206,7 +220,7 @@ const char *gdn_last_error(void);
  * dv / 16 different workgroups, so the row's norm would need a reduction
  * across workgroups; this call is one extra streaming pass over o.
  */
-gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, float *o, const void *gate, const float *weight,
+gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, void *o, const void *gate, const float *weight,
                              float eps, void *stream);
 
 /*

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib, bnd):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(1) == b"invalid argument"
     assert lib.gdn_status_string(2) == b"unsupported configuration"
@@ -86,6 +86,7 @@ def _err(lib):
     ("qkv_dtype", 7, 1, "qkv_dtype"),
     ("head_map", 2, 1, "head_map"),
     ("state_dtype", 2, 1, "state_dtype"),
+    ("o_dtype", 2, 1, "o_dtype"),
     ("scale", float("nan"), 1, "scale"),
     ("scale", float("inf"), 1, "scale"),
 ])
@@ -281,3 +282,19 @@ def test_varlen_rejects(lib, bnd):
     assert _varlen(lib, shape, cu=ADDR["o"] + 64) == 1 and "overlaps cu_seqlens" in _err(lib)
     assert _varlen(lib, shape, ws=ADDR["q"]) == 1 and "workspace overlaps q" in _err(lib)
     assert _varlen(lib, shape, sf=ADDR["s0"] + 4096) == 1 and "partially overlaps" in _err(lib)
+
+
+def test_f16_output_support_and_bytes(lib, bnd):
+    """float16 o: only the bfloat16 chunk-32/64 prefill (and decode, the epilogue); o then
+    occupies half the bytes, so a final state placed right after it passes the overlap checks
+    (the call then stops at the missing workspace)."""
+    f16 = dict(o_dtype=bnd.GDN_OUT_F16)
+    assert _prefill(lib, _shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32, **f16)) == 2 and "float16 o" in _err(lib)
+    assert _prefill(lib, _shape(bnd, chunk=16, **f16)) == 2 and "float16 o" in _err(lib)
+    o16 = 1 * 4 * 64 * 128 * 2
+    assert _prefill(lib, _shape(bnd, **f16), sf=ADDR["o"] + o16) == 1 and "workspace is NULL" in _err(lib)
+    assert _prefill(lib, _shape(bnd), sf=ADDR["o"] + o16) == 1 and "final_state overlaps o" in _err(lib)
+    # the epilogue: a gate starting where float16 o rows end overlaps float32 o rows
+    n16 = 10 * 4 * 128 * 2
+    assert _norm(lib, _shape(bnd, seq_len=10, **f16), gate=7 * GB + n16 - 16) == 1 and "overlaps" in _err(lib)
+    assert _norm(lib, _shape(bnd, seq_len=10), gate=7 * GB + n16) == 1 and "o overlaps gate" in _err(lib)
