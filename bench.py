@@ -64,9 +64,10 @@ PREFILL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_56_amd", "csrc", f)
                    for f in ("gdn_prefill_chunk.hip", "gdn_prefill_scan.hip", "gdn_frag.h", "gdn_device.h")]
 
 
-def measured_prefill_traffic():
-    """HBM bytes per gdn_prefill launch from the committed FETCH_SIZE / WRITE_SIZE summary,
-    or None when the kernel sources have changed since those counters were taken."""
+def measured_prefill_traffic(key="traffic_bytes_per_launch"):
+    """HBM bytes per gdn_prefill launch from the committed FETCH_SIZE / WRITE_SIZE summary
+    (key: the fp32-o call, or traffic_bytes_per_launch_f16_o), or None when the kernel sources
+    have changed since those counters were taken."""
     try:
         text = open(TRAFFIC_PROFILE).read()
         h = hashlib.sha256()
@@ -74,7 +75,7 @@ def measured_prefill_traffic():
             h.update(open(f, "rb").read())
     except OSError:
         return None
-    m_bytes = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_bytes = re.search(r"^" + key + r":\s*(\d+)", text, re.M)
     m_sha = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]+)", text, re.M)
     if not (m_bytes and m_sha) or h.hexdigest()[:len(m_sha.group(1))] != m_sha.group(1):
         return None
@@ -357,6 +358,7 @@ def main():
             "unit": "GB/s",
             "frac": p16_bytes / (p16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": p16_bytes,
+            "traffic": measured_prefill_traffic("traffic_bytes_per_launch_f16_o"),
         },
         "gated_rmsnorm": {
             "kernel": "gdn_gated_rmsnorm_kernel<128, bf16 gate> on the prefill output (separate pass)",
