@@ -48,6 +48,12 @@ class Oracle:
         self._lib.gdn_oracle_decode.restype = _I
         self._lib.gdn_oracle_decode.argtypes = [_I, _I, _I, _I, _I, _I, _D,
                                                 _P, _P, _P, _P, _P, _P, _I64, _P, _P, _I]
+        self._lib.gdn_oracle_kda_prefill.restype = _I
+        self._lib.gdn_oracle_kda_prefill.argtypes = [_I, _I, _I, _I, _I, _I, _I, _D,
+                                                     _P, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _I]
+        self._lib.gdn_oracle_kda_decode.restype = _I
+        self._lib.gdn_oracle_kda_decode.argtypes = [_I, _I, _I, _I, _I, _I, _D,
+                                                    _P, _P, _P, _P, _P, _P, _I64, _P, _P, _I]
         self._lib.gdn_oracle_gated_rmsnorm.restype = _I
         self._lib.gdn_oracle_gated_rmsnorm.argtypes = [_I64, _I, _P, _P, _P, _D, _P, _I]
         self._lib.gdn_oracle_qkv_prologue.restype = _I
@@ -75,10 +81,22 @@ class Oracle:
         pairs is None, else compact [npairs][T][dv] and [npairs][dv][dk] over the listed
         flattened (b * Hv + h) pairs.
         """
+        return self._prefill(self._lib.gdn_oracle_prefill, False, q, k, v, g, beta, s0, scale, head_map,
+                             pairs, threads)
+
+    def kda_prefill(self, q, k, v, g, beta, s0=None, scale: float = 1.0, head_map: int = 0,
+                    pairs: Optional[Sequence[int]] = None, threads: Optional[int] = None):
+        """Sequential float64 prefill with one log-decay per key channel: as ``prefill`` with
+        g [B][Hv][T][dk]."""
+        return self._prefill(self._lib.gdn_oracle_kda_prefill, True, q, k, v, g, beta, s0, scale, head_map,
+                             pairs, threads)
+
+    def _prefill(self, fn, per_channel, q, k, v, g, beta, s0, scale, head_map, pairs, threads):
         q, k, v, g, beta = (self._f32(x) for x in (q, k, v, g, beta))
         B, Hk, T, dk = q.shape
         Hv, dv = v.shape[1], v.shape[3]
-        if k.shape != q.shape or v.shape[:3] != (B, Hv, T) or g.shape != (B, Hv, T) \
+        gshape = (B, Hv, T, dk) if per_channel else (B, Hv, T)
+        if k.shape != q.shape or v.shape[:3] != (B, Hv, T) or g.shape != gshape \
                 or beta.shape != (B, Hv, T):
             raise ValueError("inconsistent prefill input shapes")
         s0c = None
@@ -94,10 +112,10 @@ class Oracle:
         o = np.empty((n, T, dv), dtype=np.float64)
         s = np.empty((n, dv, dk), dtype=np.float64)
         threads = threads or self.max_threads()
-        rc = self._lib.gdn_oracle_prefill(B, T, Hk, Hv, dk, dv, head_map, float(scale),
-                                          self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(g),
-                                          self._ptr(beta), self._ptr(s0c), self._ptr(pa), n,
-                                          self._ptr(o), self._ptr(s), int(threads))
+        rc = fn(B, T, Hk, Hv, dk, dv, head_map, float(scale),
+                self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(g),
+                self._ptr(beta), self._ptr(s0c), self._ptr(pa), n,
+                self._ptr(o), self._ptr(s), int(threads))
         if rc != 0:
             raise ValueError(f"oracle prefill rejected its arguments (code {rc})")
         if pairs is None:
@@ -111,9 +129,22 @@ class Oracle:
         q, k [B][Hk][dk]; v [B][Hv][dv]; g, beta [B][Hv]. state is [B][Hv][dv][dk] when pairs
         is None, else [npairs][dv][dk]. Returns o ([B][Hv][dv] or [npairs][dv]).
         """
+        return self._decode(self._lib.gdn_oracle_decode, False, q, k, v, g, beta, state, scale, head_map,
+                            pairs, threads)
+
+    def kda_decode_step(self, q, k, v, g, beta, state, scale: float = 1.0, head_map: int = 0,
+                        pairs: Optional[Sequence[int]] = None, threads: Optional[int] = None):
+        """One float64 decode step with one log-decay per key channel: as ``decode_step`` with
+        g [B][Hv][dk]."""
+        return self._decode(self._lib.gdn_oracle_kda_decode, True, q, k, v, g, beta, state, scale, head_map,
+                            pairs, threads)
+
+    def _decode(self, fn, per_channel, q, k, v, g, beta, state, scale, head_map, pairs, threads):
         q, k, v, g, beta = (self._f32(x) for x in (q, k, v, g, beta))
         B, Hk, dk = q.shape
         Hv, dv = v.shape[1], v.shape[2]
+        if g.shape != ((B, Hv, dk) if per_channel else (B, Hv)) or beta.shape != (B, Hv):
+            raise ValueError("inconsistent decode input shapes")
         if state.dtype != np.float64 or not state.flags["C_CONTIGUOUS"]:
             raise ValueError("state must be a C-contiguous float64 array")
         if pairs is None:
@@ -125,10 +156,10 @@ class Oracle:
             raise ValueError("state has the wrong size")
         o = np.empty((n, dv), dtype=np.float64)
         threads = threads or self.max_threads()
-        rc = self._lib.gdn_oracle_decode(B, Hk, Hv, dk, dv, head_map, float(scale),
-                                         self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(g),
-                                         self._ptr(beta), self._ptr(pa), n, self._ptr(state),
-                                         self._ptr(o), int(threads))
+        rc = fn(B, Hk, Hv, dk, dv, head_map, float(scale),
+                self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(g),
+                self._ptr(beta), self._ptr(pa), n, self._ptr(state),
+                self._ptr(o), int(threads))
         if rc != 0:
             raise ValueError(f"oracle decode rejected its arguments (code {rc})")
         return o.reshape(B, Hv, dv) if pairs is None else o

@@ -37,7 +37,11 @@
  * delta-rule recall with orthonormal keys, scale linearity, head-map
  * permutation and thread-count invariance; for the gated RMSNorm epilogue
  * (gdn_oracle_gated_rmsnorm, at the end), unit root-mean-square rows, the eps
- * closed form, quoted sigmoid values and per-column weights.
+ * closed form, quoted sigmoid values and per-column weights; for the
+ * per-channel decay (gdn_oracle_kda_*, at the end), agreement with the scalar
+ * rule when all channels decay alike, the beta = 0 closed form per channel,
+ * dense unrolling, one-hot recall with per-channel forgetting, continuation
+ * and decode-equals-prefill, bit for bit.
  */
 #include <math.h>
 #include <stdint.h>
@@ -285,4 +289,115 @@ int gdn_oracle_qkv_prologue(int B, int T, int Hk, int Hv, int d, int K, const fl
     }
     free(win);
     return 0;
+}
+
+/*
+ * Per-channel decay (the KDA variant: the "channel decay" of the Kimi K3 experiments on the
+ * "master..kimi_slop" page, which keeps one decay value per key channel instead of one per
+ * head). The pages give no formula; the plain reading used here replaces the scalar decay
+ * exp(g_t) of the gated delta rule by a diagonal matrix over the key channels:
+ *
+ *     S_t = S_{t-1} diag(exp(g_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t (scale * q_t)
+ *
+ * with g_t a vector of dk log-decays. S is dv x dk as above, so the decay scales the key
+ * columns of S. With every channel of g_t equal it is the gated delta rule.
+ */
+static void oracle_kda_step(double *S, int dk, int dv, const double *alpha, double beta, double scale,
+                            const float *qq, const float *kk, const float *vv, double *u, double *out) {
+    /* S <- S diag(alpha) */
+    for (int i = 0; i < dv; ++i)
+        for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] *= alpha[j];
+    /* u = S k (of the decayed state) */
+    for (int i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * (double)kk[j];
+        u[i] = acc;
+    }
+    /* S <- S (I - beta k k^T) + beta v k^T = S + beta (v - S k) k^T */
+    for (int i = 0; i < dv; ++i)
+        for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] += beta * ((double)vv[i] - u[i]) * (double)kk[j];
+    /* o = S (scale q), from the updated state */
+    for (int i = 0; i < dv; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * (scale * (double)qq[j]);
+        out[i] = acc;
+    }
+}
+
+/*
+ * KDA prefill: as gdn_oracle_prefill, with g [B][Hv][T][dk] (one log-decay per key channel).
+ */
+int gdn_oracle_kda_prefill(int B, int T, int Hk, int Hv, int dk, int dv, int head_map, double scale,
+                           const float *q, const float *k, const float *v,
+                           const float *g, const float *beta, const double *s0,
+                           const int64_t *pairs, int64_t npairs,
+                           double *o, double *s_final, int nthreads) {
+    if (check_shape(B, T, Hk, Hv, dk, dv, head_map)) return 1;
+    if (!pairs) npairs = (int64_t)B * Hv;
+    for (int64_t p = 0; pairs && p < npairs; ++p)
+        if (pairs[p] < 0 || pairs[p] >= (int64_t)B * Hv) return 1;
+    if (nthreads < 1) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+    for (int64_t p = 0; p < npairs; ++p) {
+        int64_t pair = pairs ? pairs[p] : p;
+        int b = (int)(pair / Hv), h = (int)(pair % Hv);
+        int kh = key_head_of(h, Hk, Hv, head_map);
+        double *S = (double *)calloc((size_t)dv * dk, sizeof(double));
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *out = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *alpha = (double *)malloc(sizeof(double) * (size_t)dk);
+        if (!S || !u || !out || !alpha) { bad = 1; free(S); free(u); free(out); free(alpha); continue; }
+        if (s0) {
+            const double *src = s0 + ((int64_t)b * Hv + h) * dv * dk;
+            for (int64_t e = 0; e < (int64_t)dv * dk; ++e) S[e] = src[e];
+        }
+        for (int t = 0; t < T; ++t) {
+            const float *qq = q + (((int64_t)b * Hk + kh) * T + t) * dk;
+            const float *kk = k + (((int64_t)b * Hk + kh) * T + t) * dk;
+            const float *vv = v + (((int64_t)b * Hv + h) * T + t) * dv;
+            int64_t gi = ((int64_t)b * Hv + h) * T + t;
+            for (int j = 0; j < dk; ++j) alpha[j] = exp((double)g[gi * dk + j]);
+            oracle_kda_step(S, dk, dv, alpha, (double)beta[gi], scale, qq, kk, vv, u, out);
+            if (o) memcpy(o + ((int64_t)p * T + t) * dv, out, sizeof(double) * (size_t)dv);
+        }
+        if (s_final) memcpy(s_final + (int64_t)p * dv * dk, S, sizeof(double) * (size_t)dv * dk);
+        free(S); free(u); free(out); free(alpha);
+    }
+    return bad ? 2 : 0;
+}
+
+/*
+ * KDA decode step: as gdn_oracle_decode, with g [B][Hv][dk].
+ */
+int gdn_oracle_kda_decode(int B, int Hk, int Hv, int dk, int dv, int head_map, double scale,
+                          const float *q, const float *k, const float *v,
+                          const float *g, const float *beta,
+                          const int64_t *pairs, int64_t npairs,
+                          double *state, double *o, int nthreads) {
+    if (check_shape(B, 1, Hk, Hv, dk, dv, head_map)) return 1;
+    if (!state || !o) return 1;
+    if (!pairs) npairs = (int64_t)B * Hv;
+    for (int64_t p = 0; pairs && p < npairs; ++p)
+        if (pairs[p] < 0 || pairs[p] >= (int64_t)B * Hv) return 1;
+    if (nthreads < 1) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : bad)
+    for (int64_t p = 0; p < npairs; ++p) {
+        int64_t pair = pairs ? pairs[p] : p;
+        int b = (int)(pair / Hv), h = (int)(pair % Hv);
+        int kh = key_head_of(h, Hk, Hv, head_map);
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *alpha = (double *)malloc(sizeof(double) * (size_t)dk);
+        if (!u || !alpha) { bad = 1; free(u); free(alpha); continue; }
+        const float *qq = q + ((int64_t)b * Hk + kh) * dk;
+        const float *kk = k + ((int64_t)b * Hk + kh) * dk;
+        const float *vv = v + ((int64_t)b * Hv + h) * dv;
+        for (int j = 0; j < dk; ++j) alpha[j] = exp((double)g[pair * dk + j]);
+        oracle_kda_step(state + (int64_t)p * dv * dk, dk, dv, alpha, (double)beta[pair], scale,
+                        qq, kk, vv, u, o + (int64_t)p * dv);
+        free(u); free(alpha);
+    }
+    return bad ? 2 : 0;
 }

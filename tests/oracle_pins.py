@@ -442,8 +442,121 @@ def pin_prologue_norm_and_layout(orc, seed=28):
                 assert nz.size == 0, ("leak", nm, c)
 
 
+# ---------------------------------------------------------------- per-channel decay (KDA)
+def _kda_g(rng, B, Hv, T, d):
+    """One log-decay per key channel, -softplus(N(0, 1)) as for the scalar decay."""
+    return (-np.log1p(np.exp(rng.standard_normal((B, Hv, T, d))))).astype(np.float32)
+
+
+def pin_kda_uniform_is_gdn(orc, seed=29):
+    """With every channel of g_t equal to one value, the per-channel recurrence is the gated
+    delta rule: prefill and decode agree with the scalar-decay oracle to rounding."""
+    rng = np.random.default_rng(seed)
+    B, Hk, Hv, T, d = 2, 2, 4, 12, 6
+    q, k, v, g, beta, S0 = _rand_inputs(rng, B, Hk, Hv, T, d)
+    gc = np.repeat(g[..., None], d, axis=-1)
+    for head_map in (TILED, GROUPED):
+        o1, S1 = orc.prefill(q, k, v, g, beta, S0, scale=0.7, head_map=head_map)
+        o2, S2 = orc.kda_prefill(q, k, v, gc, beta, S0, scale=0.7, head_map=head_map)
+        assert _rel(o2, o1) < 1e-13 and _rel(S2, S1) < 1e-13, ("uniform decay", head_map)
+        st1, st2 = S0.copy(), S0.copy()
+        d1 = orc.decode_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], g[:, :, 0], beta[:, :, 0], st1, scale=0.7,
+                             head_map=head_map)
+        d2 = orc.kda_decode_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], gc[:, :, 0], beta[:, :, 0], st2, scale=0.7,
+                                 head_map=head_map)
+        assert _rel(d2, d1) < 1e-13 and _rel(st2, st1) < 1e-13, ("uniform decay decode", head_map)
+
+
+def pin_kda_beta_zero(orc, seed=30):
+    """beta = 0: S_t = S_0 diag(exp(G_t)) with G_t the running sum of g over tokens, per key
+    channel (the decay scales the key columns), and o_t = S_t (scale q_t)."""
+    rng = np.random.default_rng(seed)
+    B, Hk, Hv, T, d = 1, 2, 4, 9, 5
+    q, k, v, _, beta, S0 = _rand_inputs(rng, B, Hk, Hv, T, d)
+    g = _kda_g(rng, B, Hv, T, d)
+    beta = np.zeros_like(beta)
+    o, S = orc.kda_prefill(q, k, v, g, beta, S0, scale=0.5)
+    for h in range(Hv):
+        kh = _kh(h, Hk, Hv, TILED)
+        G = np.cumsum(g[0, h].astype(np.float64), axis=0)
+        for t in range(T):
+            St = S0[0, h] * np.exp(G[t])[None, :]
+            assert _rel(o[0, h, t], St @ (0.5 * q[0, kh, t].astype(np.float64))) < 1e-13, ("beta=0 output", h, t)
+        assert _rel(S[0, h], S0[0, h] * np.exp(G[-1])[None, :]) < 1e-13, ("beta=0 state", h)
+
+
+def pin_kda_bruteforce_unroll(orc, seed=31):
+    """S_t = S_0 P(1..t) + sum_s beta_s v_s k_s^T P(s+1..t) with A_t = diag(exp(g_t)) (I - beta_t
+    k_t k_t^T): dense matrices in float64, the decay applied before the delta-rule erase."""
+    rng = np.random.default_rng(seed)
+    B, Hk, Hv, T, d = 1, 1, 2, 8, 5
+    q, k, v, _, beta, S0 = _rand_inputs(rng, B, Hk, Hv, T, d)
+    g = _kda_g(rng, B, Hv, T, d)
+    o, S = orc.kda_prefill(q, k, v, g, beta, S0, scale=0.4)
+    I = np.eye(d)
+    for h in range(Hv):
+        K = k[0, 0].astype(np.float64)
+        A = [np.diag(np.exp(g[0, h, t].astype(np.float64))) @ (I - float(beta[0, h, t]) * np.outer(K[t], K[t]))
+             for t in range(T)]
+        for t in range(T):
+            P = I.copy()
+            for r in range(t + 1):
+                P = P @ A[r]
+            St = S0[0, h] @ P
+            for s_ in range(t + 1):
+                P = I.copy()
+                for r in range(s_ + 1, t + 1):
+                    P = P @ A[r]
+                St = St + float(beta[0, h, s_]) * np.outer(v[0, h, s_].astype(np.float64), K[s_]) @ P
+            assert _rel(o[0, h, t], St @ (0.4 * q[0, 0, t].astype(np.float64))) < 1e-12, ("kda unrolled", h, t)
+            if t == T - 1:
+                assert _rel(S[0, h], St) < 1e-12, ("kda unrolled state", h)
+
+
+def pin_kda_channel_recall(orc, seed=32):
+    """One-hot keys k_t = e_{j_t} with beta = 1: after step t column j_t of S holds v_t and every
+    other column j has been multiplied by exp(g_t[j]) (recall with per-channel forgetting)."""
+    rng = np.random.default_rng(seed)
+    B, Hk, Hv, T, d = 1, 1, 2, 7, 6
+    q, _, v, _, _, S0 = _rand_inputs(rng, B, Hk, Hv, T, d)
+    g = _kda_g(rng, B, Hv, T, d)
+    cols = rng.integers(0, d, size=T)
+    k = np.zeros((B, Hk, T, d), dtype=np.float32)
+    k[0, 0, np.arange(T), cols] = 1.0
+    beta = np.ones((B, Hv, T), dtype=np.float32)
+    for h in range(Hv):
+        St = S0[0, h].copy()
+        for t in range(T):
+            _, S = orc.kda_prefill(q[:, :, :t + 1], k[:, :, :t + 1], v[:, :, :t + 1], g[:, :, :t + 1],
+                                   beta[:, :, :t + 1], S0, scale=1.0)
+            St = St * np.exp(g[0, h, t].astype(np.float64))[None, :]
+            St[:, cols[t]] = v[0, h, t]
+            assert _rel(S[0, h], St) < 1e-14, ("channel recall", h, t)
+
+
+def pin_kda_continuation_and_decode(orc, seed=33):
+    """A prefill split at any token continues bit for bit, and T decode steps equal the
+    prefill's outputs and state bit for bit."""
+    rng = np.random.default_rng(seed)
+    B, Hk, Hv, T, d = 2, 1, 2, 9, 4
+    q, k, v, _, beta, S0 = _rand_inputs(rng, B, Hk, Hv, T, d)
+    g = _kda_g(rng, B, Hv, T, d)
+    o, S = orc.kda_prefill(q, k, v, g, beta, S0, scale=0.6)
+    for m in (1, 4, T - 1):
+        o1, S1 = orc.kda_prefill(q[:, :, :m], k[:, :, :m], v[:, :, :m], g[:, :, :m], beta[:, :, :m], S0, scale=0.6)
+        o2, S2 = orc.kda_prefill(q[:, :, m:], k[:, :, m:], v[:, :, m:], g[:, :, m:], beta[:, :, m:], S1, scale=0.6)
+        assert np.array_equal(np.concatenate([o1, o2], axis=2), o) and np.array_equal(S2, S), ("split", m)
+    st = S0.copy()
+    for t in range(T):
+        ot = orc.kda_decode_step(q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t], beta[:, :, t], st, scale=0.6)
+        assert np.array_equal(ot, o[:, :, t]), ("decode output", t)
+    assert np.array_equal(st, S), "decode state"
+
+
 ALL_PINS = [pin_bruteforce_unroll, pin_exact_rational, pin_pages_one_step, pin_padded_noop,
             pin_continuation, pin_beta_zero, pin_recall, pin_scale_linear, pin_head_map,
             pin_threads, pin_decode_matches_prefill, pin_pair_subset,
             pin_rmsnorm_unit_rms, pin_rmsnorm_eps, pin_rmsnorm_gate_and_weight,
-            pin_prologue_taps, pin_prologue_continuation, pin_prologue_norm_and_layout]
+            pin_prologue_taps, pin_prologue_continuation, pin_prologue_norm_and_layout,
+            pin_kda_uniform_is_gdn, pin_kda_beta_zero, pin_kda_bruteforce_unroll, pin_kda_channel_recall,
+            pin_kda_continuation_and_decode]

@@ -64,6 +64,30 @@ MUTANTS = {
     "prologue_v_normalised": ("if (hh < 2 * Hk) {", "if (hh < 2 * Hk + Hv) {"),
     "prologue_mean_not_sum": ("f = 1.0 / sqrt(ss + eps);", "f = 1.0 / sqrt(ss / d + eps);"),
     "prologue_k_reads_q": ("k + (((size_t)b * Hk + (hh - Hk)) * T + t) * d", "k + (((size_t)b * Hk + (hh - Hk + Hk - 1) % Hk) * T + t) * d"),
+    "kda_decay_on_value_rows": ("for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] *= alpha[j];",
+                                "for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] *= alpha[i % dk];"),
+    "kda_no_decay": ("for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] *= alpha[j];",
+                     "for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] *= 1.0;"),
+    "kda_erase_sign": ("+= beta * ((double)vv[i] - u[i]) * (double)kk[j];",
+                       "+= beta * ((double)vv[i] + u[i]) * (double)kk[j];"),
+    "kda_write_without_beta": ("+= beta * ((double)vv[i] - u[i]) * (double)kk[j];",
+                               "+= ((double)vv[i] - beta * u[i]) * (double)kk[j];"),
+    "kda_channels_reversed": ("alpha[j] = exp((double)g[gi * dk + j]);", "alpha[j] = exp((double)g[gi * dk + (dk - 1 - j)]);"),
+    "kda_decay_not_exponentiated": ("alpha[j] = exp((double)g[gi * dk + j]);", "alpha[j] = 1.0 + (double)g[gi * dk + j];"),
+    "kda_decay_of_previous_token": ("alpha[j] = exp((double)g[gi * dk + j]);",
+                                    "alpha[j] = exp((double)g[(t > 0 ? gi - 1 : gi) * dk + j]);"),
+    "kda_decode_one_channel": ("alpha[j] = exp((double)g[pair * dk + j]);", "alpha[j] = exp((double)g[pair * dk]);"),
+    "kda_erase_before_decay": [
+        ("    /* S <- S diag(alpha) */\n    for (int i = 0; i < dv; ++i)\n"
+         "        for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] *= alpha[j];\n", ""),
+        ("    /* S <- S (I - beta k k^T) + beta v k^T = S + beta (v - S k) k^T */\n"
+         "    for (int i = 0; i < dv; ++i)\n"
+         "        for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] += beta * ((double)vv[i] - u[i]) * (double)kk[j];\n",
+         "    for (int i = 0; i < dv; ++i)\n"
+         "        for (int j = 0; j < dk; ++j) S[(int64_t)i * dk + j] = alpha[j] * (S[(int64_t)i * dk + j] - beta * u[i] * (double)kk[j]) + beta * (double)vv[i] * (double)kk[j];\n"),
+    ],
+    "kda_output_reads_key": ("for (int j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * (scale * (double)qq[j]);\n        out[i] = acc;\n    }\n}\n\n/*\n * KDA prefill",
+                             "for (int j = 0; j < dk; ++j) acc += S[(int64_t)i * dk + j] * (scale * (double)kk[j]);\n        out[i] = acc;\n    }\n}\n\n/*\n * KDA prefill"),
     "output_step_off_by_one": ("if (o) memcpy(o + ((int64_t)p * T + t) * dv, out,",
                                "if (o) memcpy(o + ((int64_t)p * T + (t + 1) % T) * dv, out,"),
 }
