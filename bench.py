@@ -224,6 +224,23 @@ def main():
                                                   o=po16, final_state=psf), args.steps)
     p16_bytes = prefill_bytes(B, T, Hk, Hv, d, o_bytes=2)
 
+    # the per-channel-decay variant: the long prefill (token-recurrent kernel) and the batched
+    # decode step, with one log-decay per key channel (-softplus(N(0,1)) * 0.1 and * 1)
+    kg = torch.from_numpy(inputs.generate_channel_decay((B, Hv, T, d), seed=pw.seed + 300, factor=0.1)).to(dev)
+    binding.kda_prefill(pq, pk, pv, kg, pb, None, scale=px.scale, o=po, final_state=psf)
+    kda_p_ms = time_batch(lambda i: binding.kda_prefill(pq, pk, pv, kg, pb, None, scale=px.scale, o=po,
+                                                        final_state=psf), max(1, args.steps // 10))
+    kda_p_bytes = prefill_bytes(B, T, Hk, Hv, d) + B * Hv * T * d * 4  # + the per-channel decays
+    del kg
+    kdg = torch.from_numpy(inputs.generate_channel_decay((dB, dHv, dd), seed=dw.seed + 300)).to(dev)
+    kstate = state.clone()
+    binding.kda_decode(dq[0], dk[0], dv[0], kdg, db[0], kstate, scale=dx.scale, o=do)
+    kda_d_ms = time_batch(lambda i: binding.kda_decode(dq[i % nsteps_dec], dk[i % nsteps_dec], dv[i % nsteps_dec],
+                                                       kdg, db[i % nsteps_dec], kstate, scale=dx.scale, o=do),
+                          args.steps)
+    kda_d_bytes = decode_bytes(dB, dHk, dHv, dd) + dB * dHv * dd * 4
+    del kdg, kstate
+
     # the gated RMSNorm epilogue on the prefill output (1M rows of 128 floats, bf16 gate)
     nrm = inputs.generate_norm(po.shape, "bf16", seed=pw.seed + 100)
     ngate = bf(nrm.gate_bits)
@@ -359,6 +376,23 @@ def main():
             "frac": p16_bytes / (p16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": p16_bytes,
             "traffic": measured_prefill_traffic("traffic_bytes_per_launch_f16_o"),
+        },
+        "kda": {
+            "what": "per-channel decay (one log-decay per key channel): long prefill, token-recurrent "
+                    "kernel; batched decode step",
+            "prefill_kernel": "gdn_kda_prefill_kernel<bf16>",
+            "prefill_ms": kda_p_ms,
+            "prefill_tokens_per_s": tokens / (kda_p_ms * 1e-3),
+            "prefill_achieved": kda_p_bytes / (kda_p_ms * 1e-3) / 1e9,
+            "prefill_frac": kda_p_bytes / (kda_p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "prefill_algorithmic_bytes": kda_p_bytes,
+            "decode_kernel": "gdn_decode_kernel<128, bf16, f32 state, per-channel decay>",
+            "decode_ms": kda_d_ms,
+            "decode_achieved": kda_d_bytes / (kda_d_ms * 1e-3) / 1e9,
+            "decode_frac": kda_d_bytes / (kda_d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "decode_algorithmic_bytes": kda_d_bytes,
+            "unit": "GB/s",
+            "peak": HBM_PEAK_GBPS,
         },
         "gated_rmsnorm": {
             "kernel": "gdn_gated_rmsnorm_kernel<128, bf16 gate> on the prefill output (separate pass)",

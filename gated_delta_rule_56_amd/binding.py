@@ -26,8 +26,9 @@ _STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
 _OUT_DTYPES = {torch.float32: GDN_OUT_F32, torch.float16: GDN_OUT_F16}
 
 EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_varlen_workspace_bytes",
-                    "gdn_prefill_varlen", "gdn_decode", "gdn_gated_rmsnorm", "gdn_qkv_prologue",
-                    "gdn_status_string", "gdn_last_error", "gdn_abi_version")
+                    "gdn_prefill_varlen", "gdn_decode", "gdn_kda_prefill", "gdn_kda_decode",
+                    "gdn_gated_rmsnorm", "gdn_qkv_prologue", "gdn_status_string", "gdn_last_error",
+                    "gdn_abi_version")
 
 
 class GdnShape(ctypes.Structure):
@@ -67,6 +68,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_prefill_varlen_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
     lib.gdn_prefill_varlen.restype = ctypes.c_int
     lib.gdn_prefill_varlen.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.gdn_kda_prefill.restype = ctypes.c_int
+    lib.gdn_kda_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P]
+    lib.gdn_kda_decode.restype = ctypes.c_int
+    lib.gdn_kda_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
     lib.gdn_decode.restype = ctypes.c_int
     lib.gdn_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
@@ -299,6 +304,82 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
                        head_map, scale, _STATE_DTYPES[state.dtype], _OUT_DTYPES[o.dtype])
     _check(lib, lib.gdn_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state), _ptr(o), _stream_handle(stream)))
+    return o
+
+
+def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                initial_state: Optional[torch.Tensor] = None, *, head_map: int = GDN_HEADS_TILED,
+                scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
+                state_dtype: Optional[torch.dtype] = None, o_dtype: torch.dtype = torch.float32,
+                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gdn_kda_prefill on torch tensors: as ``prefill`` with one log-decay per key channel,
+    g [B][Hv][T][dk] float32."""
+    lib = load_library()
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, nm, dtype)
+    _dev_tensor(g, "g", torch.float32)
+    _dev_tensor(beta, "beta", torch.float32)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
+        raise ValueError("q, k must be [B][Hk][T][d] and v [B][Hv][T][d]")
+    B, Hk, T, d = q.shape
+    Hv = v.shape[1]
+    if v.shape != (B, Hv, T, d) or g.shape != (B, Hv, T, d) or beta.shape != (B, Hv, T):
+        raise ValueError("v must be [B][Hv][T][d], g [B][Hv][T][d] and beta [B][Hv][T]")
+    given = [t.dtype for t in (initial_state, final_state) if t is not None]
+    sdt = given[0] if given else (state_dtype or torch.float32)
+    if sdt not in _STATE_DTYPES or any(t != sdt for t in given):
+        raise TypeError("the states must be float32 or float16, both of the same type")
+    if initial_state is not None:
+        _state_tensor(initial_state, "initial_state")
+        if initial_state.shape != (B, Hv, d, d):
+            raise ValueError("initial_state must be [B][Hv][d][d]")
+    o = _out_tensor(o, (B, Hv, T, d), o_dtype, q.device)
+    if final_state is None and write_final_state:
+        final_state = torch.empty((B, Hv, d, d), dtype=sdt, device=q.device)
+    if final_state is not None:
+        _state_tensor(final_state, "final_state")
+        if final_state.shape != (B, Hv, d, d):
+            raise ValueError("final_state must be [B][Hv][d][d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shape = make_shape(B, T, Hk, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
+                       head_map, scale, _STATE_DTYPES[sdt], _OUT_DTYPES[o.dtype])
+    _check(lib, lib.gdn_kda_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(initial_state), _ptr(o), _ptr(final_state), _stream_handle(stream)))
+    return o, final_state
+
+
+def kda_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+               state: torch.Tensor, *, head_map: int = GDN_HEADS_TILED, scale: Optional[float] = None,
+               o: Optional[torch.Tensor] = None, o_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """gdn_kda_decode on torch tensors: as ``decode`` with g [B][Hv][d] (one log-decay per key
+    channel)."""
+    lib = load_library()
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_tensor(t, nm, dtype)
+    _dev_tensor(g, "g", torch.float32)
+    _dev_tensor(beta, "beta", torch.float32)
+    _state_tensor(state, "state")
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3:
+        raise ValueError("q, k must be [B][Hk][d] and v [B][Hv][d]")
+    B, Hk, d = q.shape
+    Hv = v.shape[1]
+    if v.shape != (B, Hv, d) or g.shape != (B, Hv, d) or beta.shape != (B, Hv) or state.shape != (B, Hv, d, d):
+        raise ValueError("v [B][Hv][d], g [B][Hv][d], beta [B][Hv], state [B][Hv][d][d] expected")
+    o = _out_tensor(o, (B, Hv, d), o_dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shape = make_shape(B, 1, Hk, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
+                       head_map, scale, _STATE_DTYPES[state.dtype], _OUT_DTYPES[o.dtype])
+    _check(lib, lib.gdn_kda_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(state), _ptr(o), _stream_handle(stream)))
     return o
 
 

@@ -399,8 +399,12 @@ gdn_status gdn_qkv_prologue(const gdn_shape *s, const void *x, const float *conv
     return GDN_OK;
 }
 
-gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
-                      const float *beta, void *state, void *o, void *stream) {
+}  // extern "C"
+
+namespace {
+// gdn_decode and gdn_kda_decode: g is [B][Hv] or, with kda, [B][Hv][dk]
+gdn_status decode_impl(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, void *state, void *o, void *stream, bool kda) {
     GDN_TRY(check_common(s));
     if (s->seq_len != 1) return fail(GDN_ERR_INVALID_ARG, "decode needs seq_len == 1 (got %d)", s->seq_len);
     const int d = s->head_dim_k;
@@ -412,12 +416,12 @@ gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const vo
     GDN_TRY(check_ptr(q, "q", 16));
     GDN_TRY(check_ptr(k, "k", 16));
     GDN_TRY(check_ptr(v, "v", 16));
-    GDN_TRY(check_ptr(g, "g", 4));
+    GDN_TRY(check_ptr(g, "g", kda ? 16 : 4));
     GDN_TRY(check_ptr(beta, "beta", 4));
     GDN_TRY(check_ptr(state, "state", 16));
     GDN_TRY(check_ptr(o, "o", 16));
     const Range ins[] = {range("q", q, B * Hk * d * esz), range("k", k, B * Hk * d * esz),
-                         range("v", v, B * Hv * d * esz), range("g", g, B * Hv * 4),
+                         range("v", v, B * Hv * d * esz), range("g", g, B * Hv * (kda ? d : 1) * 4),
                          range("beta", beta, B * Hv * 4)};
     const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
     const Range outs[] = {range("o", o, B * Hv * d * (o16 ? 2 : 4)),
@@ -441,8 +445,85 @@ gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const vo
     p.scale = s->scale;
     p.state_f16 = st16;
     p.o_f16 = o16;
+    p.kda = kda;
     const hipError_t err = gdn::launch_decode(p, bf16, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
+    return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, void *state, void *o, void *stream) {
+    return decode_impl(s, q, k, v, g, beta, state, o, stream, false);
+}
+
+gdn_status gdn_kda_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, void *state, void *o, void *stream) {
+    return decode_impl(s, q, k, v, g, beta, state, o, stream, true);
+}
+
+gdn_status gdn_kda_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const void *initial_state, void *o, void *final_state,
+                           void *stream) {
+    GDN_TRY(check_common(s));
+    if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
+    const int d = s->head_dim_k;
+    if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "per-channel decay prefill supports head_dim 128 (got %d)", d);
+    const bool bf16 = s->qkv_dtype == GDN_DTYPE_BF16;
+    const int64_t B = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
+    if ((double)B * Hv * T * d > 4.0e15) return fail(GDN_ERR_UNSUPPORTED, "tensor sizes overflow");
+    const int64_t esz = bf16 ? 2 : 4;
+    const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
+    const int64_t qk_bytes = B * Hk * T * d * esz, v_bytes = B * Hv * T * d * esz, g_bytes = B * Hv * T * d * 4;
+    const int64_t b_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * (o16 ? 2 : 4);
+    const int64_t st_bytes = B * Hv * d * d * (st16 ? 2 : 4);
+    if (T > 0) {
+        GDN_TRY(check_ptr(q, "q", 16));
+        GDN_TRY(check_ptr(k, "k", 16));
+        GDN_TRY(check_ptr(v, "v", 16));
+        GDN_TRY(check_ptr(g, "g", 16));
+        GDN_TRY(check_ptr(beta, "beta", 4));
+        GDN_TRY(check_ptr(o, "o", 16));
+    }
+    if (initial_state) GDN_TRY(check_ptr(initial_state, "initial_state", 16));
+    if (final_state) GDN_TRY(check_ptr(final_state, "final_state", 16));
+    const Range ins[] = {range("q", q, T ? qk_bytes : 0), range("k", k, T ? qk_bytes : 0),
+                         range("v", v, T ? v_bytes : 0), range("g", g, T ? g_bytes : 0),
+                         range("beta", beta, T ? b_bytes : 0),
+                         range("initial_state", initial_state, initial_state ? st_bytes : 0)};
+    const Range out_o[] = {range("o", o, T ? o_bytes : 0)};
+    GDN_TRY(check_no_overlap(out_o, 1, ins, 6));
+    if (final_state) {
+        const Range out_s[] = {range("final_state", final_state, st_bytes)};
+        GDN_TRY(check_no_overlap(out_s, 1, ins, 5));
+        GDN_TRY(check_no_overlap(out_s, 1, out_o, 1));
+        if (initial_state && final_state != initial_state && overlaps(out_s[0], ins[5]))
+            return fail(GDN_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
+    }
+    if (!final_state && T == 0) return GDN_OK;
+    gdn::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.init_state = initial_state;
+    p.o = o;
+    p.final_state = final_state;
+    p.B = s->batch;
+    p.T = s->seq_len;
+    p.Ts = s->seq_len;
+    p.Hk = s->num_k_heads;
+    p.Hv = s->num_v_heads;
+    p.D = d;
+    p.head_map = (int32_t)s->head_map;
+    p.scale = s->scale;
+    p.init_f16 = p.final_f16 = st16;
+    p.o_f16 = o16;
+    const hipError_t err = gdn::launch_kda_prefill(p, bf16, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
     return GDN_OK;
 }
 

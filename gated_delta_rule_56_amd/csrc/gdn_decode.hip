@@ -82,8 +82,9 @@ __device__ __forceinline__ float row_sum(float x) {
 template <int D, typename SD>
 constexpr int cols_per_lane() { return sizeof(SD) == 2 && D >= 64 ? 8 : 4; }
 
-// T: q/k/v element (float or bfloat16 bits); SD: state element (float or _Float16)
-template <int D, typename T, typename SD>
+// T: q/k/v element (float or bfloat16 bits); SD: state element (float or _Float16);
+// kKda: one decay per key channel (g [B][Hv][D]) instead of one per head
+template <int D, typename T, typename SD, bool kKda>
 __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams p) {
     constexpr int CPL = cols_per_lane<D, SD>();
     constexpr int LPR = D / CPL;                    // lanes per state row
@@ -112,13 +113,26 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
     float kv[CPL], qv[CPL];
     load_vec<CPL>(kp, col, kv);
     load_vec<CPL>(qp, col, qv);
-    const float alpha = __expf(p.g[pair]);
     const float beta = p.beta[pair];
     float kq = 0.0f;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) kq += kv[e] * qv[e];
     kq = row_sum<LPR>(kq);
     const float kappa = p.scale * kq;
+    // per-channel decay: the decayed state S diag(alpha) meets k and q as S (alpha k), S (alpha q)
+    float alpha = 1.0f, al[CPL], ak[CPL], aq[CPL];
+    if constexpr (kKda) {
+        float gv[CPL];
+        load_vec<CPL>(p.g + (int64_t)pair * D, col, gv);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+            al[e] = __expf(gv[e]);
+            ak[e] = al[e] * kv[e];
+            aq[e] = al[e] * qv[e];
+        }
+    } else {
+        alpha = __expf(p.g[pair]);
+    }
     const float as = alpha * p.scale;
 
     float vrow[ITERS];
@@ -130,15 +144,15 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
         float rk = 0.0f, rq = 0.0f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-            rk += s[it].get(e) * kv[e];
-            rq += s[it].get(e) * qv[e];
+            rk += s[it].get(e) * (kKda ? ak[e] : kv[e]);
+            rq += s[it].get(e) * (kKda ? aq[e] : qv[e]);
         }
         rk = row_sum<LPR>(rk);
         rq = row_sum<LPR>(rq);
-        const float delta = beta * (vrow[it] - alpha * rk);
+        const float delta = beta * (vrow[it] - alpha * rk);  // alpha = 1 with per-channel decay
         float y[CPL];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) y[e] = alpha * s[it].get(e) + delta * kv[e];
+        for (int e = 0; e < CPL; ++e) y[e] = (kKda ? al[e] : alpha) * s[it].get(e) + delta * kv[e];
         const int row = row0 + it * RPA;
         StateRow<CPL, SD>::store(S + (int64_t)row * D + col, y);
         if (col == 0) {
@@ -154,10 +168,16 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
 template <int D, typename T>
 hipError_t launch_dt(const DecodeParams &p, hipStream_t stream) {
     dim3 grid((unsigned)(p.B * p.Hv)), block(kDecodeThreads);
-    if (p.state_f16)
-        hipLaunchKernelGGL((gdn_decode_kernel<D, T, _Float16>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((gdn_decode_kernel<D, T, float>), grid, block, 0, stream, p);
+    if (p.kda) {
+        if (p.state_f16)
+            hipLaunchKernelGGL((gdn_decode_kernel<D, T, _Float16, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((gdn_decode_kernel<D, T, float, true>), grid, block, 0, stream, p);
+    } else if (p.state_f16) {
+        hipLaunchKernelGGL((gdn_decode_kernel<D, T, _Float16, false>), grid, block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((gdn_decode_kernel<D, T, float, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

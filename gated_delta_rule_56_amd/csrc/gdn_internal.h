@@ -35,7 +35,7 @@ struct DecodeParams {
     const void *q;             // [B][Hk][D]
     const void *k;             // [B][Hk][D]
     const void *v;             // [B][Hv][D]
-    const float *g;            // [B][Hv]
+    const float *g;            // [B][Hv], or [B][Hv][D] with kda
     const float *beta;         // [B][Hv]
     void *state;               // [B][Hv][D][D] f32 (f16 when state_f16), in place
     void *o;                   // [B][Hv][D] f32 (f16 when o_f16)
@@ -44,6 +44,7 @@ struct DecodeParams {
     float scale;
     bool state_f16 = false;
     bool o_f16 = false;
+    bool kda = false;          // one decay per key channel
 };
 
 // bf16 q/k/v, D = 128, chunk 16: single fused chunked WY kernel on fp16 MFMA.
@@ -77,6 +78,9 @@ struct PrologueParams {
     float eps;
 };
 hipError_t launch_qkv_prologue(const PrologueParams &p, hipStream_t stream);
+
+// Per-channel decay (g [B][Hv][T][D]), D = 128: token-recurrent prefill.
+hipError_t launch_kda_prefill(const PrefillParams &p, bool bf16, hipStream_t stream);
 
 // Packed sequences: the workspace of gdn_prefill_varlen (chunk data for `nchunks` chunks, then
 // the sequence and chunk tables), and the launch that fills the tables from cu_seqlens.

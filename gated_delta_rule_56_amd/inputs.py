@@ -243,3 +243,11 @@ def generate_norm(out_shape: Sequence[int], qkv_dtype: str, seed: int) -> NormIn
     weight = rng.standard_normal(out_shape[-1]).astype(np.float16).astype(np.float32)
     gf, gb = _store(gate, qkv_dtype)
     return NormInputs(gate=gf, gate_bits=gb, weight=weight)
+
+
+def generate_channel_decay(shape: Sequence[int], seed: int, factor: float = 1.0) -> np.ndarray:
+    """Log-decays for the per-channel-decay variant: one value per key channel,
+    g = -softplus(N(0, 1)) * factor (the scalar decay's distribution, drawn per channel),
+    computed in float64 and stored as float32. shape: [B][Hv][T][dk] or [steps][B][Hv][dk]."""
+    rng = np.random.default_rng(seed)
+    return (-_softplus(rng.standard_normal(tuple(shape))) * factor).astype(np.float32)

@@ -198,6 +198,26 @@ gdn_status gdn_prefill_varlen(const gdn_shape *shape, const int32_t *cu_seqlens,
 gdn_status gdn_decode(const gdn_shape *shape, const void *q, const void *k, const void *v,
                       const float *g, const float *beta, void *state, void *o, void *stream);
 
+/*
+ * Per-channel decay (the KDA variant): the recurrence with one log-decay per key channel,
+ *     S_t = S_{t-1} diag(exp(g_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t (scale q_t),
+ * the "channel decay" of the Kimi K3 experiments on the "master..kimi_slop" page, which keeps
+ * one decay value per key channel rather than one per head. The pages give no formula; this
+ * is the gated delta rule with its scalar decay made diagonal over the key channels (with
+ * every channel of g_t equal it is gdn_prefill / gdn_decode). Layouts as gdn_prefill and
+ * gdn_decode except g:
+ *   gdn_kda_prefill  g [B][Hv][T][dk] float32, 16-byte aligned; no workspace, shape->chunk
+ *                    ignored (the prefill runs token by token)
+ *   gdn_kda_decode   g [B][Hv][dk] float32, 16-byte aligned
+ * Supported: dk = dv = 128 for the prefill (32, 64 or 128 for decode), bfloat16 or float32
+ * q/k/v, both state and output storage types.
+ */
+gdn_status gdn_kda_prefill(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const void *initial_state, void *o,
+                           void *final_state, void *stream);
+gdn_status gdn_kda_decode(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                          const float *g, const float *beta, void *state, void *o, void *stream);
+
 /* Static text for a status code. */
 const char *gdn_status_string(gdn_status status);
 

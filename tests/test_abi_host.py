@@ -298,3 +298,20 @@ def test_f16_output_support_and_bytes(lib, bnd):
     n16 = 10 * 4 * 128 * 2
     assert _norm(lib, _shape(bnd, seq_len=10, **f16), gate=7 * GB + n16 - 16) == 1 and "overlaps" in _err(lib)
     assert _norm(lib, _shape(bnd, seq_len=10), gate=7 * GB + n16) == 1 and "o overlaps gate" in _err(lib)
+
+
+def test_kda_rejects(lib, bnd):
+    a = ADDR
+    shape = _shape(bnd, seq_len=10)
+    call = lambda sh, **o: lib.gdn_kda_prefill(ctypes.byref(sh), a["q"], a["k"], a["v"], o.get("g", a["g"]), a["beta"],
+                                                a["s0"], o.get("o", a["o"]), a["sf"], None)
+    assert call(_shape(bnd, seq_len=10, head_dim=64)) == 2 and "head_dim" in _err(lib)
+    assert call(shape, g=a["g"] + 4) == 1 and "aligned" in _err(lib)  # per-channel g: 16-byte aligned
+    assert call(shape, g=None) == 1 and "g is NULL" in _err(lib)
+    assert call(shape, o=a["g"] + 4096) == 1 and "o overlaps g" in _err(lib)
+    dec = lambda sh, **o: lib.gdn_kda_decode(ctypes.byref(sh), a["q"], a["k"], a["v"], o.get("g", a["g"]), a["beta"],
+                                             a["s0"], o.get("o", a["o"]), None)
+    assert dec(_shape(bnd, seq_len=2)) == 1 and "seq_len" in _err(lib)
+    assert dec(_shape(bnd, seq_len=1), g=a["g"] + 8) == 1 and "aligned" in _err(lib)
+    # g holds B * Hv * d floats for the per-channel step: an o placed inside it overlaps
+    assert dec(_shape(bnd, seq_len=1), o=a["g"] + 4 * 4 * 64) == 1 and "o overlaps g" in _err(lib)

@@ -1,0 +1,138 @@
+"""GPU parity of the per-channel-decay variant (gdn_kda_prefill, gdn_kda_decode) against the
+float64 oracle's per-channel recurrence (needs an MI355X)."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_56_amd import inputs
+from tests.gpu_util import TOL_BF16, TOL_F32, dev, qkv_dev, rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_56_amd import binding
+    return binding
+
+
+def check(oracle_lib, x, g, o, sf, tol, head_map=0, pairs=None, label=""):
+    o_ref, s_ref = oracle_lib.kda_prefill(x.q, x.k, x.v, g, x.beta, x.s0, scale=x.scale, head_map=head_map,
+                                          pairs=pairs)
+    if pairs is not None:
+        B, Hv = x.v.shape[:2]
+        o = o.reshape(B * Hv, *o.shape[2:])[pairs]
+        sf = sf.reshape(B * Hv, *sf.shape[2:])[pairs]
+    eo, es = rel_err(o, o_ref), rel_err(sf, s_ref)
+    print(f"{label}: rel err o {eo:.3e} state {es:.3e}")
+    assert eo <= tol and es <= tol, (label, eo, es)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 37, 200])
+@pytest.mark.parametrize("head_map", [0, 1])
+def test_kda_prefill_small(gdn, oracle_lib, dtype, T, head_map):
+    x = inputs.generate(2, T, 2, 4, 128, dtype, seed=120 + T, init_state="normal")
+    g = inputs.generate_channel_decay((2, 4, T, 128), seed=121 + T)
+    q, k, v = qkv_dev(x)
+    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), head_map=head_map, scale=x.scale)
+    check(oracle_lib, x, g, o.cpu().numpy(), sf.cpu().numpy(), tol_for(x), head_map=head_map,
+          label=f"kda {dtype} T{T} map{head_map}")
+
+
+def test_kda_uniform_decay_is_gdn(gdn):
+    """Every channel of g_t equal: the per-channel prefill agrees with gdn_prefill."""
+    x = inputs.generate(1, 300, 2, 4, 128, "bf16", seed=122, init_state="normal")
+    q, k, v = qkv_dev(x)
+    gc = np.repeat(x.g[..., None], 128, axis=-1)
+    o1, s1 = gdn.kda_prefill(q, k, v, dev(gc), dev(x.beta), dev(x.s0), scale=x.scale)
+    o2, s2 = gdn.prefill(q, k, v, dev(x.g), dev(x.beta), dev(x.s0), chunk=64, scale=x.scale)
+    assert rel_err(o1.cpu().numpy(), o2.cpu().numpy()) <= TOL_BF16
+    assert rel_err(s1.cpu().numpy(), s2.cpu().numpy()) <= TOL_BF16
+
+
+def test_kda_long_sampled(gdn, oracle_lib):
+    """T = 32768 at the long workload's shape, per-channel decays -softplus(N(0,1)) * 0.1; two
+    value heads against the oracle."""
+    wl = inputs.WORKLOADS["long_prefill_32k"]
+    x = inputs.generate_workload(wl)
+    g = inputs.generate_channel_decay(x.v.shape, seed=123, factor=0.1)
+    q, k, v = qkv_dev(x)
+    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), None, scale=x.scale)
+    check(oracle_lib, x, g, o.cpu().numpy(), sf.cpu().numpy(), TOL_BF16, pairs=np.array([5, 26]),
+          label="kda long_32k (2 heads)")
+
+
+def test_kda_prefill_equals_decode_steps(gdn):
+    """A prefill of T tokens and T decode steps from the same state agree."""
+    import torch
+    T = 24
+    x = inputs.generate(2, T, 2, 4, 128, "bf16", seed=124, init_state="normal")
+    g = inputs.generate_channel_decay((2, 4, T, 128), seed=125)
+    q, k, v = qkv_dev(x)
+    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), scale=x.scale)
+    state = dev(x.s0)
+    gd, bd = dev(g), dev(x.beta)
+    for t in range(T):
+        od = gdn.kda_decode(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                            gd[:, :, t].contiguous(), bd[:, :, t].contiguous(), state, scale=x.scale)
+        assert rel_err(od.cpu().numpy(), o[:, :, t].cpu().numpy()) <= 1e-5, t
+    torch.cuda.synchronize()
+    assert rel_err(state.cpu().numpy(), sf.cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("state16", [False, True])
+def test_kda_decode(gdn, oracle_lib, d, dtype, state16):
+    import torch
+    steps = 3
+    x = inputs.generate(3, 1, 2, 6, d, dtype, seed=126 + d, init_state="normal", decode_steps=steps)
+    g = inputs.generate_channel_decay((steps, 3, 6, d), seed=127 + d)
+    s0 = x.s0.astype(np.float16) if state16 else x.s0
+    state = torch.from_numpy(np.ascontiguousarray(s0)).cuda()
+    ref = np.ascontiguousarray(s0.astype(np.float64))
+    q, k, v = qkv_dev(x)
+    bar = TOL_BF16 if (dtype == "bf16" or state16) else TOL_F32
+    for s in range(steps):
+        o = gdn.kda_decode(q[s], k[s], v[s], dev(g[s]), dev(x.beta[s]), state, scale=x.scale)
+        o_ref = oracle_lib.kda_decode_step(x.q[s], x.k[s], x.v[s], g[s], x.beta[s], ref, scale=x.scale)
+        assert rel_err(o.cpu().numpy(), o_ref) <= bar, s
+    assert rel_err(state.float().cpu().numpy(), ref) <= bar
+
+
+def test_kda_decode_batched(gdn, oracle_lib):
+    """B=256, Hk=16, Hv=32, d=128: 64 in-place steps; 128 sampled pairs at every step."""
+    import torch
+    wl = inputs.WORKLOADS["batched_decode"]
+    x = inputs.generate_workload(wl)
+    B, Hv, d = wl.batch, wl.num_v_heads, wl.head_dim
+    g = inputs.generate_channel_decay((wl.decode_steps, B, Hv, d), seed=128)
+    pairs = np.sort(np.random.default_rng(129).choice(B * Hv, size=128, replace=False))
+    idx = torch.from_numpy(pairs).cuda()
+    state = dev(x.s0)
+    ref = np.ascontiguousarray(x.s0.reshape(B * Hv, d, d)[pairs].astype(np.float64))
+    q, k, v = qkv_dev(x)
+    worst = 0.0
+    for s in range(wl.decode_steps):
+        o = gdn.kda_decode(q[s], k[s], v[s], dev(g[s]), dev(x.beta[s]), state, scale=x.scale)
+        o_ref = oracle_lib.kda_decode_step(x.q[s], x.k[s], x.v[s], g[s], x.beta[s], ref, scale=x.scale,
+                                           pairs=pairs)
+        worst = max(worst, rel_err(o.reshape(B * Hv, d)[idx].cpu().numpy(), o_ref))
+    es = rel_err(state.reshape(B * Hv, d, d)[idx].cpu().numpy(), ref)
+    print(f"kda batched decode: o {worst:.3e} state {es:.3e}")
+    assert worst <= 1e-4 and es <= 1e-4
+
+
+def test_kda_storage_options(gdn):
+    """float16 o equals the float32 o rounded; float16 states widen and round as stored."""
+    import torch
+    x = inputs.generate(1, 90, 2, 4, 128, "bf16", seed=130, init_state="normal")
+    g = dev(inputs.generate_channel_decay((1, 4, 90, 128), seed=131))
+    q, k, v = qkv_dev(x)
+    s16 = torch.from_numpy(x.s0.astype(np.float16)).cuda()
+    o32, f32 = gdn.kda_prefill(q, k, v, g, dev(x.beta), s16.float(), scale=x.scale)
+    o16, f16 = gdn.kda_prefill(q, k, v, g, dev(x.beta), s16, scale=x.scale, o_dtype=torch.float16)
+    assert torch.equal(o16, o32.half()) and torch.equal(f16, f32.half())
