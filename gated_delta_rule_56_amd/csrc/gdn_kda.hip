@@ -8,11 +8,15 @@
 // The batched decode step of this variant is the decode kernel's per-channel branch.
 //
 // A recurrent kernel, one token after the other. A workgroup keeps 16 state rows of one (b, h)
-// in registers: 8 compute waves of 2 rows (a row is 32 lanes x 4 columns), two waves per SIMD so
-// that one wave's shuffle reductions overlap the other's arithmetic. A ninth wave streams the
-// inputs in blocks of 16 tokens (k, q, the per-channel g, this block's v columns, beta) straight
-// into a 3-slot LDS ring, two blocks ahead, with exact vmcnt waits; one LDS-only barrier per
-// block. Tokens past the end run as no-op steps (g = 0, beta = 0 leave the state unchanged).
+// in registers: 8 compute waves of 2 rows (a row is 32 lanes x 4 columns), two waves per SIMD.
+// A ninth wave streams the inputs in blocks of 16 tokens (k, q, the per-channel g, this block's v
+// columns, beta) straight into a 4-slot LDS ring, three blocks ahead, with exact vmcnt waits.
+// What does not depend on the state row is formed once per block rather than once per row: while
+// the compute waves run block c, they also turn block c + 1 into alpha = exp(g), alpha k,
+// alpha q (float32), beta and k . q per token, in a double-buffered LDS area. The token step is
+// then two dot products with their 32-lane row sums (DPP adds and one swizzle), the update, and
+// o, which each row keeps in a register per token and stores once per block. One LDS-only
+// barrier per block. Tokens past the end run as no-op steps (alpha = 1, beta = 0).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -25,18 +29,32 @@ constexpr int kCompute = 8;                 // compute waves, 2 rows each
 constexpr int kThreads = 64 * (kCompute + 1);
 constexpr int kLPR = kD / 4;                // lanes per state row
 constexpr int kBlock = 16;                  // tokens per ring slot
-constexpr int kSlots = 3;
+constexpr int kSlots = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// ring slot layout (bytes), sized for float32 q/k/v
-constexpr int oK = 0;                        // [16][128] q/k element
-constexpr int oQ = oK + kBlock * kD * 4;     // [16][128]
-constexpr int oG = oQ + kBlock * kD * 4;     // [16][128] float
-constexpr int oV = oG + kBlock * kD * 4;     // [16][16] this block's v columns
-constexpr int oB = oV + kBlock * 16 * 4;     // [64] float (beta in the first 16)
-constexpr int kSlotBytes = oB + 64 * 4;
-constexpr int kSmemBytes = kSlots * kSlotBytes;
+// LDS layout (bytes) for q/k/v element E
+template <typename E>
+struct KdaSmem {
+    static constexpr int ES = sizeof(E);
+    // input ring slot
+    static constexpr int oK = 0;                          // [16][128] E
+    static constexpr int oQ = oK + kBlock * kD * ES;      // [16][128] E
+    static constexpr int oG = oQ + kBlock * kD * ES;      // [16][128] float
+    static constexpr int oV = oG + kBlock * kD * 4;       // [16][16] E (1 KB: one load of 64 lanes)
+    static constexpr int oB = oV + 1024;                  // [64] float (beta in the first 16)
+    static constexpr int kSlotBytes = oB + 256;
+    static constexpr int kRing = kSlots * kSlotBytes;
+    // per-block operands, two buffers
+    static constexpr int pAL = 0;                         // [16][128] float alpha
+    static constexpr int pAK = pAL + kBlock * kD * 4;     // [16][128] float alpha k
+    static constexpr int pAQ = pAK + kBlock * kD * 4;     // [16][128] float alpha q
+    static constexpr int pBK = pAQ + kBlock * kD * 4;     // [16] (beta, k . q)
+    static constexpr int kOpBytes = pBK + kBlock * 8;
+    static constexpr int kBytes = kRing + 2 * kOpBytes;
+    static_assert(kBytes <= 160 * 1024, "LDS");
+};
 
 __device__ __forceinline__ void dma16(const void *g, unsigned char *lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
@@ -53,21 +71,21 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// v from the lane given by a DPP control (quad permutes and row mirrors stay in the VALU)
+// x plus the value of the lane a DPP control names (all source lanes in range): folds into one
+// v_add_f32_dpp
 template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+__device__ __forceinline__ float add_dpp(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
 }
 
 // sum over the 32 lanes of a state row, in every lane of it: xor 1 and xor 2 (quad permutes),
 // the 8-lane and 16-lane mirrors, then xor 16 (a swizzle within each 32-lane half)
 __device__ __forceinline__ float row_sum(float x) {
-    x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-    x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-    x += dpp<0x141>(x);  // row_half_mirror
-    x += dpp<0x140>(x);  // row_mirror
-    x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));  // xor 16
-    return x;
+    x = add_dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x = add_dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    x = add_dpp<0x141>(x);  // row_half_mirror
+    x = add_dpp<0x140>(x);  // row_mirror
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));  // xor 16
 }
 
 template <typename E>
@@ -90,13 +108,14 @@ __device__ __forceinline__ float lds1(const unsigned char *p) {
 // E: q/k/v element (float, or uint16_t bfloat16 bits)
 template <typename E>
 __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams p) {
+    using L = KdaSmem<E>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int ES = sizeof(E);
     constexpr int kRowVec = 16 / ES;                    // elements per 16-byte load
     constexpr int kQKInstr = kBlock * kD * ES / 1024;   // 1 KB DMA instructions for k (and for q)
     constexpr int kGInstr = kBlock * kD * 4 / 1024;
     constexpr int kPerBlock = 2 * kQKInstr + kGInstr + 2;  // + v, + beta
-    static_assert(2 * kPerBlock <= 63, "vmcnt range");
+    static_assert(kPerBlock <= 63, "vmcnt range");
 
     const int pair = blockIdx.x / (kD / kRowsPerWG), rb = blockIdx.x % (kD / kRowsPerWG);
     const int b = pair / p.Hv, h = pair % p.Hv;
@@ -112,43 +131,42 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
         const E *vg = static_cast<const E *>(p.v) + (int64_t)pair * p.Ts * kD + rb * kRowsPerWG;
         const float *gg = p.g + (int64_t)pair * p.Ts * kD;
         const float *bg = p.beta + (int64_t)pair * p.Ts;
-        // block c (< nb) into slot c % 3, tokens past the end clamped to the last one
+        // block c (< nb) into slot c % 4, tokens past the end clamped to the last one
         auto issue = [&](int c) {
-            unsigned char *s = smem + (c % kSlots) * kSlotBytes;
+            unsigned char *s = smem + (c % kSlots) * L::kSlotBytes;
             const int t0 = c * kBlock;
 #pragma unroll
             for (int i = 0; i < kQKInstr; ++i) {
                 const int e = (i * 64 + lane) * kRowVec;  // element of the [16][128] block
                 const int64_t src = (int64_t)min(t0 + e / kD, T - 1) * kD + e % kD;
-                dma16(kg + src, s + oK + i * 1024);
-                dma16(qg + src, s + oQ + i * 1024);
+                dma16(kg + src, s + L::oK + i * 1024);
+                dma16(qg + src, s + L::oQ + i * 1024);
             }
 #pragma unroll
             for (int i = 0; i < kGInstr; ++i) {
                 const int e = (i * 64 + lane) * 4;
-                dma16(gg + (int64_t)min(t0 + e / kD, T - 1) * kD + e % kD, s + oG + i * 1024);
+                dma16(gg + (int64_t)min(t0 + e / kD, T - 1) * kD + e % kD, s + L::oG + i * 1024);
             }
             {  // v: 16 columns of each token, 16 / kRowVec lanes per token
                 constexpr int lpt = 16 / kRowVec;
                 const int t = min(t0 + min(lane / lpt, kBlock - 1), T - 1);
-                dma16(vg + (int64_t)t * kD + (lane % lpt) * kRowVec, s + oV);
+                dma16(vg + (int64_t)t * kD + (lane % lpt) * kRowVec, s + L::oV);
             }
-            dma4(bg + min(t0 + min(lane, kBlock - 1), T - 1), s + oB);
+            dma4(bg + min(t0 + min(lane, kBlock - 1), T - 1), s + L::oB);
         };
-        if (nb > 1) {
-            issue(0);
-            issue(1);
-            wait_vmcnt<kPerBlock>();  // block 0 has landed
-        } else if (nb == 1) {
-            issue(0);
+        for (int c = 0; c < min(nb, 3); ++c) issue(c);
+        if (nb >= 3)
+            wait_vmcnt<kPerBlock>();  // blocks 0 and 1 have landed
+        else
             wait_vmcnt<0>();
-        }
+        lds_barrier();
         lds_barrier();
         for (int c = 0; c < nb; ++c) {
-            // slot (c + 2) % 3 held block c - 1, which every compute wave finished before this barrier
-            if (c + 2 < nb) {
-                issue(c + 2);
-                wait_vmcnt<kPerBlock>();  // block c + 1 has landed
+            // slot (c + 3) % 4 held block c - 1: run in the interval before the last barrier and
+            // its operands formed in the one before that
+            if (c + 3 < nb) {
+                issue(c + 3);
+                wait_vmcnt<kPerBlock>();  // block c + 2 has landed
             } else {
                 wait_vmcnt<0>();
             }
@@ -159,53 +177,92 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
     }
 
     // -------------------------------------------------------------------- compute waves
-    const int col = (lane % kLPR) * 4;
+    const int ci = lane % kLPR;
+    const int col = ci * 4;
     const int lrow = wave * 2 + lane / kLPR;              // row within the workgroup
     const int row = rb * kRowsPerWG + lrow;
     const int64_t si = ((int64_t)pair * kD + row) * kD + col;
     f32x4 S = p.init_state ? load_state4(p.init_state, si, p.init_f16) : f32x4{0.f, 0.f, 0.f, 0.f};
     const int64_t obase = (int64_t)pair * p.Ts * kD + row;
 
+    // operands of block cb (ring slot cb % 4) into buffer cb & 1: the 512 compute lanes take
+    // token pu = (64 wave + lane) / 32, channels pj .. pj + 3
+    const int pu = (wave * 64 + lane) >> 5, pj = ci * 4;
+    auto form = [&](int cb) {
+        const unsigned char *s = smem + (cb % kSlots) * L::kSlotBytes;
+        unsigned char *ob = smem + L::kRing + (cb & 1) * L::kOpBytes;
+        const bool live = cb * kBlock + pu < T;
+        const f32x4 k = lds4<E>(s + L::oK + (pu * kD + pj) * ES);
+        const f32x4 q = lds4<E>(s + L::oQ + (pu * kD + pj) * ES);
+        const f32x4 g = *reinterpret_cast<const f32x4 *>(s + L::oG + (pu * kD + pj) * 4);
+        const float beta = *reinterpret_cast<const float *>(s + L::oB + pu * 4);
+        f32x4 al, ak, aq;
+        float kq = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            al[e] = live ? __expf(g[e]) : 1.0f;
+            ak[e] = al[e] * k[e];
+            aq[e] = al[e] * q[e];
+            kq += k[e] * q[e];
+        }
+        kq = row_sum(kq);
+        const int off = (pu * kD + pj) * 4;
+        *reinterpret_cast<f32x4 *>(ob + L::pAL + off) = al;
+        *reinterpret_cast<f32x4 *>(ob + L::pAK + off) = ak;
+        *reinterpret_cast<f32x4 *>(ob + L::pAQ + off) = aq;
+        if (ci == 0) *reinterpret_cast<f32x2 *>(ob + L::pBK + pu * 8) = f32x2{live ? beta : 0.0f, kq};
+    };
+
+    lds_barrier();  // blocks 0 and 1 have landed
+    if (nb > 0) form(0);
     lds_barrier();
     for (int c = 0; c < nb; ++c) {
-        const unsigned char *s = smem + (c % kSlots) * kSlotBytes;
+        if (c + 1 < nb) form(c + 1);
+        const unsigned char *s = smem + (c % kSlots) * L::kSlotBytes;
+        const unsigned char *ob = smem + L::kRing + (c & 1) * L::kOpBytes;
+        float ov = 0.0f;  // o of token c * 16 + ci, row lrow (lanes ci < 16)
 #pragma unroll
         for (int u = 0; u < kBlock; ++u) {
-            const int t = c * kBlock + u;
-            const bool live = t < T;
-            const f32x4 k = lds4<E>(s + oK + (u * kD + col) * ES);
-            const f32x4 q = lds4<E>(s + oQ + (u * kD + col) * ES);
-            const f32x4 g = *reinterpret_cast<const f32x4 *>(s + oG + (u * kD + col) * 4);
-            const float v = lds1<E>(s + oV + (u * 16 + lrow) * ES);
-            const float beta = live ? *reinterpret_cast<const float *>(s + oB + u * 4) : 0.0f;
-            f32x4 al, ak, aq;
-            float kq = 0.0f, r = 0.0f, pq = 0.0f;
+            const int off = (u * kD + col) * 4;
+            const f32x4 al = *reinterpret_cast<const f32x4 *>(ob + L::pAL + off);
+            const f32x4 ak = *reinterpret_cast<const f32x4 *>(ob + L::pAK + off);
+            const f32x4 aq = *reinterpret_cast<const f32x4 *>(ob + L::pAQ + off);
+            const f32x2 bk = *reinterpret_cast<const f32x2 *>(ob + L::pBK + u * 8);
+            const f32x4 k = lds4<E>(s + L::oK + (u * kD + col) * ES);
+            const float v = lds1<E>(s + L::oV + (u * 16 + lrow) * ES);
+            float r = 0.0f, pq = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                al[e] = live ? __expf(g[e]) : 1.0f;
-                ak[e] = al[e] * k[e];
-                aq[e] = al[e] * q[e];
-                kq += k[e] * q[e];
                 r += S[e] * ak[e];
                 pq += S[e] * aq[e];
             }
-            kq = row_sum(kq);
             r = row_sum(r);
             pq = row_sum(pq);
-            const float delta = beta * (v - r);
+            const float delta = bk[0] * (v - r);
 #pragma unroll
             for (int e = 0; e < 4; ++e) S[e] = al[e] * S[e] + delta * k[e];
-            if (col == 0 && live) {
-                const float oi = p.scale * (pq + delta * kq);
-                if (p.o_f16)
-                    static_cast<_Float16 *>(p.o)[obase + (int64_t)t * kD] = (_Float16)oi;
-                else
-                    static_cast<float *>(p.o)[obase + (int64_t)t * kD] = oi;
-            }
+            if (ci == u) ov = p.scale * (pq + delta * bk[1]);
+        }
+        const int t = c * kBlock + ci;
+        if (ci < kBlock && t < T) {
+            if (p.o_f16)
+                static_cast<_Float16 *>(p.o)[obase + (int64_t)t * kD] = (_Float16)ov;
+            else
+                static_cast<float *>(p.o)[obase + (int64_t)t * kD] = ov;
         }
         lds_barrier();
     }
     if (p.final_state) store_state4(p.final_state, si, S, p.final_f16);
+}
+
+template <typename E>
+hipError_t launch_e(const PrefillParams &p, int64_t blocks, hipStream_t stream) {
+    constexpr int bytes = KdaSmem<E>::kBytes;
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_kda_prefill_kernel<E>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((gdn_kda_prefill_kernel<E>), dim3((unsigned)blocks), dim3(kThreads), bytes, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -214,17 +271,7 @@ hipError_t launch_kda_prefill(const PrefillParams &p, bool bf16, hipStream_t str
     if (p.D != kD) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)p.B * p.Hv * (kD / kRowsPerWG);
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    const void *fn = bf16 ? reinterpret_cast<const void *>(&gdn_kda_prefill_kernel<uint16_t>)
-                          : reinterpret_cast<const void *>(&gdn_kda_prefill_kernel<float>);
-    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
-    if (err != hipSuccess) return err;
-    if (bf16)
-        hipLaunchKernelGGL((gdn_kda_prefill_kernel<uint16_t>), dim3((unsigned)blocks), dim3(kThreads), kSmemBytes,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((gdn_kda_prefill_kernel<float>), dim3((unsigned)blocks), dim3(kThreads), kSmemBytes,
-                           stream, p);
-    return hipGetLastError();
+    return bf16 ? launch_e<uint16_t>(p, blocks, stream) : launch_e<float>(p, blocks, stream);
 }
 
 }  // namespace gdn
