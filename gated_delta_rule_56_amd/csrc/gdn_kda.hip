@@ -13,7 +13,8 @@
 // columns, beta) straight into a 4-slot LDS ring, three blocks ahead, with exact vmcnt waits.
 // What does not depend on the state row is formed once per block rather than once per row: while
 // the compute waves run block c, they also turn block c + 1 into alpha = exp(g), alpha k,
-// alpha q (float32), beta and k . q per token, in a double-buffered LDS area. The token step is
+// alpha q (float32; also k itself for bfloat16 inputs), beta and k . q per token, in a
+// double-buffered LDS area. The token step is
 // then two dot products with their 32-lane row sums (DPP adds and one swizzle), the update, and
 // o, which each row keeps in a register per token and stores once per block. One LDS-only
 // barrier per block. Tokens past the end run as no-op steps (alpha = 1, beta = 0).
@@ -51,7 +52,8 @@ struct KdaSmem {
     static constexpr int pAK = pAL + kBlock * kD * 4;     // [16][128] float alpha k
     static constexpr int pAQ = pAK + kBlock * kD * 4;     // [16][128] float alpha q
     static constexpr int pBK = pAQ + kBlock * kD * 4;     // [16] (beta, k . q)
-    static constexpr int kOpBytes = pBK + kBlock * 8;
+    static constexpr int pKF = pBK + kBlock * 8;          // [16][128] float k (bfloat16 inputs only)
+    static constexpr int kOpBytes = pKF + (ES == 2 ? kBlock * kD * 4 : 0);
     static constexpr int kBytes = kRing + 2 * kOpBytes;
     static_assert(kBytes <= 160 * 1024, "LDS");
 };
@@ -210,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
         *reinterpret_cast<f32x4 *>(ob + L::pAL + off) = al;
         *reinterpret_cast<f32x4 *>(ob + L::pAK + off) = ak;
         *reinterpret_cast<f32x4 *>(ob + L::pAQ + off) = aq;
+        if constexpr (ES == 2) *reinterpret_cast<f32x4 *>(ob + L::pKF + off) = k;
         if (ci == 0) *reinterpret_cast<f32x2 *>(ob + L::pBK + pu * 8) = f32x2{live ? beta : 0.0f, kq};
     };
 
@@ -228,7 +231,11 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
             const f32x4 ak = *reinterpret_cast<const f32x4 *>(ob + L::pAK + off);
             const f32x4 aq = *reinterpret_cast<const f32x4 *>(ob + L::pAQ + off);
             const f32x2 bk = *reinterpret_cast<const f32x2 *>(ob + L::pBK + u * 8);
-            const f32x4 k = lds4<E>(s + L::oK + (u * kD + col) * ES);
+            f32x4 k;
+            if constexpr (ES == 2)
+                k = *reinterpret_cast<const f32x4 *>(ob + L::pKF + off);
+            else
+                k = lds4<E>(s + L::oK + (u * kD + col) * ES);
             const float v = lds1<E>(s + L::oV + (u * 16 + lrow) * ES);
             float r = 0.0f, pq = 0.0f;
 #pragma unroll
