@@ -212,6 +212,33 @@ def main():
                                                  dg[i % nsteps_dec], db[i % nsteps_dec], dstate16,
                                                  scale=dx.scale, o=do), args.steps)
     d16_bytes = decode_bytes(dB, dHk, dHv, dd, state_bytes=2)
+
+    # one sequence (B = 1): a step moves 4.2 MB, so launch overhead decides; the decode sequence
+    # back to back as eager calls, and captured in one HIP graph
+    s1 = state[:1].clone()
+    o1 = torch.empty((1, dHv, dd), dtype=torch.float32, device=dev)
+
+    def one(s):
+        binding.decode(dq[s][:1], dk[s][:1], dv[s][:1], dg[s][:1], db[s][:1], s1, scale=dx.scale, o=o1)
+
+    for s in range(max(1, args.warmup)):
+        one(s)
+    torch.cuda.synchronize()
+    b1_eager_ms = time_batch(lambda i: one(i % nsteps_dec), nsteps_dec)
+    g1 = torch.cuda.CUDAGraph()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g1, stream=side):
+            for s in range(nsteps_dec):
+                one(s)
+    stream.wait_stream(side)
+    g1.replay()
+    torch.cuda.synchronize()
+    b1_graph_ms = time_batch(lambda i: g1.replay(), 4) / nsteps_dec
+    if not torch.isfinite(s1).all():
+        raise RuntimeError("non-finite state after the single-sequence decode")
+    b1_bytes = decode_bytes(1, dHk, dHv, dd)
+    del g1, s1, o1
     if not torch.isfinite(dstate16).all():
         raise RuntimeError("non-finite float16 state")
     del dstate16
@@ -357,6 +384,14 @@ def main():
                 "frac": d16_bytes / (d16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 "algorithmic_bytes_per_launch": d16_bytes,
                 "sequence_updates_per_s": dB / (d16_ms * 1e-3),
+            },
+            "single_sequence": {
+                "what": f"B = 1, {nsteps_dec} consecutive in-place steps, per step: eager calls back to back, "
+                        "and the same steps captured in one HIP graph",
+                "eager_step_us": b1_eager_ms * 1e3,
+                "graph_step_us": b1_graph_ms * 1e3,
+                "algorithmic_bytes_per_step": b1_bytes,
+                "graph_achieved": b1_bytes / (b1_graph_ms * 1e-3) / 1e9,
             },
             "graph": {
                 "what": f"{nsteps_dec} consecutive in-place steps captured in one HIP graph, per step",

@@ -11,7 +11,9 @@
 // reference test (compare page "27b 935/47", gated_delta_decode test), which
 // reads the output off the pre-update state as alpha S q + delta (k . q).
 //
-// Mapping: one workgroup (4 waves) per (b, h); a state row is spread over
+// Mapping: one workgroup (4 waves) per (b, h), or, when there are fewer (b, h) pairs than
+// compute units (a single sequence has 32), SPLIT workgroups per (b, h) that take D / SPLIT
+// state rows each, so that every CU streams its share; a state row is spread over
 // lanes holding 16 bytes each (4 float32 or 8 float16 values; 8 bytes for
 // float16 at D = 32), so each access of a wave covers whole 128-byte lines. Each lane first issues all of its
 // row loads (D/4 * 16 bytes per lane for D = 128) to keep HBM busy, then
@@ -65,7 +67,12 @@ struct StateRow {
     __device__ __forceinline__ static void store(SD *p, const float *y) {
         vec v;
 #pragma unroll
-        for (int e = 0; e < N; ++e) v[e] = (SD)y[e];  // float16: round to nearest even
+        for (int e = 0; e < N; ++e) {
+            if constexpr (sizeof(SD) == 2)
+                v[e] = f16_out(y[e]);  // round to nearest even
+            else
+                v[e] = y[e];
+        }
         __builtin_nontemporal_store(v, reinterpret_cast<vec *>(p));
     }
 };
@@ -83,17 +90,28 @@ template <int D, typename SD>
 constexpr int cols_per_lane() { return sizeof(SD) == 2 && D >= 64 ? 8 : 4; }
 
 // T: q/k/v element (float or bfloat16 bits); SD: state element (float or _Float16);
-// kKda: one decay per key channel (g [B][Hv][D]) instead of one per head
-template <int D, typename T, typename SD, bool kKda>
+// workgroups per (b, h) when the pairs alone do not fill the GPU: as many as keep every wave at
+// one full access of rows or more, at most 8
+template <int D, typename SD>
+constexpr int max_split() {
+    constexpr int rpa = 64 / (D / cols_per_lane<D, SD>());
+    constexpr int s = D / ((kDecodeThreads / 64) * rpa);
+    return s > 8 ? 8 : s;
+}
+
+// kKda: one decay per key channel (g [B][Hv][D]) instead of one per head; SPLIT: workgroups per
+// (b, h), each taking D / SPLIT consecutive rows
+template <int D, typename T, typename SD, bool kKda, int SPLIT>
 __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams p) {
     constexpr int CPL = cols_per_lane<D, SD>();
     constexpr int LPR = D / CPL;                    // lanes per state row
     constexpr int RPA = 64 / LPR;                   // rows per wave per access
-    constexpr int ROWS_PER_WAVE = D / (kDecodeThreads / 64);
+    constexpr int ROWS_PER_WAVE = D / SPLIT / (kDecodeThreads / 64);
     constexpr int ITERS = ROWS_PER_WAVE / RPA;
     static_assert(ITERS >= 1 && ROWS_PER_WAVE % RPA == 0, "row split");
 
-    const int pair = blockIdx.x;
+    const int pair = blockIdx.x / SPLIT;
+    const int part = blockIdx.x % SPLIT;
     const int b = pair / p.Hv, h = pair % p.Hv;
     const int kh = key_head(h, p.Hk, p.Hv, p.head_map);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -105,7 +123,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
     const T *vp = static_cast<const T *>(p.v) + ((int64_t)b * p.Hv + h) * D;
     SD *S = static_cast<SD *>(p.state) + (int64_t)pair * D * D;
 
-    const int row0 = wave * ROWS_PER_WAVE + sub;
+    const int row0 = part * (D / SPLIT) + wave * ROWS_PER_WAVE + sub;
     StateRow<CPL, SD> s[ITERS];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) s[it].load(S + (int64_t)(row0 + it * RPA) * D + col);
@@ -152,31 +170,46 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
         const float delta = beta * (vrow[it] - alpha * rk);  // alpha = 1 with per-channel decay
         float y[CPL];
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) y[e] = (kKda ? al[e] : alpha) * s[it].get(e) + delta * kv[e];
+        for (int e = 0; e < CPL; ++e)  // one explicit fma: every instantiation rounds the same way
+            y[e] = __builtin_fmaf(delta, kv[e], (kKda ? al[e] : alpha) * s[it].get(e));
         const int row = row0 + it * RPA;
         StateRow<CPL, SD>::store(S + (int64_t)row * D + col, y);
         if (col == 0) {
             const float oi = as * rq + delta * kappa;
             if (p.o_f16)
-                static_cast<_Float16 *>(p.o)[(int64_t)pair * D + row] = (_Float16)oi;
+                static_cast<_Float16 *>(p.o)[(int64_t)pair * D + row] = f16_out(oi);
             else
                 static_cast<float *>(p.o)[(int64_t)pair * D + row] = oi;
         }
     }
 }
 
+// fewer (b, h) pairs than this: split each pair's rows over max_split workgroups
+constexpr int64_t kSplitBelow = 256;
+
+template <int D, typename T, typename SD, bool kKda>
+void launch_sd(const DecodeParams &p, hipStream_t stream) {
+    constexpr int S = max_split<D, SD>();
+    const int64_t pairs = (int64_t)p.B * p.Hv;
+    if (S > 1 && pairs < kSplitBelow)
+        hipLaunchKernelGGL((gdn_decode_kernel<D, T, SD, kKda, S>), dim3((unsigned)(pairs * S)), dim3(kDecodeThreads),
+                           0, stream, p);
+    else
+        hipLaunchKernelGGL((gdn_decode_kernel<D, T, SD, kKda, 1>), dim3((unsigned)pairs), dim3(kDecodeThreads), 0,
+                           stream, p);
+}
+
 template <int D, typename T>
 hipError_t launch_dt(const DecodeParams &p, hipStream_t stream) {
-    dim3 grid((unsigned)(p.B * p.Hv)), block(kDecodeThreads);
     if (p.kda) {
         if (p.state_f16)
-            hipLaunchKernelGGL((gdn_decode_kernel<D, T, _Float16, true>), grid, block, 0, stream, p);
+            launch_sd<D, T, _Float16, true>(p, stream);
         else
-            hipLaunchKernelGGL((gdn_decode_kernel<D, T, float, true>), grid, block, 0, stream, p);
+            launch_sd<D, T, float, true>(p, stream);
     } else if (p.state_f16) {
-        hipLaunchKernelGGL((gdn_decode_kernel<D, T, _Float16, false>), grid, block, 0, stream, p);
+        launch_sd<D, T, _Float16, false>(p, stream);
     } else {
-        hipLaunchKernelGGL((gdn_decode_kernel<D, T, float, false>), grid, block, 0, stream, p);
+        launch_sd<D, T, float, false>(p, stream);
     }
     return hipGetLastError();
 }

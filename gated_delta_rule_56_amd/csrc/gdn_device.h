@@ -43,6 +43,15 @@ __device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
     return f16x4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
 }
 
+// A stored result in float16: its float32 value rounded to nearest even. The empty asm hides
+// how x was computed, so the compiler cannot merge the conversion into the operation that
+// produced x (an fma with a float16 result rounds once from the exact value, which can differ
+// in the last place and would make results depend on how a kernel was instantiated).
+__device__ __forceinline__ _Float16 f16_out(float x) {
+    asm("" : "+v"(x));
+    return (_Float16)x;
+}
+
 // 4 consecutive state values at element index i of a float32 or float16 state.
 __device__ __forceinline__ f32x4 load_state4(const void *base, int64_t i, bool f16) {
     if (f16) {
@@ -55,7 +64,8 @@ __device__ __forceinline__ f32x4 load_state4(const void *base, int64_t i, bool f
 // ... and stored, float16 rounded to nearest even.
 __device__ __forceinline__ void store_state4(void *base, int64_t i, f32x4 v, bool f16) {
     if (f16)
-        *reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(base) + i) = to_f16x4(v);
+        *reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(base) + i) =
+            f16x4{f16_out(v[0]), f16_out(v[1]), f16_out(v[2]), f16_out(v[3])};
     else
         *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + i) = v;
 }

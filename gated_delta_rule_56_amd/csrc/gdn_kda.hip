@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
         const int t = c * kBlock + ci;
         if (ci < kBlock && t < T) {
             if (p.o_f16)
-                static_cast<_Float16 *>(p.o)[obase + (int64_t)t * kD] = (_Float16)ov;
+                static_cast<_Float16 *>(p.o)[obase + (int64_t)t * kD] = f16_out(ov);
             else
                 static_cast<float *>(p.o)[obase + (int64_t)t * kD] = ov;
         }

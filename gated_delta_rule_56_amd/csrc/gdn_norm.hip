@@ -45,7 +45,8 @@ __device__ __forceinline__ void store_o4(float *p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
 }
 __device__ __forceinline__ void store_o4(_Float16 *p, f32x4 v) {
-    __builtin_nontemporal_store(to_f16x4(v), reinterpret_cast<f16x4 *>(p));
+    __builtin_nontemporal_store(f16x4{f16_out(v[0]), f16_out(v[1]), f16_out(v[2]), f16_out(v[3])},
+                                reinterpret_cast<f16x4 *>(p));
 }
 
 // OT: float or _Float16 o; GT: uint16_t (bfloat16 bits) or float gate; kGate false: no gate factor

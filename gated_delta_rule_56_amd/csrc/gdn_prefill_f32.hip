@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
             const int i = e / D, j = e % D;
             const int64_t si = sbase + (int64_t)i * D + j;
             if (p.final_f16)
-                static_cast<_Float16 *>(p.final_state)[si] = (_Float16)S[i * L::QP + j];
+                static_cast<_Float16 *>(p.final_state)[si] = f16_out(S[i * L::QP + j]);
             else
                 static_cast<float *>(p.final_state)[si] = S[i * L::QP + j];
         }

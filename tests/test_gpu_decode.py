@@ -92,3 +92,28 @@ def test_decode_repeatable(gdn):
         torch.cuda.synchronize()
         outs.append((o.cpu().numpy(), state.cpu().numpy()))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("state16", [False, True])
+@pytest.mark.parametrize("kda", [False, True])
+def test_decode_row_split_is_exact(gdn, state16, kda):
+    """Fewer (b, h) pairs than compute units split each pair's rows over several workgroups; the
+    arithmetic of a row does not change, so one sequence alone (32 pairs, split) and the same
+    sequence first in a batch of 8 (256 pairs, not split) agree bit for bit."""
+    import torch
+    B, Hk, Hv, d = 8, 16, 32, 128
+    x = inputs.generate(B, 1, Hk, Hv, d, "bf16", seed=91, init_state="normal", decode_steps=1)
+    st = _step_inputs(x, 0)
+    q, k, v = qkv_dev(st)
+    beta = dev(st.beta)
+    g = dev(inputs.generate_channel_decay((B, Hv, d), seed=92)) if kda else dev(st.g)
+    sdt = torch.float16 if state16 else torch.float32
+    full = dev(x.s0).to(sdt)
+    one = full[:1].clone()
+    call = gdn.kda_decode if kda else gdn.decode
+    o_full = call(q, k, v, g, beta, full, scale=x.scale)
+    o_one = call(q[:1], k[:1], v[:1], g[:1], beta[:1], one, scale=x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_one[0], o_full[0])
+    assert torch.equal(one[0], full[0])
+

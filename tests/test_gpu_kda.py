@@ -31,7 +31,8 @@ def check(oracle_lib, x, g, o, sf, tol, head_map=0, pairs=None, label=""):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("T", [1, 37, 200])
+# the kernel streams 16-token blocks three ahead: one, two, three and four blocks, whole and ragged
+@pytest.mark.parametrize("T", [1, 16, 37, 48, 64, 200])
 @pytest.mark.parametrize("head_map", [0, 1])
 def test_kda_prefill_small(gdn, oracle_lib, dtype, T, head_map):
     x = inputs.generate(2, T, 2, 4, 128, dtype, seed=120 + T, init_state="normal")
@@ -40,6 +41,18 @@ def test_kda_prefill_small(gdn, oracle_lib, dtype, T, head_map):
     o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), head_map=head_map, scale=x.scale)
     check(oracle_lib, x, g, o.cpu().numpy(), sf.cpu().numpy(), tol_for(x), head_map=head_map,
           label=f"kda {dtype} T{T} map{head_map}")
+
+
+def test_kda_prefill_empty(gdn):
+    """No tokens: o is empty and the final state is the initial state, bit for bit."""
+    import torch
+    x = inputs.generate(2, 0, 2, 4, 128, "bf16", seed=126, init_state="normal")
+    g = inputs.generate_channel_decay((2, 4, 0, 128), seed=127)
+    q, k, v = qkv_dev(x)
+    s0 = dev(x.s0)
+    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), s0, scale=x.scale)
+    assert o.shape == (2, 4, 0, 128)
+    assert torch.equal(sf, s0)
 
 
 def test_kda_uniform_decay_is_gdn(gdn):
