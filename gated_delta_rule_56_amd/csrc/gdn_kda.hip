@@ -119,7 +119,12 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
     constexpr int kPerBlock = 2 * kQKInstr + kGInstr + 2;  // + v, + beta
     static_assert(kPerBlock <= 63, "vmcnt range");
 
-    const int pair = blockIdx.x / (kD / kRowsPerWG), rb = blockIdx.x % (kD / kRowsPerWG);
+    // workgroup -> (b, h, row block): the 8 row blocks of one (b, h), which read the same k, q and
+    // g, sit on one XCD and share its L2 (workgroups go round-robin over the 8 XCDs)
+    const int nwg = gridDim.x;
+    int lin = blockIdx.x;
+    if ((nwg & 7) == 0) lin = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int pair = lin / (kD / kRowsPerWG), rb = lin % (kD / kRowsPerWG);
     const int b = pair / p.Hv, h = pair % p.Hv;
     const int kh = key_head(h, p.Hk, p.Hv, p.head_map);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
