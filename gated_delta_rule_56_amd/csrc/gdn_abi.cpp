@@ -331,11 +331,12 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *s, void *o, const void *gate, cons
     const int64_t rows = (int64_t)s->batch * s->num_v_heads * s->seq_len;
     if (rows == 0) return GDN_OK;
     const bool bf16 = s->qkv_dtype == GDN_DTYPE_BF16;
+    const bool o16 = s->o_dtype == GDN_OUT_F16;
     GDN_TRY(check_ptr(o, "o", 16));
     GDN_TRY(check_ptr(weight, "weight", 16));
-    if (gate) GDN_TRY(check_ptr(gate, "gate", bf16 ? 8 : 16));
+    // a lane reads 4 (float32 o) or 8 (float16 o) gate values at once
+    if (gate) GDN_TRY(check_ptr(gate, "gate", bf16 && !o16 ? 8 : 16));
     const Range ins[] = {range("gate", gate, gate ? rows * d * (bf16 ? 2 : 4) : 0), range("weight", weight, d * 4)};
-    const bool o16 = s->o_dtype == GDN_OUT_F16;
     const Range outs[] = {range("o", o, rows * d * (o16 ? 2 : 4))};
     GDN_TRY(check_no_overlap(outs, 1, ins, 2));
     gdn::NormParams p;

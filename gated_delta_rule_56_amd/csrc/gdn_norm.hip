@@ -6,9 +6,10 @@
 // with weight [D] shared by all rows and the gate factor left out when there is
 // no gate.
 //
-// A pure streaming pass (HBM-bound): a row is D / 4 lanes x 16 bytes, so a
-// wave covers 64 / (D / 4) rows with coalesced 16-byte loads and stores; the
-// sum of squares is reduced across the row's lanes with xor shuffles.
+// A pure streaming pass (HBM-bound): a row is D / V lanes x 16 bytes (V = 4 float32
+// or 8 float16 values per lane), so a wave covers 64 V / D rows with coalesced
+// 16-byte loads and stores; the sum of squares is reduced across the row's lanes
+// with xor shuffles.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -19,64 +20,99 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-template <typename GT>
-__device__ __forceinline__ f32x4 load_gate(const GT *g);
+// A lane handles 16 bytes of o: 4 float32 or 8 float16 values (V), with the gate and the
+// weight loaded to match.
+template <int V>
+struct Vals {
+    float x[V];
+};
 
-template <>
-__device__ __forceinline__ f32x4 load_gate<uint16_t>(const uint16_t *g) {
-    const u16x4 u = __builtin_nontemporal_load(reinterpret_cast<const u16x4 *>(g));
-    return f32x4{bf16_bits_to_f32(u[0]), bf16_bits_to_f32(u[1]), bf16_bits_to_f32(u[2]), bf16_bits_to_f32(u[3])};
+__device__ __forceinline__ Vals<4> load_o(const float *p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return Vals<4>{{v[0], v[1], v[2], v[3]}};
+}
+__device__ __forceinline__ Vals<8> load_o(const _Float16 *p) {
+    const f16x8 h = __builtin_nontemporal_load(reinterpret_cast<const f16x8 *>(p));
+    Vals<8> r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.x[e] = (float)h[e];
+    return r;
+}
+// float16 o is rounded to nearest even on store
+__device__ __forceinline__ void store_o(float *p, const Vals<4> &y) {
+    __builtin_nontemporal_store(f32x4{y.x[0], y.x[1], y.x[2], y.x[3]}, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ void store_o(_Float16 *p, const Vals<8> &y) {
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = f16_out(y.x[e]);
+    __builtin_nontemporal_store(h, reinterpret_cast<f16x8 *>(p));
 }
 
-template <>
-__device__ __forceinline__ f32x4 load_gate<float>(const float *g) {
-    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(g));
+template <int V>
+__device__ __forceinline__ Vals<V> load_gate(const uint16_t *g) {  // bfloat16 bits
+    Vals<V> r;
+    if constexpr (V == 4) {
+        const u16x4 u = __builtin_nontemporal_load(reinterpret_cast<const u16x4 *>(g));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.x[e] = bf16_bits_to_f32(u[e]);
+    } else {
+        const u16x8 u = __builtin_nontemporal_load(reinterpret_cast<const u16x8 *>(g));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.x[e] = bf16_bits_to_f32(u[e]);
+    }
+    return r;
 }
-
-// 4 consecutive o values, float32 or float16 (rounded to nearest even on store)
-__device__ __forceinline__ f32x4 load_o4(const float *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-}
-__device__ __forceinline__ f32x4 load_o4(const _Float16 *p) {
-    const f16x4 h = __builtin_nontemporal_load(reinterpret_cast<const f16x4 *>(p));
-    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-}
-__device__ __forceinline__ void store_o4(float *p, f32x4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
-}
-__device__ __forceinline__ void store_o4(_Float16 *p, f32x4 v) {
-    __builtin_nontemporal_store(f16x4{f16_out(v[0]), f16_out(v[1]), f16_out(v[2]), f16_out(v[3])},
-                                reinterpret_cast<f16x4 *>(p));
+template <int V>
+__device__ __forceinline__ Vals<V> load_gate(const float *g) {
+    Vals<V> r;
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(g) + h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.x[4 * h + e] = v[e];
+    }
+    return r;
 }
 
 // OT: float or _Float16 o; GT: uint16_t (bfloat16 bits) or float gate; kGate false: no gate factor
 template <int D, typename OT, typename GT, bool kGate>
 __global__ __launch_bounds__(kThreads) void gdn_gated_rmsnorm_kernel(OT *o, const GT *gate, const float *weight,
                                                                      float eps, int64_t rows) {
-    constexpr int LPR = D / 4;     // lanes per row
-    constexpr int RPW = 64 / LPR;  // rows per wave
+    constexpr int V = 16 / sizeof(OT);  // values per lane
+    constexpr int LPR = D / V;          // lanes per row
+    constexpr int RPW = 64 / LPR;       // rows per wave
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int li = lane % LPR;
     const int64_t row = ((int64_t)blockIdx.x * (kThreads / 64) + w) * RPW + lane / LPR;
     if (row >= rows) return;  // whole row groups: the shuffles below stay inside a group
-    OT *px = o + row * D + 4 * li;
-    const f32x4 x = load_o4(px);
-    float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    OT *px = o + row * D + V * li;
+    const Vals<V> x = load_o(px);
+    Vals<V> g;
+    if constexpr (kGate) g = load_gate<V>(gate + row * D + V * li);
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) ss += x.x[e] * x.x[e];
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
     const float inv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-    const f32x4 wt = *reinterpret_cast<const f32x4 *>(weight + 4 * li);
-    f32x4 y = (x * inv) * wt;
-    if constexpr (kGate) {
-        const f32x4 g = load_gate<GT>(gate + row * D + 4 * li);
-        y = y * f32x4{silu(g[0]), silu(g[1]), silu(g[2]), silu(g[3])};
+    Vals<V> y;
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        const f32x4 wt = *reinterpret_cast<const f32x4 *>(weight + V * li + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float t = (x.x[4 * h + e] * inv) * wt[e];
+            if constexpr (kGate) t = t * silu(g.x[4 * h + e]);
+            y.x[4 * h + e] = t;
+        }
     }
-    store_o4(px, y);
+    store_o(px, y);
 }
 
 template <int D, typename OT>
 hipError_t launch_do(const NormParams &p, hipStream_t stream) {
-    constexpr int rows_per_block = (kThreads / 64) * (64 / (D / 4));
+    constexpr int rows_per_block = (kThreads / 64) * (64 / (D / (16 / (int)sizeof(OT))));
     const int64_t blocks = (p.rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(kThreads);

@@ -236,6 +236,8 @@ const char *gdn_last_error(void);
  *   weight  [dv] float32, the same for every head and token
  *   eps     finite, >= 0
  * Supported: head_dim_v in {16, 32, 64, 128}. gate and weight must not overlap o.
+ * Alignment: o, weight and a float32 gate 16 bytes; a bfloat16 gate 8 bytes with
+ * float32 o and 16 bytes with float16 o.
  * Not fused into gdn_prefill: there the dv values of one output row come from
  * dv / 16 different workgroups, so the row's norm would need a reduction
  * across workgroups; this call is one extra streaming pass over o.

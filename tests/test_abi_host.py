@@ -219,6 +219,9 @@ def test_gated_rmsnorm_rejects(lib, bnd):
     assert _norm(lib, shape, weight=None) == 1 and "weight is NULL" in _err(lib)
     assert _norm(lib, shape, o=7 * GB + 4) == 1 and "aligned" in _err(lib)
     assert _norm(lib, shape, gate=8 * GB + 2) == 1 and "aligned" in _err(lib)  # bf16 gate: 8-byte aligned
+    # with float16 o a lane reads 8 bf16 gate values: 16-byte aligned
+    f16 = _shape(bnd, seq_len=10, o_dtype=bnd.GDN_OUT_F16)
+    assert _norm(lib, f16, gate=8 * GB + 8) == 1 and "gate" in _err(lib) and "aligned" in _err(lib)
     assert _norm(lib, shape, gate=7 * GB + 4096) == 1 and "o overlaps gate" in _err(lib)
     assert _norm(lib, shape, weight=7 * GB + 512) == 1 and "o overlaps weight" in _err(lib)
     # no rows: nothing to check or launch
