@@ -2,20 +2,24 @@
 //   S_t = S_{t-1} diag(exp(g_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t (scale q_t)
 // with g_t one log-decay per key channel (the channel decay of the Kimi K3 experiments on the
 // "master..kimi_slop" page; with every channel alike it is the gated delta rule). Per token,
-// with alpha = exp(g_t) and the decayed state S diag(alpha):
-//   r = S (alpha k),  p = S (alpha q),  delta = beta (v - r)
-//   S <- S diag(alpha) + delta k^T,  o = scale (p + delta (k . q))
+// with alpha = exp(g_t) and the decayed state D = S diag(alpha):
+//   r = D k,  p = D q,  delta = beta (v - r)
+//   S <- D + delta k^T,  o = scale (p + delta (k . q))
 // The batched decode step of this variant is the decode kernel's per-channel branch.
 //
 // A recurrent kernel, one token after the other. A workgroup keeps 16 state rows of one (b, h)
-// in registers: 8 compute waves of 2 rows (a row is 32 lanes x 4 columns), two waves per SIMD.
-// A ninth wave streams the inputs in blocks of 16 tokens (k, q, the per-channel g, this block's v
+// in registers: 4 compute waves of 4 rows, one per SIMD; a row is 16 lanes x 8 columns (lane i
+// holds columns 4i .. 4i + 3 and 64 + 4i .. 64 + 4i + 3, so that the 16 lanes of a row read
+// 256 contiguous bytes of an operand row per LDS instruction). The row sums of the token step
+// then stay inside one 16-lane DPP row: four DPP adds, no cross-row swizzle.
+// A fifth wave streams the inputs in blocks of 16 tokens (k, q, the per-channel g, this block's v
 // columns, beta) straight into a 4-slot LDS ring, three blocks ahead, with exact vmcnt waits.
 // What does not depend on the state row is formed once per block rather than once per row: while
-// the compute waves run block c, they also turn block c + 1 into alpha = exp(g), alpha k,
-// alpha q (float32; also k itself for bfloat16 inputs), beta and k . q per token, in a
-// double-buffered LDS area. The token step is
-// then two dot products with their 32-lane row sums (DPP adds and one swizzle), the update, and
+// the compute waves run block c, they also turn block c + 1 into alpha = exp(g), k and q (all
+// float32), beta and k . q per token, in a double-buffered LDS area. Every row reads the three
+// vectors of every token, so the step is bound by LDS bandwidth (24 KB per token and
+// workgroup) about as much as by VALU issue. The token step is
+// then two dot products with their 16-lane row sums, the update, and
 // o, which each row keeps in a register per token and stores once per block. One LDS-only
 // barrier per block. Tokens past the end run as no-op steps (alpha = 1, beta = 0).
 #include "gdn_device.h"
@@ -26,11 +30,12 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kRowsPerWG = 16;
-constexpr int kCompute = 8;                 // compute waves, 2 rows each
+constexpr int kCompute = 4;                 // compute waves, 4 rows each
 constexpr int kThreads = 64 * (kCompute + 1);
-constexpr int kLPR = kD / 4;                // lanes per state row
+constexpr int kLPR = 16;                    // lanes per state row (8 columns each)
 constexpr int kBlock = 16;                  // tokens per ring slot
 constexpr int kSlots = 4;
+static_assert(kBlock == kLPR, "lane i of a row keeps the o of token i of a block");
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -49,11 +54,10 @@ struct KdaSmem {
     static constexpr int kRing = kSlots * kSlotBytes;
     // per-block operands, two buffers
     static constexpr int pAL = 0;                         // [16][128] float alpha
-    static constexpr int pAK = pAL + kBlock * kD * 4;     // [16][128] float alpha k
-    static constexpr int pAQ = pAK + kBlock * kD * 4;     // [16][128] float alpha q
-    static constexpr int pBK = pAQ + kBlock * kD * 4;     // [16] (beta, k . q)
-    static constexpr int pKF = pBK + kBlock * 8;          // [16][128] float k (bfloat16 inputs only)
-    static constexpr int kOpBytes = pKF + (ES == 2 ? kBlock * kD * 4 : 0);
+    static constexpr int pKF = pAL + kBlock * kD * 4;     // [16][128] float k
+    static constexpr int pQF = pKF + kBlock * kD * 4;     // [16][128] float q
+    static constexpr int pBK = pQF + kBlock * kD * 4;     // [16] (beta, k . q)
+    static constexpr int kOpBytes = pBK + kBlock * 8;
     static constexpr int kBytes = kRing + 2 * kOpBytes;
     static_assert(kBytes <= 160 * 1024, "LDS");
 };
@@ -80,14 +84,13 @@ __device__ __forceinline__ float add_dpp(float x) {
     return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
 }
 
-// sum over the 32 lanes of a state row, in every lane of it: xor 1 and xor 2 (quad permutes),
-// the 8-lane and 16-lane mirrors, then xor 16 (a swizzle within each 32-lane half)
+// sum over the 16 lanes of a state row (one DPP row), in every lane of it: xor 1 and xor 2
+// (quad permutes), then the 8-lane and 16-lane mirrors
 __device__ __forceinline__ float row_sum(float x) {
     x = add_dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
     x = add_dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
     x = add_dpp<0x141>(x);  // row_half_mirror
-    x = add_dpp<0x140>(x);  // row_mirror
-    return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));  // xor 16
+    return add_dpp<0x140>(x);  // row_mirror
 }
 
 template <typename E>
@@ -108,8 +111,19 @@ __device__ __forceinline__ float lds1(const unsigned char *p) {
 }
 
 // E: q/k/v element (float, or uint16_t bfloat16 bits)
+// Operands of one token for one lane: alpha, k and q at the lane's 8 columns, beta and k . q,
+// and v of the lane's row
+struct TokenOps {
+    f32x4 al0, al1, k0, k1, q0, q1;
+    f32x2 bk;
+    float v;
+};
+
+// At most two waves share a SIMD (one compute wave, plus the loader on one of them), so the
+// compiler may spend registers on holding the next token's operands.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void gdn_kda_prefill_kernel(PrefillParams p) {
     using L = KdaSmem<E>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     constexpr int ES = sizeof(E);
@@ -184,40 +198,46 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
     }
 
     // -------------------------------------------------------------------- compute waves
+    // lane: row lrow of the workgroup, columns col .. col + 3 and col + 64 .. col + 67
     const int ci = lane % kLPR;
     const int col = ci * 4;
-    const int lrow = wave * 2 + lane / kLPR;              // row within the workgroup
+    const int lrow = wave * (64 / kLPR) + lane / kLPR;
     const int row = rb * kRowsPerWG + lrow;
     const int64_t si = ((int64_t)pair * kD + row) * kD + col;
-    f32x4 S = p.init_state ? load_state4(p.init_state, si, p.init_f16) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = S0;
+    if (p.init_state) {
+        S0 = load_state4(p.init_state, si, p.init_f16);
+        S1 = load_state4(p.init_state, si + 64, p.init_f16);
+    }
     const int64_t obase = (int64_t)pair * p.Ts * kD + row;
 
-    // operands of block cb (ring slot cb % 4) into buffer cb & 1: the 512 compute lanes take
-    // token pu = (64 wave + lane) / 32, channels pj .. pj + 3
-    const int pu = (wave * 64 + lane) >> 5, pj = ci * 4;
+    // operands of block cb (ring slot cb % 4) into buffer cb & 1: the 256 compute lanes take
+    // token pu = (64 wave + lane) / 16, channels col .. col + 3 and col + 64 .. col + 67
+    const int pu = (wave * 64 + lane) / kLPR;
     auto form = [&](int cb) {
         const unsigned char *s = smem + (cb % kSlots) * L::kSlotBytes;
         unsigned char *ob = smem + L::kRing + (cb & 1) * L::kOpBytes;
         const bool live = cb * kBlock + pu < T;
-        const f32x4 k = lds4<E>(s + L::oK + (pu * kD + pj) * ES);
-        const f32x4 q = lds4<E>(s + L::oQ + (pu * kD + pj) * ES);
-        const f32x4 g = *reinterpret_cast<const f32x4 *>(s + L::oG + (pu * kD + pj) * 4);
         const float beta = *reinterpret_cast<const float *>(s + L::oB + pu * 4);
-        f32x4 al, ak, aq;
         float kq = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            al[e] = live ? __expf(g[e]) : 1.0f;
-            ak[e] = al[e] * k[e];
-            aq[e] = al[e] * q[e];
-            kq += k[e] * q[e];
+        for (int hh = 0; hh < 2; ++hh) {
+            const int pj = col + 64 * hh;
+            const f32x4 k = lds4<E>(s + L::oK + (pu * kD + pj) * ES);
+            const f32x4 q = lds4<E>(s + L::oQ + (pu * kD + pj) * ES);
+            const f32x4 g = *reinterpret_cast<const f32x4 *>(s + L::oG + (pu * kD + pj) * 4);
+            f32x4 al;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                al[e] = live ? __expf(g[e]) : 1.0f;
+                kq += k[e] * q[e];
+            }
+            const int off = (pu * kD + pj) * 4;
+            *reinterpret_cast<f32x4 *>(ob + L::pAL + off) = al;
+            *reinterpret_cast<f32x4 *>(ob + L::pKF + off) = k;
+            *reinterpret_cast<f32x4 *>(ob + L::pQF + off) = q;
         }
         kq = row_sum(kq);
-        const int off = (pu * kD + pj) * 4;
-        *reinterpret_cast<f32x4 *>(ob + L::pAL + off) = al;
-        *reinterpret_cast<f32x4 *>(ob + L::pAK + off) = ak;
-        *reinterpret_cast<f32x4 *>(ob + L::pAQ + off) = aq;
-        if constexpr (ES == 2) *reinterpret_cast<f32x4 *>(ob + L::pKF + off) = k;
         if (ci == 0) *reinterpret_cast<f32x2 *>(ob + L::pBK + pu * 8) = f32x2{live ? beta : 0.0f, kq};
     };
 
@@ -225,38 +245,56 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
     if (nb > 0) form(0);
     lds_barrier();
     for (int c = 0; c < nb; ++c) {
-        if (c + 1 < nb) form(c + 1);
+        // branch-free, so that the compiler can spread the forming of block c + 1 over the token
+        // steps of block c; past the last block it reads a ring slot no load is still writing
+        // and fills the buffer that no token step reads any more
+        form(c + 1);
         const unsigned char *s = smem + (c % kSlots) * L::kSlotBytes;
         const unsigned char *ob = smem + L::kRing + (c & 1) * L::kOpBytes;
-        float ov = 0.0f;  // o of token c * 16 + ci, row lrow (lanes ci < 16)
+        float ov = 0.0f;  // o of token c * 16 + ci, row lrow
+        auto load_ops = [&](int u) {
+            TokenOps x;
+            const int off0 = (u * kD + col) * 4, off1 = off0 + 64 * 4;
+            x.al0 = *reinterpret_cast<const f32x4 *>(ob + L::pAL + off0);
+            x.al1 = *reinterpret_cast<const f32x4 *>(ob + L::pAL + off1);
+            x.k0 = *reinterpret_cast<const f32x4 *>(ob + L::pKF + off0);
+            x.k1 = *reinterpret_cast<const f32x4 *>(ob + L::pKF + off1);
+            x.q0 = *reinterpret_cast<const f32x4 *>(ob + L::pQF + off0);
+            x.q1 = *reinterpret_cast<const f32x4 *>(ob + L::pQF + off1);
+            x.bk = *reinterpret_cast<const f32x2 *>(ob + L::pBK + u * 8);
+            x.v = lds1<E>(s + L::oV + (u * 16 + lrow) * ES);
+            return x;
+        };
+        // the operands of token u + 1 are read while token u runs: the state chain never waits on
+        // an LDS round trip
+        TokenOps cur = load_ops(0);
 #pragma unroll
         for (int u = 0; u < kBlock; ++u) {
-            const int off = (u * kD + col) * 4;
-            const f32x4 al = *reinterpret_cast<const f32x4 *>(ob + L::pAL + off);
-            const f32x4 ak = *reinterpret_cast<const f32x4 *>(ob + L::pAK + off);
-            const f32x4 aq = *reinterpret_cast<const f32x4 *>(ob + L::pAQ + off);
-            const f32x2 bk = *reinterpret_cast<const f32x2 *>(ob + L::pBK + u * 8);
-            f32x4 k;
-            if constexpr (ES == 2)
-                k = *reinterpret_cast<const f32x4 *>(ob + L::pKF + off);
-            else
-                k = lds4<E>(s + L::oK + (u * kD + col) * ES);
-            const float v = lds1<E>(s + L::oV + (u * 16 + lrow) * ES);
-            float r = 0.0f, pq = 0.0f;
+            TokenOps nxt;
+            if (u + 1 < kBlock) nxt = load_ops(u + 1);
+            float r0 = 0.0f, r1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                r += S[e] * ak[e];
-                pq += S[e] * aq[e];
+                S0[e] *= cur.al0[e];  // D = S diag(alpha)
+                S1[e] *= cur.al1[e];
+                r0 += S0[e] * cur.k0[e];
+                r1 += S1[e] * cur.k1[e];
+                p0 += S0[e] * cur.q0[e];
+                p1 += S1[e] * cur.q1[e];
             }
-            r = row_sum(r);
-            pq = row_sum(pq);
-            const float delta = bk[0] * (v - r);
+            const float r = row_sum(r0 + r1);
+            const float pq = row_sum(p0 + p1);
+            const float delta = cur.bk[0] * (cur.v - r);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[e] = al[e] * S[e] + delta * k[e];
-            if (ci == u) ov = p.scale * (pq + delta * bk[1]);
+            for (int e = 0; e < 4; ++e) {
+                S0[e] += delta * cur.k0[e];
+                S1[e] += delta * cur.k1[e];
+            }
+            if (ci == u) ov = p.scale * (pq + delta * cur.bk[1]);
+            if (u + 1 < kBlock) cur = nxt;
         }
         const int t = c * kBlock + ci;
-        if (ci < kBlock && t < T) {
+        if (t < T) {
             if (p.o_f16)
                 static_cast<_Float16 *>(p.o)[obase + (int64_t)t * kD] = f16_out(ov);
             else
@@ -264,7 +302,10 @@ __global__ __launch_bounds__(kThreads) void gdn_kda_prefill_kernel(PrefillParams
         }
         lds_barrier();
     }
-    if (p.final_state) store_state4(p.final_state, si, S, p.final_f16);
+    if (p.final_state) {
+        store_state4(p.final_state, si, S0, p.final_f16);
+        store_state4(p.final_state, si + 64, S1, p.final_f16);
+    }
 }
 
 template <typename E>
