@@ -77,10 +77,25 @@ struct StateRow {
     }
 };
 
+// x plus the value of the lane a DPP control names (all source lanes in range)
+template <int kCtrl>
+__device__ __forceinline__ float add_dpp(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
+}
+
+// sum over aligned groups of LPR lanes, in every lane of the group: xor 1 and xor 2 (quad
+// permutes), then the 8- and 16-lane mirrors (once the smaller groups hold one value each, the
+// mirror partner holds the same value as the xor partner), then xor 16 by a swizzle. The
+// additions are those of an xor butterfly, so the result does not depend on the mapping.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) x += __shfl_xor(x, m, 64);
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row width");
+    x = add_dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x = add_dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    x = add_dpp<0x141>(x);  // row_half_mirror
+    if constexpr (LPR >= 16) x = add_dpp<0x140>(x);  // row_mirror
+    if constexpr (LPR >= 32)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));  // xor 16
     return x;
 }
 
