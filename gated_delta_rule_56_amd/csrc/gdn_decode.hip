@@ -77,28 +77,6 @@ struct StateRow {
     }
 };
 
-// x plus the value of the lane a DPP control names (all source lanes in range)
-template <int kCtrl>
-__device__ __forceinline__ float add_dpp(float x) {
-    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
-}
-
-// sum over aligned groups of LPR lanes, in every lane of the group: xor 1 and xor 2 (quad
-// permutes), then the 8- and 16-lane mirrors (once the smaller groups hold one value each, the
-// mirror partner holds the same value as the xor partner), then xor 16 by a swizzle. The
-// additions are those of an xor butterfly, so the result does not depend on the mapping.
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
-    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row width");
-    x = add_dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-    x = add_dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-    x = add_dpp<0x141>(x);  // row_half_mirror
-    if constexpr (LPR >= 16) x = add_dpp<0x140>(x);  // row_mirror
-    if constexpr (LPR >= 32)
-        x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));  // xor 16
-    return x;
-}
-
 // columns per lane: 16 bytes of state, except where a wave would cover more rows than
 // it owns (float16 states at D = 32)
 template <int D, typename SD>
@@ -150,7 +128,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
     float kq = 0.0f;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) kq += kv[e] * qv[e];
-    kq = row_sum<LPR>(kq);
+    kq = group_sum<LPR>(kq);
     const float kappa = p.scale * kq;
     // per-channel decay: the decayed state S diag(alpha) meets k and q as S (alpha k), S (alpha q)
     float alpha = 1.0f, al[CPL], ak[CPL], aq[CPL];
@@ -180,8 +158,8 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
             rk += s[it].get(e) * (kKda ? ak[e] : kv[e]);
             rq += s[it].get(e) * (kKda ? aq[e] : qv[e]);
         }
-        rk = row_sum<LPR>(rk);
-        rq = row_sum<LPR>(rq);
+        rk = group_sum<LPR>(rk);
+        rq = group_sum<LPR>(rq);
         const float delta = beta * (vrow[it] - alpha * rk);  // alpha = 1 with per-channel decay
         float y[CPL];
 #pragma unroll

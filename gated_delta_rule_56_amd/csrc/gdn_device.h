@@ -1,5 +1,5 @@
 // Device-side helpers shared by the gfx950 kernels: vector types, element
-// conversions, MFMA wrappers and the value-head -> key-head mapping.
+// conversions, MFMA wrappers, lane-group sums and the value-head -> key-head mapping.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,6 +50,28 @@ __device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
 __device__ __forceinline__ _Float16 f16_out(float x) {
     asm("" : "+v"(x));
     return (_Float16)x;
+}
+
+// x plus the value of the lane a DPP control names (all source lanes in range)
+template <int kCtrl>
+__device__ __forceinline__ float add_dpp(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N lanes (N = 2 .. 32), in every lane of the group, on the VALU:
+// xor 1 and xor 2 (quad permutes), then the 8- and 16-lane mirrors (once the smaller groups
+// hold one value each, the mirror partner holds the same value as the xor partner), then
+// xor 16 by a swizzle. The additions are those of an xor butterfly from xor 1 upwards.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "group width");
+    x = add_dpp<0xB1>(x);                             // quad_perm [1, 0, 3, 2]
+    if constexpr (N >= 4) x = add_dpp<0x4E>(x);       // quad_perm [2, 3, 0, 1]
+    if constexpr (N >= 8) x = add_dpp<0x141>(x);      // row_half_mirror
+    if constexpr (N >= 16) x = add_dpp<0x140>(x);     // row_mirror
+    if constexpr (N >= 32)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));  // xor 16
+    return x;
 }
 
 // 4 consecutive state values at element index i of a float32 or float16 state.

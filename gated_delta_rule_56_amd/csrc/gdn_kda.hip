@@ -77,22 +77,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// x plus the value of the lane a DPP control names (all source lanes in range): folds into one
-// v_add_f32_dpp
-template <int kCtrl>
-__device__ __forceinline__ float add_dpp(float x) {
-    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, true));
-}
-
-// sum over the 16 lanes of a state row (one DPP row), in every lane of it: xor 1 and xor 2
-// (quad permutes), then the 8-lane and 16-lane mirrors
-__device__ __forceinline__ float row_sum(float x) {
-    x = add_dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-    x = add_dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-    x = add_dpp<0x141>(x);  // row_half_mirror
-    return add_dpp<0x140>(x);  // row_mirror
-}
-
 template <typename E>
 __device__ __forceinline__ f32x4 lds4(const unsigned char *p) {
     if constexpr (sizeof(E) == 4) {
@@ -237,7 +221,7 @@ void gdn_kda_prefill_kernel(PrefillParams p) {
             *reinterpret_cast<f32x4 *>(ob + L::pKF + off) = k;
             *reinterpret_cast<f32x4 *>(ob + L::pQF + off) = q;
         }
-        kq = row_sum(kq);
+        kq = group_sum<kLPR>(kq);
         if (ci == 0) *reinterpret_cast<f32x2 *>(ob + L::pBK + pu * 8) = f32x2{live ? beta : 0.0f, kq};
     };
 
@@ -282,8 +266,8 @@ void gdn_kda_prefill_kernel(PrefillParams p) {
                 p0 += S0[e] * cur.q0[e];
                 p1 += S1[e] * cur.q1[e];
             }
-            const float r = row_sum(r0 + r1);
-            const float pq = row_sum(p0 + p1);
+            const float r = group_sum<kLPR>(r0 + r1);
+            const float pq = group_sum<kLPR>(p0 + p1);
             const float delta = cur.bk[0] * (cur.v - r);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {

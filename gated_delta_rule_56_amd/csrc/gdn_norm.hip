@@ -9,7 +9,7 @@
 // A pure streaming pass (HBM-bound): a row is D / V lanes x 16 bytes (V = 4 float32
 // or 8 float16 values per lane), so a wave covers 64 V / D rows with coalesced
 // 16-byte loads and stores; the sum of squares is reduced across the row's lanes
-// with xor shuffles.
+// with DPP adds.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -93,8 +93,7 @@ __global__ __launch_bounds__(kThreads) void gdn_gated_rmsnorm_kernel(OT *o, cons
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < V; ++e) ss += x.x[e] * x.x[e];
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    ss = group_sum<LPR>(ss);
     const float inv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
     Vals<V> y;
 #pragma unroll

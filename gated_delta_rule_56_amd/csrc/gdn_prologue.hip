@@ -15,7 +15,7 @@
 // at once (addresses clamped into the sequence, out-of-range rows replaced by
 // state rows or zeros after the load), slides a 4-row window over them in
 // registers and stores each output row right away; for q and k the head's
-// D / 4 lanes reduce the sum of squares with xor shuffles. No LDS and no
+// D / 4 lanes reduce the sum of squares with DPP adds. No LDS and no
 // barrier: HBM-bound, x read once (plus 3 rows per run, which hit in L2), q, k,
 // v written once.
 #include "gdn_device.h"
@@ -137,8 +137,7 @@ __global__ __launch_bounds__(kThreads) void gdn_qkv_prologue_kernel(ProloguePara
             float ss = 0.0f;
 #pragma unroll
             for (int e = 0; e < kCpl; ++e) ss += y[e] * y[e];
-#pragma unroll
-            for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+            ss = group_sum<LPR>(ss);
             const float f = __builtin_amdgcn_rsqf(ss + p.eps);
 #pragma unroll
             for (int e = 0; e < kCpl; ++e) y[e] *= f;
