@@ -198,41 +198,55 @@ void gdn_kda_prefill_kernel(PrefillParams p) {
     // operands of block cb (ring slot cb % 4) into buffer cb & 1: the 256 compute lanes take
     // token pu = (64 wave + lane) / 16, channels col .. col + 3 and col + 64 .. col + 67
     const int pu = (wave * 64 + lane) / kLPR;
-    auto form = [&](int cb) {
+    // in two parts, so that the forming of block c + 1 can sit between the token steps of block c:
+    // the LDS reads, then the exponentials, k . q and the writes
+    struct FormIn {
+        f32x4 k[2], q[2], g[2];
+        float beta;
+    };
+    auto form_load = [&](int cb) {
         const unsigned char *s = smem + (cb % kSlots) * L::kSlotBytes;
+        FormIn in;
+        in.beta = *reinterpret_cast<const float *>(s + L::oB + pu * 4);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int pj = col + 64 * hh;
+            in.k[hh] = lds4<E>(s + L::oK + (pu * kD + pj) * ES);
+            in.q[hh] = lds4<E>(s + L::oQ + (pu * kD + pj) * ES);
+            in.g[hh] = *reinterpret_cast<const f32x4 *>(s + L::oG + (pu * kD + pj) * 4);
+        }
+        return in;
+    };
+    auto form_store = [&](int cb, const FormIn &in) {
         unsigned char *ob = smem + L::kRing + (cb & 1) * L::kOpBytes;
         const bool live = cb * kBlock + pu < T;
-        const float beta = *reinterpret_cast<const float *>(s + L::oB + pu * 4);
         float kq = 0.0f;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int pj = col + 64 * hh;
-            const f32x4 k = lds4<E>(s + L::oK + (pu * kD + pj) * ES);
-            const f32x4 q = lds4<E>(s + L::oQ + (pu * kD + pj) * ES);
-            const f32x4 g = *reinterpret_cast<const f32x4 *>(s + L::oG + (pu * kD + pj) * 4);
             f32x4 al;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                al[e] = live ? __expf(g[e]) : 1.0f;
-                kq += k[e] * q[e];
+                al[e] = live ? __expf(in.g[hh][e]) : 1.0f;
+                kq += in.k[hh][e] * in.q[hh][e];
             }
             const int off = (pu * kD + pj) * 4;
             *reinterpret_cast<f32x4 *>(ob + L::pAL + off) = al;
-            *reinterpret_cast<f32x4 *>(ob + L::pKF + off) = k;
-            *reinterpret_cast<f32x4 *>(ob + L::pQF + off) = q;
+            *reinterpret_cast<f32x4 *>(ob + L::pKF + off) = in.k[hh];
+            *reinterpret_cast<f32x4 *>(ob + L::pQF + off) = in.q[hh];
         }
         kq = group_sum<kLPR>(kq);
-        if (ci == 0) *reinterpret_cast<f32x2 *>(ob + L::pBK + pu * 8) = f32x2{live ? beta : 0.0f, kq};
+        if (ci == 0) *reinterpret_cast<f32x2 *>(ob + L::pBK + pu * 8) = f32x2{live ? in.beta : 0.0f, kq};
     };
 
     lds_barrier();  // blocks 0 and 1 have landed
-    if (nb > 0) form(0);
+    if (nb > 0) form_store(0, form_load(0));
     lds_barrier();
     for (int c = 0; c < nb; ++c) {
-        // branch-free, so that the compiler can spread the forming of block c + 1 over the token
-        // steps of block c; past the last block it reads a ring slot no load is still writing
-        // and fills the buffer that no token step reads any more
-        form(c + 1);
+        // the forming of block c + 1 runs inside the token steps of block c, branch-free: past
+        // the last block it reads a ring slot no load is still writing and fills the buffer that
+        // no token step reads any more
+        const FormIn fin = form_load(c + 1);
         const unsigned char *s = smem + (c % kSlots) * L::kSlotBytes;
         const unsigned char *ob = smem + L::kRing + (c & 1) * L::kOpBytes;
         float ov = 0.0f;  // o of token c * 16 + ci, row lrow
@@ -249,13 +263,17 @@ void gdn_kda_prefill_kernel(PrefillParams p) {
             x.v = lds1<E>(s + L::oV + (u * 16 + lrow) * ES);
             return x;
         };
-        // the operands of token u + 1 are read while token u runs: the state chain never waits on
+        // the operands of token u + 2 are read while token u runs: the state chain never waits on
         // an LDS round trip
-        TokenOps cur = load_ops(0);
+        TokenOps cur = load_ops(0), nx1 = load_ops(1);
 #pragma unroll
         for (int u = 0; u < kBlock; ++u) {
-            TokenOps nxt;
-            if (u + 1 < kBlock) nxt = load_ops(u + 1);
+            TokenOps nx2;
+            if (u + 2 < kBlock) nx2 = load_ops(u + 2);
+            // keep those reads ahead of this token's arithmetic (the scheduler would otherwise sink
+            // them next to their first use, and each token would wait on a full LDS round trip)
+            __builtin_amdgcn_sched_barrier(0);
+            if (u == 2) form_store(c + 1, fin);
             float r0 = 0.0f, r1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -275,7 +293,8 @@ void gdn_kda_prefill_kernel(PrefillParams p) {
                 S1[e] += delta * cur.k1[e];
             }
             if (ci == u) ov = p.scale * (pq + delta * cur.bk[1]);
-            if (u + 1 < kBlock) cur = nxt;
+            cur = nx1;
+            if (u + 2 < kBlock) nx1 = nx2;
         }
         const int t = c * kBlock + ci;
         if (t < T) {
