@@ -82,16 +82,24 @@ def test_decode_f16_o(gdn):
     assert torch.equal(o16, o32.half()) and torch.equal(s_a, s_b)
 
 
-@pytest.mark.parametrize("gated", [True, False])
-def test_gated_rmsnorm_f16_rows(gdn, oracle_lib, gated):
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("gate_dtype", ["bf16", "f32", None])
+def test_gated_rmsnorm_f16_rows(gdn, oracle_lib, d, gate_dtype):
+    """float16 rows (8 values per lane: rows of 2, 4, 8 or 16 lanes), bfloat16, float32 or no gate."""
     import torch
-    rng = np.random.default_rng(115)
-    o = (rng.standard_normal((2, 4, 300, 128)) * 0.05).astype(np.float16)
-    nrm = inputs.generate_norm(o.shape, "bf16", seed=116)
+    rng = np.random.default_rng(115 + d)
+    o = (rng.standard_normal((2, 4, 300, d)) * 0.05).astype(np.float16)
+    nrm = inputs.generate_norm(o.shape, gate_dtype or "bf16", seed=116 + d)
     t = torch.from_numpy(o).cuda()
-    gate = torch.from_numpy(np.ascontiguousarray(nrm.gate_bits).view(np.int16)).view(torch.bfloat16).cuda()
-    gdn.gated_rmsnorm(t, dev(nrm.weight), gate if gated else None, eps=1e-6)
-    want = oracle_lib.gated_rmsnorm(o.astype(np.float64), nrm.weight, gate=nrm.gate if gated else None, eps=1e-6)
+    if gate_dtype == "bf16":
+        gate = torch.from_numpy(np.ascontiguousarray(nrm.gate_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    elif gate_dtype == "f32":
+        gate = dev(nrm.gate)
+    else:
+        gate = None
+    gdn.gated_rmsnorm(t, dev(nrm.weight), gate, eps=1e-6)
+    want = oracle_lib.gated_rmsnorm(o.astype(np.float64), nrm.weight, gate=nrm.gate if gate_dtype else None,
+                                    eps=1e-6)
     got = t.float().cpu().numpy()
     bound = 2.0 ** -11 * np.abs(want) + 1e-5 * np.max(np.abs(want))
     assert np.max(np.abs(got - want) - bound) <= 0.0
