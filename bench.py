@@ -64,6 +64,26 @@ PREFILL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_56_amd", "csrc", f)
                    for f in ("gdn_prefill_chunk.hip", "gdn_prefill_scan.hip", "gdn_frag.h", "gdn_device.h")]
 
 
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "prefill_long32k_mfma_counters.md")
+
+
+def measured_prefill_mfma_flops():
+    """MFMA FLOPs per gdn_prefill launch counted by rocprofv3 (SQ_INSTS_VALU_MFMA_MOPS_* x 512)
+    from the committed summary, or None when the kernel sources have changed since."""
+    try:
+        text = open(MFMA_PROFILE).read()
+        h = hashlib.sha256()
+        for f in PREFILL_SOURCES:
+            h.update(open(f, "rb").read())
+    except OSError:
+        return None
+    m_flops = re.search(r"^counted_mfma_flops_per_launch:\s*(\d+)", text, re.M)
+    m_sha = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not (m_flops and m_sha) or h.hexdigest()[:len(m_sha.group(1))] != m_sha.group(1):
+        return None
+    return int(m_flops.group(1))
+
+
 def measured_prefill_traffic(key="traffic_bytes_per_launch"):
     """HBM bytes per gdn_prefill launch from the committed FETCH_SIZE / WRITE_SIZE summary
     (key: the fp32-o call, or traffic_bytes_per_launch_f16_o), or None when the kernel sources
@@ -325,6 +345,7 @@ def main():
     p_gbps = p_bytes / (p_avg * 1e-3) / 1e9
     d_gbps = d_bytes / (d_avg * 1e-3) / 1e9
     p_tflops = flops / (p_avg * 1e-3) / 1e12
+    counted_flops = measured_prefill_mfma_flops()  # rocprofv3 MFMA op counters, when current
 
     result = {
         "metric": "GDN prefill tokens/s (Hv=32,d=128,T=32k) + MFMA util; decode HBM GB/s",
@@ -365,6 +386,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": p_tflops / MFMA_PEAK_TFLOPS,
             "algorithmic_flops_per_launch": flops,
+            "counted_flops_per_launch": counted_flops,
+            "counted_achieved": counted_flops / (p_avg * 1e-3) / 1e12 if counted_flops else None,
         },
         "decode": {
             "kernel": "gdn_decode_kernel<128, bf16>",
