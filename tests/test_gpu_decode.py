@@ -53,31 +53,25 @@ def test_decode_small(gdn, oracle_lib, d, dtype, head_map):
 
 
 def test_decode_batched_full(gdn, oracle_lib):
-    """B=256, Hk=16, Hv=32, d=128, 64 in-place steps on a 537 MB fp32 state; every
-    output and the final state of 256 sampled (b, h) pairs against the oracle."""
+    """B=256, Hk=16, Hv=32, d=128, 64 in-place steps on a 537 MB fp32 state, as the benchmark
+    runs them: every output of every step and the whole final state against the oracle."""
     import torch
     wl = inputs.WORKLOADS["batched_decode"]
     x = inputs.generate_workload(wl)
-    B, Hv, d = wl.batch, wl.num_v_heads, wl.head_dim
-    rng = np.random.default_rng(99)
-    pairs = np.sort(rng.choice(B * Hv, size=256, replace=False))
     state = dev(x.s0)
-    ref_state = np.ascontiguousarray(x.s0.reshape(B * Hv, d, d)[pairs].astype(np.float64))
+    ref_state = np.ascontiguousarray(x.s0.astype(np.float64))
     worst = 0.0
     for s in range(wl.decode_steps):
         st = _step_inputs(x, s)
         q, k, v = qkv_dev(st)
         o = gdn.decode(q, k, v, dev(st.g), dev(st.beta), state, scale=x.scale)
-        o_ref = oracle_lib.decode_step(st.q, st.k, st.v, st.g, st.beta, ref_state, scale=x.scale,
-                                       pairs=pairs)
-        got = o.reshape(B * Hv, d)[torch.from_numpy(pairs).cuda()].cpu().numpy()
-        worst = max(worst, rel_err(got, o_ref))
-    got_state = state.reshape(B * Hv, d, d)[torch.from_numpy(pairs).cuda()].cpu().numpy()
-    es = rel_err(got_state, ref_state)
+        o_ref = oracle_lib.decode_step(st.q, st.k, st.v, st.g, st.beta, ref_state, scale=x.scale)
+        worst = max(worst, rel_err(o.cpu().numpy(), o_ref))
+    assert torch.isfinite(state).all()
+    es = rel_err(state.cpu().numpy(), ref_state)
     print(f"batched decode: max rel err o {worst:.3e}, state {es:.3e}")
     assert worst <= TOL_BF16 and es <= TOL_BF16
     assert worst <= 1e-4 and es <= 1e-4  # fp32 arithmetic: far inside the bf16 bar
-    assert torch.isfinite(state).all()
 
 
 def test_decode_repeatable(gdn):

@@ -86,14 +86,14 @@ def test_ragged_continuation_workload(gdn, oracle_lib, chunk, head_map):
         assert np.all(o[b, :, length:] == 0.0)
 
 
-def test_long_prefill_32k_sampled(gdn, oracle_lib):
-    """T = 32768 at the benchmarked launch shape; 4 sampled value heads checked in full."""
+def test_long_prefill_32k_full(gdn, oracle_lib):
+    """T = 32768 at the benchmarked launch shape (chunk 64, fp32 o): every output and the final
+    state of all 32 value heads against the oracle (about a second of oracle time on 16 cores)."""
     wl = inputs.WORKLOADS["long_prefill_32k"]
     x = inputs.generate_workload(wl)
     o, sf = run_prefill(gdn, x, wl.chunk)
-    pairs = np.array([0, 9, 22, 31])
-    check(oracle_lib, x, o, sf, pairs=pairs, label="long_32k (4 heads)")
     assert np.isfinite(o).all() and np.isfinite(sf).all()
+    check(oracle_lib, x, o, sf, label="long_32k (all heads)")
 
 
 def test_segmented_prefill(gdn, oracle_lib, monkeypatch):
