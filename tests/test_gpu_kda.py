@@ -116,24 +116,23 @@ def test_kda_decode(gdn, oracle_lib, d, dtype, state16):
 
 
 def test_kda_decode_batched(gdn, oracle_lib):
-    """B=256, Hk=16, Hv=32, d=128: 64 in-place steps; 128 sampled pairs at every step."""
+    """B=256, Hk=16, Hv=32, d=128: 64 in-place steps; every output of every step and the whole
+    final state against the oracle."""
     import torch
     wl = inputs.WORKLOADS["batched_decode"]
     x = inputs.generate_workload(wl)
     B, Hv, d = wl.batch, wl.num_v_heads, wl.head_dim
     g = inputs.generate_channel_decay((wl.decode_steps, B, Hv, d), seed=128)
-    pairs = np.sort(np.random.default_rng(129).choice(B * Hv, size=128, replace=False))
-    idx = torch.from_numpy(pairs).cuda()
     state = dev(x.s0)
-    ref = np.ascontiguousarray(x.s0.reshape(B * Hv, d, d)[pairs].astype(np.float64))
+    ref = np.ascontiguousarray(x.s0.astype(np.float64))
     q, k, v = qkv_dev(x)
     worst = 0.0
     for s in range(wl.decode_steps):
         o = gdn.kda_decode(q[s], k[s], v[s], dev(g[s]), dev(x.beta[s]), state, scale=x.scale)
-        o_ref = oracle_lib.kda_decode_step(x.q[s], x.k[s], x.v[s], g[s], x.beta[s], ref, scale=x.scale,
-                                           pairs=pairs)
-        worst = max(worst, rel_err(o.reshape(B * Hv, d)[idx].cpu().numpy(), o_ref))
-    es = rel_err(state.reshape(B * Hv, d, d)[idx].cpu().numpy(), ref)
+        o_ref = oracle_lib.kda_decode_step(x.q[s], x.k[s], x.v[s], g[s], x.beta[s], ref, scale=x.scale)
+        worst = max(worst, rel_err(o.cpu().numpy(), o_ref))
+    assert torch.isfinite(state).all()
+    es = rel_err(state.cpu().numpy(), ref)
     print(f"kda batched decode: o {worst:.3e} state {es:.3e}")
     assert worst <= 1e-4 and es <= 1e-4
 
