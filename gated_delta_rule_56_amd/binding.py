@@ -21,11 +21,11 @@ GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
 GDN_STATE_F32, GDN_STATE_F16 = 0, 1
 GDN_OUT_F32, GDN_OUT_F16 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 _STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
 _OUT_DTYPES = {torch.float32: GDN_OUT_F32, torch.float16: GDN_OUT_F16}
 
-EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill", "gdn_prefill_varlen_workspace_bytes",
+EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill_segments", "gdn_prefill", "gdn_prefill_varlen_workspace_bytes",
                     "gdn_prefill_varlen", "gdn_decode", "gdn_kda_prefill", "gdn_kda_decode",
                     "gdn_gated_rmsnorm", "gdn_qkv_prologue", "gdn_status_string", "gdn_last_error",
                     "gdn_abi_version")
@@ -62,6 +62,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     P, SZ = ctypes.c_void_p, ctypes.c_size_t
     lib.gdn_prefill_workspace_bytes.restype = SZ
     lib.gdn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
+    lib.gdn_prefill_segments.restype = ctypes.c_int
+    lib.gdn_prefill_segments.argtypes = [ctypes.POINTER(GdnShape), SZ]
     lib.gdn_prefill.restype = ctypes.c_int
     lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, SZ, P]
     lib.gdn_prefill_varlen_workspace_bytes.restype = SZ
@@ -118,6 +120,13 @@ def _stream_handle(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def _scratch(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace for one call, allocated on the stream the call runs on: the caching
+    allocator hands a freed block out again only to work ordered after it on that stream."""
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(device)):
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
 def make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, qkv_dtype, head_map, scale,
                state_dtype=GDN_STATE_F32, o_dtype=GDN_OUT_F32):
     return GdnShape(batch, seq_len, num_k_heads, num_v_heads, head_dim, head_dim, chunk,
@@ -144,13 +153,25 @@ def _state_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
     return _dev_tensor(t, name, t.dtype)
 
 
+def _prefill_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, dtype, head_map):
+    return make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk,
+                      GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, 1.0)
+
+
 def prefill_workspace_bytes(batch: int, seq_len: int, num_k_heads: int, num_v_heads: int, head_dim: int, *,
                             chunk: int = 64, dtype: torch.dtype = torch.bfloat16,
                             head_map: int = GDN_HEADS_TILED) -> int:
-    """gdn_prefill_workspace_bytes for a prefill of this shape (0 when none is needed)."""
-    shape = make_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk,
-                       GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, 1.0)
+    """gdn_prefill_workspace_bytes: the workspace of the preferred segment count (0: none used)."""
+    shape = _prefill_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, dtype, head_map)
     return int(load_library().gdn_prefill_workspace_bytes(ctypes.byref(shape)))
+
+
+def prefill_segments(batch: int, seq_len: int, num_k_heads: int, num_v_heads: int, head_dim: int,
+                     workspace_bytes: int, *, chunk: int = 64, dtype: torch.dtype = torch.bfloat16,
+                     head_map: int = GDN_HEADS_TILED) -> int:
+    """gdn_prefill_segments: the segment count a prefill of this shape runs with this workspace."""
+    shape = _prefill_shape(batch, seq_len, num_k_heads, num_v_heads, head_dim, chunk, dtype, head_map)
+    return int(load_library().gdn_prefill_segments(ctypes.byref(shape), int(workspace_bytes)))
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
@@ -166,7 +187,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     final_state=initial_state to update a state in place. The states share one storage type:
     that of the state tensors passed, else state_dtype (default float32). o is float32, or
     float16 (o_dtype, or the type of the o passed). workspace: a uint8 device tensor of at
-    least prefill_workspace_bytes(...) bytes, or None to allocate one for this call.
+    any size (prefill_workspace_bytes(...) gives the preferred one; less means fewer segments of
+    the sequence run in parallel, see prefill_segments), or None to allocate the preferred size
+    for this call.
     """
     lib = load_library()
     dtype = q.dtype
@@ -206,12 +229,10 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
                        _STATE_DTYPES[sdt], _OUT_DTYPES[o.dtype])
     ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
     if workspace is None:
-        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device) if ws else None
+        workspace = _scratch(ws, q.device, stream) if ws else None
     else:
         _dev_tensor(workspace, "workspace", torch.uint8)
-        if workspace.numel() < ws:
-            raise ValueError(f"workspace holds {workspace.numel()} bytes; {ws} needed")
-        ws = workspace.numel()
+        ws = workspace.numel()  # a smaller workspace than preferred means fewer segments
     _check(lib, lib.gdn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), ws,
                                 _stream_handle(stream)))
@@ -267,7 +288,7 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                        _OUT_DTYPES[o.dtype])
     ws = lib.gdn_prefill_varlen_workspace_bytes(ctypes.byref(shape))
     if workspace is None:
-        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(ws, q.device, stream)
     else:
         _dev_tensor(workspace, "workspace", torch.uint8)
     _check(lib, lib.gdn_prefill_varlen(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),

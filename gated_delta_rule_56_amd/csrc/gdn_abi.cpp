@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdint>
 
 #include "gdn_internal.h"
 
@@ -104,10 +105,21 @@ const char *gdn_status_string(gdn_status st) {
 
 const char *gdn_last_error(void) { return g_last_error; }
 
+// the segmented MFMA path: bfloat16 q/k/v, head_dim 128, chunk 32 or 64
+static bool segmented_path(const gdn_shape *s) {
+    return s->qkv_dtype == GDN_DTYPE_BF16 && s->head_dim_k == 128 && (s->chunk == 32 || s->chunk == 64);
+}
+
 size_t gdn_prefill_workspace_bytes(const gdn_shape *s) {
+    if (check_common(s) != GDN_OK || s->seq_len < 0 || !segmented_path(s)) return 0;
+    const int P = gdn::seg_count(s->batch, s->num_v_heads, s->seq_len, s->chunk, SIZE_MAX, true);
+    return (size_t)gdn::seg_workspace_bytes((int64_t)s->batch * s->num_v_heads, P);
+}
+
+int gdn_prefill_segments(const gdn_shape *s, size_t workspace_bytes) {
     if (check_common(s) != GDN_OK || s->seq_len < 0) return 0;
-    if (s->qkv_dtype != GDN_DTYPE_BF16 || (s->chunk != 32 && s->chunk != 64)) return 0;
-    return gdn::prefill_workspace_bytes(s->batch, s->num_k_heads, s->num_v_heads, s->seq_len, s->chunk);
+    if (!segmented_path(s)) return 1;
+    return gdn::seg_count(s->batch, s->num_v_heads, s->seq_len, s->chunk, workspace_bytes, true);
 }
 
 gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
@@ -119,9 +131,8 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
         return fail(GDN_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", s->chunk);
     const int d = s->head_dim_k;
     const bool bf16 = s->qkv_dtype == GDN_DTYPE_BF16;
-    if (bf16 && d != 128) return fail(GDN_ERR_UNSUPPORTED, "bfloat16 prefill supports head_dim 128 (got %d)", d);
-    if (!bf16 && d != 16 && d != 32 && d != 64 && d != 128)
-        return fail(GDN_ERR_UNSUPPORTED, "float32 prefill supports head_dim 16, 32, 64 or 128 (got %d)", d);
+    if (d != 16 && d != 32 && d != 64 && d != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "prefill supports head_dim 16, 32, 64 or 128 (got %d)", d);
     const double tokens = (double)s->batch * s->num_v_heads * s->seq_len * d;
     if (tokens > 4.0e15) return fail(GDN_ERR_UNSUPPORTED, "tensor sizes overflow");
 
@@ -129,8 +140,6 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     const int64_t esz = bf16 ? 2 : 4;
     const int64_t qk_bytes = B * Hk * T * d * esz, v_bytes = B * Hv * T * d * esz;
     const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
-    if (o16 && !(bf16 && s->chunk != 16))
-        return fail(GDN_ERR_UNSUPPORTED, "float16 o needs bfloat16 q/k/v and chunk 32 or 64");
     const int64_t gb_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * (o16 ? 2 : 4);
     const int64_t st_bytes = B * Hv * d * d * (st16 ? 2 : 4);
     if (T > 0) {
@@ -177,54 +186,32 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     p.scale = s->scale;
     p.init_f16 = p.final_f16 = st16;
     p.o_f16 = o16;
-    const bool two_pass = bf16 && s->chunk != 16;
-    const size_t ws_need = two_pass ? gdn::prefill_workspace_bytes(B, Hk, Hv, T, s->chunk) : 0;
-    if (ws_need > 0) {
-        if (!workspace) return fail(GDN_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", ws_need);
-        if (workspace_bytes < ws_need)
-            return fail(GDN_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed", workspace_bytes, ws_need);
-        if (!aligned(workspace, 16)) return fail(GDN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-        const Range wsr[] = {range("workspace", workspace, (int64_t)ws_need)};
-        GDN_TRY(check_no_overlap(wsr, 1, ins, 6));
-        GDN_TRY(check_no_overlap(wsr, 1, out_o, 1));
-        if (final_state) {
-            const Range fs[] = {range("final_state", final_state, st_bytes)};
-            GDN_TRY(check_no_overlap(wsr, 1, fs, 1));
+    // the segmented path splits every sequence into as many segments as its preferred count
+    // allows within the workspace the caller passes (one segment, no workspace, at the least)
+    int P = 1;
+    if (segmented_path(s)) {
+        P = gdn::seg_count(B, Hv, T, s->chunk, workspace_bytes, workspace != nullptr);
+        if (P > 1) {
+            const int64_t used = gdn::seg_workspace_bytes(B * Hv, P);
+            if (!aligned(workspace, 16)) return fail(GDN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+            const Range wsr[] = {range("workspace", workspace, used)};
+            GDN_TRY(check_no_overlap(wsr, 1, ins, 6));
+            GDN_TRY(check_no_overlap(wsr, 1, out_o, 1));
+            if (final_state) {
+                const Range fs[] = {range("final_state", final_state, st_bytes)};
+                GDN_TRY(check_no_overlap(wsr, 1, fs, 1));
+            }
         }
     }
     if (!final_state && T == 0) return GDN_OK;  // nothing to compute or write
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t err = hipSuccess;
-    if (!bf16) {
-        err = gdn::launch_prefill_f32(p, s->chunk, st);
-    } else if (!two_pass) {
-        err = gdn::launch_prefill_mfma(p, s->chunk, st);
-    } else if (T == 0) {
-        err = gdn::launch_prefill_scan(p, s->chunk, workspace, st);  // copies or zeroes the state
-    } else {
-        // consecutive token segments; the state is carried through a float32 final_state (in
-        // place per workgroup), or through the workspace (float32) when the caller wants no final
-        // state or a float16 one
-        const gdn::PrefillSegments sg = gdn::prefill_segments(B, Hk, Hv, T, s->chunk);
-        void *carry = final_state && !st16 ? final_state : static_cast<char *>(workspace) + sg.state_offset;
-        for (int64_t i = 0; i < sg.count && err == hipSuccess; ++i) {
-            const int64_t t0 = i * sg.chunks * s->chunk;
-            gdn::PrefillParams ps = p;
-            ps.T = (int32_t)std::min<int64_t>(T - t0, sg.chunks * s->chunk);
-            ps.q = static_cast<const char *>(q) + t0 * d * esz;
-            ps.k = static_cast<const char *>(k) + t0 * d * esz;
-            ps.v = static_cast<const char *>(v) + t0 * d * esz;
-            ps.g = g + t0;
-            ps.beta = beta + t0;
-            ps.o = static_cast<char *>(o) + t0 * d * (o16 ? 2 : 4);
-            ps.init_state = i == 0 ? initial_state : carry;
-            ps.final_state = i == sg.count - 1 ? final_state : carry;
-            ps.init_f16 = i == 0 && st16;
-            ps.final_f16 = i == sg.count - 1 && st16;
-            err = gdn::launch_chunk_prep(ps, s->chunk, workspace, st);
-            if (err == hipSuccess) err = gdn::launch_prefill_scan(ps, s->chunk, workspace, st);
-        }
-    }
+    hipError_t err;
+    if (segmented_path(s))
+        err = gdn::launch_prefill_seg(p, s->chunk, P, workspace, st);
+    else if (bf16 && d == 128)
+        err = gdn::launch_prefill_mfma(p, s->chunk, st);  // chunk 16
+    else
+        err = gdn::launch_prefill_f32(p, s->chunk, bf16, st);
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
     return GDN_OK;
 }

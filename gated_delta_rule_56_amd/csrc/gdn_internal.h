@@ -49,9 +49,8 @@ struct DecodeParams {
 
 // bf16 q/k/v, D = 128, chunk 16: single fused chunked WY kernel on fp16 MFMA.
 hipError_t launch_prefill_mfma(const PrefillParams &p, int chunk, hipStream_t stream);
-// bf16 q/k/v, D = 128, chunk in {32, 64}: chunk-parallel kernel (T and A_qk per
-// chunk into the workspace), then the sequential state pass reading them.
-size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk);
+// Packed sequences (bf16 q/k/v, D = 128, chunk in {32, 64}): chunk-parallel kernel (T and
+// A_qk per chunk into the workspace), then the sequential state pass reading them.
 hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStream_t stream);
 
 // Gated RMSNorm of `rows` output rows of D floats, in place.
@@ -91,16 +90,28 @@ VarlenLayout varlen_layout(int64_t nseq, int64_t Hk, int64_t Hv, int64_t T, int 
 hipError_t launch_varlen_tables(const int32_t *cu_seqlens, int32_t nseq, int32_t T, int chunk, int32_t *seqs,
                                 int32_t *chunks, int32_t nchunks, hipStream_t stream);
 
-// Token segments of a bf16 prefill with chunk 32 or 64: `count` segments of `chunks` chunks
-// (the last may be shorter); the workspace holds one segment's chunk data and, at byte
-// `state_offset`, room for the state carried between segments (`bytes` in all).
-struct PrefillSegments {
-    int64_t count, chunks, state_offset, bytes;
+// Segmented bf16 prefill (chunk 32 or 64, D = 128, fixed-length sequences): P segments per
+// sequence run in parallel; the workspace holds three float32 D x D matrices per (pair, segment):
+// segment start states, the end states from a zero start (N) and the segment maps (M).
+struct SegParams {
+    PrefillParams p;
+    float *ws_start;     // [B * Hv][P][D][D]
+    float *ws_n;         // [B * Hv][P][D][D]
+    float *ws_m;         // [B * Hv][P][D][D]
+    int32_t P;           // segments
+    int32_t seg_chunks;  // chunks per segment (the last segment may hold fewer)
 };
-PrefillSegments prefill_segments(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk);
+// Workspace bytes for P segments (0 for P = 1).
+int64_t seg_workspace_bytes(int64_t pairs, int P);
+// Segments used for this shape: as many as give every CU a workgroup in the output pass
+// (at most one per chunk), reduced until their workspace fits workspace_bytes.
+int seg_count(int64_t B, int64_t Hv, int64_t T, int chunk, size_t workspace_bytes, bool have_workspace);
+hipError_t launch_prefill_seg(const PrefillParams &p, int chunk, int P, void *ws, hipStream_t stream);
+
 hipError_t launch_prefill_scan(const PrefillParams &p, int chunk, const void *ws, hipStream_t stream);
-// f32 q/k/v, D in {16, 32, 64, 128}, chunk in {16, 32, 64}: fp32 VALU chunked kernel.
-hipError_t launch_prefill_f32(const PrefillParams &p, int chunk, hipStream_t stream);
+// fp32 VALU chunked kernel, chunk in {16, 32, 64}: f32 q/k/v with D in {16, 32, 64, 128},
+// or bf16 q/k/v (bf16 = true) with D in {16, 32, 64}.
+hipError_t launch_prefill_f32(const PrefillParams &p, int chunk, bool bf16, hipStream_t stream);
 // one decode step, D in {32, 64, 128}; bf16 selects bf16 q/k/v, else f32.
 hipError_t launch_decode(const DecodeParams &p, bool bf16, hipStream_t stream);
 

@@ -30,8 +30,6 @@
 // 16 x 16 blocks: the diagonal blocks by substitution in fp32 (one wave each),
 // then the off-diagonal blocks by MFMA recursive doubling,
 //   T_ul = -T_uu A_ul T_ll  (16-blocks, then 32-blocks).
-#include <cstdlib>
-
 #include "gdn_device.h"
 #include "gdn_frag.h"
 #include "gdn_internal.h"
@@ -206,7 +204,7 @@ __global__ __launch_bounds__(C * 4) void gdn_chunk_prep_kernel(PrefillParams p, 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = 16 * nt + 4 * q4 + r;
-                    const float gate = __expf(fminf(Gt - Gs[r], 0.0f));
+                    const float gate = __expf(Gt - Gs[r]);
                     a[nt][r] = s < t ? bt * gate * rk[nt][r] : 0.0f;
                     aq[nt][r] = s <= t ? p.scale * gate * rq[nt][r] : 0.0f;
                 }
@@ -335,41 +333,6 @@ int64_t chunk_ws_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t nc, int chunk)
     return 0;
 }
 }  // namespace
-
-// A prefill runs as consecutive token segments (chunk prep, then the state pass, per segment)
-// so that the workspace stays bounded: a segment holds as many chunks as fit a budget of
-// workspace + v + o bytes (1.5 GiB, or GDN_PREFILL_SEGMENT_BYTES). Splitting costs a pipeline
-// start per segment, so the budget is large: smaller segments were measured slower.
-int64_t prefill_segment_budget() {
-    const char *e = std::getenv("GDN_PREFILL_SEGMENT_BYTES");
-    if (e && *e) {
-        const long long v = std::atoll(e);
-        if (v > 0) return v;
-    }
-    return 1536ll << 20;
-}
-
-PrefillSegments prefill_segments(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
-    PrefillSegments sg{0, 0, 0, 0};
-    if (T <= 0 || (chunk != 32 && chunk != 64)) return sg;
-    const int64_t nc = (T + chunk - 1) / chunk;
-    const int64_t per_chunk = chunk_ws_bytes(B, Hk, Hv, 1, chunk) + B * Hv * chunk * kD * (2 + 4);
-    const int64_t budget = prefill_segment_budget();
-    int64_t seg = budget / per_chunk;
-    if (seg < 1) seg = 1;
-    if (seg > nc) seg = nc;
-    sg.count = (nc + seg - 1) / seg;
-    sg.chunks = (nc + sg.count - 1) / sg.count;  // balanced: every segment but the last has this many
-    sg.state_offset = (chunk_ws_bytes(B, Hk, Hv, sg.chunks, chunk) + 255) / 256 * 256;
-    // a float32 state carried between segments, for callers that pass no final_state or a
-    // float16 one
-    sg.bytes = sg.count > 1 ? sg.state_offset + B * Hv * kD * kD * 4 : chunk_ws_bytes(B, Hk, Hv, sg.chunks, chunk);
-    return sg;
-}
-
-size_t prefill_workspace_bytes(int64_t B, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
-    return (size_t)prefill_segments(B, Hk, Hv, T, chunk).bytes;
-}
 
 VarlenLayout varlen_layout(int64_t nseq, int64_t Hk, int64_t Hv, int64_t T, int chunk) {
     VarlenLayout v{0, 0, 0, 0};

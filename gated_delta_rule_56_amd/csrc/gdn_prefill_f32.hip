@@ -1,6 +1,7 @@
-// Chunked (WY-form) gated delta rule prefill for float32 q/k/v, computed in
-// fp32 on the vector ALUs. This is the precise path (small shapes, d <= 128);
-// the bfloat16 path uses the MFMA kernel in gdn_prefill_mfma.hip.
+// Chunked (WY-form) gated delta rule prefill computed in fp32 on the vector ALUs,
+// for float32 q/k/v (the precise path, d <= 128) and for bfloat16 q/k/v with head
+// dimensions below 128 (widened exactly to fp32 on load); bfloat16 at d = 128 runs
+// on the MFMA kernels.
 //
 // Per (b, h) and chunk of C tokens with start state S (dv x dk), local t = 0..C-1:
 //   G_t = sum_{s<=t} g_s,  gamma_t = exp(G_t),  Gamma_ts = exp(G_t - G_s) (s <= t)
@@ -33,7 +34,14 @@ struct F32Smem {
     static constexpr size_t kBytes = sizeof(float) * kFloats;
 };
 
-template <int D, int C>
+// element i of q, k or v: float32, or bfloat16 bits widened exactly
+template <bool BF>
+__device__ __forceinline__ float ld_in(const void *base, int64_t i) {
+    if constexpr (BF) return bf16_bits_to_f32(static_cast<const uint16_t *>(base)[i]);
+    return static_cast<const float *>(base)[i];
+}
+
+template <int D, int C, bool BF>
 __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillParams p) {
     using L = F32Smem<D, C>;
     extern __shared__ float smem[];
@@ -59,12 +67,11 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
     const int b = pair / p.Hv, h = pair % p.Hv;
     const int kh = key_head(h, p.Hk, p.Hv, p.head_map);
     const int T = p.T;
-    const float *qg = static_cast<const float *>(p.q) + ((int64_t)b * p.Hk + kh) * T * D;
-    const float *kg = static_cast<const float *>(p.k) + ((int64_t)b * p.Hk + kh) * T * D;
-    const float *vg = static_cast<const float *>(p.v) + ((int64_t)b * p.Hv + h) * T * D;
+    const int64_t qk0 = ((int64_t)b * p.Hk + kh) * T * D;
+    const int64_t v0 = ((int64_t)b * p.Hv + h) * T * D;
     const float *gg = p.g + ((int64_t)b * p.Hv + h) * T;
     const float *bg = p.beta + ((int64_t)b * p.Hv + h) * T;
-    float *og = static_cast<float *>(p.o) + ((int64_t)b * p.Hv + h) * T * D;
+    const int64_t o0 = ((int64_t)b * p.Hv + h) * T * D;
     const int64_t sbase = ((int64_t)pair * D + blk * kRows) * D;
 
     for (int e = tid; e < kRows * D; e += kF32Threads) {
@@ -81,12 +88,12 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
         for (int e = tid; e < C * D; e += kF32Threads) {
             const int t = e / D, j = e % D;
             const bool in = t < n;
-            Qs[t * L::QP + j] = in ? qg[(int64_t)(t0 + t) * D + j] : 0.0f;
-            Ks[t * L::QP + j] = in ? kg[(int64_t)(t0 + t) * D + j] : 0.0f;
+            Qs[t * L::QP + j] = in ? ld_in<BF>(p.q, qk0 + (int64_t)(t0 + t) * D + j) : 0.0f;
+            Ks[t * L::QP + j] = in ? ld_in<BF>(p.k, qk0 + (int64_t)(t0 + t) * D + j) : 0.0f;
         }
         for (int e = tid; e < C * kRows; e += kF32Threads) {
             const int t = e / kRows, i = e % kRows;
-            Vs[e] = t < n ? vg[(int64_t)(t0 + t) * D + blk * kRows + i] : 0.0f;
+            Vs[e] = t < n ? ld_in<BF>(p.v, v0 + (int64_t)(t0 + t) * D + blk * kRows + i) : 0.0f;
         }
         if (tid < 64) {
             // inclusive prefix sum of g over the chunk (lanes >= n hold g = 0)
@@ -172,7 +179,11 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
             if (t < n) {
                 float acc = Gam[t] * p.scale * Y[t * L::RP + i];
                 for (int s = 0; s <= t; ++s) acc += Aqk[t * L::CP + s] * U[s * L::RP + i];
-                og[(int64_t)(t0 + t) * D + blk * kRows + i] = acc;
+                const int64_t oi = o0 + (int64_t)(t0 + t) * D + blk * kRows + i;
+                if (p.o_f16)
+                    static_cast<_Float16 *>(p.o)[oi] = f16_out(acc);
+                else
+                    static_cast<float *>(p.o)[oi] = acc;
             }
         }
         // S <- gamma_C S + (diag(exp(G_C - G)) U)^T K
@@ -197,35 +208,47 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
     }
 }
 
-template <int D, int C>
+template <int D, int C, bool BF>
 hipError_t launch_dc(const PrefillParams &p, hipStream_t stream) {
     const size_t bytes = F32Smem<D, C>::kBytes;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_prefill_f32_kernel<D, C>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (err != hipSuccess) return err;
+    static bool attr_set = false;  // a property of the function: set once
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_prefill_f32_kernel<D, C, BF>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
     dim3 grid((unsigned)(p.B * p.Hv * (D / kRows))), block(kF32Threads);
-    hipLaunchKernelGGL((gdn_prefill_f32_kernel<D, C>), grid, block, bytes, stream, p);
+    hipLaunchKernelGGL((gdn_prefill_f32_kernel<D, C, BF>), grid, block, bytes, stream, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool BF>
 hipError_t launch_d(const PrefillParams &p, int chunk, hipStream_t stream) {
     switch (chunk) {
-        case 16: return launch_dc<D, 16>(p, stream);
-        case 32: return launch_dc<D, 32>(p, stream);
-        case 64: return launch_dc<D, 64>(p, stream);
+        case 16: return launch_dc<D, 16, BF>(p, stream);
+        case 32: return launch_dc<D, 32, BF>(p, stream);
+        case 64: return launch_dc<D, 64, BF>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_prefill_f32(const PrefillParams &p, int chunk, hipStream_t stream) {
+hipError_t launch_prefill_f32(const PrefillParams &p, int chunk, bool bf16, hipStream_t stream) {
+    if (bf16) {
+        switch (p.D) {
+            case 16: return launch_d<16, true>(p, chunk, stream);
+            case 32: return launch_d<32, true>(p, chunk, stream);
+            case 64: return launch_d<64, true>(p, chunk, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (p.D) {
-        case 16: return launch_d<16>(p, chunk, stream);
-        case 32: return launch_d<32>(p, chunk, stream);
-        case 64: return launch_d<64>(p, chunk, stream);
-        case 128: return launch_d<128>(p, chunk, stream);
+        case 16: return launch_d<16, false>(p, chunk, stream);
+        case 32: return launch_d<32, false>(p, chunk, stream);
+        case 64: return launch_d<64, false>(p, chunk, stream);
+        case 128: return launch_d<128, false>(p, chunk, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_mfma_kernel(PrefillParam
     const uint16_t *vg = static_cast<const uint16_t *>(p.v) + (int64_t)pair * T * kD;
     const float *gg = p.g + (int64_t)pair * T;
     const float *bg = p.beta + (int64_t)pair * T;
-    float *og = static_cast<float *>(p.o) + (int64_t)pair * T * kD;
+    const int64_t o0 = (int64_t)pair * T * kD;
 
     // ---- state fragment: S[jl][r] = state[16 dvb + li][32 w + 16 jl + 4 q4 + r]
     const int64_t srow = ((int64_t)pair * kD + kRows * dvb + li) * kD + 32 * w + 4 * q4;
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_mfma_kernel(PrefillParam
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * mt + 4 * q4 + r;
-                const float gate = __expf(fminf(Gs[t] - gs, 0.0f));
+                const float gate = __expf(Gs[t] - gs);
                 if (!isq) {
                     const float a = (s < t) ? Bs[t] * gate * acc[r] : 0.0f;
                     Ah[t * CP + s] = (_Float16)a;
@@ -330,7 +330,14 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_mfma_kernel(PrefillParam
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * w + 4 * q4 + r;
-                if (t < n) og[(int64_t)(t0 + t) * kD + kRows * dvb + li] = Gam[t] * p.scale * yw[r] + acc[r];
+                if (t < n) {
+                    const float ov = Gam[t] * p.scale * yw[r] + acc[r];
+                    const int64_t oi = o0 + (int64_t)(t0 + t) * kD + kRows * dvb + li;
+                    if (p.o_f16)
+                        static_cast<_Float16 *>(p.o)[oi] = f16_out(ov);
+                    else
+                        static_cast<float *>(p.o)[oi] = ov;
+                }
             }
         }
 

@@ -22,7 +22,9 @@
  *     symbolic-length prefill entry;
  *   - key heads shared by value heads: the gdn_qkv test on page "27b 935/47"
  *     repeats (tiles) the key heads over the value heads (GDN_HEADS_TILED).
- * The decay is passed as g (log-decay); the library forms alpha = exp(g).
+ * The decay is passed as g (log-decay); the library forms alpha = exp(g). g <= 0 is
+ * a precondition (alpha in (0, 1]: a decay, as the pages' gates are); g > 0 is not
+ * rejected but leaves the range in which the float16 operands below are safe.
  * Callers pass q and k already L2-normalised and q without the scale.
  *
  * Memory: every tensor pointer is a DEVICE pointer to memory the caller owns
@@ -39,12 +41,22 @@
  *
  * Precision: g and beta are float32; o is float32, or float16 when
  * shape->o_dtype says so; the states are float32, or float16 when
- * shape->state_dtype says so (below). q/k/v are float32 or bfloat16. The bfloat16 path runs its matrix products on fp16 MFMA operands
- * with fp32 accumulation (bfloat16 inputs convert exactly while their
- * magnitudes stay within fp16 range, about 6e-5 .. 6.5e4); the float32 path
- * computes in fp32 throughout. Results depend on the chunk length through the
- * order of reductions, so different chunk lengths agree within rounding, not
+ * shape->state_dtype says so (below). q/k/v are float32 or bfloat16. The bfloat16
+ * path at head_dim 128 runs its matrix products on float16 MFMA operands with
+ * float32 accumulation; the float32 path, and bfloat16 at head_dims below 128,
+ * compute in fp32 on the vector ALUs. Results depend on the chunk length through
+ * the order of reductions, so different chunk lengths agree within rounding, not
  * bit for bit.
+ *
+ * Float16 operand range (bfloat16 at head_dim 128, prefill and its segment maps):
+ * k and q, the state, the values R = beta (v - gamma K S^T) and U = T R of a chunk,
+ * and the chunk matrices T and A_qk are rounded to float16 as MFMA operands.
+ * bfloat16 inputs convert exactly while their magnitudes lie in about 6e-5 .. 65504
+ * (smaller ones lose at most 3e-8 absolutely). A value beyond +-65504 becomes
+ * infinite, and the outputs and final state that depend on it become non-finite
+ * (inf or NaN): nothing is clamped and no error is reported. With L2-normalised q, k,
+ * g <= 0 and |v|, |state| up to a few thousand every operand stays far inside the
+ * range. Decode and the float32 paths have no such limit.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -56,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
     GDN_OK = 0,
@@ -117,30 +129,40 @@ typedef struct {
 
 /*
  * Supported set (GDN_ERR_UNSUPPORTED otherwise):
- *   bfloat16: dk = dv = 128; C in {16, 32, 64}.
- *   float32:  dk = dv in {16, 32, 64, 128}; C in {16, 32, 64}.
+ *   prefill:  dk = dv in {16, 32, 64, 128}, C in {16, 32, 64}, either dtype.
  *   decode:   dk = dv in {32, 64, 128}, either dtype.
- *   float16 states: decode and every prefill path.
- *   float16 o: decode, the gated RMSNorm, and the bfloat16 prefill with C in
- *   {32, 64} (fixed-length and packed).
- * Speed: the bfloat16 prefill with C in {32, 64} runs a chunk-parallel kernel and then
- * the pass over the chunks (0.71 ms for B = 1, Hk = 16, Hv = 32, T = 32768 on an
- * MI355X); with C = 16 it runs one fused kernel that redoes the chunk products in every
- * block of state rows, about ten times slower on long sequences (7.5 ms there). The
- * float32 path is a VALU kernel meant for precision checks and short sequences.
+ *   float16 states and float16 o: every prefill path, decode (and the gated RMSNorm for o).
+ *   (float16 o rounds each output, at most 2^-11 of its value: within the bfloat16 path's
+ *   accuracy, beyond the float32 path's.)
+ * Paths: bfloat16 with dk = 128 and C in {32, 64} runs the segmented MFMA prefill (below);
+ * bfloat16 with dk = 128 and C = 16 one fused MFMA kernel that redoes the chunk products in
+ * every block of 16 state rows (about ten times slower on long sequences); float32 q/k/v,
+ * and bfloat16 with dk < 128, a float32 VALU kernel.
+ *
+ * Segmented prefill (bfloat16, dk = 128, C in {32, 64}): the chunks of each sequence are cut
+ * into P segments of equal chunk counts that run in parallel: a map pass computes, per
+ * segment, the end state of segment 0 and the affine map S -> S M + N of each later segment
+ * (the chunk update is affine in the start state), a combine chains the maps into every
+ * segment's start state, and an output pass runs every segment from its start. P is as
+ * large as needed to give each of the GPU's 256 CUs a workgroup in the output pass
+ * (ceil(256 / (B Hv)), at most the chunk count and 64), reduced until its workspace fits the
+ * workspace_bytes the caller passes: 3 * B * Hv * P * dk * dk * 4 bytes for P > 1, nothing
+ * for P = 1 (one workgroup per (b, value head) runs the whole sequence). Any workspace size,
+ * NULL included, is valid; gdn_prefill_segments() tells which P a size gives.
  */
 
 /*
- * Bytes of scratch memory gdn_prefill needs for this shape (0: pass NULL, 0).
- * The bfloat16 path with chunk 32 or 64 runs the sequence as consecutive token
- * segments, each needing about 16.4 KB of workspace per token at B * Hv = 32 (it
- * scales with B * Hv), so that the workspace stays bounded: a segment takes as many
- * chunks as fit 1.5 GiB of workspace + v + o, or the byte count in the environment
- * variable GDN_PREFILL_SEGMENT_BYTES when set (read by this call and by gdn_prefill,
- * which must see the same value). With more than one segment the workspace also holds
- * the state carried between segments.
+ * Bytes of workspace for the preferred segment count of this shape (0 when the path uses no
+ * workspace, or when one segment is preferred, or for an invalid shape). A smaller workspace
+ * is accepted and means fewer segments (see above).
  */
 size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
+
+/*
+ * The number of segments P that gdn_prefill runs for this shape with workspace_bytes of
+ * workspace: 1 for the paths that do not segment, 0 for an invalid shape. Pure host code.
+ */
+int gdn_prefill_segments(const gdn_shape *shape, size_t workspace_bytes);
 
 /*
  * Chunked prefill of T tokens from a given state; writes every output and the
@@ -152,9 +174,14 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
  *   o              [B][Hv][T][dv]   o_dtype, output; must not overlap any input
  *   final_state    [B][Hv][dv][dk]  state_dtype, output, or NULL to skip; may be
  *                                   the same pointer as initial_state (in place)
- *   workspace      device scratch of gdn_prefill_workspace_bytes(shape) bytes
+ *   workspace      device scratch of workspace_bytes bytes, 16-byte aligned, or NULL; the
+ *                  segmented path uses as much of it as its segment count needs (above),
+ *                  the other paths none. It must not overlap any other argument.
  * A ragged batch passes every sequence padded to the common T with beta = 0,
  * g = 0 (and zero q/k/v) on the padded steps, which leave the state unchanged.
+ * With initial_state == final_state (in place) every workgroup reads the state it starts
+ * from before any workgroup writes the final state (the segmented path's output pass starts
+ * segment 0 from the map pass's float32 copy of the initial state).
  */
 gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, const void *v,
                        const float *g, const float *beta, const void *initial_state,

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib, bnd):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(1) == b"invalid argument"
     assert lib.gdn_status_string(2) == b"unsupported configuration"
@@ -58,11 +58,25 @@ GB = 1 << 30
 ADDR = dict(q=1 * GB, k=2 * GB, v=3 * GB, g=4 * GB, beta=5 * GB, s0=6 * GB, o=7 * GB, sf=8 * GB)
 
 
-def _prefill(lib, shape, **over):
+def _prefill(lib, shape, ws=None, nbytes=0, **over):
     a = dict(ADDR)
     a.update(over)
     return lib.gdn_prefill(ctypes.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
-                           a["o"], a["sf"], None, 0, None)
+                           a["o"], a["sf"], ws, nbytes, None)
+
+
+# A shape that splits into segments (2 chunks of 32, four value heads) and a misaligned
+# workspace of its preferred size: a call that passes every other check stops at the
+# workspace alignment check, so the tests below see validation succeed without a launch.
+def _seg_shape(bnd, **kw):
+    return _shape(bnd, chunk=32, **kw)
+
+
+def _passes_until_workspace(lib, shape, **over):
+    need = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
+    assert need > 0
+    st = _prefill(lib, shape, ws=9 * GB + 8, nbytes=need, **over)
+    return st == 1 and "workspace is not 16-byte aligned" in _err(lib)
 
 
 def _decode(lib, shape, **over):
@@ -101,11 +115,13 @@ def test_prefill_rejects_null_shape(lib):
     assert "shape" in _err(lib)
 
 
-def test_prefill_f32_head_dims(lib, bnd):
-    shape = _shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32, head_dim=48)
-    assert _prefill(lib, shape) == 2
-    shape = _shape(bnd, qkv_dtype=bnd.GDN_DTYPE_BF16, head_dim=64)
-    assert _prefill(lib, shape) == 2 and "bfloat16" in _err(lib)
+def test_prefill_head_dims(lib, bnd):
+    """head_dim 16, 32, 64 and 128 for both dtypes (bfloat16 below 128 on the VALU kernel)."""
+    assert _prefill(lib, _shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32, head_dim=48)) == 2 and "head_dim" in _err(lib)
+    assert _prefill(lib, _shape(bnd, head_dim=48)) == 2 and "head_dim" in _err(lib)
+    for d in (16, 32, 64):  # accepted: with T = 0 and no final state there is nothing to launch
+        assert _prefill(lib, _shape(bnd, head_dim=d, seq_len=0), sf=None) == 0, _err(lib)
+        assert _prefill(lib, _shape(bnd, head_dim=d), o=None) == 1 and "o is NULL" in _err(lib)
 
 
 @pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "o"])
@@ -130,12 +146,11 @@ def test_prefill_rejects_overlaps(lib, bnd):
 
 def test_state_bytes_follow_state_dtype(lib, bnd):
     """A float16 state occupies half the bytes: a final state right after a float16 initial
-    state passes the overlap checks (the call then stops at the missing workspace), the same
-    placement with float32 states overlaps."""
+    state passes the overlap checks, the same placement with float32 states overlaps."""
     st16 = 1 * 4 * 128 * 128 * 2
-    f16 = _shape(bnd, state_dtype=bnd.GDN_STATE_F16)
-    assert _prefill(lib, f16, sf=ADDR["s0"] + st16) == 1 and "workspace is NULL" in _err(lib)
-    assert _prefill(lib, _shape(bnd), sf=ADDR["s0"] + st16) == 1 and "partially overlaps" in _err(lib)
+    f16 = _seg_shape(bnd, state_dtype=bnd.GDN_STATE_F16)
+    assert _passes_until_workspace(lib, f16, sf=ADDR["s0"] + st16)
+    assert _prefill(lib, _seg_shape(bnd), sf=ADDR["s0"] + st16) == 1 and "partially overlaps" in _err(lib)
     assert _prefill(lib, f16, sf=ADDR["s0"] + st16 - 16) == 1 and "partially overlaps" in _err(lib)
     assert _decode(lib, _shape(bnd, seq_len=1, state_dtype=bnd.GDN_STATE_F16), o=ADDR["s0"] + st16 - 16) == 1
     assert "o overlaps state" in _err(lib)
@@ -149,54 +164,58 @@ def test_decode_rejects(lib, bnd):
     assert _decode(lib, _shape(bnd, seq_len=1), s0=ADDR["k"]) == 1 and "state overlaps k" in _err(lib)
 
 
-def _ws_bytes(B, Hk, Hv, T, C, budget=1536 << 20):
-    """One token segment's chunk data: fp16 T and A_qk plus three float gate vectors per
-    (b, value head, chunk), and the fp16 k tile and q fragments per (b, key head, chunk);
-    plus, when the sequence takes several segments, the fp32 state carried between them.
-    Segments hold as many chunks as fit `budget` bytes of workspace, v and o, balanced."""
-    nc = -(-T // C)
-    chunk_bytes = lambda n: 2 * (B * Hv * n * (2 * C * C + 6 * C) + B * Hk * n * C * 256)
-    per_chunk = chunk_bytes(1) + B * Hv * C * 128 * 6
-    seg = min(max(budget // per_chunk, 1), nc)
-    count = -(-nc // seg)
-    chunks = -(-nc // count)
-    if count == 1:
-        return chunk_bytes(chunks)
-    return -(-chunk_bytes(chunks) // 256) * 256 + B * Hv * 128 * 128 * 4
+def _segments(B, Hv, T, C):
+    """Preferred segment count: enough output-pass workgroups for 256 CUs, at most one per
+    chunk and 64."""
+    return max(1, min(-(-256 // (B * Hv)), -(-T // C), 64))
+
+
+def _ws_bytes(B, Hv, P):
+    """Three float32 128 x 128 matrices per (b, value head, segment) when P > 1."""
+    return 3 * B * Hv * P * 128 * 128 * 4 if P > 1 else 0
 
 
 def test_workspace_query(lib, bnd):
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd))) == _ws_bytes(1, 2, 4, 64, 64)
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, seq_len=100, chunk=32))) == \
-        _ws_bytes(1, 2, 4, 100, 32)
-    # the long workload (T = 32768, 16 key / 32 value heads) is one segment by default
+    q = lambda sh: lib.gdn_prefill_workspace_bytes(ctypes.byref(sh))
+    assert q(_shape(bnd)) == 0  # one chunk: one segment
+    assert q(_shape(bnd, seq_len=100, chunk=32)) == _ws_bytes(1, 4, _segments(1, 4, 100, 32)) == 3 * 4 * 4 * 65536
+    # the long workload (T = 32768, 16 key / 32 value heads): 8 segments of 64 chunks
     big = _shape(bnd, seq_len=32768, num_k_heads=16, num_v_heads=32)
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(big)) == _ws_bytes(1, 16, 32, 32768, 64)
-    assert _ws_bytes(1, 16, 32, 32768, 64) == 2 * 512 * (32 * (2 * 64 * 64 + 6 * 64) + 16 * 64 * 256)
+    assert _segments(1, 32, 32768, 64) == 8
+    assert q(big) == _ws_bytes(1, 32, 8) == 50331648
+    # a batch that fills the GPU by itself needs no segments
+    assert q(_shape(bnd, batch=8, seq_len=32768, num_k_heads=16, num_v_heads=32)) == 0
+    # paths that do not segment, invalid shapes
+    assert q(_shape(bnd, seq_len=4096, chunk=16)) == 0
+    assert q(_shape(bnd, seq_len=4096, qkv_dtype=bnd.GDN_DTYPE_F32)) == 0
+    assert q(_shape(bnd, seq_len=4096, head_dim=64)) == 0
+    assert q(_shape(bnd, batch=0)) == 0
 
 
-def test_workspace_segments(lib, bnd, monkeypatch):
-    """A smaller segment budget splits the sequence: 9 segments of 57 chunks at 160 MiB."""
-    monkeypatch.setenv("GDN_PREFILL_SEGMENT_BYTES", str(160 << 20))
+def test_segments_follow_workspace(lib, bnd):
+    """The workspace passed decides the segment count: the largest count up to the preferred
+    one whose matrices fit, one with none."""
     big = _shape(bnd, seq_len=32768, num_k_heads=16, num_v_heads=32)
-    got = lib.gdn_prefill_workspace_bytes(ctypes.byref(big))
-    assert got == _ws_bytes(1, 16, 32, 32768, 64, budget=160 << 20)
-    assert got < 80 << 20
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, chunk=16))) == 0
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32))) == 0
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(_shape(bnd, batch=0))) == 0
+    seg = lambda n: lib.gdn_prefill_segments(ctypes.byref(big), n)
+    assert seg(_ws_bytes(1, 32, 8)) == 8
+    assert seg(1 << 40) == 8
+    assert seg(_ws_bytes(1, 32, 8) - 1) == 7
+    assert seg(_ws_bytes(1, 32, 3)) == 3
+    assert seg(_ws_bytes(1, 32, 2) - 1) == 1
+    assert seg(0) == 1
+    assert lib.gdn_prefill_segments(ctypes.byref(_shape(bnd, seq_len=4096, chunk=16)), 1 << 30) == 1
+    assert lib.gdn_prefill_segments(ctypes.byref(_shape(bnd, batch=0)), 1 << 30) == 0
+    short = _shape(bnd, seq_len=65, chunk=32)  # 3 chunks: at most 3 segments
+    assert lib.gdn_prefill_segments(ctypes.byref(short), 1 << 40) == 3
 
 
 def test_prefill_checks_workspace(lib, bnd):
-    shape = _shape(bnd)
+    shape = _seg_shape(bnd)
     need = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
-    a = ADDR
-    call = lambda ws, n: lib.gdn_prefill(ctypes.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
-                                         a["o"], a["sf"], ws, n, None)
-    assert call(None, need) == 1 and "workspace is NULL" in _err(lib)
-    assert call(9 * GB, need - 1) == 1 and "needed" in _err(lib)
-    assert call(9 * GB + 8, need) == 1 and "aligned" in _err(lib)
-    assert call(a["v"], need) == 1 and "workspace overlaps v" in _err(lib)
+    assert need == _ws_bytes(1, 4, 2)
+    assert _prefill(lib, shape, ws=9 * GB + 8, nbytes=need) == 1 and "aligned" in _err(lib)
+    assert _prefill(lib, shape, ws=ADDR["v"], nbytes=need) == 1 and "workspace overlaps v" in _err(lib)
+    assert _prefill(lib, shape, ws=ADDR["sf"] - 4096, nbytes=need) == 1 and "overlaps" in _err(lib)
 
 
 def test_binding_rejects_cpu_tensors(bnd):
@@ -288,15 +307,14 @@ def test_varlen_rejects(lib, bnd):
 
 
 def test_f16_output_support_and_bytes(lib, bnd):
-    """float16 o: only the bfloat16 chunk-32/64 prefill (and decode, the epilogue); o then
-    occupies half the bytes, so a final state placed right after it passes the overlap checks
-    (the call then stops at the missing workspace)."""
+    """float16 o on every prefill path; o then occupies half the bytes, so a final state
+    placed right after it passes the overlap checks."""
     f16 = dict(o_dtype=bnd.GDN_OUT_F16)
-    assert _prefill(lib, _shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32, **f16)) == 2 and "float16 o" in _err(lib)
-    assert _prefill(lib, _shape(bnd, chunk=16, **f16)) == 2 and "float16 o" in _err(lib)
     o16 = 1 * 4 * 64 * 128 * 2
-    assert _prefill(lib, _shape(bnd, **f16), sf=ADDR["o"] + o16) == 1 and "workspace is NULL" in _err(lib)
-    assert _prefill(lib, _shape(bnd), sf=ADDR["o"] + o16) == 1 and "final_state overlaps o" in _err(lib)
+    assert _passes_until_workspace(lib, _seg_shape(bnd, **f16), sf=ADDR["o"] + o16)
+    assert _prefill(lib, _seg_shape(bnd), sf=ADDR["o"] + o16) == 1 and "final_state overlaps o" in _err(lib)
+    for sh in (_shape(bnd, qkv_dtype=bnd.GDN_DTYPE_F32, **f16), _shape(bnd, chunk=16, **f16)):
+        assert _prefill(lib, sh, sf=ADDR["o"] + o16 - 16) == 1 and "final_state overlaps o" in _err(lib)
     # the epilogue: a gate starting where float16 o rows end overlaps float32 o rows
     n16 = 10 * 4 * 128 * 2
     assert _norm(lib, _shape(bnd, seq_len=10, **f16), gate=7 * GB + n16 - 16) == 1 and "overlaps" in _err(lib)

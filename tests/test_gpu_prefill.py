@@ -96,34 +96,6 @@ def test_long_prefill_32k_full(gdn, oracle_lib):
     check(oracle_lib, x, o, sf, label="long_32k (all heads)")
 
 
-def test_segmented_prefill(gdn, oracle_lib, monkeypatch):
-    """A prefill run as several token segments (B=2, Hv=32, T=2000 at chunk 64 under a 160 MiB
-    segment budget: two segments of 16 chunks, the last ragged), with the carried state in the
-    caller's final_state, in the workspace (no final state asked for), and in place."""
-    import torch
-    monkeypatch.setenv("GDN_PREFILL_SEGMENT_BYTES", str(160 << 20))
-    x = inputs.generate(2, 2000, 16, 32, 128, "bf16", seed=12, init_state="normal")
-    shape = gdn.make_shape(batch=2, seq_len=2000, num_k_heads=16, num_v_heads=32, head_dim=128, chunk=64,
-                           qkv_dtype=gdn.GDN_DTYPE_BF16, head_map=0, scale=x.scale)
-    lib = gdn.load_library()
-    import ctypes
-    ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
-    full = 2 * (2 * 32 * 32 * (2 * 64 * 64 + 6 * 64) + 2 * 16 * 32 * 64 * 256)
-    assert 0 < ws < full  # smaller than one workspace for the whole sequence
-    o, sf = run_prefill(gdn, x, 64)
-    o_ref, s_ref = check(oracle_lib, x, o, sf, label="segmented, state via final_state")
-    q, k, v = qkv_dev(x)
-    o2, none = gdn.prefill(q, k, v, dev(x.g), dev(x.beta), dev(x.s0), chunk=64, scale=x.scale,
-                           write_final_state=False)
-    assert none is None
-    assert rel_err(o2.cpu().numpy(), o_ref) <= TOL_BF16
-    state = dev(x.s0)
-    o3, s3 = gdn.prefill(q, k, v, dev(x.g), dev(x.beta), state, chunk=64, scale=x.scale, final_state=state)
-    torch.cuda.synchronize()
-    assert rel_err(o3.cpu().numpy(), o_ref) <= TOL_BF16
-    assert rel_err(state.cpu().numpy(), s_ref) <= TOL_BF16
-
-
 # ---------------------------------------------------------------- semantics
 def test_zero_length_copies_state(gdn):
     import torch

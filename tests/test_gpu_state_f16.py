@@ -122,11 +122,12 @@ def test_prefill_f16_state(gdn, oracle_lib, dtype, chunk):
     assert torch.equal(sf, sf32.half())
 
 
-def test_prefill_f16_state_in_place_and_segmented(gdn, oracle_lib, monkeypatch):
-    """float16 state updated in place, over two token segments (160 MiB budget, B=2, Hv=32,
-    T=2000): the state is carried between segments in float32 in the workspace."""
+def test_prefill_f16_state_in_place_and_segmented(gdn, oracle_lib):
+    """float16 state updated in place, over four segments (B=2, Hv=32, T=2000 at chunk 64 with
+    the preferred workspace): segment starts are kept in float32 in the workspace and the final
+    state is rounded once."""
     import torch
-    monkeypatch.setenv("GDN_PREFILL_SEGMENT_BYTES", str(160 << 20))
+    assert gdn.prefill_segments(2, 2000, 16, 32, 128, 1 << 40, chunk=64) == 4
     x = inputs.generate(2, 2000, 16, 32, 128, "bf16", seed=97, init_state="normal")
     s16 = x.s0.astype(np.float16)
     q, k, v = qkv_dev(x)
