@@ -4,8 +4,8 @@
 //
 // Chunked WY form, per chunk of C tokens with start state S (dv x dk), local t:
 //   G_t = sum_{s<=t} g_s,  Gamma_ts = exp(G_t - G_s) (s <= t)
-//   A = strict_lower(diag(beta) (K K^T o Gamma)),  T = (I + A)^{-1}
-//   X = K S^T,  R = diag(beta) V - diag(beta gamma) X,  U = T R
+//   A = strict_lower(diag(beta) (K K^T o Gamma))
+//   X = K S^T,  R = diag(beta) V - diag(beta gamma) X,  U solves (I + A) U = R
 //   O = diag(gamma) (scale Q S^T) + lower_incl(scale Q K^T o Gamma) U
 //   S <- gamma_C S + (diag(exp(G_C - G)) U)^T K
 // (of S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
@@ -13,6 +13,11 @@
 // state are those of the gated-delta reference tests on the "27b 935/47" compare
 // page; padded steps with beta = 0, g = 0 are exact no-ops, the symbolic-length
 // prefill entry of the "mergable fast RDNA3 Qwen 3.6" commit log).
+//
+// The unit-lower system is solved in 16-token blocks, U_m = T_mm (R_m - sum_{j<m} A_mj U_j)
+// with T_mm = (I + A_mm)^{-1}: the 16 x 16 diagonal inverses and the blocks of A below them
+// are all the chunk preparation has to deliver (the block form of the forward substitution
+// in the tinygrad helper inverse_unit_lower, compare page "27b 935/47", llm/kernels/generic.py).
 //
 // The chunk update is affine in the start state: S_new = S M_c + N_c. A segment
 // of chunks therefore maps its start S_p to S_p M_p + N_p, with N_p the end state
@@ -26,20 +31,20 @@
 //      in the last segment, the final state.
 // With P = 1 only the output pass runs.
 //
-// Workgroup of 8 waves (wave i on SIMD i % 4):
+// Workgroup of 8 waves (wave i on SIMD i % 4), two barriers per chunk:
 //   waves 0-3, "row waves": state rows 32 w .. 32 w + 31 as two 16-row MFMA blocks
-//     held in registers for the whole segment; per chunk X, R, U, the update and
-//     (OUT) Y = S Q^T and O^T. Every operand of chunk i is in LDS slot i & 1 when
-//     the chunk starts.
+//     held in registers for the whole segment; per chunk X and (OUT) Y = S Q^T before
+//     the first barrier, then R, U, O^T and the update. Every operand of chunk i is in
+//     LDS slot i & 1 when the chunk starts; LDS operands are requested in batches one
+//     batch ahead of the MFMAs that use them.
 //   waves 4-7, "prep waves", token tile m = w - 4: prepare chunk i + 1 into slot
-//     (i + 1) & 1 during chunk i, in three phases separated by workgroup barriers:
-//     P1 converts the raw bf16 k, q rows of tile m (loaded one chunk earlier into
-//     registers) to the fp16 k and q tiles and stores the v rows, then issues the
-//     loads of chunk i + 2; P2 forms K K^T and Q K^T of tile m against tiles <= m
-//     on MFMA, the gates, A and A_qk, and the 16 x 16 diagonal block of T by
-//     substitution; P3 (wave 4) joins the diagonal blocks into T by MFMA doubling
-//     and writes the T fragments.
-//   Every wave runs exactly three barriers per chunk.
+//     (i + 1) & 1 during chunk i. Before the first barrier (P1) each converts its
+//     16 raw bf16 k and q rows (loaded one chunk earlier into registers) to the fp16
+//     tiles and stores its v rows, wave 4 also forms the gate vectors, and each
+//     issues the loads of chunk i + 2; after it (P2) each forms K K^T and Q K^T of
+//     its tile against the tiles at or before it on MFMA, the gated blocks of A
+//     and A_qk, and the inverse of its diagonal block row by row. No prep wave
+//     waits for another.
 //
 // LDS tiles of k and q: row-major 256-byte token rows, each 32-column block in
 // fragment order (gdn_frag.h), 16-byte groups XOR-swizzled by row; v is stored
@@ -58,38 +63,39 @@ constexpr int kD = 128;
 constexpr int kSegThreads = 512;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 // fragment block of token tile m, k block kb (kb <= m / 2), counted over the blocks on or
 // below the diagonal: (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 __host__ __device__ constexpr int fblk(int m, int kb) { return m + (m > 2 ? m - 2 : 0) + kb; }
+// 16 x 16 block (m, j), j < m, of A below the diagonal: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+__host__ __device__ constexpr int ablk(int m, int j) { return m * (m - 1) / 2 + j; }
 
 template <int C, bool OUT>
 struct SegSmem {
     static constexpr int NT = C / 16, KBC = C / 32;
-    static constexpr int CP = C + 8;                             // fp16 pitch of Ah, Tm
-    static constexpr int DP = 20;                                // f32 pitch of a transposed diagonal block
-    static constexpr int kFr = fblk(NT - 1, (NT - 1) / 2) + 1;   // fragment blocks of T / A_qk
+    static constexpr int kFr = fblk(NT - 1, (NT - 1) / 2) + 1;   // A_qk fragment blocks
+    static constexpr int kNA = NT * (NT - 1) / 2;                // blocks of A below the diagonal
     static constexpr size_t kTile = (size_t)C * 256;             // C x 128 16-bit values
     static constexpr size_t oK = 0;                              // [2] fp16 k tiles
     static constexpr size_t oQ = oK + 2 * kTile;                 // [2] fp16 q tiles (OUT)
     static constexpr size_t oV = oQ + (OUT ? 2 * kTile : 0);     // [2] bf16 v tiles
-    static constexpr size_t oT = oV + 2 * kTile;                 // [2][kFr][64] x 16 B T fragments
-    static constexpr size_t oA = oT + 2 * kFr * 1024;            // [2][kFr][64] x 16 B A_qk fragments (OUT)
-    static constexpr size_t oG = oA + (OUT ? 2 * kFr * 1024 : 0);  // [2][4][C] f32: gamma, beta, exp(G_C-G), beta gamma
-    static constexpr size_t oAh = oG + 2 * 16 * C;               // fp16 [C][CP]: A below the diagonal blocks
-    static constexpr size_t oTm = oAh + 2 * C * CP;              // fp16 [C][CP]: T
-    static constexpr size_t oAd = oTm + 2 * C * CP;              // f32 [NT][16][DP]: diagonal blocks of A, transposed
-    static constexpr size_t oGt = oAd + 4 * NT * 16 * DP;        // f32 [4][2][64]: G and beta per prep wave
-    static constexpr size_t kBytes = oGt + 4 * 2 * 64 * 4;
-    static_assert(oQ % 16 == 0 && oV % 16 == 0 && oT % 16 == 0 && oA % 16 == 0 && oG % 16 == 0 &&
-                      oAh % 16 == 0 && oTm % 16 == 0 && oAd % 16 == 0 && oGt % 16 == 0,
+    static constexpr size_t oA = oV + 2 * kTile;                 // [2][kFr][64] x 16 B A_qk fragments (OUT)
+    static constexpr size_t oNA = oA + (OUT ? 2 * kFr * 1024 : 0);  // [2][kNA][64] x 8 B: -A blocks
+    static constexpr size_t oTd = oNA + 2 * kNA * 512;           // [2][NT][2][64] x 8 B: T_mm, diag(exp(G_C-G)) T_mm
+    static constexpr size_t oG = oTd + 2 * NT * 1024;             // [2][5][C] f32: gamma, beta, exp(G_C-G), beta gamma, G
+    static constexpr size_t oRG = oG + 2 * 20 * C;               // f32 [2][2][64]: raw g and beta of a chunk
+    static constexpr size_t oAt = oRG + 2 * 2 * 64 * 4;          // f32 [NT][16][20]: diagonal blocks of A, transposed
+    static constexpr size_t kBytes = oAt + NT * 16 * 20 * 4;
+    static_assert(oQ % 16 == 0 && oV % 16 == 0 && oA % 16 == 0 && oNA % 16 == 0 && oTd % 16 == 0 &&
+                      oG % 16 == 0 && oRG % 16 == 0 && oAt % 16 == 0,
                   "alignment");
     static_assert(kBytes <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ f16x8 ld8(const unsigned char *p) { return *reinterpret_cast<const f16x8 *>(p); }
+__device__ __forceinline__ f16x4 ld4(const unsigned char *p) { return *reinterpret_cast<const f16x4 *>(p); }
 __device__ __forceinline__ f32x4 ldf4(const unsigned char *p) { return *reinterpret_cast<const f32x4 *>(p); }
-__device__ __forceinline__ f16x4 ld4h(const _Float16 *p) { return *reinterpret_cast<const f16x4 *>(p); }
 
 __device__ __forceinline__ f16x8 pack8(f32x4 lo, f32x4 hi) {
     return f16x8{(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
@@ -103,8 +109,19 @@ __device__ __forceinline__ s16x4 ld_tr_raw(const unsigned char *p) {
 }
 __device__ __forceinline__ f16x4 ld_tr(const unsigned char *p) { return __builtin_bit_cast(f16x4, ld_tr_raw(p)); }
 
+// 4 bytes per lane from global memory straight into LDS (lane l at lds + 4 l)
+__device__ __forceinline__ void dma4(const void *g, unsigned char *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Workgroup barrier for LDS traffic only: outstanding global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// keeps the compiler from moving instructions across this point (so that a batch of LDS
+// reads is issued before the MFMAs of the previous batch)
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int N>
 using IC = std::integral_constant<int, N>;
@@ -115,10 +132,32 @@ __device__ __forceinline__ f16x4 bf4_to_h4(uint16_t a, uint16_t b, uint16_t c, u
                  (_Float16)bf16_bits_to_f32(d)};
 }
 
+// x of lane k of this lane's row of 16 lanes (DPP row_newbcast:k)
+template <int k>
+__device__ __forceinline__ float row_lane(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + k, 0xF, 0xF, false));
+}
+
+// T = (I + A)^{-1} for a strictly lower 16 x 16 A, by forward substitution over the rows,
+// T[r][c] = [r == c] - sum_{k<r} A[r][k] T[k][c]: lane (q, i) holds nrow = -A[i][0..15] and
+// builds t[e] = T[i][4 q + e], the A-operand fragment of a 16 x 16 x 16 product. Step k takes
+// the finished row k from lane k of each row of 16 lanes.
+template <int k>
+__device__ __forceinline__ void inv_rows(f32x4 &t, const float (&nrow)[16]) {
+    if constexpr (k < 15) {
+        const float ak = nrow[k];
+        f32x4 tk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tk[e] = row_lane<k>(t[e]);
+        t += ak * tk;
+        inv_rows<k + 1>(t, nrow);
+    }
+}
+
 template <int C, bool OUT>
 __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams sp) {
     using L = SegSmem<C, OUT>;
-    constexpr int NT = L::NT, KBC = L::KBC, CP = L::CP, DP = L::DP;
+    constexpr int NT = L::NT, KBC = L::KBC;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // every argument into a scalar local: a reference to the argument structure would make
     // the compiler copy it to scratch memory
@@ -164,8 +203,8 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
     const int NC = (T + C - 1) / C;
     const int cb = seg * p.seg_chunks;
     const int n = max(0, min(NC, cb + p.seg_chunks) - cb);  // chunks of this segment
-    const int64_t ktok = ((int64_t)b * p.Hk + kh) * p.Ts;      // first token row of q, k
-    const int64_t vtok = (int64_t)pair * p.Ts;                 // first token row of v, g, beta, o
+    const int64_t ktok = ((int64_t)b * p.Hk + kh) * p.Ts;     // first token row of q, k
+    const int64_t vtok = (int64_t)pair * p.Ts;                // first token row of v, g, beta, o
     const int64_t wsi = ((int64_t)pair * p.P + seg) * (kD * kD);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -224,128 +263,159 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) sb[bb][kb] = pack8(S[bb][2 * kb], S[bb][2 * kb + 1]);
 
-        // per-lane LDS addresses (slot, tile and block offsets are immediates)
-        int xo[4];  // offset in a k / q tile: row li, group 4 kb + q4
+        // per-lane LDS offsets (slot, tile and block offsets are immediates)
+        int xo[4];  // k / q tile: row li, group 4 kb + q4
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) xo[kb] = li * 256 + (((4 * kb + q4) ^ ksw(li)) << 4);
-        const unsigned char *ta[8];  // k tile read transposed: column tile jt of the update
+        int ta[8];  // k tile read transposed: column tile jt of the update
         {
             const int rt = 4 * q4 + (li >> 2);
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) {
                 const int g = 4 * (jt >> 1) + (li & 3);
-                ta[jt] = smem + L::oK + rt * 256 + ((g ^ ksw(rt)) << 4) + (jt & 1) * 8;
+                ta[jt] = rt * 256 + ((g ^ ksw(rt)) << 4) + (jt & 1) * 8;
             }
         }
-        const unsigned char *va[2];  // v tile read transposed: tokens 4 q4 + (li >> 2), columns r0 + 4 (li & 3)
+        int va[2];  // v tile read transposed: tokens 4 q4 + (li >> 2), columns r0 + 4 (li & 3)
         {
             const int rt = 4 * q4 + (li >> 2);
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
                 const int c = 32 * w + 16 * bb + 4 * (li & 3);
-                va[bb] = smem + L::oV + rt * 256 + (((c >> 3) ^ ksw(rt)) << 4) + (c & 7) * 2;
+                va[bb] = rt * 256 + (((c >> 3) ^ ksw(rt)) << 4) + (c & 7) * 2;
             }
         }
-        const unsigned char *fa = smem + lane * 16;          // T / A_qk fragments
-        const unsigned char *ga = smem + L::oG + 16 * q4;    // gate vectors, tokens 4 q4 .. + 3 of a tile
         float *o_f32 = static_cast<float *>(p.o);
         _Float16 *o_f16 = static_cast<_Float16 *>(p.o);
 
-        lds_barrier();
         lds_barrier();
         lds_barrier();
 
         auto interval = [&](auto sl, int i) __attribute__((always_inline)) {
             constexpr int s = decltype(sl)::value;
             const unsigned char *Kt = smem + L::oK + s * L::kTile;
-            const float *gts = reinterpret_cast<const float *>(smem + L::oG + s * 16 * C);
+            const unsigned char *Qt = smem + L::oQ + s * L::kTile;
+            const unsigned char *Vt = smem + L::oV + s * L::kTile;
+            const unsigned char *gt = smem + L::oG + s * 20 * C;  // gate vectors of this chunk
+            const unsigned char *na = smem + L::oNA + s * L::kNA * 512 + lane * 8;
+            const unsigned char *td = smem + L::oTd + s * 2 * NT * 512 + lane * 8;
+            const unsigned char *aq = smem + L::oA + s * L::kFr * 1024 + lane * 16;
 
-            // X = K S^T for both row blocks
-            f32x4 X[2][NT];
+            // ---- X = K S^T and (OUT) Y^T = S Q^T, k block by k block: the fragments of block
+            // kb + 1 are requested before the products of block kb
+            f32x4 X[2][NT], Y[2][NT];
+#pragma unroll
+            for (int m = 0; m < NT; ++m) X[0][m] = X[1][m] = Y[0][m] = Y[1][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f16x8 kf[2][NT], qf[2][NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-                X[0][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-                X[1][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const f16x8 kf = ld8(Kt + xo[kb] + m * 4096);
-                    X[0][m] = mfma16x16x32(kf, sb[0][kb], X[0][m]);
-                    X[1][m] = mfma16x16x32(kf, sb[1][kb], X[1][m]);
-                }
+                kf[0][m] = ld8(Kt + xo[0] + m * 4096);
+                if (OUT) qf[0][m] = ld8(Qt + xo[0] + m * 4096);
             }
-            lds_barrier();  // b1
-            // Y^T = S Q^T (lane: row 4 q4 + r of the block, token 16 m + li), from the chunk-start S
-            f32x4 Y[2][NT];
-            if constexpr (OUT) {
-                const unsigned char *Qt = smem + L::oQ + s * L::kTile;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int cur = kb & 1, nxt = cur ^ 1;
+                if (kb + 1 < 4) {
+#pragma unroll
+                    for (int m = 0; m < NT; ++m) {
+                        kf[nxt][m] = ld8(Kt + xo[kb + 1] + m * 4096);
+                        if (OUT) qf[nxt][m] = ld8(Qt + xo[kb + 1] + m * 4096);
+                    }
+                }
+                fence();
 #pragma unroll
                 for (int m = 0; m < NT; ++m) {
-                    Y[0][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    Y[1][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    X[0][m] = mfma16x16x32(kf[cur][m], sb[0][kb], X[0][m]);
+                    X[1][m] = mfma16x16x32(kf[cur][m], sb[1][kb], X[1][m]);
+                }
+                if constexpr (OUT) {
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) {
-                        const f16x8 qf = ld8(Qt + xo[kb] + m * 4096);
-                        Y[0][m] = mfma16x16x32(sb[0][kb], qf, Y[0][m]);
-                        Y[1][m] = mfma16x16x32(sb[1][kb], qf, Y[1][m]);
+                    for (int m = 0; m < NT; ++m) {
+                        Y[0][m] = mfma16x16x32(sb[0][kb], qf[cur][m], Y[0][m]);
+                        Y[1][m] = mfma16x16x32(sb[1][kb], qf[cur][m], Y[1][m]);
                     }
                 }
+                fence();
             }
-            // R = beta V - beta gamma X  (v read transposed: tokens 16 m + 4 q4 + r, column r0 + li)
-            f16x8 rb[2][KBC];
-#pragma unroll
-            for (int kb = 0; kb < KBC; ++kb) {
-                f32x4 R[2][2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int m = 2 * kb + hh;
-                    const f32x4 bt = ldf4(ga + s * 16 * C + 4 * C + 64 * m);
-                    const f32x4 bg = ldf4(ga + s * 16 * C + 12 * C + 64 * m);
-#pragma unroll
-                    for (int bb = 0; bb < 2; ++bb) {
-                        f32x4 vv = {0.f, 0.f, 0.f, 0.f};
-                        if (has_v) {
-                            const s16x4 raw = ld_tr_raw(va[bb] + s * L::kTile + m * 4096);
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) vv[r] = bf16_bits_to_f32((uint16_t)raw[r]);
-                        }
-                        R[bb][hh] = bt * vv - bg * X[bb][m];
-                    }
-                }
-                rb[0][kb] = pack8(R[0][0], R[0][1]);
-                rb[1][kb] = pack8(R[1][0], R[1][1]);
-            }
-            // U = T R
-            f32x4 U[2][NT];
+            lds_barrier();  // b1: the prep waves' rows of chunk i + 1 are in place
+            // ---- operands of the rest of the chunk, requested together: v (transposed), the
+            // gate vectors, the diagonal inverses and -A blocks, the A_qk fragments
+            s16x4 vraw[2][NT];
+            f32x4 bt[NT], bg[NT];
+            f16x4 tdf[NT], tef[NT], naf[L::kNA > 0 ? L::kNA : 1];
+            f16x8 aqf[L::kFr];
+            float gam[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-                U[0][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-                U[1][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb <= m / 2; ++kb) {
-                    const f16x8 tf = ld8(fa + L::oT + s * L::kFr * 1024 + fblk(m, kb) * 1024);
-                    U[0][m] = mfma16x16x32(tf, rb[0][kb], U[0][m]);
-                    U[1][m] = mfma16x16x32(tf, rb[1][kb], U[1][m]);
+                if (has_v) {
+                    vraw[0][m] = ld_tr_raw(Vt + va[0] + m * 4096);
+                    vraw[1][m] = ld_tr_raw(Vt + va[1] + m * 4096);
                 }
+                bt[m] = ldf4(gt + 4 * C + 64 * m + 16 * q4);
+                bg[m] = ldf4(gt + 12 * C + 64 * m + 16 * q4);
+                tdf[m] = ld4(td + m * 1024);
+                tef[m] = ld4(td + m * 1024 + 512);
             }
-            // O^T = scale Y^T diag(gamma) + U^T A_qk^T; lane: token 16 m + li, columns r0 + 4 q4 .. + 3
+#pragma unroll
+            for (int e = 0; e < L::kNA; ++e) naf[e] = ld4(na + e * 512);
+            fence();
+            // R = beta V - beta gamma X  (v: tokens 16 m + 4 q4 + r, column r0 + li)
+            f32x4 R[2][NT];
+#pragma unroll
+            for (int m = 0; m < NT; ++m)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+                    if (has_v) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) vv[r] = bf16_bits_to_f32((uint16_t)vraw[bb][m][r]);
+                    }
+                    R[bb][m] = bt[m] * vv - bg[m] * X[bb][m];
+                }
+            if constexpr (OUT) {
+#pragma unroll
+                for (int f = 0; f < L::kFr; ++f) aqf[f] = ld8(aq + f * 1024);
+#pragma unroll
+                for (int m = 0; m < NT; ++m) gam[m] = *reinterpret_cast<const float *>(gt + 4 * (16 * m + li));
+            }
+            fence();
+            // ---- U_m = T_mm (R_m - sum_{j<m} A_mj U_j), the two row blocks interleaved, and the
+            // update's values diag(exp(G_C - G)) U_m from the scaled inverse
+            f16x4 uh[2][NT], ue[2][NT];
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+                f32x4 a0 = R[0][m], a1 = R[1][m];
+#pragma unroll
+                for (int j = 0; j < m; ++j) {
+                    a0 = mfma16x16x16(naf[ablk(m, j)], uh[0][j], a0);
+                    a1 = mfma16x16x16(naf[ablk(m, j)], uh[1][j], a1);
+                }
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f16x4 h0 = to_f16x4(a0), h1 = to_f16x4(a1);
+                uh[0][m] = to_f16x4(mfma16x16x16(tdf[m], h0, z));
+                uh[1][m] = to_f16x4(mfma16x16x16(tdf[m], h1, z));
+                ue[0][m] = to_f16x4(mfma16x16x16(tef[m], h0, z));
+                ue[1][m] = to_f16x4(mfma16x16x16(tef[m], h1, z));
+            }
+            // ---- O^T = scale Y^T diag(gamma) + U^T A_qk^T; lane: token 16 m + li,
+            // columns r0 + 4 q4 .. + 3
             if constexpr (OUT) {
                 f16x8 ua[2][KBC];
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb) {
-                    ua[0][kb] = pack8(U[0][2 * kb], U[0][2 * kb + 1]);
-                    ua[1][kb] = pack8(U[1][2 * kb], U[1][2 * kb + 1]);
+                    ua[0][kb] = cat(uh[0][2 * kb], uh[0][2 * kb + 1]);
+                    ua[1][kb] = cat(uh[1][2 * kb], uh[1][2 * kb + 1]);
                 }
                 const int c = cb + i;
                 const int ntok = min(C, T - c * C);
 #pragma unroll
                 for (int m = 0; m < NT; ++m) {
-                    const float gs = gts[16 * m + li] * p.scale;
+                    const float gs = gam[m] * p.scale;
                     f32x4 O0 = gs * Y[0][m], O1 = gs * Y[1][m];
 #pragma unroll
                     for (int kb = 0; kb <= m / 2; ++kb) {
-                        const f16x8 af = ld8(fa + L::oA + s * L::kFr * 1024 + fblk(m, kb) * 1024);
-                        O0 = mfma16x16x32(ua[0][kb], af, O0);
-                        O1 = mfma16x16x32(ua[1][kb], af, O1);
+                        O0 = mfma16x16x32(ua[0][kb], aqf[fblk(m, kb)], O0);
+                        O1 = mfma16x16x32(ua[1][kb], aqf[fblk(m, kb)], O1);
                     }
                     const int t = 16 * m + li;
                     if (t < ntok) {
@@ -362,34 +432,44 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     }
                 }
             }
-            lds_barrier();  // b2
-            // S <- gamma_C S + K^T (diag(exp(G_C - G)) U)
+            // ---- S <- gamma_C S + K^T (diag(exp(G_C - G)) U), k block by k block of tokens
             f16x8 ub[2][KBC];
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) {
-                const f32x4 e0 = ldf4(ga + s * 16 * C + 8 * C + 64 * (2 * kb));
-                const f32x4 e1 = ldf4(ga + s * 16 * C + 8 * C + 64 * (2 * kb + 1));
-                ub[0][kb] = pack8(e0 * U[0][2 * kb], e1 * U[0][2 * kb + 1]);
-                ub[1][kb] = pack8(e0 * U[1][2 * kb], e1 * U[1][2 * kb + 1]);
+                ub[0][kb] = cat(ue[0][2 * kb], ue[0][2 * kb + 1]);
+                ub[1][kb] = cat(ue[1][2 * kb], ue[1][2 * kb + 1]);
             }
-            const float gC = gts[C - 1];
+            const float gC = *reinterpret_cast<const float *>(gt + 4 * (C - 1));
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) {
                 S[0][jt] *= gC;
                 S[1][jt] *= gC;
+            }
+            f16x8 kt[2][8];
 #pragma unroll
-                for (int kb = 0; kb < KBC; ++kb) {
-                    const f16x8 kt = cat(ld_tr(ta[jt] + s * L::kTile + kb * 8192),
-                                         ld_tr(ta[jt] + s * L::kTile + kb * 8192 + 4096));
-                    S[0][jt] = mfma16x16x32(kt, ub[0][kb], S[0][jt]);
-                    S[1][jt] = mfma16x16x32(kt, ub[1][kb], S[1][jt]);
+            for (int jt = 0; jt < 8; ++jt) kt[0][jt] = cat(ld_tr(Kt + ta[jt]), ld_tr(Kt + ta[jt] + 4096));
+#pragma unroll
+            for (int kb = 0; kb < KBC; ++kb) {
+                const int cur = kb & 1, nxt = cur ^ 1;
+                if (kb + 1 < KBC) {
+#pragma unroll
+                    for (int jt = 0; jt < 8; ++jt)
+                        kt[nxt][jt] = cat(ld_tr(Kt + ta[jt] + (kb + 1) * 8192),
+                                          ld_tr(Kt + ta[jt] + (kb + 1) * 8192 + 4096));
                 }
+                fence();
+#pragma unroll
+                for (int jt = 0; jt < 8; ++jt) {
+                    S[0][jt] = mfma16x16x32(kt[cur][jt], ub[0][kb], S[0][jt]);
+                    S[1][jt] = mfma16x16x32(kt[cur][jt], ub[1][kb], S[1][jt]);
+                }
+                fence();
             }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) sb[bb][kb] = pack8(S[bb][2 * kb], S[bb][2 * kb + 1]);
-            lds_barrier();  // b3
+            lds_barrier();  // b2: chunk i + 1 is prepared
         };
         for (int i = 0; i < n; i += 2) {
             interval(IC<0>{}, i);
@@ -418,34 +498,28 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         }
     } else {
         // ================================================================ prep waves
-        const int m = w - 4;  // token tile of this wave
+        const int m = __builtin_amdgcn_readfirstlane(w - 4);  // token tile of this wave
         const bool tile = m < NT;
-        _Float16 *Ah = reinterpret_cast<_Float16 *>(smem + L::oAh);
-        _Float16 *Tm = reinterpret_cast<_Float16 *>(smem + L::oTm);
-        float *adt = reinterpret_cast<float *>(smem + L::oAd) + (tile ? m : 0) * 16 * DP;
-        float *gtab = reinterpret_cast<float *>(smem + L::oGt) + m * 128;
         const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ktok * kD;
         const uint16_t *qg = static_cast<const uint16_t *>(p.q) + ktok * kD;
         const uint16_t *vg = static_cast<const uint16_t *>(p.v) + vtok * kD;
         const float *gg = p.g + vtok;
         const float *bgp = p.beta + vtok;
 
-        // the upper blocks inside written T fragments ((0,1), (2,3)) stay zero
-        if (m == 0) {
-            for (int e = lane; e < 16 * 16; e += 64) {
-                Tm[(e >> 4) * CP + 16 + (e & 15)] = (_Float16)0.0f;
-                if (NT == 4) Tm[(32 + (e >> 4)) * CP + 48 + (e & 15)] = (_Float16)0.0f;
-            }
-        }
-
         // raw rows of tile m of one chunk: lane l holds token 16 m + l / 4; k and q columns
         // 32 kb + 8 j + 0..7 and 32 kb + 16 + 8 j + 0..7 (kb = l % 4, j = 0, 1); v columns
-        // 32 (l % 4) + 0..31; g and beta of token l (all C tokens of the chunk)
+        // 32 (l % 4) + 0..31. g and beta of the chunk's 64 token slots go straight into the LDS
+        // ring (wave 4, issued before its row loads: waiting for those covers them too), so no
+        // register holds a value still in flight across the loop.
         u16x8 kr[4], qr[4], vr[4];
-        float graw = 0.f, braw = 0.f;
         const int lt = lane >> 2, lkb = lane & 3;
-        auto issue = [&](int c) __attribute__((always_inline)) {  // chunk c (absolute), loads into the registers above
+        auto issue = [&](int c, int sl) __attribute__((always_inline)) {  // chunk c (absolute) into ring slot sl
             const int t0 = c * C;
+            if (m == 0) {
+                const int tg = min(t0 + lane, T - 1);
+                dma4(gg + tg, smem + L::oRG + sl * 512);
+                dma4(bgp + tg, smem + L::oRG + sl * 512 + 256);
+            }
             const int tt = min(t0 + 16 * m + lt, T - 1);
             if (tile) {
 #pragma unroll
@@ -463,14 +537,13 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                         vr[j] = *reinterpret_cast<const u16x8 *>(vg + (int64_t)tt * kD + 32 * lkb + 8 * j);
                 }
             }
-            const int tg = min(t0 + lane, T - 1);
-            graw = gg[tg];
-            braw = bgp[tg];
         };
-        // P1: chunk c into slot s (waits for its loads)
+        // P1: tile m's rows of chunk c into slot s (waits for their loads); wave 4 also forms the
+        // gate vectors of the chunk
         auto phase1 = [&](int c, int s) __attribute__((always_inline)) {
             const int t0 = c * C;
-            const bool live = t0 + 16 * m + lt < T;
+            // rows past the end of the sequence hold the last token's values (the loads are clamped):
+            // finite, and with beta = g = 0 on those tokens they contribute nothing
             if (tile) {
                 const int t = 16 * m + lt;
                 unsigned char *krow = smem + L::oK + s * L::kTile + t * 256;
@@ -480,93 +553,104 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const u16x8 a = kr[2 * j], bq = kr[2 * j + 1];
-                    f16x8 g0 = cat(bf4_to_h4(a[0], a[1], a[2], a[3]), bf4_to_h4(bq[0], bq[1], bq[2], bq[3]));
-                    f16x8 g1 = cat(bf4_to_h4(a[4], a[5], a[6], a[7]), bf4_to_h4(bq[4], bq[5], bq[6], bq[7]));
-                    if (!live) g0 = g1 = f16x8{};
+                    const f16x8 g0 = cat(bf4_to_h4(a[0], a[1], a[2], a[3]), bf4_to_h4(bq[0], bq[1], bq[2], bq[3]));
+                    const f16x8 g1 = cat(bf4_to_h4(a[4], a[5], a[6], a[7]), bf4_to_h4(bq[4], bq[5], bq[6], bq[7]));
                     *reinterpret_cast<f16x8 *>(krow + (((4 * lkb + 2 * j) ^ sw) << 4)) = g0;
                     *reinterpret_cast<f16x8 *>(krow + (((4 * lkb + 2 * j + 1) ^ sw) << 4)) = g1;
                     if (OUT) {
                         const u16x8 qa = qr[2 * j], qb = qr[2 * j + 1];
-                        f16x8 h0 = cat(bf4_to_h4(qa[0], qa[1], qa[2], qa[3]), bf4_to_h4(qb[0], qb[1], qb[2], qb[3]));
-                        f16x8 h1 = cat(bf4_to_h4(qa[4], qa[5], qa[6], qa[7]), bf4_to_h4(qb[4], qb[5], qb[6], qb[7]));
-                        if (!live) h0 = h1 = f16x8{};
+                        const f16x8 h0 = cat(bf4_to_h4(qa[0], qa[1], qa[2], qa[3]), bf4_to_h4(qb[0], qb[1], qb[2], qb[3]));
+                        const f16x8 h1 = cat(bf4_to_h4(qa[4], qa[5], qa[6], qa[7]), bf4_to_h4(qb[4], qb[5], qb[6], qb[7]));
                         *reinterpret_cast<f16x8 *>(qrow + (((4 * lkb + 2 * j) ^ sw) << 4)) = h0;
                         *reinterpret_cast<f16x8 *>(qrow + (((4 * lkb + 2 * j + 1) ^ sw) << 4)) = h1;
                     }
                 }
                 if (has_v) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        u16x8 x = vr[j];
-                        if (!live) x = u16x8{};
-                        *reinterpret_cast<u16x8 *>(vrow + (((4 * lkb + j) ^ sw) << 4)) = x;
-                    }
+                    for (int j = 0; j < 4; ++j) *reinterpret_cast<u16x8 *>(vrow + (((4 * lkb + j) ^ sw) << 4)) = vr[j];
+                }
+            }
+            if (m == 0) {
+                // G = inclusive prefix sum of g over the chunk; tokens past the end have g = beta = 0
+                const float *rg = reinterpret_cast<const float *>(smem + L::oRG + s * 512);
+                const bool gl = lane < C && t0 + lane < T;
+                const float gv = gl ? rg[lane] : 0.f, bv = gl ? rg[64 + lane] : 0.f;
+                float G = gv;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const float y = __shfl_up(G, o, 64);
+                    if (lane >= o) G += y;
+                }
+                const float gC = __shfl(G, C - 1, 64);
+                if (lane < C) {
+                    float *gts = reinterpret_cast<float *>(smem + L::oG + s * 20 * C);
+                    const float gam = __expf(G);
+                    gts[lane] = gam;
+                    gts[C + lane] = bv;
+                    gts[2 * C + lane] = __expf(gC - G);
+                    gts[3 * C + lane] = bv * gam;
+                    gts[4 * C + lane] = G;
                 }
             }
         };
-        // P2: gates, K K^T and Q K^T of tile m, A, A_qk, the diagonal block of T (chunk c, slot s)
-        auto phase2 = [&](int c, int s, float graw_c, float braw_c) __attribute__((always_inline)) {
-            const int t0 = c * C;
-            const bool gl = lane < C && t0 + lane < T;
-            const float gv = gl ? graw_c : 0.f, bv = gl ? braw_c : 0.f;
-            float G = gv;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float y = __shfl_up(G, o, 64);
-                if (lane >= o) G += y;
-            }
+        // P2: K K^T and Q K^T of tile m against tiles nt <= m, the gated blocks of A (negated,
+        // below the diagonal) and A_qk, and the inverse of the diagonal block (chunk in slot s)
+        auto phase2 = [&](int s) __attribute__((always_inline)) {
             if (!tile) return;
-            gtab[lane] = G;
-            gtab[64 + lane] = bv;
-            if (m == 0 && lane < C) {
-                const float gC = __shfl(G, C - 1, 64);
-                float *gts = reinterpret_cast<float *>(smem + L::oG + s * 16 * C);
-                const float gam = __expf(G);
-                gts[lane] = gam;
-                gts[C + lane] = bv;
-                gts[2 * C + lane] = __expf(gC - G);
-                gts[3 * C + lane] = bv * gam;
-            }
-            // raw products, lane (q4, li): t = 16 m + li, s = 16 nt + 4 q4 + r
             const unsigned char *Kt = smem + L::oK + s * L::kTile;
             const unsigned char *Qt = smem + L::oQ + s * L::kTile;
-            f32x4 rk[NT], rq[NT];
-            f16x8 bk[4], bq[4];
+            const float *gts = reinterpret_cast<const float *>(smem + L::oG + s * 20 * C);
+            // every fragment first: lane (q4, li) reads row 16 nt + li, group 4 kb + q4
+            f16x8 ka[NT][4], bk[4], bq[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                bk[kb] = ld8(Kt + (16 * m + li) * 256 + (((4 * kb + q4) ^ ksw(li)) << 4));
-                if (OUT) bq[kb] = ld8(Qt + (16 * m + li) * 256 + (((4 * kb + q4) ^ ksw(li)) << 4));
-            }
+                const int off = li * 256 + (((4 * kb + q4) ^ ksw(li)) << 4);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                rk[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                rq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (nt <= m) {
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) {
-                        const f16x8 a = ld8(Kt + (16 * nt + li) * 256 + (((4 * kb + q4) ^ ksw(li)) << 4));
-                        rk[nt] = mfma16x16x32(a, bk[kb], rk[nt]);
-                        if (OUT) rq[nt] = mfma16x16x32(a, bq[kb], rq[nt]);
-                    }
-                }
+                for (int nt = 0; nt < NT; ++nt)
+                    if (nt <= m) ka[nt][kb] = ld8(Kt + off + nt * 4096);
+                bk[kb] = ld8(Kt + off + m * 4096);
+                if (OUT) bq[kb] = ld8(Qt + off + m * 4096);
             }
             const int t = 16 * m + li;
-            const float Gt = gtab[t], bt = gtab[64 + t];
-            f32x4 a[NT], aq[NT];
+            const float Gt = gts[4 * C + t], btt = gts[C + t];
+            f32x4 Gs[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                if (nt <= m) Gs[nt] = *reinterpret_cast<const f32x4 *>(gts + 4 * C + 16 * nt + 4 * q4);
+            fence();
+            // raw products, lane (q4, li): t = 16 m + li, s = 16 nt + 4 q4 + r
+            f32x4 rk[NT], rq[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) rk[nt] = rq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    if (nt <= m) {
+                        rk[nt] = mfma16x16x32(ka[nt][kb], bk[kb], rk[nt]);
+                        if (OUT) rq[nt] = mfma16x16x32(ka[nt][kb], bq[kb], rq[nt]);
+                    }
+            // gating; only the diagonal tile needs the triangular mask
+            f32x4 a[NT], aqv[NT];
+            const float sct = p.scale;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                a[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                aq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (nt <= m) {
-                    const f32x4 Gs = *reinterpret_cast<const f32x4 *>(gtab + 16 * nt + 4 * q4);
+                a[nt] = aqv[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (nt < m) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int sidx = 16 * nt + 4 * q4 + r;
-                        const float gate = __expf(Gt - Gs[r]);
-                        a[nt][r] = sidx < t ? bt * gate * rk[nt][r] : 0.0f;
-                        if (OUT) aq[nt][r] = sidx <= t ? p.scale * gate * rq[nt][r] : 0.0f;
+                        const float gate = __expf(Gt - Gs[nt][r]);
+                        a[nt][r] = btt * gate * rk[nt][r];
+                        if (OUT) aqv[nt][r] = sct * gate * rq[nt][r];
                     }
-                    if (nt < m) *reinterpret_cast<f16x4 *>(Ah + t * CP + 16 * nt + 4 * q4) = to_f16x4(a[nt]);
+                } else if (nt == m) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int sidx = 4 * q4 + r;
+                        const float gate = __expf(Gt - Gs[nt][r]);
+                        a[nt][r] = sidx < li ? btt * gate * rk[nt][r] : 0.0f;
+                        if (OUT) aqv[nt][r] = sidx <= li ? sct * gate * rq[nt][r] : 0.0f;
+                    }
                 }
             }
             if (OUT) {
@@ -574,162 +658,101 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 for (int kb = 0; kb < KBC; ++kb)
                     if (2 * kb <= m)
                         *reinterpret_cast<f16x8 *>(smem + L::oA + s * L::kFr * 1024 + fblk(m, kb) * 1024 + lane * 16) =
-                            cat(to_f16x4(aq[2 * kb]), to_f16x4(aq[2 * kb + 1]));
+                            cat(to_f16x4(aqv[2 * kb]), to_f16x4(aqv[2 * kb + 1]));
             }
-            // diagonal block T_mm = (I + A_mm)^{-1}: lane li computes column li by forward
-            // substitution in fp32; A_mm goes through LDS transposed, adt[s][i] = A[i][s]
-            {
-                f32x4 dm = a[0];
+            // -A_mj below the diagonal (A operands of the block substitution)
 #pragma unroll
-                for (int nt = 1; nt < NT; ++nt)
-                    if (nt == m) dm = a[nt];
+            for (int j = 0; j < NT; ++j)
+                if (j < m)
+                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(m, j) * 512 + lane * 8) =
+                        to_f16x4(-a[j]);
+            // T_mm = (I + A_mm)^{-1}: lane (q4, li) builds T[li][4 q4 + e]. Its row of A_mm goes
+            // through this wave's LDS scratch (written as accumulators, read back by rows).
+            f32x4 dm = a[0];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) adt[(4 * q4 + r) * DP + li] = dm[r];
-                float x[16];
+            for (int nt = 1; nt < NT; ++nt)
+                if (nt == m) dm = a[nt];
+            float *at = reinterpret_cast<float *>(smem + L::oAt) + m * 16 * 20;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = r == li ? 1.0f : 0.0f;
+            for (int r = 0; r < 4; ++r) at[(4 * q4 + r) * 20 + li] = -dm[r];  // at[s][i] = -A[i][s]
+            float nrow[16];
 #pragma unroll
-                for (int s2 = 0; s2 < 15; ++s2) {
-                    float col[16];
+            for (int k = 0; k < 16; ++k) nrow[k] = at[k * 20 + li];
+            f32x4 tq;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const f32x4 c4 = *reinterpret_cast<const f32x4 *>(adt + s2 * DP + 4 * v);
-                        col[4 * v] = c4[0];
-                        col[4 * v + 1] = c4[1];
-                        col[4 * v + 2] = c4[2];
-                        col[4 * v + 3] = c4[3];
-                    }
-#pragma unroll
-                    for (int r = s2 + 1; r < 16; ++r) x[r] -= col[r] * x[s2];
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = q4 == 0 ? x[r] : q4 == 1 ? x[4 + r] : q4 == 2 ? x[8 + r] : x[12 + r];
-                    Tm[(16 * m + 4 * q4 + r) * CP + 16 * m + li] = (_Float16)v;
-                }
-            }
-        };
-        // P3 (wave 4): off-diagonal blocks of T by MFMA doubling, then the T fragments into slot s
-        auto phase3 = [&](int s) __attribute__((always_inline)) {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            // level 1: T_ul = -T_uu A_ul T_ll for (l, u) = (0, 1) and (2, 3)
-#pragma unroll
-            for (int pr = 0; pr < NT / 2; ++pr) {
-                const int lo = 2 * pr, up = 2 * pr + 1;
-                f16x4 btl;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) btl[e] = Tm[(16 * lo + 4 * q4 + e) * CP + 16 * lo + li];
-                const f32x4 pm = mfma16x16x16(ld4h(Ah + (16 * up + li) * CP + 16 * lo + 4 * q4), btl, z);
-                const f32x4 out = mfma16x16x16(ld4h(Tm + (16 * up + li) * CP + 16 * up + 4 * q4), to_f16x4(-pm), z);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Tm[(16 * up + 4 * q4 + r) * CP + 16 * lo + li] = (_Float16)out[r];
-            }
-            if constexpr (NT == 4) {
-                // level 2: T[32:64, 0:32] = -T[32:64, 32:64] A[32:64, 0:32] T[0:32, 0:32], column block jc
-#pragma unroll
-                for (int jc = 0; jc < 2; ++jc) {
-                    f16x4 t0j, t1j;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        t0j[e] = Tm[(4 * q4 + e) * CP + 16 * jc + li];
-                        t1j[e] = Tm[(16 + 4 * q4 + e) * CP + 16 * jc + li];
-                    }
-                    f32x4 p0 = mfma16x16x16(ld4h(Ah + (32 + li) * CP + 16 + 4 * q4), t1j, z);
-                    f32x4 p1 = mfma16x16x16(ld4h(Ah + (48 + li) * CP + 16 + 4 * q4), t1j, z);
-                    if (jc == 0) {
-                        p0 = mfma16x16x16(ld4h(Ah + (32 + li) * CP + 4 * q4), t0j, p0);
-                        p1 = mfma16x16x16(ld4h(Ah + (48 + li) * CP + 4 * q4), t0j, p1);
-                    }
-                    const f16x4 b0 = to_f16x4(-p0), b1 = to_f16x4(-p1);
-                    const f32x4 o0 = mfma16x16x16(ld4h(Tm + (32 + li) * CP + 32 + 4 * q4), b0, z);
-                    f32x4 o1 = mfma16x16x16(ld4h(Tm + (48 + li) * CP + 32 + 4 * q4), b0, z);
-                    o1 = mfma16x16x16(ld4h(Tm + (48 + li) * CP + 48 + 4 * q4), b1, o1);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        Tm[(32 + 4 * q4 + r) * CP + 16 * jc + li] = (_Float16)o0[r];
-                        Tm[(48 + 4 * q4 + r) * CP + 16 * jc + li] = (_Float16)o1[r];
-                    }
-                }
-            }
-            // T fragments: tile mm, k block kb: lane (q4, li) holds row 16 mm + li at columns
-            // frag_col(kb, q4, 0..7)
-#pragma unroll
-            for (int mm = 0; mm < NT; ++mm)
-#pragma unroll
-                for (int kb = 0; kb <= mm / 2; ++kb) {
-                    const _Float16 *src = Tm + (16 * mm + li) * CP + 32 * kb + 4 * q4;
-                    *reinterpret_cast<f16x8 *>(smem + L::oT + s * L::kFr * 1024 + fblk(mm, kb) * 1024 + lane * 16) =
-                        cat(ld4h(src), ld4h(src + 16));
-                }
+            for (int e = 0; e < 4; ++e) tq[e] = 4 * q4 + e == li ? 1.0f : 0.0f;
+            inv_rows<0>(tq, nrow);
+            // T_mm and diag(exp(G_C - G)) T_mm (row li scaled): the latter gives the scaled values
+            // of the state update straight from the substitution
+            const float egt = gts[2 * C + t];
+            unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + m * 1024 + lane * 8;
+            *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
+            *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(egt * tq);
         };
 
-        // prologue: chunk 0 of the segment into slot 0
-        float g0 = 0.f, b0 = 0.f;
-        if (n > 0) {
-            issue(cb);
-            phase1(cb, 0);
-            g0 = graw;
-            b0 = braw;
-            if (n > 1) issue(cb + 1);
-        }
+        // prologue: chunk 0 of the segment into slot 0. Every load is issued, the chunk index
+        // clamped to the segment, so that the loop carries no register whose load is optional.
+        const int clast = cb + max(n, 1) - 1;
+        issue(cb, 0);
+        if (n > 0) phase1(cb, 0);
+        issue(min(cb + 1, clast), 1);
         lds_barrier();
-        if (n > 0) phase2(cb, 0, g0, b0);
-        lds_barrier();
-        if (n > 0 && m == 0) phase3(0);
+        if (n > 0) phase2(0);
         lds_barrier();
 
         auto interval = [&](auto sl, int i) __attribute__((always_inline)) {
             constexpr int s1 = 1 - decltype(sl)::value;  // slot of chunk i + 1
             const int c1 = cb + i + 1;
-            float g1 = 0.f, b1 = 0.f;
-            if (i + 1 < n) {
-                phase1(c1, s1);
-                g1 = graw;
-                b1 = braw;
-                if (i + 2 < n) issue(c1 + 1);
-            }
+            if (i + 1 < n) phase1(c1, s1);
+            issue(min(c1 + 1, clast), 1 - s1);
             lds_barrier();  // b1
-            if (i + 1 < n) phase2(c1, s1, g1, b1);
+            if (i + 1 < n) phase2(s1);
             lds_barrier();  // b2
-            if (i + 1 < n && m == 0) phase3(s1);
-            lds_barrier();  // b3
         };
         for (int i = 0; i < n; i += 2) {
             interval(IC<0>{}, i);
             if (i + 1 < n) interval(IC<1>{}, i + 1);
         }
+        wait_vmcnt0();  // the last (clamped, unused) g/beta copies write into this workgroup's LDS
     }
 }
 
 // S_{p+1} = S_p M_p + N_p for p = 1 .. P-2, one workgroup per (pair, block of 16 rows), fp32.
-// Thread (r, cg) owns row r of the block, columns 8 cg .. 8 cg + 7; M_p is staged through LDS
-// in halves of 64 rows.
+// Thread (r, cg) owns row r of the block, columns 8 cg .. 8 cg + 7. M_p goes through LDS; the
+// next map is loaded into registers while the current one is applied (only the chain of S is
+// sequential).
 __global__ __launch_bounds__(256) void gdn_seg_combine_kernel(SegParams sp) {
-    __shared__ __attribute__((aligned(16))) float srow[16][kD + 4];
-    __shared__ __attribute__((aligned(16))) float mt[kD / 2][kD];
+    extern __shared__ __attribute__((aligned(16))) unsigned char csmem[];
+    float(*srow)[kD + 4] = reinterpret_cast<float(*)[kD + 4]>(csmem);
+    float(*mt)[kD] = reinterpret_cast<float(*)[kD]>(csmem + 16 * (kD + 4) * 4);
     const int pair = blockIdx.x >> 3, rb = blockIdx.x & 7;
     const int tid = threadIdx.x, r = tid >> 4, cg = tid & 15;
     const int64_t base = (int64_t)pair * sp.P;
     const float *s1 = sp.ws_start + (base + 1) * (kD * kD) + rb * 16 * kD;
     for (int e = tid; e < 16 * kD; e += 256) srow[e / kD][e % kD] = s1[e];
+    constexpr int kPer = kD * kD / 4 / 256;  // f32x4 of a map per thread
+    f32x4 mnext[kPer];
+    auto load_map = [&](int seg) {
+        const f32x4 *M = reinterpret_cast<const f32x4 *>(sp.ws_m + (base + seg) * (kD * kD));
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) mnext[j] = M[tid + 256 * j];
+    };
+    if (sp.P > 2) load_map(1);
     for (int seg = 1; seg + 1 < sp.P; ++seg) {
-        const float *M = sp.ws_m + (base + seg) * (kD * kD);
         const float *N = sp.ws_n + (base + seg) * (kD * kD) + rb * 16 * kD;
         float *Sn = sp.ws_start + (base + seg + 1) * (kD * kD) + rb * 16 * kD;
         f32x4 a0 = *reinterpret_cast<const f32x4 *>(N + r * kD + 8 * cg);
         f32x4 a1 = *reinterpret_cast<const f32x4 *>(N + r * kD + 8 * cg + 4);
-        for (int half = 0; half < 2; ++half) {
-            __syncthreads();  // srow written; earlier reads of mt done
-            for (int e = tid; e < kD * kD / 8; e += 256)
-                reinterpret_cast<f32x4 *>(&mt[0][0])[e] =
-                    reinterpret_cast<const f32x4 *>(M + half * (kD / 2) * kD)[e];
-            __syncthreads();
+        __syncthreads();  // srow written; earlier reads of mt done
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) reinterpret_cast<f32x4 *>(&mt[0][0])[tid + 256 * j] = mnext[j];
+        if (seg + 2 < sp.P) load_map(seg + 1);
+        __syncthreads();
 #pragma unroll 8
-            for (int k = 0; k < kD / 2; ++k) {
-                const float sv = srow[r][half * (kD / 2) + k];
-                a0 += sv * *reinterpret_cast<const f32x4 *>(&mt[k][8 * cg]);
-                a1 += sv * *reinterpret_cast<const f32x4 *>(&mt[k][8 * cg + 4]);
-            }
+        for (int k = 0; k < kD; ++k) {
+            const float sv = srow[r][k];
+            a0 += sv * *reinterpret_cast<const f32x4 *>(&mt[k][8 * cg]);
+            a1 += sv * *reinterpret_cast<const f32x4 *>(&mt[k][8 * cg + 4]);
         }
         *reinterpret_cast<f32x4 *>(Sn + r * kD + 8 * cg) = a0;
         *reinterpret_cast<f32x4 *>(Sn + r * kD + 8 * cg + 4) = a1;
@@ -738,6 +761,7 @@ __global__ __launch_bounds__(256) void gdn_seg_combine_kernel(SegParams sp) {
         *reinterpret_cast<f32x4 *>(&srow[r][8 * cg + 4]) = a1;
     }
 }
+constexpr size_t kCombineLds = 16 * (kD + 4) * 4 + kD * kD * 4;
 
 // T = 0: the final state is the initial state (converted to its storage type), or zero.
 __global__ __launch_bounds__(256) void gdn_state_copy_kernel(PrefillParams p, int64_t count) {
@@ -771,7 +795,14 @@ hipError_t launch_seg_c(const SegParams &sp, hipStream_t stream) {
         err = launch_pass<C, false>(sp, pairs * (2 * sp.P - 3), stream);
         if (err != hipSuccess) return err;
         if (sp.P > 2) {
-            hipLaunchKernelGGL(gdn_seg_combine_kernel, dim3((unsigned)(pairs * 8)), dim3(256), 0, stream, sp);
+            static bool attr_set = false;
+            if (!attr_set) {
+                err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_seg_combine_kernel),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kCombineLds);
+                if (err != hipSuccess) return err;
+                attr_set = true;
+            }
+            hipLaunchKernelGGL(gdn_seg_combine_kernel, dim3((unsigned)(pairs * 8)), dim3(256), kCombineLds, stream, sp);
             err = hipGetLastError();
             if (err != hipSuccess) return err;
         }

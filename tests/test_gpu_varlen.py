@@ -51,14 +51,15 @@ def check_against_padded(gdn, oracle_lib, x, lengths, chunk, label, tol=TOL_BF16
     eo, es = rel_err(got, want), rel_err(sf.cpu().numpy(), s_ref)
     print(f"{label}: rel err o {eo:.3e} state {es:.3e}")
     assert eo <= tol and es <= tol, (label, eo, es)
-    # the GPU's padded batch: the same chunks of real tokens (a sequence's tail chunk is masked
-    # in one and zero-padded in the other), so the same results on the real tokens
+    # the GPU's padded batch on the real tokens: another kernel (the padded prefill sums in its
+    # own order), so agreement to the same tolerance rather than bit for bit
     q, k, v = qkv_dev(x)
     op, sp = gdn.prefill(q, k, v, dev(x.g), dev(x.beta), s0, chunk=chunk, scale=x.scale)
+    torch.cuda.synchronize()
     opn = op.cpu().numpy()
     padded = np.concatenate([opn[i, :, :n] for i, n in enumerate(lengths)], axis=1)
-    assert np.array_equal(got, padded), label
-    assert torch.equal(sf, sp), label
+    assert rel_err(got, padded) <= tol, label
+    assert rel_err(sf.cpu().numpy(), sp.cpu().numpy()) <= tol, label
     return o, sf
 
 
@@ -82,13 +83,16 @@ def test_many_short_sequences(gdn, oracle_lib):
 
 
 def test_single_sequence_matches_prefill(gdn):
-    """One packed sequence is gdn_prefill on that sequence, bit for bit."""
+    """One packed sequence agrees with gdn_prefill on that sequence (another kernel, so to the
+    bfloat16 tolerance rather than bit for bit)."""
     import torch
     x = inputs.generate(1, 300, 2, 4, 128, "bf16", seed=103, init_state="normal")
     o, sf, _ = run_varlen(gdn, x, [300], 64, dev(x.s0))
     q, k, v = qkv_dev(x)
     o2, sf2 = gdn.prefill(q, k, v, dev(x.g), dev(x.beta), dev(x.s0), chunk=64, scale=x.scale)
-    assert torch.equal(o, o2[0]) and torch.equal(sf, sf2)
+    torch.cuda.synchronize()
+    assert rel_err(o.cpu().numpy(), o2[0].cpu().numpy()) <= TOL_BF16
+    assert rel_err(sf.cpu().numpy(), sf2.cpu().numpy()) <= TOL_BF16
 
 
 def test_varlen_f16_states_in_place(gdn):
