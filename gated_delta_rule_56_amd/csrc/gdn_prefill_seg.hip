@@ -63,7 +63,6 @@ constexpr int kD = 128;
 constexpr int kSegThreads = 512;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 // fragment block of token tile m, k block kb (kb <= m / 2), counted over the blocks on or
 // below the diagonal: (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
@@ -84,11 +83,10 @@ struct SegSmem {
     static constexpr size_t oNA = oA + (OUT ? 2 * kFr * 1024 : 0);  // [2][kNA][64] x 8 B: -A blocks
     static constexpr size_t oTd = oNA + 2 * kNA * 512;           // [2][NT][2][64] x 8 B: T_mm, diag(exp(G_C-G)) T_mm
     static constexpr size_t oG = oTd + 2 * NT * 1024;             // [2][5][C] f32: gamma, beta, exp(G_C-G), beta gamma, G
-    static constexpr size_t oRG = oG + 2 * 20 * C;               // f32 [2][2][64]: raw g and beta of a chunk
-    static constexpr size_t oAt = oRG + 2 * 2 * 64 * 4;          // f32 [NT][16][20]: diagonal blocks of A, transposed
+    static constexpr size_t oAt = oG + 2 * 20 * C;               // f32 [NT][16][20]: diagonal blocks of A, transposed
     static constexpr size_t kBytes = oAt + NT * 16 * 20 * 4;
     static_assert(oQ % 16 == 0 && oV % 16 == 0 && oA % 16 == 0 && oNA % 16 == 0 && oTd % 16 == 0 &&
-                      oG % 16 == 0 && oRG % 16 == 0 && oAt % 16 == 0,
+                      oG % 16 == 0 && oAt % 16 == 0,
                   "alignment");
     static_assert(kBytes <= 160 * 1024, "LDS");
 };
@@ -109,13 +107,6 @@ __device__ __forceinline__ s16x4 ld_tr_raw(const unsigned char *p) {
 }
 __device__ __forceinline__ f16x4 ld_tr(const unsigned char *p) { return __builtin_bit_cast(f16x4, ld_tr_raw(p)); }
 
-// 4 bytes per lane from global memory straight into LDS (lane l at lds + 4 l)
-__device__ __forceinline__ void dma4(const void *g, unsigned char *lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Workgroup barrier for LDS traffic only: outstanding global loads stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -130,6 +121,26 @@ using IC = std::integral_constant<int, N>;
 __device__ __forceinline__ f16x4 bf4_to_h4(uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
     return f16x4{(_Float16)bf16_bits_to_f32(a), (_Float16)bf16_bits_to_f32(b), (_Float16)bf16_bits_to_f32(c),
                  (_Float16)bf16_bits_to_f32(d)};
+}
+
+// DPP-modified copy of x (ctrl: the DPP control; rows outside row_mask, and with bound_ctrl
+// lanes whose source is out of range, read 0)
+template <int ctrl, int row_mask, bool bound_ctrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, row_mask, 0xF, bound_ctrl));
+}
+
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each row of 16 lanes, then
+// the last lane of row 0 (2) broadcast into row 1 (3), then lane 31 into rows 2 and 3
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_f<0x111, 0xF, true>(x);   // row_shr:1
+    x += dpp_f<0x112, 0xF, true>(x);   // row_shr:2
+    x += dpp_f<0x114, 0xF, true>(x);   // row_shr:4
+    x += dpp_f<0x118, 0xF, true>(x);   // row_shr:8
+    x += dpp_f<0x142, 0xA, false>(x);  // row_bcast:15
+    x += dpp_f<0x143, 0xC, false>(x);  // row_bcast:31
+    return x;
 }
 
 // T = (I + A)^{-1} for a strictly lower 16 x 16 A, by forward substitution over the rows,
@@ -562,82 +573,48 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         const float *gg = p.g + vtok;
         const float *bgp = p.beta + vtok;
 
-        // raw rows of tile m of one chunk: lane l holds token 16 m + l / 4; k and q columns
-        // 32 kb + 8 j + 0..7 and 32 kb + 16 + 8 j + 0..7 (kb = l % 4, j = 0, 1); v columns
-        // 32 (l % 4) + 0..31. g and beta of the chunk's 64 token slots go straight into the LDS
-        // ring (wave 4, issued before its row loads: waiting for those covers them too), so no
-        // register holds a value still in flight across the loop.
+        // raw rows of tile m of one chunk: register j of lane l holds columns 8 (l % 16) + 0..7 of
+        // token 16 m + 4 j + l / 16 (of k, q and v), so that each load instruction reads four whole
+        // rows, 1 KB in eight 128-byte lines; wave 4 also holds g and beta of the chunk's token
+        // slots (lane = slot; one pair per ring slot). Each tensor's values of the next chunk are
+        // requested as soon as those of this chunk have been used (g and beta at the start of
+        // P1), about one interval ahead of their use.
         u16x8 kr[4], qr[4], vr[4];
-        const int lt = lane >> 2, lkb = lane & 3;
-        auto issue = [&](int c, int sl) __attribute__((always_inline)) {  // chunk c (absolute) into ring slot sl
-            const int t0 = c * C;
-            if (m == 0) {
-                const int tg = min(t0 + lane, T - 1);
-                dma4(gg + tg, smem + L::oRG + sl * 512);
-                dma4(bgp + tg, smem + L::oRG + sl * 512 + 256);
-            }
-            const int tt = min(t0 + 16 * m + lt, T - 1);
+        float gr[2] = {0.f, 0.f}, br[2] = {0.f, 0.f};
+        const int lrow = lane >> 4, lp = lane & 15;
+        // requests of chunk c (absolute): g and beta, the rows of one tensor
+        auto request_gb = [&](int c, auto slc) __attribute__((always_inline)) {
+            constexpr int sl = decltype(slc)::value;
+            // every prep wave loads them (only wave 4 uses them): unconditional loads keep the
+            // wait counts before their use exact
+            const int tg = min(c * C + lane, T - 1);
+            gr[sl] = gg[tg];
+            br[sl] = bgp[tg];
+        };
+        auto request_rows = [&](u16x8 (&r)[4], const uint16_t *src, int c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                r[j] = *reinterpret_cast<const u16x8 *>(src + (int64_t)min(c * C + 16 * m + 4 * j + lrow, T - 1) * kD + 8 * lp);
+        };
+        auto issue = [&](int c) __attribute__((always_inline)) {  // all of chunk c, into slot 0
+            request_gb(c, IC<0>{});
             if (tile) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    kr[2 * j] = *reinterpret_cast<const u16x8 *>(kg + (int64_t)tt * kD + 32 * lkb + 8 * j);
-                    kr[2 * j + 1] = *reinterpret_cast<const u16x8 *>(kg + (int64_t)tt * kD + 32 * lkb + 16 + 8 * j);
-                    if (OUT) {
-                        qr[2 * j] = *reinterpret_cast<const u16x8 *>(qg + (int64_t)tt * kD + 32 * lkb + 8 * j);
-                        qr[2 * j + 1] = *reinterpret_cast<const u16x8 *>(qg + (int64_t)tt * kD + 32 * lkb + 16 + 8 * j);
-                    }
-                }
-                if (has_v) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        vr[j] = *reinterpret_cast<const u16x8 *>(vg + (int64_t)tt * kD + 32 * lkb + 8 * j);
-                }
+                request_rows(kr, kg, c);
+                if (OUT) request_rows(qr, qg, c);
+                if (has_v) request_rows(vr, vg, c);
             }
         };
-        // P1: tile m's rows of chunk c into slot s (waits for their loads); wave 4 also forms the
-        // gate vectors of the chunk
-        auto phase1 = [&](int c, int s) __attribute__((always_inline)) {
+        // P1: wave 4 forms the gate vectors of chunk c; tile m's rows of chunk c into slot s (waits
+        // for their loads), each tensor's rows of chunk cn requested right after
+        auto phase1 = [&](int c, int cn, auto sc) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc)::value;
             const int t0 = c * C;
-            // rows past the end of the sequence hold the last token's values (the loads are clamped):
-            // finite, and with beta = g = 0 on those tokens they contribute nothing
-            if (tile) {
-                const int t = 16 * m + lt;
-                unsigned char *krow = smem + L::oK + s * L::kTile + t * 256;
-                unsigned char *qrow = smem + L::oQ + s * L::kTile + t * 256;
-                unsigned char *vrow = smem + L::oV + s * L::kTile + t * 256;
-                const int sw = ksw(t & 15);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const u16x8 a = kr[2 * j], bq = kr[2 * j + 1];
-                    const f16x8 g0 = cat(bf4_to_h4(a[0], a[1], a[2], a[3]), bf4_to_h4(bq[0], bq[1], bq[2], bq[3]));
-                    const f16x8 g1 = cat(bf4_to_h4(a[4], a[5], a[6], a[7]), bf4_to_h4(bq[4], bq[5], bq[6], bq[7]));
-                    *reinterpret_cast<f16x8 *>(krow + (((4 * lkb + 2 * j) ^ sw) << 4)) = g0;
-                    *reinterpret_cast<f16x8 *>(krow + (((4 * lkb + 2 * j + 1) ^ sw) << 4)) = g1;
-                    if (OUT) {
-                        const u16x8 qa = qr[2 * j], qb = qr[2 * j + 1];
-                        const f16x8 h0 = cat(bf4_to_h4(qa[0], qa[1], qa[2], qa[3]), bf4_to_h4(qb[0], qb[1], qb[2], qb[3]));
-                        const f16x8 h1 = cat(bf4_to_h4(qa[4], qa[5], qa[6], qa[7]), bf4_to_h4(qb[4], qb[5], qb[6], qb[7]));
-                        *reinterpret_cast<f16x8 *>(qrow + (((4 * lkb + 2 * j) ^ sw) << 4)) = h0;
-                        *reinterpret_cast<f16x8 *>(qrow + (((4 * lkb + 2 * j + 1) ^ sw) << 4)) = h1;
-                    }
-                }
-                if (has_v) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) *reinterpret_cast<u16x8 *>(vrow + (((4 * lkb + j) ^ sw) << 4)) = vr[j];
-                }
-            }
             if (m == 0) {
                 // G = inclusive prefix sum of g over the chunk; tokens past the end have g = beta = 0
-                const float *rg = reinterpret_cast<const float *>(smem + L::oRG + s * 512);
                 const bool gl = lane < C && t0 + lane < T;
-                const float gv = gl ? rg[lane] : 0.f, bv = gl ? rg[64 + lane] : 0.f;
-                float G = gv;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const float y = __shfl_up(G, o, 64);
-                    if (lane >= o) G += y;
-                }
-                const float gC = __shfl(G, C - 1, 64);
+                const float gv = gl ? gr[s] : 0.f, bv = gl ? br[s] : 0.f;
+                const float G = wave_prefix_sum(gv);
+                const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), C - 1));
                 if (lane < C) {
                     float *gts = reinterpret_cast<float *>(smem + L::oG + s * 20 * C);
                     const float gam = __expf(G);
@@ -646,6 +623,52 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     gts[2 * C + lane] = __expf(gC - G);
                     gts[3 * C + lane] = bv * gam;
                     gts[4 * C + lane] = G;
+                }
+            }
+            request_gb(cn, IC<1 - s>{});  // after the scan: its wait then covers only older requests
+            fence();
+            // rows past the end of the sequence hold the last token's values (the loads are clamped):
+            // finite, and with beta = g = 0 on those tokens they contribute nothing
+            if (tile) {
+                // the fp16 tile's 16-byte group 4 Q + g of a row holds columns 32 Q + 4 g + 0..3 and
+                // 32 Q + 16 + 4 g + 0..3: columns 8 p + 0..3 of this lane go to group
+                // 4 (p / 4) + 2 (p % 2), 8 p + 4..7 to the next group, both at byte 8 ((p / 2) % 2)
+                const int g0 = 4 * (lp >> 2) + 2 * (lp & 1), hb = 8 * ((lp >> 1) & 1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 16 * m + 4 * j + lrow;
+                    const int sw = ksw(t & 15);
+                    unsigned char *krow = smem + L::oK + s * L::kTile + t * 256;
+                    const u16x8 a = kr[j];
+                    *reinterpret_cast<f16x4 *>(krow + (((g0 ^ sw) << 4) + hb)) = bf4_to_h4(a[0], a[1], a[2], a[3]);
+                    *reinterpret_cast<f16x4 *>(krow + ((((g0 + 1) ^ sw) << 4) + hb)) = bf4_to_h4(a[4], a[5], a[6], a[7]);
+                }
+                fence();
+                request_rows(kr, kg, cn);
+                fence();
+                if (OUT) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 16 * m + 4 * j + lrow;
+                        const int sw = ksw(t & 15);
+                        unsigned char *qrow = smem + L::oQ + s * L::kTile + t * 256;
+                        const u16x8 b = qr[j];
+                        *reinterpret_cast<f16x4 *>(qrow + (((g0 ^ sw) << 4) + hb)) = bf4_to_h4(b[0], b[1], b[2], b[3]);
+                        *reinterpret_cast<f16x4 *>(qrow + ((((g0 + 1) ^ sw) << 4) + hb)) = bf4_to_h4(b[4], b[5], b[6], b[7]);
+                    }
+                    fence();
+                    request_rows(qr, qg, cn);
+                    fence();
+                }
+                if (has_v) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 16 * m + 4 * j + lrow;
+                        *reinterpret_cast<u16x8 *>(smem + L::oV + s * L::kTile + t * 256 + ((lp ^ ksw(t & 15)) << 4)) = vr[j];
+                    }
+                    fence();
+                    request_rows(vr, vg, cn);
+                    fence();
                 }
             }
         };
@@ -746,12 +769,12 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(egt * tq);
         };
 
-        // prologue: chunk 0 of the segment into slot 0. Every load is issued, the chunk index
-        // clamped to the segment, so that the loop carries no register whose load is optional.
+        // prologue: chunk 0 of the segment into slot 0. Every load is issued and every P1 runs, the
+        // chunk indices clamped to the segment (a clamped P1 fills the slot no one reads next),
+        // so that the loop carries no register whose load is optional.
         const int clast = cb + max(n, 1) - 1;
-        issue(cb, 0);
-        if (n > 0) phase1(cb, 0);
-        issue(min(cb + 1, clast), 1);
+        issue(cb);
+        phase1(cb, min(cb + 1, clast), IC<0>{});
         lds_barrier();
         if (n > 0) phase2(0);
         lds_barrier();
@@ -759,8 +782,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         auto interval = [&](auto sl, int i) __attribute__((always_inline)) {
             constexpr int s1 = 1 - decltype(sl)::value;  // slot of chunk i + 1
             const int c1 = cb + i + 1;
-            if (i + 1 < n) phase1(c1, s1);
-            issue(min(c1 + 1, clast), 1 - s1);
+            phase1(min(c1, clast), min(c1 + 1, clast), IC<s1>{});
             lds_barrier();  // b1
             if (i + 1 < n) phase2(s1);
             lds_barrier();  // b2
@@ -769,7 +791,6 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             interval(IC<0>{}, i);
             if (i + 1 < n) interval(IC<1>{}, i + 1);
         }
-        wait_vmcnt0();  // the last (clamped, unused) g/beta copies write into this workgroup's LDS
     }
 }
 
