@@ -60,8 +60,10 @@ def decode_bytes(B, Hk, Hv, d, qkv_bytes=2, state_bytes=4) -> int:
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "prefill_long32k_decode_b256_hbm_traffic.md")
+# the sources of the benchmarked prefill path: the segmented kernels and the C ABI that picks the
+# segment count (the committed counter summaries are only used while these are unchanged)
 PREFILL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_56_amd", "csrc", f)
-                   for f in ("gdn_prefill_chunk.hip", "gdn_prefill_scan.hip", "gdn_frag.h", "gdn_device.h")]
+                   for f in ("gdn_prefill_seg.hip", "gdn_frag.h", "gdn_device.h", "gdn_internal.h", "gdn_abi.cpp")]
 
 
 MFMA_PROFILE = os.path.join(ROOT, "profiles", "prefill_long32k_mfma_counters.md")
@@ -346,6 +348,9 @@ def main():
     d_gbps = d_bytes / (d_avg * 1e-3) / 1e9
     p_tflops = flops / (p_avg * 1e-3) / 1e12
     counted_flops = measured_prefill_mfma_flops()  # rocprofv3 MFMA op counters, when current
+    segments = binding.prefill_segments(B, T, Hk, Hv, d, binding.prefill_workspace_bytes(B, T, Hk, Hv, d, chunk=pw.chunk),
+                                        chunk=pw.chunk)
+    map_wgs = B * Hv * (2 * segments - 3) if segments > 1 else 0
 
     result = {
         "metric": "GDN prefill tokens/s (Hv=32,d=128,T=32k) + MFMA util; decode HBM GB/s",
@@ -364,30 +369,31 @@ def main():
             "workload": f"{PREFILL_WL} prefill (B={B}, Hk={Hk}, Hv={Hv}, T={T}, d={d}, chunk={pw.chunk}) + "
                         f"{DECODE_WL} step (B={dB}, Hk={dHk}, Hv={dHv}, d={dd}, fp32 state in place)",
             "prefill": {"batch": B, "seq_len": T, "num_k_heads": Hk, "num_v_heads": Hv, "head_dim": d,
-                        "chunk": pw.chunk, "qkv_dtype": "bf16", "o_dtype": "f32"},
+                        "chunk": pw.chunk, "qkv_dtype": "bf16", "o_dtype": "f32", "segments": segments},
             "decode": {"batch": dB, "num_k_heads": dHk, "num_v_heads": dHv, "head_dim": dd,
                        "state_bytes": dB * dHv * dd * dd * 4},
         },
         "roofline": {
-            "kernel": "gdn_prefill call: gdn_chunk_prep_kernel<64> + gdn_prefill_scan_kernel<64>",
-            "bound": "hbm",
-            "achieved": p_gbps,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": p_gbps / HBM_PEAK_GBPS,
-            "traffic": measured_prefill_traffic(),
-            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_bytes_per_launch": p_bytes,
-            "avg_launch_ms": p_avg,
-        },
-        "mfma": {
+            "kernel": (f"gdn_prefill call, {segments} segments: gdn_seg_pass_kernel<64, false> (map pass, "
+                       f"{map_wgs} workgroups) + gdn_seg_combine_kernel + gdn_seg_pass_kernel<64, true> "
+                       f"(output pass, {B * Hv * segments} workgroups)"),
+            "bound": "mfma",
             "achieved": p_tflops,
             "peak": MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": p_tflops / MFMA_PEAK_TFLOPS,
+            "traffic": measured_prefill_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flops_per_launch": flops,
-            "counted_flops_per_launch": counted_flops,
-            "counted_achieved": counted_flops / (p_avg * 1e-3) / 1e12 if counted_flops else None,
+            "counted_mfma_flops_per_launch": counted_flops,
+            "avg_launch_ms": p_avg,
+            "hbm": {
+                "achieved": p_gbps,
+                "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s",
+                "frac": p_gbps / HBM_PEAK_GBPS,
+                "algorithmic_bytes_per_launch": p_bytes,
+            },
         },
         "decode": {
             "kernel": "gdn_decode_kernel<128, bf16>",
