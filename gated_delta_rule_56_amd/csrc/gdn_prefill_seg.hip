@@ -672,101 +672,111 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 }
             }
         };
-        // P2: K K^T and Q K^T of tile m against tiles nt <= m, the gated blocks of A (negated,
-        // below the diagonal) and A_qk, and the inverse of the diagonal block (chunk in slot s)
-        auto phase2 = [&](int s) __attribute__((always_inline)) {
-            if (!tile) return;
-            const unsigned char *Kt = smem + L::oK + s * L::kTile;
-            const unsigned char *Qt = smem + L::oQ + s * L::kTile;
-            const float *gts = reinterpret_cast<const float *>(smem + L::oG + s * 20 * C);
-            // every fragment first: lane (q4, li) reads row 16 nt + li, group 4 kb + q4
-            f16x8 ka[NT][4], bk[4], bq[4];
+        // P2: the gated blocks of A (negated, below the diagonal; the diagonal block inverted) and
+        // A_qk of chunk slot s. A tile (mm, nt) is the 16 x 16 block of rows 16 mm .. and columns
+        // 16 nt .. (nt <= mm) from K K^T and Q K^T; prep wave W forms its diagonal tile (W, W),
+        // whose inverse it builds, and off-diagonal tiles chosen so that no wave forms more than
+        // three (C = 64: W0 (3,0) (3,1), W1 (1,0) (2,0), W2 (2,1), W3 (3,2); C = 32: W1 (1,0)).
+        auto phase2w = [&](int s, auto wc) __attribute__((always_inline)) {
+            constexpr int W = decltype(wc)::value;
+            constexpr int nT = C == 64 ? (W < 2 ? 3 : 2) : (W == 0 ? 1 : W == 1 ? 2 : 0);
+            constexpr int MMs[3] = {W, C == 64 ? (W == 0 ? 3 : W == 1 ? 1 : W) : W, C == 64 ? (W == 0 ? 3 : 2) : 0};
+            constexpr int NTs[3] = {W, C == 64 ? (W == 0 ? 0 : W == 1 ? 0 : W - 1) : 0, C == 64 ? (W == 0 ? 1 : 0) : 0};
+            if constexpr (nT > 0) {
+                const unsigned char *Kt = smem + L::oK + s * L::kTile;
+                const unsigned char *Qt = smem + L::oQ + s * L::kTile;
+                const float *gts = reinterpret_cast<const float *>(smem + L::oG + s * 20 * C);
+                // every fragment first: lane (q4, li) reads row 16 x + li, group 4 kb + q4
+                f16x8 ka[nT][4], bk[nT][4], bq[nT][4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int off = li * 256 + (((4 * kb + q4) ^ ksw(li)) << 4);
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int off = li * 256 + (((4 * kb + q4) ^ ksw(li)) << 4);
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    if (nt <= m) ka[nt][kb] = ld8(Kt + off + nt * 4096);
-                bk[kb] = ld8(Kt + off + m * 4096);
-                if (OUT) bq[kb] = ld8(Qt + off + m * 4096);
-            }
-            const int t = 16 * m + li;
-            const float Gt = gts[4 * C + t], btt = gts[C + t];
-            f32x4 Gs[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                if (nt <= m) Gs[nt] = *reinterpret_cast<const f32x4 *>(gts + 4 * C + 16 * nt + 4 * q4);
-            fence();
-            // raw products, lane (q4, li): t = 16 m + li, s = 16 nt + 4 q4 + r
-            f32x4 rk[NT], rq[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) rk[nt] = rq[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    if (nt <= m) {
-                        rk[nt] = mfma16x16x32(ka[nt][kb], bk[kb], rk[nt]);
-                        if (OUT) rq[nt] = mfma16x16x32(ka[nt][kb], bq[kb], rq[nt]);
-                    }
-            // gating; only the diagonal tile needs the triangular mask
-            f32x4 a[NT], aqv[NT];
-            const float sct = p.scale;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                a[nt] = aqv[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (nt < m) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float gate = __expf(Gt - Gs[nt][r]);
-                        a[nt][r] = btt * gate * rk[nt][r];
-                        if (OUT) aqv[nt][r] = sct * gate * rq[nt][r];
-                    }
-                } else if (nt == m) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int sidx = 4 * q4 + r;
-                        const float gate = __expf(Gt - Gs[nt][r]);
-                        a[nt][r] = sidx < li ? btt * gate * rk[nt][r] : 0.0f;
-                        if (OUT) aqv[nt][r] = sidx <= li ? sct * gate * rq[nt][r] : 0.0f;
+                    for (int j = 0; j < nT; ++j) {
+                        ka[j][kb] = ld8(Kt + off + NTs[j] * 4096);
+                        bk[j][kb] = ld8(Kt + off + MMs[j] * 4096);
+                        if (OUT) bq[j][kb] = ld8(Qt + off + MMs[j] * 4096);
                     }
                 }
+                float Gt[nT], btt[nT];
+                f32x4 Gs[nT];
+#pragma unroll
+                for (int j = 0; j < nT; ++j) {
+                    Gt[j] = gts[4 * C + 16 * MMs[j] + li];
+                    btt[j] = gts[C + 16 * MMs[j] + li];
+                    Gs[j] = *reinterpret_cast<const f32x4 *>(gts + 4 * C + 16 * NTs[j] + 4 * q4);
+                }
+                fence();
+                // raw products, lane (q4, li): t = 16 mm + li, s = 16 nt + 4 q4 + r
+                f32x4 rk[nT], rq[nT];
+#pragma unroll
+                for (int j = 0; j < nT; ++j) rk[j] = rq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int j = 0; j < nT; ++j) {
+                        rk[j] = mfma16x16x32(ka[j][kb], bk[j][kb], rk[j]);
+                        if (OUT) rq[j] = mfma16x16x32(ka[j][kb], bq[j][kb], rq[j]);
+                    }
+                // gating; only the diagonal tile (j = 0) needs the triangular mask
+                f32x4 a[nT], aqv[nT];
+                const float sct = p.scale;
+#pragma unroll
+                for (int j = 0; j < nT; ++j) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float gate = __expf(Gt[j] - Gs[j][r]);
+                        if (j == 0) {
+                            const int sidx = 4 * q4 + r;
+                            a[j][r] = sidx < li ? btt[j] * gate * rk[j][r] : 0.0f;
+                            if (OUT) aqv[j][r] = sidx <= li ? sct * gate * rq[j][r] : 0.0f;
+                        } else {
+                            a[j][r] = btt[j] * gate * rk[j][r];
+                            if (OUT) aqv[j][r] = sct * gate * rq[j][r];
+                        }
+                    }
+                }
+                // A_qk: the tile's half of its 16-byte fragment (the block above the diagonal
+                // next to an even diagonal tile is zero)
+                if (OUT) {
+                    unsigned char *aqb = smem + L::oA + s * L::kFr * 1024 + lane * 16;
+#pragma unroll
+                    for (int j = 0; j < nT; ++j)
+                        *reinterpret_cast<f16x4 *>(aqb + fblk(MMs[j], NTs[j] / 2) * 1024 + (NTs[j] & 1) * 8) =
+                            to_f16x4(aqv[j]);
+                    if constexpr ((W & 1) == 0)
+                        *reinterpret_cast<f16x4 *>(aqb + fblk(W, W / 2) * 1024 + 8) = f16x4{};
+                }
+                // -A below the diagonal (A operands of the block substitution)
+#pragma unroll
+                for (int j = 1; j < nT; ++j)
+                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(MMs[j], NTs[j]) * 512 +
+                                               lane * 8) = to_f16x4(-a[j]);
+                // T_WW = (I + A_WW)^{-1}: lane (q4, li) builds T[li][4 q4 + e]. Its row of A_WW goes
+                // through this wave's LDS scratch (written as accumulators, read back by rows).
+                float *at = reinterpret_cast<float *>(smem + L::oAt) + W * 16 * 20;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) at[(4 * q4 + r) * 20 + li] = -a[0][r];  // at[s][i] = -A[i][s]
+                float nrow[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) nrow[k] = at[k * 20 + li];
+                f32x4 tq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tq[e] = 4 * q4 + e == li ? 1.0f : 0.0f;
+                inv_rows(tq, nrow);
+                // T_WW and diag(exp(G_C - G)) T_WW (row li scaled): the latter gives the scaled
+                // values of the state update straight from the substitution
+                const float egt = gts[2 * C + 16 * W + li];
+                unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + W * 1024 + lane * 8;
+                *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
+                *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(egt * tq);
             }
-            if (OUT) {
-#pragma unroll
-                for (int kb = 0; kb < KBC; ++kb)
-                    if (2 * kb <= m)
-                        *reinterpret_cast<f16x8 *>(smem + L::oA + s * L::kFr * 1024 + fblk(m, kb) * 1024 + lane * 16) =
-                            cat(to_f16x4(aqv[2 * kb]), to_f16x4(aqv[2 * kb + 1]));
-            }
-            // -A_mj below the diagonal (A operands of the block substitution)
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-                if (j < m)
-                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(m, j) * 512 + lane * 8) =
-                        to_f16x4(-a[j]);
-            // T_mm = (I + A_mm)^{-1}: lane (q4, li) builds T[li][4 q4 + e]. Its row of A_mm goes
-            // through this wave's LDS scratch (written as accumulators, read back by rows).
-            f32x4 dm = a[0];
-#pragma unroll
-            for (int nt = 1; nt < NT; ++nt)
-                if (nt == m) dm = a[nt];
-            float *at = reinterpret_cast<float *>(smem + L::oAt) + m * 16 * 20;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) at[(4 * q4 + r) * 20 + li] = -dm[r];  // at[s][i] = -A[i][s]
-            float nrow[16];
-#pragma unroll
-            for (int k = 0; k < 16; ++k) nrow[k] = at[k * 20 + li];
-            f32x4 tq;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tq[e] = 4 * q4 + e == li ? 1.0f : 0.0f;
-            inv_rows(tq, nrow);
-            // T_mm and diag(exp(G_C - G)) T_mm (row li scaled): the latter gives the scaled values
-            // of the state update straight from the substitution
-            const float egt = gts[2 * C + t];
-            unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + m * 1024 + lane * 8;
-            *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
-            *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(egt * tq);
+        };
+        auto phase2 = [&](int s) __attribute__((always_inline)) {
+            if (m == 0) phase2w(s, IC<0>{});
+            else if (m == 1) phase2w(s, IC<1>{});
+            else if (m == 2) phase2w(s, IC<2>{});
+            else phase2w(s, IC<3>{});
         };
 
         // prologue: chunk 0 of the segment into slot 0. Every load is issued and every P1 runs, the
