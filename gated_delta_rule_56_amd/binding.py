@@ -21,7 +21,7 @@ GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
 GDN_STATE_F32, GDN_STATE_F16 = 0, 1
 GDN_OUT_F32, GDN_OUT_F16 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 _STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
 _OUT_DTYPES = {torch.float32: GDN_OUT_F32, torch.float16: GDN_OUT_F16}
 
@@ -39,6 +39,11 @@ class GdnShape(ctypes.Structure):
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int),
                 ("head_map", ctypes.c_int), ("scale", ctypes.c_float), ("state_dtype", ctypes.c_int),
                 ("o_dtype", ctypes.c_int)]
+
+
+class GdnNorm(ctypes.Structure):
+    """Mirror of gdn_norm in include/gdn.h (the optional output norm of prefill and decode)."""
+    _fields_ = [("weight", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
 class GdnError(RuntimeError):
@@ -65,7 +70,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_prefill_segments.restype = ctypes.c_int
     lib.gdn_prefill_segments.argtypes = [ctypes.POINTER(GdnShape), SZ]
     lib.gdn_prefill.restype = ctypes.c_int
-    lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, SZ, ctypes.POINTER(GdnNorm), P]
     lib.gdn_prefill_varlen_workspace_bytes.restype = SZ
     lib.gdn_prefill_varlen_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
     lib.gdn_prefill_varlen.restype = ctypes.c_int
@@ -75,7 +80,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_kda_decode.restype = ctypes.c_int
     lib.gdn_kda_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
     lib.gdn_decode.restype = ctypes.c_int
-    lib.gdn_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
+    lib.gdn_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, ctypes.POINTER(GdnNorm), P]
     lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm.argtypes = [ctypes.POINTER(GdnShape), P, P, P, ctypes.c_float, P]
     lib.gdn_qkv_prologue.restype = ctypes.c_int
@@ -118,6 +123,28 @@ def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
 def _stream_handle(stream) -> Optional[int]:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def _norm_arg(weight: Optional[torch.Tensor], gate: Optional[torch.Tensor], eps: float, o_shape, dtype: torch.dtype,
+              d: int):
+    """The gdn_norm argument (None without a weight): weight [d] float32, gate of o's shape in
+    the q/k/v dtype or None."""
+    if weight is None:
+        if gate is not None:
+            raise ValueError("norm_gate needs norm_weight")
+        return None
+    _dev_tensor(weight, "norm_weight", torch.float32)
+    if tuple(weight.shape) != (d,):
+        raise ValueError(f"norm_weight must be [{d}]")
+    if gate is not None:
+        _dev_tensor(gate, "norm_gate", dtype)
+        if tuple(gate.shape) != tuple(o_shape):
+            raise ValueError(f"norm_gate must have o's shape {tuple(o_shape)}")
+    return GdnNorm(weight.data_ptr(), gate.data_ptr() if gate is not None else None, float(eps))
+
+
+def _norm_ref(n: Optional[GdnNorm]):
+    return ctypes.byref(n) if n is not None else None
 
 
 def _scratch(nbytes: int, device, stream) -> torch.Tensor:
@@ -179,7 +206,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
             scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
             workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
-            o_dtype: torch.dtype = torch.float32, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            o_dtype: torch.dtype = torch.float32, norm_weight: Optional[torch.Tensor] = None,
+            norm_gate: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """gdn_prefill on torch tensors.
 
     q, k [B][Hk][T][d] and v [B][Hv][T][d] (bfloat16 or float32); g, beta [B][Hv][T] float32;
@@ -189,7 +218,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     float16 (o_dtype, or the type of the o passed). workspace: a uint8 device tensor of at
     any size (prefill_workspace_bytes(...) gives the preferred one; less means fewer segments of
     the sequence run in parallel, see prefill_segments), or None to allocate the preferred size
-    for this call.
+    for this call. norm_weight [d] float32 (and optionally norm_gate, o's shape in the q/k/v
+    dtype) applies the gated RMSNorm to every output row before it is stored (gdn_norm).
     """
     lib = load_library()
     dtype = q.dtype
@@ -227,6 +257,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     shape = make_shape(B, T, Hk, Hv, d, chunk,
                        GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, scale,
                        _STATE_DTYPES[sdt], _OUT_DTYPES[o.dtype])
+    norm = _norm_arg(norm_weight, norm_gate, norm_eps, (B, Hv, T, d), dtype, d)
     ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
     if workspace is None:
         workspace = _scratch(ws, q.device, stream) if ws else None
@@ -235,7 +266,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
         ws = workspace.numel()  # a smaller workspace than preferred means fewer segments
     _check(lib, lib.gdn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), ws,
-                                _stream_handle(stream)))
+                                _norm_ref(norm), _stream_handle(stream)))
     return o, final_state
 
 
@@ -299,10 +330,13 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
 
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
            state: torch.Tensor, *, head_map: int = GDN_HEADS_TILED, scale: Optional[float] = None,
-           o: Optional[torch.Tensor] = None, o_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+           o: Optional[torch.Tensor] = None, o_dtype: torch.dtype = torch.float32,
+           norm_weight: Optional[torch.Tensor] = None, norm_gate: Optional[torch.Tensor] = None,
+           norm_eps: float = 1e-6, stream=None) -> torch.Tensor:
     """gdn_decode on torch tensors: q, k [B][Hk][d], v [B][Hv][d], g, beta [B][Hv],
     state [B][Hv][d][d] float32 or float16 (updated in place). Returns o [B][Hv][d] float32 or
-    float16 (o_dtype, or the type of the o passed)."""
+    float16 (o_dtype, or the type of the o passed); with norm_weight (and optionally norm_gate
+    [B][Hv][d]) the gated RMSNorm of every output row (gdn_norm)."""
     lib = load_library()
     dtype = q.dtype
     if dtype not in (torch.bfloat16, torch.float32):
@@ -323,8 +357,9 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
         scale = 1.0 / math.sqrt(d)
     shape = make_shape(B, 1, Hk, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
                        head_map, scale, _STATE_DTYPES[state.dtype], _OUT_DTYPES[o.dtype])
+    norm = _norm_arg(norm_weight, norm_gate, norm_eps, (B, Hv, d), dtype, d)
     _check(lib, lib.gdn_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                               _ptr(state), _ptr(o), _stream_handle(stream)))
+                               _ptr(state), _ptr(o), _norm_ref(norm), _stream_handle(stream)))
     return o
 
 

@@ -87,6 +87,18 @@ gdn_status check_no_overlap(const Range *outs, int nout, const Range *ins, int n
         if (st_ != GDN_OK) return st_;     \
     } while (0)
 
+// An output norm over `rows` output rows of d values: its eps, pointers, and that its weight
+// and gate overlap none of the call's outputs.
+gdn_status check_norm(const gdn_norm *n, int d, int64_t rows, bool bf16, const Range *outs, int nout) {
+    if (!n) return GDN_OK;
+    if (!std::isfinite(n->eps) || n->eps < 0.0f) return fail(GDN_ERR_INVALID_ARG, "norm eps must be finite and >= 0");
+    GDN_TRY(check_ptr(n->weight, "norm weight", 16));
+    if (n->gate) GDN_TRY(check_ptr(n->gate, "norm gate", 16));
+    const Range nr[] = {range("norm weight", n->weight, (int64_t)d * 4),
+                        range("norm gate", n->gate, n->gate ? rows * d * (bf16 ? 2 : 4) : 0)};
+    return check_no_overlap(outs, nout, nr, 2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,7 +136,7 @@ int gdn_prefill_segments(const gdn_shape *s, size_t workspace_bytes) {
 
 gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
                        const float *beta, const void *initial_state, void *o, void *final_state,
-                       void *workspace, size_t workspace_bytes, void *stream) {
+                       void *workspace, size_t workspace_bytes, const gdn_norm *norm, void *stream) {
     GDN_TRY(check_common(s));
     if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
     if (s->chunk != 16 && s->chunk != 32 && s->chunk != 64)
@@ -166,6 +178,10 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
         if (initial_state && final_state != initial_state && overlaps(out_s[0], ins[5]))
             return fail(GDN_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
     }
+    {
+        const Range outs[] = {out_o[0], range("final_state", final_state, final_state ? st_bytes : 0)};
+        GDN_TRY(check_norm(norm, d, B * Hv * T, bf16, outs, 2));
+    }
 
     gdn::PrefillParams p;
     p.q = q;
@@ -196,6 +212,7 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
             if (!aligned(workspace, 16)) return fail(GDN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
             const Range wsr[] = {range("workspace", workspace, used)};
             GDN_TRY(check_no_overlap(wsr, 1, ins, 6));
+            GDN_TRY(check_norm(norm, d, B * Hv * T, bf16, wsr, 1));
             GDN_TRY(check_no_overlap(wsr, 1, out_o, 1));
             if (final_state) {
                 const Range fs[] = {range("final_state", final_state, st_bytes)};
@@ -206,12 +223,31 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     if (!final_state && T == 0) return GDN_OK;  // nothing to compute or write
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t err;
-    if (segmented_path(s))
+    if (segmented_path(s)) {
+        if (norm) {  // fused into the output pass
+            p.norm_w = norm->weight;
+            p.norm_gate = norm->gate;
+            p.norm_eps = norm->eps;
+        }
         err = gdn::launch_prefill_seg(p, s->chunk, P, workspace, st);
-    else if (bf16 && d == 128)
-        err = gdn::launch_prefill_mfma(p, s->chunk, st);  // chunk 16
-    else
-        err = gdn::launch_prefill_f32(p, s->chunk, bf16, st);
+    } else {
+        if (bf16 && d == 128)
+            err = gdn::launch_prefill_mfma(p, s->chunk, st);  // chunk 16
+        else
+            err = gdn::launch_prefill_f32(p, s->chunk, bf16, st);
+        if (err == hipSuccess && norm && T > 0) {  // the norm as one more pass over o
+            gdn::NormParams np;
+            np.o = o;
+            np.gate = norm->gate;
+            np.weight = norm->weight;
+            np.rows = B * Hv * T;
+            np.D = d;
+            np.gate_bf16 = bf16;
+            np.eps = norm->eps;
+            np.o_f16 = o16;
+            err = gdn::launch_gated_rmsnorm(np, st);
+        }
+    }
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
     return GDN_OK;
 }
@@ -392,7 +428,7 @@ gdn_status gdn_qkv_prologue(const gdn_shape *s, const void *x, const float *conv
 namespace {
 // gdn_decode and gdn_kda_decode: g is [B][Hv] or, with kda, [B][Hv][dk]
 gdn_status decode_impl(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
-                       const float *beta, void *state, void *o, void *stream, bool kda) {
+                       const float *beta, void *state, void *o, const gdn_norm *norm, void *stream, bool kda) {
     GDN_TRY(check_common(s));
     if (s->seq_len != 1) return fail(GDN_ERR_INVALID_ARG, "decode needs seq_len == 1 (got %d)", s->seq_len);
     const int d = s->head_dim_k;
@@ -416,6 +452,7 @@ gdn_status decode_impl(const gdn_shape *s, const void *q, const void *k, const v
                           range("state", state, B * Hv * d * d * (st16 ? 2 : 4))};
     GDN_TRY(check_no_overlap(outs, 2, ins, 5));
     if (overlaps(outs[0], outs[1])) return fail(GDN_ERR_INVALID_ARG, "o overlaps state");
+    GDN_TRY(check_norm(norm, d, B * Hv, bf16, outs, 2));
 
     gdn::DecodeParams p;
     p.q = q;
@@ -434,6 +471,11 @@ gdn_status decode_impl(const gdn_shape *s, const void *q, const void *k, const v
     p.state_f16 = st16;
     p.o_f16 = o16;
     p.kda = kda;
+    if (norm) {
+        p.norm_w = norm->weight;
+        p.norm_gate = norm->gate;
+        p.norm_eps = norm->eps;
+    }
     const hipError_t err = gdn::launch_decode(p, bf16, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
     return GDN_OK;
@@ -443,13 +485,13 @@ gdn_status decode_impl(const gdn_shape *s, const void *q, const void *k, const v
 extern "C" {
 
 gdn_status gdn_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
-                      const float *beta, void *state, void *o, void *stream) {
-    return decode_impl(s, q, k, v, g, beta, state, o, stream, false);
+                      const float *beta, void *state, void *o, const gdn_norm *norm, void *stream) {
+    return decode_impl(s, q, k, v, g, beta, state, o, norm, stream, false);
 }
 
 gdn_status gdn_kda_decode(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
                           const float *beta, void *state, void *o, void *stream) {
-    return decode_impl(s, q, k, v, g, beta, state, o, stream, true);
+    return decode_impl(s, q, k, v, g, beta, state, o, nullptr, stream, true);
 }
 
 gdn_status gdn_kda_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,

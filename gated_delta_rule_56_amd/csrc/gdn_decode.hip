@@ -93,8 +93,10 @@ constexpr int max_split() {
 }
 
 // kKda: one decay per key channel (g [B][Hv][D]) instead of one per head; SPLIT: workgroups per
-// (b, h), each taking D / SPLIT consecutive rows
-template <int D, typename T, typename SD, bool kKda, int SPLIT>
+// (b, h), each taking D / SPLIT consecutive rows; kNorm (SPLIT = 1): the output row of the pair
+// is normalised before it is stored, o_i = x_i / sqrt(mean(x^2) + eps) * w_i * silu(gate_i), its
+// sum of squares reduced over the workgroup through LDS
+template <int D, typename T, typename SD, bool kKda, int SPLIT, bool kNorm = false>
 __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams p) {
     constexpr int CPL = cols_per_lane<D, SD>();
     constexpr int LPR = D / CPL;                    // lanes per state row
@@ -149,6 +151,23 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
     float vrow[ITERS];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) vrow[it] = load_elem<T>(vp, row0 + it * RPA);
+    // the norm's gate and weight of this lane's rows, requested with the rows (lanes that hold
+    // column 0 of a row produce its output)
+    float gw[kNorm ? ITERS : 1], ov[kNorm ? ITERS : 1];
+    if constexpr (kNorm) {
+        static_assert(SPLIT == 1, "the fused norm needs whole rows of the pair in the workgroup");
+        const T *gp = static_cast<const T *>(p.norm_gate) + (int64_t)pair * D;
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int row = row0 + it * RPA;
+            float gz = 1.0f;
+            if (p.norm_gate) {
+                const float z = load_elem<T>(gp, row);
+                gz = z / (1.0f + __expf(-z));
+            }
+            gw[it] = gz * p.norm_w[row];
+        }
+    }
 
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -167,12 +186,39 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
             y[e] = __builtin_fmaf(delta, kv[e], (kKda ? al[e] : alpha) * s[it].get(e));
         const int row = row0 + it * RPA;
         StateRow<CPL, SD>::store(S + (int64_t)row * D + col, y);
-        if (col == 0) {
-            const float oi = as * rq + delta * kappa;
+        const float oi = as * rq + delta * kappa;
+        if constexpr (kNorm) {
+            ov[it] = oi;
+        } else if (col == 0) {
             if (p.o_f16)
                 static_cast<_Float16 *>(p.o)[(int64_t)pair * D + row] = f16_out(oi);
             else
                 static_cast<float *>(p.o)[(int64_t)pair * D + row] = oi;
+        }
+    }
+    if constexpr (kNorm) {
+        // sum of squares of the pair's D outputs: per lane over its rows, then over the row
+        // holders of each wave and the waves through LDS (every lane of a row holds its output)
+        __shared__ float red[(kDecodeThreads / 64) * RPA];
+        float ss = 0.0f;
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) ss += ov[it] * ov[it];
+        if (col == 0) red[wave * RPA + sub] = ss;
+        __syncthreads();
+        float tot = 0.0f;
+#pragma unroll
+        for (int j = 0; j < (kDecodeThreads / 64) * RPA; ++j) tot += red[j];
+        const float rinv = rsqrtf(tot / D + p.norm_eps);
+        if (col == 0) {
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                const int row = row0 + it * RPA;
+                const float y = ov[it] * rinv * gw[it];
+                if (p.o_f16)
+                    static_cast<_Float16 *>(p.o)[(int64_t)pair * D + row] = f16_out(y);
+                else
+                    static_cast<float *>(p.o)[(int64_t)pair * D + row] = y;
+            }
         }
     }
 }
@@ -181,30 +227,40 @@ __global__ __launch_bounds__(kDecodeThreads) void gdn_decode_kernel(DecodeParams
 constexpr int64_t kSplitBelow = 256;
 
 template <int D, typename T, typename SD, bool kKda>
-void launch_sd(const DecodeParams &p, hipStream_t stream) {
+hipError_t launch_sd(const DecodeParams &p, hipStream_t stream) {
     constexpr int S = max_split<D, SD>();
     const int64_t pairs = (int64_t)p.B * p.Hv;
-    if (S > 1 && pairs < kSplitBelow)
+    const bool split = S > 1 && pairs < kSplitBelow;
+    if (split)
         hipLaunchKernelGGL((gdn_decode_kernel<D, T, SD, kKda, S>), dim3((unsigned)(pairs * S)), dim3(kDecodeThreads),
                            0, stream, p);
+    else if (!kKda && p.norm_w)
+        hipLaunchKernelGGL((gdn_decode_kernel<D, T, SD, false, 1, true>), dim3((unsigned)pairs),
+                           dim3(kDecodeThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((gdn_decode_kernel<D, T, SD, kKda, 1>), dim3((unsigned)pairs), dim3(kDecodeThreads), 0,
                            stream, p);
+    hipError_t err = hipGetLastError();
+    if (err == hipSuccess && p.norm_w && split) {
+        // a pair's rows are spread over S workgroups: the norm as its own pass over o
+        NormParams np;
+        np.o = p.o;
+        np.gate = p.norm_gate;
+        np.weight = p.norm_w;
+        np.rows = pairs;
+        np.D = D;
+        np.gate_bf16 = sizeof(T) == 2;
+        np.eps = p.norm_eps;
+        np.o_f16 = p.o_f16;
+        err = launch_gated_rmsnorm(np, stream);
+    }
+    return err;
 }
 
 template <int D, typename T>
 hipError_t launch_dt(const DecodeParams &p, hipStream_t stream) {
-    if (p.kda) {
-        if (p.state_f16)
-            launch_sd<D, T, _Float16, true>(p, stream);
-        else
-            launch_sd<D, T, float, true>(p, stream);
-    } else if (p.state_f16) {
-        launch_sd<D, T, _Float16, false>(p, stream);
-    } else {
-        launch_sd<D, T, float, false>(p, stream);
-    }
-    return hipGetLastError();
+    if (p.kda) return p.state_f16 ? launch_sd<D, T, _Float16, true>(p, stream) : launch_sd<D, T, float, true>(p, stream);
+    return p.state_f16 ? launch_sd<D, T, _Float16, false>(p, stream) : launch_sd<D, T, float, false>(p, stream);
 }
 
 template <int D>

@@ -29,6 +29,11 @@ struct PrefillParams {
     const int32_t *seqs = nullptr;    // [B][4]: first token, tokens, first workspace chunk, 0
     const int32_t *chunks = nullptr;  // [nchunks][2]: first token, tokens (0: unused slot)
     int32_t nchunks = 0;              // workspace chunks of the packed layout
+    // output norm fused into the o store (the segmented path): o = x / sqrt(mean(x^2) + eps)
+    // * w * silu(gate) per output row; norm_w == nullptr: none
+    const float *norm_w = nullptr;    // [D]
+    const void *norm_gate = nullptr;  // o's shape, q/k/v element type, or nullptr (no gate factor)
+    float norm_eps = 0.0f;
 };
 
 struct DecodeParams {
@@ -45,6 +50,10 @@ struct DecodeParams {
     bool state_f16 = false;
     bool o_f16 = false;
     bool kda = false;          // one decay per key channel
+    // output norm fused into the o store (one workgroup per pair): as PrefillParams
+    const float *norm_w = nullptr;
+    const void *norm_gate = nullptr;
+    float norm_eps = 0.0f;
 };
 
 // bf16 q/k/v, D = 128, chunk 16: single fused chunked WY kernel on fp16 MFMA.

@@ -70,7 +70,7 @@ __host__ __device__ constexpr int fblk(int m, int kb) { return m + (m > 2 ? m - 
 // 16 x 16 block (m, j), j < m, of A below the diagonal: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 __host__ __device__ constexpr int ablk(int m, int j) { return m * (m - 1) / 2 + j; }
 
-template <int C, bool OUT>
+template <int C, bool OUT, bool NORM = false>
 struct SegSmem {
     static constexpr int NT = C / 16, KBC = C / 32;
     static constexpr int kFr = fblk(NT - 1, (NT - 1) / 2) + 1;   // A_qk fragment blocks
@@ -84,9 +84,18 @@ struct SegSmem {
     static constexpr size_t oTd = oNA + 2 * kNA * 512;           // [2][NT][2][64] x 8 B: T_mm, diag(exp(G_C-G)) T_mm
     static constexpr size_t oG = oTd + 2 * NT * 1024;             // [2][5][C] f32: gamma, beta, exp(G_C-G), beta gamma, G
     static constexpr size_t oAt = oG + 2 * 20 * C;               // f32 [NT][16][20]: diagonal blocks of A, transposed
-    static constexpr size_t kBytes = oAt + NT * 16 * 20 * 4;
+    // output norm (NORM): a chunk's un-normalised o rows in fp16, each lane's 8 values scaled
+    // by a power of two taken from their own sum of squares (stage_scale), rows padded to 272 B
+    // so that the 8-byte accesses of 32 lanes (16 tokens, two column groups) meet all 64 banks;
+    // the partial sums of squares [C][20] f32 (16 used: 4 row waves x 4 lanes of 8 columns);
+    // the norm weight [128] f32
+    static constexpr size_t oNO = oAt + NT * 16 * 20 * 4;
+    static constexpr size_t oNP = oNO + (NORM ? (size_t)C * 272 : 0);
+    static constexpr size_t oNW = oNP + (NORM ? (size_t)C * 80 : 0);
+    static constexpr size_t kBytes = oNW + (NORM ? 512 : 0);
+    static_assert(!NORM || OUT, "the norm belongs to the output pass");
     static_assert(oQ % 16 == 0 && oV % 16 == 0 && oA % 16 == 0 && oNA % 16 == 0 && oTd % 16 == 0 &&
-                      oG % 16 == 0 && oAt % 16 == 0,
+                      oG % 16 == 0 && oAt % 16 == 0 && oNO % 16 == 0 && oNP % 16 == 0 && oNW % 16 == 0,
                   "alignment");
     static_assert(kBytes <= 160 * 1024, "LDS");
 };
@@ -221,9 +230,23 @@ __device__ __forceinline__ void inv_rows(f32x4 &t, const float (&nrow)[16]) {
     t = f32x4{t0, t1, t2, t3};
 }
 
-template <int C, bool OUT>
+// Power-of-two factor 2^(14 - floor(e / 2)), e the binary exponent of ss >= 0 (its biased
+// exponent field minus 127, so 0 and subnormal sums give e = -127), and its inverse. With ss
+// the sum of squares of a few values, every value times the factor has magnitude below 2^15:
+// in float16 range, and rounded to 11 significant bits whatever the values' own magnitude.
+__device__ __forceinline__ float stage_scale(float ss) {
+    const int h = ((int)((__float_as_uint(ss) >> 23) & 0xff) - 127) >> 1;
+    return __uint_as_float((uint32_t)(127 + 14 - h) << 23);
+}
+__device__ __forceinline__ float stage_unscale(float ss) {
+    const int h = ((int)((__float_as_uint(ss) >> 23) & 0xff) - 127) >> 1;
+    return __uint_as_float((uint32_t)(127 - 14 + h) << 23);
+}
+
+// NORM: 0 no output norm, 1 the norm without a gate, 2 with a gate
+template <int C, bool OUT, int NORM = 0>
 __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams sp) {
-    using L = SegSmem<C, OUT>;
+    using L = SegSmem<C, OUT, (NORM > 0)>;
     constexpr int NT = L::NT, KBC = L::KBC;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // every argument into a scalar local: a reference to the argument structure would make
@@ -236,10 +259,14 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         int B, T, Hk, Hv, Ts, head_map, P, seg_chunks;
         float scale;
         bool init_f16, final_f16, o_f16;
+        const float *norm_w;
+        const uint16_t *norm_gate;
+        float norm_eps;
     };
     const Args p = {sp.p.q, sp.p.k, sp.p.v, sp.p.init_state, sp.p.g, sp.p.beta, sp.p.o, sp.p.final_state,
                     sp.ws_start, sp.ws_n, sp.ws_m, sp.p.B, sp.p.T, sp.p.Hk, sp.p.Hv, sp.p.Ts, sp.p.head_map,
-                    sp.P, sp.seg_chunks, sp.p.scale, sp.p.init_f16, sp.p.final_f16, sp.p.o_f16};
+                    sp.P, sp.seg_chunks, sp.p.scale, sp.p.init_f16, sp.p.final_f16, sp.p.o_f16,
+                    sp.p.norm_w, static_cast<const uint16_t *>(sp.p.norm_gate), sp.p.norm_eps};
 
     // ---- workgroup -> (b, key head, unit, value head of the key head). Consecutive indices
     // share the key head's k and q and sit on one XCD (workgroups go round-robin over 8 XCDs).
@@ -354,6 +381,25 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         }
         float *o_f32 = static_cast<float *>(p.o);
         _Float16 *o_f16 = static_cast<_Float16 *>(p.o);
+
+        // output norm: the weight into LDS for the prep waves (visible after the setup barriers);
+        // store_normed writes this lane's 8 normalised values of token row tok (of the pair) from
+        // their float16 staging slot xo
+        if constexpr (NORM > 0) {
+            if (w == 0 && lane < kD / 4)
+                *reinterpret_cast<f32x4 *>(smem + L::oNW + 16 * lane) = *reinterpret_cast<const f32x4 *>(p.norm_w + 4 * lane);
+        }
+        auto store_normed = [&](const unsigned char *xo, int64_t tok) __attribute__((always_inline)) {
+            const f16x4 y0 = ld4(xo), y1 = ld4(xo + 32);
+            const int64_t row = (vtok + tok) * kD + 32 * w + 4 * q4;
+            if (p.o_f16) {
+                *reinterpret_cast<f16x4 *>(o_f16 + row) = y0;
+                *reinterpret_cast<f16x4 *>(o_f16 + row + 16) = y1;
+            } else {
+                *reinterpret_cast<f32x4 *>(o_f32 + row) = f32x4{(float)y0[0], (float)y0[1], (float)y0[2], (float)y0[3]};
+                *reinterpret_cast<f32x4 *>(o_f32 + row + 16) = f32x4{(float)y1[0], (float)y1[1], (float)y1[2], (float)y1[3]};
+            }
+        };
 
         lds_barrier();
         lds_barrier();
@@ -485,7 +531,19 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                         O1 = mfma16x16x32(ua[1][kb], aqf[fblk(m, kb)], O1);
                     }
                     const int t = 16 * m + li;
-                    if (t < ntok) {
+                    if constexpr (NORM > 0) {
+                        unsigned char *xo = smem + L::oNO + t * 272 + 2 * (32 * w + 4 * q4);
+                        if (i > 0) store_normed(xo, (int64_t)(c - 1) * C + t);  // chunk c - 1: all C rows
+                        // stage for the prep waves' norm (next interval): this lane's 8 columns
+                        // in fp16, scaled, and their sum of squares in fp32
+                        float ss = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ss += O0[e] * O0[e] + O1[e] * O1[e];
+                        *reinterpret_cast<float *>(smem + L::oNP + t * 80 + 4 * (4 * w + q4)) = ss;
+                        const float sc = stage_scale(ss);
+                        *reinterpret_cast<f16x4 *>(xo) = to_f16x4(O0 * sc);
+                        *reinterpret_cast<f16x4 *>(xo + 32) = to_f16x4(O1 * sc);
+                    } else if (t < ntok) {
                         const int64_t row = (vtok + (int64_t)c * C + t) * kD + 32 * w + 4 * q4;
                         if (p.o_f16) {
                             *reinterpret_cast<f16x4 *>(o_f16 + row) =
@@ -541,6 +599,18 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         for (int i = 0; i < n; i += 2) {
             interval(IC<0>{}, i);
             if (i + 1 < n) interval(IC<1>{}, i + 1);
+        }
+        if constexpr (NORM > 0) {
+            lds_barrier();  // the prep waves have normalised the last chunk's rows
+            if (n > 0) {
+                const int c = cb + n - 1;
+                const int ntok = min(C, T - c * C);
+#pragma unroll
+                for (int m = 0; m < NT; ++m) {
+                    const int t = 16 * m + li;
+                    if (t < ntok) store_normed(smem + L::oNO + t * 272 + 2 * (32 * w + 4 * q4), (int64_t)c * C + t);
+                }
+            }
         }
 
         // ---- the segment's end state
@@ -602,6 +672,55 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 request_rows(kr, kg, c);
                 if (OUT) request_rows(qr, qg, c);
                 if (has_v) request_rows(vr, vg, c);
+            }
+        };
+        // output norm (NORM): the row waves stage chunk c's o rows between b1 and b2 of its
+        // interval; in the next interval, before b1, the tile waves normalise them in place,
+        // lane by lane the rows and columns of kr (NORM 2: the gate of chunk c requested one
+        // interval ahead into gz), and after b1 the row waves store them. The prep waves issue
+        // no global stores: with stores outstanding, every later wait for a load would have to
+        // wait for all memory operations (one counter, completed out of order across the two
+        // kinds), the next chunk's rows included.
+        u16x8 gz[NORM == 2 ? 4 : 1];
+        const uint16_t *gzp = NORM == 2 ? p.norm_gate + vtok * kD : nullptr;
+        auto request_gate = [&](int c) __attribute__((always_inline)) {
+            if constexpr (NORM == 2) {
+                if (tile) request_rows(gz, gzp, c);
+            }
+        };
+        auto norm_rows = [&]() __attribute__((always_inline)) {
+            if constexpr (NORM > 0) {
+                if (tile) {
+                    const f32x4 w0 = ldf4(smem + L::oNW + 32 * lp), w1 = ldf4(smem + L::oNW + 32 * lp + 16);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 16 * m + 4 * j + lrow;
+                        // the row's 16 partial sums; columns 8 lp + 0..3 and + 4..7 were staged by
+                        // two lanes of row wave lp / 4, whose sums sit in slots 4 (lp / 4) + 2 (lp % 2)
+                        // and the next
+                        const unsigned char *pp = smem + L::oNP + t * 80;
+                        const f32x4 a = (ldf4(pp) + ldf4(pp + 16)) + (ldf4(pp + 32) + ldf4(pp + 48));
+                        const float *own = reinterpret_cast<const float *>(pp) + 4 * (lp >> 2) + 2 * (lp & 1);
+                        const float r = rsqrtf(((a[0] + a[1]) + (a[2] + a[3])) * (1.0f / kD) + p.norm_eps);
+                        const float ra = r * stage_unscale(own[0]), rb = r * stage_unscale(own[1]);
+                        unsigned char *xp = smem + L::oNO + t * 272 + 16 * lp;
+                        const f16x8 x = ld8(xp);
+                        f16x8 y;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            float f = e < 4 ? ra * w0[e] : rb * w1[e - 4];
+                            if constexpr (NORM == 2) {
+                                // silu(z) = z / (1 + exp(-z)) with the hardware reciprocal (1 ulp);
+                                // exp(-z) = inf for z < -88 gives 0
+                                const float z = bf16_bits_to_f32(gz[j][e]);
+                                f *= z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+                            }
+                            y[e] = f16_out((float)x[e] * f);
+                        }
+                        // the normalised row in place of the staged one, for the row waves' store
+                        *reinterpret_cast<f16x8 *>(xp) = y;
+                    }
+                }
             }
         };
         // P1: wave 4 forms the gate vectors of chunk c; tile m's rows of chunk c into slot s (waits
@@ -783,6 +902,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         // chunk indices clamped to the segment (a clamped P1 fills the slot no one reads next),
         // so that the loop carries no register whose load is optional.
         const int clast = cb + max(n, 1) - 1;
+        request_gate(cb);
         issue(cb);
         phase1(cb, min(cb + 1, clast), IC<0>{});
         lds_barrier();
@@ -792,6 +912,8 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         auto interval = [&](auto sl, int i) __attribute__((always_inline)) {
             constexpr int s1 = 1 - decltype(sl)::value;  // slot of chunk i + 1
             const int c1 = cb + i + 1;
+            if (i > 0) norm_rows();  // chunk i - 1, staged in the previous interval
+            request_gate(min(cb + i, clast));
             phase1(min(c1, clast), min(c1 + 1, clast), IC<s1>{});
             lds_barrier();  // b1
             if (i + 1 < n) phase2(s1);
@@ -800,6 +922,10 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         for (int i = 0; i < n; i += 2) {
             interval(IC<0>{}, i);
             if (i + 1 < n) interval(IC<1>{}, i + 1);
+        }
+        if constexpr (NORM > 0) {
+            if (n > 0) norm_rows();  // the last chunk, staged before the last b2
+            lds_barrier();           // for the row waves' store of it
         }
     }
 }
@@ -859,18 +985,19 @@ __global__ __launch_bounds__(256) void gdn_state_copy_kernel(PrefillParams p, in
     store_state4(p.final_state, i, x, p.final_f16);
 }
 
-template <int C, bool OUT>
+template <int C, bool OUT, int NORM = 0>
 hipError_t launch_pass(const SegParams &sp, int64_t nblocks, hipStream_t stream) {
-    const size_t bytes = SegSmem<C, OUT>::kBytes;
+    const size_t bytes = SegSmem<C, OUT, (NORM > 0)>::kBytes;
     static bool attr_set = false;  // the attribute is a property of the function: set once
     if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_seg_pass_kernel<C, OUT>),
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_seg_pass_kernel<C, OUT, NORM>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
         if (err != hipSuccess) return err;
         attr_set = true;
     }
     if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gdn_seg_pass_kernel<C, OUT>), dim3((unsigned)nblocks), dim3(kSegThreads), bytes, stream, sp);
+    hipLaunchKernelGGL((gdn_seg_pass_kernel<C, OUT, NORM>), dim3((unsigned)nblocks), dim3(kSegThreads), bytes, stream,
+                       sp);
     return hipGetLastError();
 }
 
@@ -894,7 +1021,9 @@ hipError_t launch_seg_c(const SegParams &sp, hipStream_t stream) {
             if (err != hipSuccess) return err;
         }
     }
-    return launch_pass<C, true>(sp, pairs * sp.P, stream);
+    if (!sp.p.norm_w) return launch_pass<C, true>(sp, pairs * sp.P, stream);
+    return sp.p.norm_gate ? launch_pass<C, true, 2>(sp, pairs * sp.P, stream)
+                          : launch_pass<C, true, 1>(sp, pairs * sp.P, stream);
 }
 
 }  // namespace

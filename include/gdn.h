@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
     GDN_OK = 0,
@@ -128,6 +128,32 @@ typedef struct {
 } gdn_shape;
 
 /*
+ * Optional output norm of gdn_prefill and gdn_decode: the gated RMSNorm that the gated delta
+ * calls on the "27b 935/47" compare page take as arguments (gated_delta's norm_weight and
+ * norm_eps, gated_delta_prefill's weight and eps; the q8_gated_rmsnorm test). With it, each
+ * output row x of head_dim_v values (one token of one value head) is written as
+ *     x / sqrt(mean(x^2) + eps) * weight * silu(gate),  silu(z) = z / (1 + exp(-z))
+ * instead of x; the un-normalised x is not written. gdn_gated_rmsnorm gives the same values
+ * as a separate pass.
+ *   weight  [dv] float32, the same for every head and token; 16-byte aligned
+ *   gate    o's shape ([B][Hv][T][dv] for prefill, [B][Hv][dv] for decode) in qkv_dtype, or
+ *           NULL for no gate factor; 16-byte aligned
+ *   eps     finite, >= 0
+ * weight and gate must not overlap any output. Fused into the output store of the segmented
+ * bf16 prefill (dk = 128, C in {32, 64}) and of decode when B * Hv >= 256 (a workgroup then
+ * owns whole output rows); the other paths apply it as one more pass over o after the scan.
+ * In the segmented prefill a row passes through float16 twice: before the norm, each group of
+ * 8 values scaled by a power of two taken from its own sum of squares (so one rounding to 11
+ * significant bits at any magnitude; the float32 sums of squares are not rounded), and after
+ * it (one more rounding of each normalised value, also with float32 o).
+ */
+typedef struct {
+    const float *weight;
+    const void *gate;
+    float eps;
+} gdn_norm;
+
+/*
  * Supported set (GDN_ERR_UNSUPPORTED otherwise):
  *   prefill:  dk = dv in {16, 32, 64, 128}, C in {16, 32, 64}, either dtype.
  *   decode:   dk = dv in {32, 64, 128}, either dtype.
@@ -177,6 +203,7 @@ int gdn_prefill_segments(const gdn_shape *shape, size_t workspace_bytes);
  *   workspace      device scratch of workspace_bytes bytes, 16-byte aligned, or NULL; the
  *                  segmented path uses as much of it as its segment count needs (above),
  *                  the other paths none. It must not overlap any other argument.
+ *   norm           the output norm (gdn_norm above), or NULL to write o as computed
  * A ragged batch passes every sequence padded to the common T with beta = 0,
  * g = 0 (and zero q/k/v) on the padded steps, which leave the state unchanged.
  * With initial_state == final_state (in place) every workgroup reads the state it starts
@@ -186,7 +213,7 @@ int gdn_prefill_segments(const gdn_shape *shape, size_t workspace_bytes);
 gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, const void *v,
                        const float *g, const float *beta, const void *initial_state,
                        void *o, void *final_state, void *workspace, size_t workspace_bytes,
-                       void *stream);
+                       const gdn_norm *norm, void *stream);
 
 /*
  * Prefill of B sequences of different lengths packed end to end along one token axis,
@@ -226,9 +253,11 @@ gdn_status gdn_prefill_varlen(const gdn_shape *shape, const int32_t *cu_seqlens,
  *   g, beta  [B][Hv]           float32
  *   state    [B][Hv][dv][dk]   state_dtype, read and overwritten
  *   o        [B][Hv][dv]       o_dtype, output; must not overlap any input or the state
+ *   norm     the output norm (gdn_norm above), or NULL to write o as computed
  */
 gdn_status gdn_decode(const gdn_shape *shape, const void *q, const void *k, const void *v,
-                      const float *g, const float *beta, void *state, void *o, void *stream);
+                      const float *g, const float *beta, void *state, void *o, const gdn_norm *norm,
+                      void *stream);
 
 /*
  * Per-channel decay (the KDA variant): the recurrence with one log-decay per key channel,
@@ -270,9 +299,9 @@ const char *gdn_last_error(void);
  * Supported: head_dim_v in {16, 32, 64, 128}. gate and weight must not overlap o.
  * Alignment: o, weight and a float32 gate 16 bytes; a bfloat16 gate 8 bytes with
  * float32 o and 16 bytes with float16 o.
- * Not fused into gdn_prefill: there the dv values of one output row come from
- * dv / 16 different workgroups, so the row's norm would need a reduction
- * across workgroups; this call is one extra streaming pass over o.
+ * The same norm is an optional argument of gdn_prefill and gdn_decode (gdn_norm), fused into
+ * their output stores where a workgroup owns whole output rows; this call is one extra
+ * streaming pass over o.
  */
 gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, void *o, const void *gate, const float *weight,
                              float eps, void *stream);

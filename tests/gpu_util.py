@@ -1,6 +1,8 @@
 """Helpers of the GPU parity tests: move seeded inputs to the device and compare."""
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 
 # Parity bars: max|got - ref| / max|ref| over all elements of a case.
@@ -39,3 +41,20 @@ def qkv_dev(x):
 
 def tol_for(x) -> float:
     return TOL_BF16 if x.qkv_dtype == "bf16" else TOL_F32
+
+
+def with_values(x, **kw):
+    """x with some arrays replaced (q, k, v given as float64 values, re-rounded to the dtype)."""
+    from gated_delta_rule_56_amd import inputs
+    upd = {}
+    for name in ("q", "k", "v"):
+        if name in kw:
+            f32 = np.asarray(kw.pop(name), dtype=np.float64).astype(np.float32)
+            if x.qkv_dtype == "bf16":
+                bits = inputs.bf16_round(f32)
+                upd[name], upd[name + "_bits"] = inputs.bf16_to_f32(bits), bits
+            else:
+                upd[name] = f32
+    for name, val in kw.items():
+        upd[name] = None if val is None else np.ascontiguousarray(val, dtype=np.float32)
+    return dataclasses.replace(x, **upd)

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib, bnd):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(1) == b"invalid argument"
     assert lib.gdn_status_string(2) == b"unsupported configuration"
@@ -58,11 +58,11 @@ GB = 1 << 30
 ADDR = dict(q=1 * GB, k=2 * GB, v=3 * GB, g=4 * GB, beta=5 * GB, s0=6 * GB, o=7 * GB, sf=8 * GB)
 
 
-def _prefill(lib, shape, ws=None, nbytes=0, **over):
+def _prefill(lib, shape, ws=None, nbytes=0, norm=None, **over):
     a = dict(ADDR)
     a.update(over)
     return lib.gdn_prefill(ctypes.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
-                           a["o"], a["sf"], ws, nbytes, None)
+                           a["o"], a["sf"], ws, nbytes, None if norm is None else ctypes.byref(norm), None)
 
 
 # A shape that splits into segments (2 chunks of 32, four value heads) and a misaligned
@@ -79,11 +79,11 @@ def _passes_until_workspace(lib, shape, **over):
     return st == 1 and "workspace is not 16-byte aligned" in _err(lib)
 
 
-def _decode(lib, shape, **over):
+def _decode(lib, shape, norm=None, **over):
     a = dict(ADDR)
     a.update(over)
     return lib.gdn_decode(ctypes.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
-                          a["o"], None)
+                          a["o"], None if norm is None else ctypes.byref(norm), None)
 
 
 def _err(lib):
@@ -111,7 +111,7 @@ def test_prefill_rejects_bad_shapes(lib, bnd, field, value, status, needle):
 
 
 def test_prefill_rejects_null_shape(lib):
-    assert lib.gdn_prefill(None, 1, 2, 3, 4, 5, 6, 7, 8, None, 0, None) == 1
+    assert lib.gdn_prefill(None, 1, 2, 3, 4, 5, 6, 7, 8, None, 0, None, None) == 1
     assert "shape" in _err(lib)
 
 
@@ -162,6 +162,42 @@ def test_decode_rejects(lib, bnd):
     assert _decode(lib, _shape(bnd, seq_len=1), s0=None) == 1 and "state is NULL" in _err(lib)
     assert _decode(lib, _shape(bnd, seq_len=1), o=ADDR["s0"] + 512) == 1 and "overlaps" in _err(lib)
     assert _decode(lib, _shape(bnd, seq_len=1), s0=ADDR["k"]) == 1 and "state overlaps k" in _err(lib)
+
+
+def _norm_arg(bnd, weight=10 * GB, gate=11 * GB, eps=1e-6):
+    n = bnd.GdnNorm()
+    n.weight, n.gate, n.eps = weight, gate, eps
+    return n
+
+
+def test_prefill_checks_norm(lib, bnd):
+    """The output norm: eps finite and >= 0, weight present and 16-byte aligned, gate NULL or
+    16-byte aligned, neither overlapping an output; a valid norm passes on to the workspace check."""
+    sh = _seg_shape(bnd)
+    for eps in (float("nan"), float("inf"), -1e-6):
+        assert _prefill(lib, sh, norm=_norm_arg(bnd, eps=eps)) == 1 and "norm eps" in _err(lib)
+    assert _prefill(lib, sh, norm=_norm_arg(bnd, weight=None)) == 1 and "norm weight is NULL" in _err(lib)
+    assert _prefill(lib, sh, norm=_norm_arg(bnd, weight=10 * GB + 8)) == 1 and "norm weight is not 16-byte" in _err(lib)
+    assert _prefill(lib, sh, norm=_norm_arg(bnd, gate=11 * GB + 4)) == 1 and "norm gate is not 16-byte" in _err(lib)
+    assert _prefill(lib, sh, norm=_norm_arg(bnd, gate=ADDR["o"] + 4096)) == 1
+    assert "overlaps" in _err(lib) and "norm gate" in _err(lib)
+    assert _prefill(lib, sh, norm=_norm_arg(bnd, weight=ADDR["sf"] + 256)) == 1
+    assert "overlaps" in _err(lib) and "norm weight" in _err(lib)
+    # the gate spans o's extent: B Hv T dv elements of the q/k/v type, here 4 * 64 * 128 * 2 bytes
+    assert _prefill(lib, sh, norm=_norm_arg(bnd, gate=ADDR["o"] - 4 * 64 * 128 * 2 + 16)) == 1
+    assert "overlaps" in _err(lib)
+    assert _passes_until_workspace(lib, sh, norm=_norm_arg(bnd, gate=ADDR["o"] - 4 * 64 * 128 * 2))
+    assert _passes_until_workspace(lib, sh, norm=_norm_arg(bnd, gate=None))
+
+
+def test_decode_checks_norm(lib, bnd):
+    sh = _shape(bnd, seq_len=1)
+    assert _decode(lib, sh, norm=_norm_arg(bnd, eps=float("nan"))) == 1 and "norm eps" in _err(lib)
+    assert _decode(lib, sh, norm=_norm_arg(bnd, weight=None)) == 1 and "norm weight is NULL" in _err(lib)
+    assert _decode(lib, sh, norm=_norm_arg(bnd, gate=ADDR["s0"] + 64)) == 1
+    assert "overlaps" in _err(lib) and "norm gate" in _err(lib)
+    assert _decode(lib, sh, norm=_norm_arg(bnd, weight=ADDR["o"])) == 1
+    assert "overlaps" in _err(lib) and "norm weight" in _err(lib)
 
 
 def _segments(B, Hv, T, C):

@@ -14,13 +14,11 @@ every prefill path and on decode (needs an MI355X):
   paths, finite and exact ones on the float32 path and on decode);
 * a prefill on a stream other than the current one, its workspace allocated by the binding.
 """
-import dataclasses
-
 import numpy as np
 import pytest
 
 from gated_delta_rule_56_amd import inputs
-from tests.gpu_util import TOL_BF16, TOL_F32, dev, qkv_dev, rel_err
+from tests.gpu_util import TOL_BF16, TOL_F32, dev, qkv_dev, rel_err, with_values
 
 pytestmark = pytest.mark.gpu
 
@@ -40,22 +38,6 @@ def gdn():
 # both chunk lengths, the fused chunk-16 MFMA kernel, the float32 VALU kernel
 PATHS = [("bf16", 64, 1), ("bf16", 64, 4), ("bf16", 32, 3), ("bf16", 16, 1), ("f32", 64, 1), ("f32", 16, 1)]
 PATH_IDS = [f"{d}-C{c}-P{p}" for d, c, p in PATHS]
-
-
-def with_values(x, **kw):
-    """x with some arrays replaced (q, k, v given as float64 values, re-rounded to the dtype)."""
-    upd = {}
-    for name in ("q", "k", "v"):
-        if name in kw:
-            f32 = np.asarray(kw.pop(name), dtype=np.float64).astype(np.float32)
-            if x.qkv_dtype == "bf16":
-                bits = inputs.bf16_round(f32)
-                upd[name], upd[name + "_bits"] = inputs.bf16_to_f32(bits), bits
-            else:
-                upd[name] = f32
-    for name, val in kw.items():
-        upd[name] = None if val is None else np.ascontiguousarray(val, dtype=np.float32)
-    return dataclasses.replace(x, **upd)
 
 
 def run_prefill(gdn, x, chunk, P):
