@@ -22,10 +22,13 @@ GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
 GDN_STATE_F32, GDN_STATE_F16 = 0, 1
 GDN_OUT_F32, GDN_OUT_F16 = 0, 1
 ABI_VERSION = 6
+# GDN_STATIC_SCRATCH_BYTES: the largest workspace_bytes of gdn_prefill_static
+STATIC_SCRATCH_BYTES = 96 << 20
 _STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
 _OUT_DTYPES = {torch.float32: GDN_OUT_F32, torch.float16: GDN_OUT_F16}
 
-EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill_segments", "gdn_prefill", "gdn_prefill_varlen_workspace_bytes",
+EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill_segments", "gdn_prefill", "gdn_prefill_static",
+                    "gdn_prefill_varlen_workspace_bytes",
                     "gdn_prefill_varlen", "gdn_decode", "gdn_kda_prefill", "gdn_kda_decode",
                     "gdn_gated_rmsnorm", "gdn_qkv_prologue", "gdn_status_string", "gdn_last_error",
                     "gdn_abi_version")
@@ -71,6 +74,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_prefill_segments.argtypes = [ctypes.POINTER(GdnShape), SZ]
     lib.gdn_prefill.restype = ctypes.c_int
     lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, SZ, ctypes.POINTER(GdnNorm), P]
+    lib.gdn_prefill_static.restype = ctypes.c_int
+    lib.gdn_prefill_static.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, SZ, ctypes.POINTER(GdnNorm), P]
     lib.gdn_prefill_varlen_workspace_bytes.restype = SZ
     lib.gdn_prefill_varlen_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
     lib.gdn_prefill_varlen.restype = ctypes.c_int
@@ -201,26 +206,10 @@ def prefill_segments(batch: int, seq_len: int, num_k_heads: int, num_v_heads: in
     return int(load_library().gdn_prefill_segments(ctypes.byref(shape), int(workspace_bytes)))
 
 
-def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-            initial_state: Optional[torch.Tensor] = None, *, chunk: int = 64, head_map: int = GDN_HEADS_TILED,
-            scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
-            final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
-            workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
-            o_dtype: torch.dtype = torch.float32, norm_weight: Optional[torch.Tensor] = None,
-            norm_gate: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
-            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """gdn_prefill on torch tensors.
-
-    q, k [B][Hk][T][d] and v [B][Hv][T][d] (bfloat16 or float32); g, beta [B][Hv][T] float32;
-    initial_state [B][Hv][d][d] float32 or float16, or None. Returns (o, final_state). Pass
-    final_state=initial_state to update a state in place. The states share one storage type:
-    that of the state tensors passed, else state_dtype (default float32). o is float32, or
-    float16 (o_dtype, or the type of the o passed). workspace: a uint8 device tensor of at
-    any size (prefill_workspace_bytes(...) gives the preferred one; less means fewer segments of
-    the sequence run in parallel, see prefill_segments), or None to allocate the preferred size
-    for this call. norm_weight [d] float32 (and optionally norm_gate, o's shape in the q/k/v
-    dtype) applies the gated RMSNorm to every output row before it is stored (gdn_norm).
-    """
+def _prefill_marshal(q, k, v, g, beta, initial_state, chunk, head_map, scale, o, final_state, write_final_state,
+                     state_dtype, o_dtype, norm_weight, norm_gate, norm_eps):
+    """Checks and shapes the arguments of gdn_prefill / gdn_prefill_static: returns
+    (lib, shape, o, final_state, norm)."""
     lib = load_library()
     dtype = q.dtype
     if dtype not in (torch.bfloat16, torch.float32):
@@ -258,6 +247,32 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
                        GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32, head_map, scale,
                        _STATE_DTYPES[sdt], _OUT_DTYPES[o.dtype])
     norm = _norm_arg(norm_weight, norm_gate, norm_eps, (B, Hv, T, d), dtype, d)
+    return lib, shape, o, final_state, norm
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+            initial_state: Optional[torch.Tensor] = None, *, chunk: int = 64, head_map: int = GDN_HEADS_TILED,
+            scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+            final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
+            workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
+            o_dtype: torch.dtype = torch.float32, norm_weight: Optional[torch.Tensor] = None,
+            norm_gate: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gdn_prefill on torch tensors.
+
+    q, k [B][Hk][T][d] and v [B][Hv][T][d] (bfloat16 or float32); g, beta [B][Hv][T] float32;
+    initial_state [B][Hv][d][d] float32 or float16, or None. Returns (o, final_state). Pass
+    final_state=initial_state to update a state in place. The states share one storage type:
+    that of the state tensors passed, else state_dtype (default float32). o is float32, or
+    float16 (o_dtype, or the type of the o passed). workspace: a uint8 device tensor of at
+    any size (prefill_workspace_bytes(...) gives the preferred one; less means fewer segments of
+    the sequence run in parallel, see prefill_segments), or None to allocate the preferred size
+    for this call. norm_weight [d] float32 (and optionally norm_gate, o's shape in the q/k/v
+    dtype) applies the gated RMSNorm to every output row before it is stored (gdn_norm).
+    """
+    lib, shape, o, final_state, norm = _prefill_marshal(q, k, v, g, beta, initial_state, chunk, head_map, scale, o,
+                                                        final_state, write_final_state, state_dtype, o_dtype,
+                                                        norm_weight, norm_gate, norm_eps)
     ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
     if workspace is None:
         workspace = _scratch(ws, q.device, stream) if ws else None
@@ -267,6 +282,29 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     _check(lib, lib.gdn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), ws,
                                 _norm_ref(norm), _stream_handle(stream)))
+    return o, final_state
+
+
+def prefill_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                   initial_state: Optional[torch.Tensor] = None, *, chunk: int = 64,
+                   head_map: int = GDN_HEADS_TILED, scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                   final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
+                   workspace_bytes: Optional[int] = None, state_dtype: Optional[torch.dtype] = None,
+                   o_dtype: torch.dtype = torch.float32, norm_weight: Optional[torch.Tensor] = None,
+                   norm_gate: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gdn_prefill_static on torch tensors: prefill() with the library's static device scratch
+    as the workspace, workspace_bytes of it (None: the preferred size; at most
+    STATIC_SCRATCH_BYTES). The library call allocates nothing; pass o (and final_state, or
+    write_final_state=False) to keep this wrapper from allocating them."""
+    lib, shape, o, final_state, norm = _prefill_marshal(q, k, v, g, beta, initial_state, chunk, head_map, scale, o,
+                                                        final_state, write_final_state, state_dtype, o_dtype,
+                                                        norm_weight, norm_gate, norm_eps)
+    if workspace_bytes is None:
+        workspace_bytes = lib.gdn_prefill_workspace_bytes(ctypes.byref(shape))
+    _check(lib, lib.gdn_prefill_static(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(initial_state), _ptr(o), _ptr(final_state), int(workspace_bytes),
+                                       _norm_ref(norm), _stream_handle(stream)))
     return o, final_state
 
 

@@ -20,7 +20,7 @@ ARCH = "gfx950"
 
 SOURCES = ["gdn_abi.cpp", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_prefill_mfma.hip",
            "gdn_prefill_chunk.hip", "gdn_prefill_scan.hip", "gdn_norm.hip",
-           "gdn_prologue.hip", "gdn_varlen.hip", "gdn_kda.hip", "gdn_prefill_seg.hip"]
+           "gdn_prologue.hip", "gdn_varlen.hip", "gdn_kda.hip", "gdn_prefill_seg.hip", "gdn_static.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

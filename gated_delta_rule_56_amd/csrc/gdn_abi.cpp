@@ -134,9 +134,15 @@ int gdn_prefill_segments(const gdn_shape *s, size_t workspace_bytes) {
     return gdn::seg_count(s->batch, s->num_v_heads, s->seq_len, s->chunk, workspace_bytes, true);
 }
 
-gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
-                       const float *beta, const void *initial_state, void *o, void *final_state,
-                       void *workspace, size_t workspace_bytes, const gdn_norm *norm, void *stream) {
+}  // extern "C"
+
+namespace {
+// gdn_prefill and gdn_prefill_static: with use_static, the workspace is the current GPU's static
+// scratch (looked up only when the segmented path uses one)
+gdn_status prefill_impl(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const void *initial_state, void *o, void *final_state,
+                        void *workspace, size_t workspace_bytes, const gdn_norm *norm, void *stream,
+                        bool use_static) {
     GDN_TRY(check_common(s));
     if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
     if (s->chunk != 16 && s->chunk != 32 && s->chunk != 64)
@@ -206,8 +212,12 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     // allows within the workspace the caller passes (one segment, no workspace, at the least)
     int P = 1;
     if (segmented_path(s)) {
-        P = gdn::seg_count(B, Hv, T, s->chunk, workspace_bytes, workspace != nullptr);
+        P = gdn::seg_count(B, Hv, T, s->chunk, workspace_bytes, use_static || workspace != nullptr);
         if (P > 1) {
+            if (use_static) {
+                const hipError_t e = gdn::static_scratch(&workspace);
+                if (e != hipSuccess) return fail(GDN_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+            }
             const int64_t used = gdn::seg_workspace_bytes(B * Hv, P);
             if (!aligned(workspace, 16)) return fail(GDN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
             const Range wsr[] = {range("workspace", workspace, used)};
@@ -250,6 +260,26 @@ gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const v
     }
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
     return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const void *initial_state, void *o, void *final_state,
+                       void *workspace, size_t workspace_bytes, const gdn_norm *norm, void *stream) {
+    return prefill_impl(s, q, k, v, g, beta, initial_state, o, final_state, workspace, workspace_bytes, norm,
+                        stream, false);
+}
+
+gdn_status gdn_prefill_static(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, const void *initial_state, void *o, void *final_state,
+                              size_t workspace_bytes, const gdn_norm *norm, void *stream) {
+    if (workspace_bytes > GDN_STATIC_SCRATCH_BYTES)
+        return fail(GDN_ERR_INVALID_ARG, "workspace_bytes %zu exceeds the static scratch of %zu bytes", workspace_bytes,
+                    (size_t)GDN_STATIC_SCRATCH_BYTES);
+    return prefill_impl(s, q, k, v, g, beta, initial_state, o, final_state, nullptr, workspace_bytes, norm, stream,
+                        true);
 }
 
 size_t gdn_prefill_varlen_workspace_bytes(const gdn_shape *s) {

@@ -116,6 +116,9 @@ int64_t seg_workspace_bytes(int64_t pairs, int P);
 // (at most one per chunk), reduced until their workspace fits workspace_bytes.
 int seg_count(int64_t B, int64_t Hv, int64_t T, int chunk, size_t workspace_bytes, bool have_workspace);
 hipError_t launch_prefill_seg(const PrefillParams &p, int chunk, int P, void *ws, hipStream_t stream);
+// device address of the current GPU's static scratch (GDN_STATIC_SCRATCH_BYTES), looked up on the
+// first call on each GPU and kept
+hipError_t static_scratch(void **out);
 
 hipError_t launch_prefill_scan(const PrefillParams &p, int chunk, const void *ws, hipStream_t stream);
 // fp32 VALU chunked kernel, chunk in {16, 32, 64}: f32 q/k/v with D in {16, 32, 64, 128},

@@ -216,6 +216,28 @@ gdn_status gdn_prefill(const gdn_shape *shape, const void *q, const void *k, con
                        const gdn_norm *norm, void *stream);
 
 /*
+ * gdn_prefill for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, hosts that forbid allocation): the same computation and arguments,
+ * except that the workspace is the library's own static scratch on the current GPU, of which
+ * the call uses workspace_bytes (the segment count follows it as in gdn_prefill; 0: one
+ * segment, no scratch). The call allocates nothing.
+ *   workspace_bytes  at most GDN_STATIC_SCRATCH_BYTES (96 MiB, which holds the preferred
+ *                    segment count of every shape, gdn_prefill_workspace_bytes);
+ *                    GDN_ERR_INVALID_ARG beyond it
+ * The scratch is one array per GPU, set aside when the library's code object is loaded on that
+ * GPU and held until the process ends; its address is looked up on the first call on each GPU
+ * (GDN_ERR_HIP if that fails). The stream must belong to the current device. Every call on a
+ * GPU shares its array and leaves its last contents there; no part of it needs to start at
+ * zero (every value the kernels read is written earlier in the same call). Calls that overlap
+ * in time on one GPU (on different streams, or from different host threads) race on it.
+ */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
+gdn_status gdn_prefill_static(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                              const float *g, const float *beta, const void *initial_state,
+                              void *o, void *final_state, size_t workspace_bytes,
+                              const gdn_norm *norm, void *stream);
+
+/*
  * Prefill of B sequences of different lengths packed end to end along one token axis,
  * without padding: sequence i holds tokens cu_seqlens[i] .. cu_seqlens[i + 1] - 1 and runs
  * as its own recurrence from initial state i. The result equals gdn_prefill on each

@@ -200,6 +200,27 @@ def test_decode_checks_norm(lib, bnd):
     assert "overlaps" in _err(lib) and "norm weight" in _err(lib)
 
 
+def _prefill_static(lib, shape, nbytes, **over):
+    a = dict(ADDR)
+    a.update(over)
+    return lib.gdn_prefill_static(ctypes.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"],
+                                  a["o"], a["sf"], nbytes, None, None)
+
+
+def test_prefill_static_rejects(lib, bnd):
+    """The allocation-free prefill: workspace_bytes beyond the static scratch (whose size the
+    message states, the binding's STATIC_SCRATCH_BYTES), and the checks it shares with
+    gdn_prefill, all before any device call."""
+    sh = _seg_shape(bnd)
+    assert _prefill_static(lib, sh, bnd.STATIC_SCRATCH_BYTES + 1) == 1
+    assert f"exceeds the static scratch of {bnd.STATIC_SCRATCH_BYTES} bytes" in _err(lib)
+    assert bnd.STATIC_SCRATCH_BYTES == 96 << 20
+    assert lib.gdn_prefill_static(None, 1, 2, 3, 4, 5, 6, 7, 8, 0, None, None) == 1 and "shape" in _err(lib)
+    assert _prefill_static(lib, sh, 1 << 20, o=None) == 1 and "o is NULL" in _err(lib)
+    assert _prefill_static(lib, _shape(bnd, chunk=48), 0) == 2 and "chunk" in _err(lib)
+    assert _prefill_static(lib, sh, 1 << 20, q=ADDR["o"]) == 1 and "overlaps" in _err(lib)
+
+
 def _segments(B, Hv, T, C):
     """Preferred segment count: enough output-pass workgroups for 256 CUs, at most one per
     chunk and 64."""
