@@ -932,41 +932,65 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
 
 // S_{p+1} = S_p M_p + N_p for p = 1 .. P-2, one workgroup per (pair, block of 16 rows), fp32.
 // Thread (r, cg) owns row r of the block, columns 8 cg .. 8 cg + 7. M_p goes through LDS; the
-// next map is loaded into registers while the current one is applied (only the chain of S is
-// sequential).
+// next map and the next N rows are loaded into registers while the current product runs, so
+// that only the chain of S (LDS and arithmetic) is sequential.
 __global__ __launch_bounds__(256) void gdn_seg_combine_kernel(SegParams sp) {
     extern __shared__ __attribute__((aligned(16))) unsigned char csmem[];
     float(*srow)[kD + 4] = reinterpret_cast<float(*)[kD + 4]>(csmem);
     float(*mt)[kD] = reinterpret_cast<float(*)[kD]>(csmem + 16 * (kD + 4) * 4);
-    const int pair = blockIdx.x >> 3, rb = blockIdx.x & 7;
+    // workgroups go round-robin over the 8 XCDs: the 8 row blocks of a pair share one XCD (and
+    // its L2 for the maps they all read) when the grid is a multiple of 64
+    const int nb = gridDim.x;
+    const int lin = (nb & 63) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    const int pair = lin >> 3, rb = lin & 7;
     const int tid = threadIdx.x, r = tid >> 4, cg = tid & 15;
     const int64_t base = (int64_t)pair * sp.P;
-    const float *s1 = sp.ws_start + (base + 1) * (kD * kD) + rb * 16 * kD;
-    for (int e = tid; e < 16 * kD; e += 256) srow[e / kD][e % kD] = s1[e];
     constexpr int kPer = kD * kD / 4 / 256;  // f32x4 of a map per thread
-    f32x4 mnext[kPer];
-    auto load_map = [&](int seg) {
+    f32x4 mnext[kPer], n0, n1;
+    auto load_next = [&](int seg) {  // this thread's 8 values of N_seg (first: needed first), M_seg
+        const float *N = sp.ws_n + (base + seg) * (kD * kD) + rb * 16 * kD + r * kD + 8 * cg;
+        n0 = *reinterpret_cast<const f32x4 *>(N);
+        n1 = *reinterpret_cast<const f32x4 *>(N + 4);
         const f32x4 *M = reinterpret_cast<const f32x4 *>(sp.ws_m + (base + seg) * (kD * kD));
 #pragma unroll
         for (int j = 0; j < kPer; ++j) mnext[j] = M[tid + 256 * j];
     };
-    if (sp.P > 2) load_map(1);
+    // S_1's rows of this block and the first map requested together
+    const float *s1 = sp.ws_start + (base + 1) * (kD * kD) + rb * 16 * kD + r * kD + 8 * cg;
+    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(s1), x1 = *reinterpret_cast<const f32x4 *>(s1 + 4);
+    load_next(1);
+    *reinterpret_cast<f32x4 *>(&srow[r][8 * cg]) = x0;
+    *reinterpret_cast<f32x4 *>(&srow[r][8 * cg + 4]) = x1;
     for (int seg = 1; seg + 1 < sp.P; ++seg) {
-        const float *N = sp.ws_n + (base + seg) * (kD * kD) + rb * 16 * kD;
         float *Sn = sp.ws_start + (base + seg + 1) * (kD * kD) + rb * 16 * kD;
-        f32x4 a0 = *reinterpret_cast<const f32x4 *>(N + r * kD + 8 * cg);
-        f32x4 a1 = *reinterpret_cast<const f32x4 *>(N + r * kD + 8 * cg + 4);
         __syncthreads();  // srow written; earlier reads of mt done
 #pragma unroll
         for (int j = 0; j < kPer; ++j) reinterpret_cast<f32x4 *>(&mt[0][0])[tid + 256 * j] = mnext[j];
-        if (seg + 2 < sp.P) load_map(seg + 1);
+        const f32x4 c0 = n0, c1 = n1;
+        if (seg + 2 < sp.P) load_next(seg + 1);
         __syncthreads();
-#pragma unroll 8
-        for (int k = 0; k < kD; ++k) {
-            const float sv = srow[r][k];
-            a0 += sv * *reinterpret_cast<const f32x4 *>(&mt[k][8 * cg]);
-            a1 += sv * *reinterpret_cast<const f32x4 *>(&mt[k][8 * cg + 4]);
+        // eight rows of the map per group, read into their own registers before they are used
+        // (with one buffer reused, every read would wait out the LDS latency)
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < kD; k0 += 8) {
+            const f32x4 sa = *reinterpret_cast<const f32x4 *>(&srow[r][k0]);
+            const f32x4 sb = *reinterpret_cast<const f32x4 *>(&srow[r][k0 + 4]);
+            f32x4 m0[8], m1[8];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                m0[kk] = *reinterpret_cast<const f32x4 *>(&mt[k0 + kk][8 * cg]);
+                m1[kk] = *reinterpret_cast<const f32x4 *>(&mt[k0 + kk][8 * cg + 4]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const float sv = kk < 4 ? sa[kk] : sb[kk - 4];
+                a0 += sv * m0[kk];
+                a1 += sv * m1[kk];
+            }
         }
+        a0 += c0;
+        a1 += c1;
         *reinterpret_cast<f32x4 *>(Sn + r * kD + 8 * cg) = a0;
         *reinterpret_cast<f32x4 *>(Sn + r * kD + 8 * cg + 4) = a1;
         __syncthreads();  // every read of srow done
@@ -974,6 +998,7 @@ __global__ __launch_bounds__(256) void gdn_seg_combine_kernel(SegParams sp) {
         *reinterpret_cast<f32x4 *>(&srow[r][8 * cg + 4]) = a1;
     }
 }
+
 constexpr size_t kCombineLds = 16 * (kD + 4) * 4 + kD * kD * 4;
 
 // T = 0: the final state is the initial state (converted to its storage type), or zero.
