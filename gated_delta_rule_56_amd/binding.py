@@ -21,7 +21,7 @@ GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
 GDN_STATE_F32, GDN_STATE_F16 = 0, 1
 GDN_OUT_F32, GDN_OUT_F16 = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 # GDN_STATIC_SCRATCH_BYTES: the largest workspace_bytes of gdn_prefill_static
 STATIC_SCRATCH_BYTES = 96 << 20
 _STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
@@ -81,7 +81,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gdn_prefill_varlen.restype = ctypes.c_int
     lib.gdn_prefill_varlen.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.gdn_kda_prefill.restype = ctypes.c_int
-    lib.gdn_kda_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P]
+    lib.gdn_kda_prefill.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P, P, SZ, P]
     lib.gdn_kda_decode.restype = ctypes.c_int
     lib.gdn_kda_decode.argtypes = [ctypes.POINTER(GdnShape), P, P, P, P, P, P, P, P]
     lib.gdn_decode.restype = ctypes.c_int
@@ -402,13 +402,15 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
 
 
 def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-                initial_state: Optional[torch.Tensor] = None, *, head_map: int = GDN_HEADS_TILED,
+                initial_state: Optional[torch.Tensor] = None, *, chunk: int = 32, head_map: int = GDN_HEADS_TILED,
                 scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
                 final_state: Optional[torch.Tensor] = None, write_final_state: bool = True,
-                state_dtype: Optional[torch.dtype] = None, o_dtype: torch.dtype = torch.float32,
-                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
+                o_dtype: torch.dtype = torch.float32, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """gdn_kda_prefill on torch tensors: as ``prefill`` with one log-decay per key channel,
-    g [B][Hv][T][dk] float32."""
+    g [B][Hv][T][dk] float32. bfloat16 with chunk 32 or 64 runs the chunked form (segment-
+    parallel within the workspace, None: the preferred size allocated for this call); chunk 16
+    or float32 runs token by token."""
     lib = load_library()
     dtype = q.dtype
     if dtype not in (torch.bfloat16, torch.float32):
@@ -440,10 +442,20 @@ def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
             raise ValueError("final_state must be [B][Hv][d][d]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    shape = make_shape(B, T, Hk, Hv, d, 0, GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32,
-                       head_map, scale, _STATE_DTYPES[sdt], _OUT_DTYPES[o.dtype])
+    qdt = GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32
+    shape = make_shape(B, T, Hk, Hv, d, chunk, qdt, head_map, scale, _STATE_DTYPES[sdt], _OUT_DTYPES[o.dtype])
+    ws = 0
+    if dtype == torch.bfloat16 and chunk in (32, 64):
+        ws_shape = make_shape(B, T, Hk, Hv, d, 32, qdt, head_map, scale, _STATE_DTYPES[sdt], _OUT_DTYPES[o.dtype])
+        ws = lib.gdn_prefill_workspace_bytes(ctypes.byref(ws_shape))
+    if workspace is None:
+        workspace = _scratch(ws, q.device, stream) if ws else None
+    else:
+        _dev_tensor(workspace, "workspace", torch.uint8)
+        ws = workspace.numel()
     _check(lib, lib.gdn_kda_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                    _ptr(initial_state), _ptr(o), _ptr(final_state), _stream_handle(stream)))
+                                    _ptr(initial_state), _ptr(o), _ptr(final_state), _ptr(workspace), ws,
+                                    _stream_handle(stream)))
     return o, final_state
 
 

@@ -526,7 +526,7 @@ gdn_status gdn_kda_decode(const gdn_shape *s, const void *q, const void *k, cons
 
 gdn_status gdn_kda_prefill(const gdn_shape *s, const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const void *initial_state, void *o, void *final_state,
-                           void *stream) {
+                           void *workspace, size_t workspace_bytes, void *stream) {
     GDN_TRY(check_common(s));
     if (s->seq_len < 0) return fail(GDN_ERR_INVALID_ARG, "seq_len must be >= 0 (got %d)", s->seq_len);
     const int d = s->head_dim_k;
@@ -562,6 +562,24 @@ gdn_status gdn_kda_prefill(const gdn_shape *s, const void *q, const void *k, con
         if (initial_state && final_state != initial_state && overlaps(out_s[0], ins[5]))
             return fail(GDN_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
     }
+    // bf16 with chunk 32 or 64: the chunked form in 32-token chunks, segment-parallel within the
+    // workspace given (as gdn_prefill); otherwise token by token
+    const bool chunked = bf16 && (s->chunk == 32 || s->chunk == 64);
+    int P = 1;
+    if (chunked) {
+        P = gdn::seg_count(B, Hv, T, 32, workspace_bytes, workspace != nullptr);
+        if (P > 1) {
+            const int64_t used = gdn::seg_workspace_bytes(B * Hv, P);
+            if (!aligned(workspace, 16)) return fail(GDN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+            const Range wsr[] = {range("workspace", workspace, used)};
+            GDN_TRY(check_no_overlap(wsr, 1, ins, 6));
+            GDN_TRY(check_no_overlap(wsr, 1, out_o, 1));
+            if (final_state) {
+                const Range fs[] = {range("final_state", final_state, st_bytes)};
+                GDN_TRY(check_no_overlap(wsr, 1, fs, 1));
+            }
+        }
+    }
     if (!final_state && T == 0) return GDN_OK;
     gdn::PrefillParams p;
     p.q = q;
@@ -582,7 +600,8 @@ gdn_status gdn_kda_prefill(const gdn_shape *s, const void *q, const void *k, con
     p.scale = s->scale;
     p.init_f16 = p.final_f16 = st16;
     p.o_f16 = o16;
-    const hipError_t err = gdn::launch_kda_prefill(p, bf16, static_cast<hipStream_t>(stream));
+    const hipError_t err = chunked ? gdn::launch_prefill_seg(p, 32, P, workspace, static_cast<hipStream_t>(stream), true)
+                                   : gdn::launch_kda_prefill(p, bf16, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
     return GDN_OK;
 }

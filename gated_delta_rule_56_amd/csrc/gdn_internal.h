@@ -115,7 +115,9 @@ int64_t seg_workspace_bytes(int64_t pairs, int P);
 // Segments used for this shape: as many as give every CU a workgroup in the output pass
 // (at most one per chunk), reduced until their workspace fits workspace_bytes.
 int seg_count(int64_t B, int64_t Hv, int64_t T, int chunk, size_t workspace_bytes, bool have_workspace);
-hipError_t launch_prefill_seg(const PrefillParams &p, int chunk, int P, void *ws, hipStream_t stream);
+// kda: g is [B][Hv][T][dk] (one log-decay per key channel; chunk 32 only)
+hipError_t launch_prefill_seg(const PrefillParams &p, int chunk, int P, void *ws, hipStream_t stream,
+                              bool kda = false);
 // device address of the current GPU's static scratch (GDN_STATIC_SCRATCH_BYTES), looked up on the
 // first call on each GPU and kept
 hipError_t static_scratch(void **out);

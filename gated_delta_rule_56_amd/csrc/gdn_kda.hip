@@ -314,9 +314,13 @@ void gdn_kda_prefill_kernel(PrefillParams p) {
 template <typename E>
 hipError_t launch_e(const PrefillParams &p, int64_t blocks, hipStream_t stream) {
     constexpr int bytes = KdaSmem<E>::kBytes;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_kda_prefill_kernel<E>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (err != hipSuccess) return err;
+    static bool attr_set = false;  // the attribute is a property of the function: set once
+    if (!attr_set) {
+        const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_kda_prefill_kernel<E>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
     hipLaunchKernelGGL((gdn_kda_prefill_kernel<E>), dim3((unsigned)blocks), dim3(kThreads), bytes, stream, p);
     return hipGetLastError();
 }

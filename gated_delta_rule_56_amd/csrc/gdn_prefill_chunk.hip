@@ -313,9 +313,13 @@ __global__ __launch_bounds__(C * 4) void gdn_chunk_prep_kernel(PrefillParams p, 
 template <int C>
 hipError_t launch_c(const PrefillParams &p, _Float16 *ws, hipStream_t stream) {
     const size_t bytes = PrepSmem<C>::kBytes;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_chunk_prep_kernel<C>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (err != hipSuccess) return err;
+    static bool attr_set = false;  // the attribute is a property of the function: set once
+    if (!attr_set) {
+        const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_chunk_prep_kernel<C>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
     const int64_t NC = p.chunks ? p.nchunks : (p.T + C - 1) / C;
     const int64_t nb = (p.chunks ? 1 : p.B) * p.Hk * NC;
     if (nb > 0x7fffffff) return hipErrorInvalidValue;

@@ -390,9 +390,13 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_mfma_kernel(PrefillParam
 template <int C>
 hipError_t launch_c(const PrefillParams &p, hipStream_t stream) {
     const size_t bytes = MfmaSmem<C>::kBytes;
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_prefill_mfma_kernel<C>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (err != hipSuccess) return err;
+    static bool attr_set = false;  // the attribute is a property of the function: set once
+    if (!attr_set) {
+        const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_prefill_mfma_kernel<C>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
     dim3 grid((unsigned)(p.B * p.Hv * (kD / kRows))), block(kThreads);
     hipLaunchKernelGGL((gdn_prefill_mfma_kernel<C>), grid, block, bytes, stream, p);
     return hipGetLastError();

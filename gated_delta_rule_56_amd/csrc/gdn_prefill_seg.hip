@@ -63,6 +63,7 @@ constexpr int kD = 128;
 constexpr int kSegThreads = 512;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // fragment block of token tile m, k block kb (kb <= m / 2), counted over the blocks on or
 // below the diagonal: (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
@@ -70,7 +71,21 @@ __host__ __device__ constexpr int fblk(int m, int kb) { return m + (m > 2 ? m - 
 // 16 x 16 block (m, j), j < m, of A below the diagonal: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 __host__ __device__ constexpr int ablk(int m, int j) { return m * (m - 1) / 2 + j; }
 
-template <int C, bool OUT, bool NORM = false>
+// channel vectors of a chunk (KDA; r0 = token 7, r1 = token 23, b = token 15, the last of tile 0,
+// C - 1 = token 31)
+constexpr int kVecR0 = 0;   // e^{G_r0}
+constexpr int kVecR1 = 1;   // e^{G_r1}
+constexpr int kVecCR0 = 2;  // e^{G_C-1 - G_r0}
+constexpr int kVecCR1 = 3;  // e^{G_C-1 - G_r1}
+constexpr int kVecR1B = 4;  // e^{G_r1 - G_b}
+constexpr int kVecBR0 = 5;  // e^{G_b - G_r0}
+constexpr int kVecC = 6;    // e^{G_C-1}
+constexpr int kNVec = 7;
+// the chunked per-channel-decay form takes log-decays below this as this: every factor of its
+// diagonal-block products then lies within e^{+-80}
+constexpr float kKdaGMin = -10.0f;
+
+template <int C, bool OUT, bool NORM = false, bool KDA = false>
 struct SegSmem {
     static constexpr int NT = C / 16, KBC = C / 32;
     static constexpr int kFr = fblk(NT - 1, (NT - 1) / 2) + 1;   // A_qk fragment blocks
@@ -84,21 +99,36 @@ struct SegSmem {
     static constexpr size_t oTd = oNA + 2 * kNA * 512;           // [2][NT][2][64] x 8 B: T_mm, diag(exp(G_C-G)) T_mm
     static constexpr size_t oG = oTd + 2 * NT * 1024;             // [2][5][C] f32: gamma, beta, exp(G_C-G), beta gamma, G
     static constexpr size_t oAt = oG + 2 * 20 * C;               // f32 [NT][16][20]: diagonal blocks of A, transposed
+    // per-channel decay (KDA): [2] k o e^{G_C - G} tiles (read transposed by the state update);
+    // the raw k and q tiles of the chunk being prepared (fp16, for the block products); [2]
+    // factors E[t][c] = e^{G_tc - G_rc}, r the 8th token of t's 16-token tile, f32 rows padded to
+    // 528 B; [2][kNVec][128] f32 channel vectors (kVec*); [2][128] f32 e^{G_C} for the row waves
+    static constexpr size_t kERow = 528;
+    static constexpr size_t oKT = oAt + NT * 16 * 20 * 4;
+    static constexpr size_t oRK = oKT + (KDA ? 2 * kTile : 0);
+    static constexpr size_t oRQ = oRK + (KDA ? kTile : 0);
+    static constexpr size_t oE = oRQ + (KDA && OUT ? kTile : 0);
+    static constexpr size_t oEV = oE + (KDA ? 2 * C * kERow : 0);
+    static constexpr size_t oEC = oEV + (KDA ? 2 * kNVec * 512 : 0);
     // output norm (NORM): a chunk's un-normalised o rows in fp16, each lane's 8 values scaled
     // by a power of two taken from their own sum of squares (stage_scale), rows padded to 272 B
     // so that the 8-byte accesses of 32 lanes (16 tokens, two column groups) meet all 64 banks;
     // the partial sums of squares [C][20] f32 (16 used: 4 row waves x 4 lanes of 8 columns);
     // the norm weight [128] f32
-    static constexpr size_t oNO = oAt + NT * 16 * 20 * 4;
+    static constexpr size_t oNO = oEC + (KDA ? 2 * 512 : 0);
     static constexpr size_t oNP = oNO + (NORM ? (size_t)C * 272 : 0);
     static constexpr size_t oNW = oNP + (NORM ? (size_t)C * 80 : 0);
     static constexpr size_t kBytes = oNW + (NORM ? 512 : 0);
     static_assert(!NORM || OUT, "the norm belongs to the output pass");
+    static_assert(!KDA || (C == 32 && !NORM), "the per-channel decay runs at C = 32, without the norm");
     static_assert(oQ % 16 == 0 && oV % 16 == 0 && oA % 16 == 0 && oNA % 16 == 0 && oTd % 16 == 0 &&
-                      oG % 16 == 0 && oAt % 16 == 0 && oNO % 16 == 0 && oNP % 16 == 0 && oNW % 16 == 0,
+                      oG % 16 == 0 && oAt % 16 == 0 && oKT % 16 == 0 && oRK % 16 == 0 && oRQ % 16 == 0 &&
+                      oE % 16 == 0 && oEV % 16 == 0 && oEC % 16 == 0 && oNO % 16 == 0 && oNP % 16 == 0 &&
+                      oNW % 16 == 0,
                   "alignment");
     static_assert(kBytes <= 160 * 1024, "LDS");
 };
+
 
 __device__ __forceinline__ f16x8 ld8(const unsigned char *p) { return *reinterpret_cast<const f16x8 *>(p); }
 __device__ __forceinline__ f16x4 ld4(const unsigned char *p) { return *reinterpret_cast<const f16x4 *>(p); }
@@ -243,10 +273,11 @@ __device__ __forceinline__ float stage_unscale(float ss) {
     return __uint_as_float((uint32_t)(127 - 14 + h) << 23);
 }
 
-// NORM: 0 no output norm, 1 the norm without a gate, 2 with a gate
-template <int C, bool OUT, int NORM = 0>
+// NORM: 0 no output norm, 1 the norm without a gate, 2 with a gate. KDA: one log-decay per key
+// channel (g [B][Hv][T][dk]), C = 32.
+template <int C, bool OUT, int NORM = 0, bool KDA = false>
 __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams sp) {
-    using L = SegSmem<C, OUT, (NORM > 0)>;
+    using L = SegSmem<C, OUT, (NORM > 0), KDA>;
     constexpr int NT = L::NT, KBC = L::KBC;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // every argument into a scalar local: a reference to the argument structure would make
@@ -403,6 +434,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
 
         lds_barrier();
         lds_barrier();
+        if constexpr (KDA) lds_barrier();  // the preparation waves' first factors
 
         auto interval = [&](auto sl, int i) __attribute__((always_inline)) {
             constexpr int s = decltype(sl)::value;
@@ -564,23 +596,36 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 ub[0][kb] = cat(ue[0][2 * kb], ue[0][2 * kb + 1]);
                 ub[1][kb] = cat(ue[1][2 * kb], ue[1][2 * kb + 1]);
             }
-            const float gC = *reinterpret_cast<const float *>(gt + 4 * (C - 1));
+            // per-channel decay: the state's columns decay by e^{G_C} each, and the update reads
+            // the k o e^{G_C - G} tile
+            const unsigned char *Ku = KDA ? smem + L::oKT + s * L::kTile : Kt;
+            if constexpr (KDA) {
+                const unsigned char *ec = smem + L::oEC + s * 512 + 16 * q4;
 #pragma unroll
-            for (int jt = 0; jt < 8; ++jt) {
-                S[0][jt] *= gC;
-                S[1][jt] *= gC;
+                for (int jt = 0; jt < 8; ++jt) {
+                    const f32x4 e = ldf4(ec + 64 * jt);  // columns 16 jt + 4 q4 .. + 3
+                    S[0][jt] *= e;
+                    S[1][jt] *= e;
+                }
+            } else {
+                const float gC = *reinterpret_cast<const float *>(gt + 4 * (C - 1));
+#pragma unroll
+                for (int jt = 0; jt < 8; ++jt) {
+                    S[0][jt] *= gC;
+                    S[1][jt] *= gC;
+                }
             }
             f16x8 kt[2][8];
 #pragma unroll
-            for (int jt = 0; jt < 8; ++jt) kt[0][jt] = cat(ld_tr(Kt + ta[jt]), ld_tr(Kt + ta[jt] + 4096));
+            for (int jt = 0; jt < 8; ++jt) kt[0][jt] = cat(ld_tr(Ku + ta[jt]), ld_tr(Ku + ta[jt] + 4096));
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) {
                 const int cur = kb & 1, nxt = cur ^ 1;
                 if (kb + 1 < KBC) {
 #pragma unroll
                     for (int jt = 0; jt < 8; ++jt)
-                        kt[nxt][jt] = cat(ld_tr(Kt + ta[jt] + (kb + 1) * 8192),
-                                          ld_tr(Kt + ta[jt] + (kb + 1) * 8192 + 4096));
+                        kt[nxt][jt] = cat(ld_tr(Ku + ta[jt] + (kb + 1) * 8192),
+                                          ld_tr(Ku + ta[jt] + (kb + 1) * 8192 + 4096));
                 }
                 fence();
 #pragma unroll
@@ -658,8 +703,54 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             // every prep wave loads them (only wave 4 uses them): unconditional loads keep the
             // wait counts before their use exact
             const int tg = min(c * C + lane, T - 1);
-            gr[sl] = gg[tg];
+            if constexpr (!KDA) gr[sl] = gg[tg];
             br[sl] = bgp[tg];
+        };
+        // per-channel decay: prep wave 6 loads the log-decays of a chunk one interval ahead (lane:
+        // channels 2 lane, 2 lane + 1, every token) and forms the chunk's factors E and channel
+        // vectors into slot sl (the chunk's parity): the inclusive prefix G over the chunk's
+        // tokens (log-decays below kKdaGMin taken as kKdaGMin, tokens past the end as 0), then
+        // E[t] = e^{G_t - G_r} with r = token 7 of t's tile, and the channel vectors kVec*
+        f32x2 gq[KDA ? C : 1];
+        const float *gch = KDA ? p.g + vtok * kD + 2 * lane : nullptr;
+        auto request_g = [&](int c) __attribute__((always_inline)) {
+            if constexpr (KDA) {
+#pragma unroll
+                for (int t = 0; t < C; ++t)
+                    gq[t] = *reinterpret_cast<const f32x2 *>(gch + (int64_t)min(c * C + t, T - 1) * kD);
+            }
+        };
+        auto form_factors = [&](int c, int sl) __attribute__((always_inline)) {
+            if constexpr (KDA) {
+                const int t0 = c * C;
+                f32x2 G = {0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const f32x2 x = gq[t];
+                    const bool live = t0 + t < T;
+                    G[0] += live ? fmaxf(x[0], kKdaGMin) : 0.f;
+                    G[1] += live ? fmaxf(x[1], kKdaGMin) : 0.f;
+                    gq[t] = G;
+                }
+                const f32x2 r0 = gq[7], r1 = gq[23], bd = gq[15], cl = gq[C - 1];
+                unsigned char *Es = smem + L::oE + sl * C * L::kERow + 8 * lane;
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const f32x2 r = t < 16 ? r0 : r1;
+                    *reinterpret_cast<f32x2 *>(Es + t * L::kERow) = f32x2{__expf(gq[t][0] - r[0]), __expf(gq[t][1] - r[1])};
+                }
+                unsigned char *EV = smem + L::oEV + sl * kNVec * 512 + 8 * lane;
+                auto put = [&](int v, f32x2 x) {
+                    *reinterpret_cast<f32x2 *>(EV + v * 512) = f32x2{__expf(x[0]), __expf(x[1])};
+                };
+                put(kVecR0, r0);
+                put(kVecR1, r1);
+                put(kVecCR0, cl - r0);
+                put(kVecCR1, cl - r1);
+                put(kVecR1B, r1 - bd);
+                put(kVecBR0, bd - r0);
+                put(kVecC, cl);
+            }
         };
         auto request_rows = [&](u16x8 (&r)[4], const uint16_t *src, int c) __attribute__((always_inline)) {
 #pragma unroll
@@ -728,7 +819,20 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         auto phase1 = [&](int c, int cn, auto sc) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
             const int t0 = c * C;
-            if (m == 0) {
+            if (KDA && m == 0) {
+                // per-channel decay: the decays live in the tiles and channel vectors; the token
+                // vectors are beta, with gamma = e^{G_C - G} = 1
+                const bool gl = lane < C && t0 + lane < T;
+                const float bv = gl ? br[s] : 0.f;
+                if (lane < C) {
+                    float *gts = reinterpret_cast<float *>(smem + L::oG + s * 20 * C);
+                    gts[lane] = 1.0f;
+                    gts[C + lane] = bv;
+                    gts[2 * C + lane] = 1.0f;
+                    gts[3 * C + lane] = bv;
+                    gts[4 * C + lane] = 0.0f;
+                }
+            } else if (m == 0) {
                 // G = inclusive prefix sum of g over the chunk; tokens past the end have g = beta = 0
                 const bool gl = lane < C && t0 + lane < T;
                 const float gv = gl ? gr[s] : 0.f, bv = gl ? br[s] : 0.f;
@@ -753,31 +857,85 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 // 32 Q + 16 + 4 g + 0..3: columns 8 p + 0..3 of this lane go to group
                 // 4 (p / 4) + 2 (p % 2), 8 p + 4..7 to the next group, both at byte 8 ((p / 2) % 2)
                 const int g0 = 4 * (lp >> 2) + 2 * (lp & 1), hb = 8 * ((lp >> 1) & 1);
+                if constexpr (KDA) {
+                    // per-channel decay: this lane's 8 channels 8 lp .. of each row as raw fp16 (for
+                    // the block products), scaled by e^{G} = E e^{G_r} (the X / Y operand tiles),
+                    // and k scaled by e^{G_C-1 - G} = e^{G_C-1 - G_r} / E (the update's tile)
+                    const unsigned char *Es = smem + L::oE + s * C * L::kERow + 32 * lp;
+                    const unsigned char *EV = smem + L::oEV + s * kNVec * 512;
+                    const int vr = m == 0 ? kVecR0 : kVecR1, vcr = m == 0 ? kVecCR0 : kVecCR1;
+                    const f32x4 eR0 = ldf4(EV + vr * 512 + 32 * lp), eR1 = ldf4(EV + vr * 512 + 32 * lp + 16);
+                    const f32x4 eC0 = ldf4(EV + vcr * 512 + 32 * lp), eC1 = ldf4(EV + vcr * 512 + 32 * lp + 16);
+                    if (m == 0 && lane < 32)  // e^{G_C-1} of the chunk for the row waves' state decay
+                        *reinterpret_cast<f32x4 *>(smem + L::oEC + s * 512 + 16 * lane) = ldf4(EV + kVecC * 512 + 16 * lane);
+                    auto put = [&](size_t base, int t, f32x4 x0, f32x4 x1) {
+                        const int sw = ksw(t & 15);
+                        unsigned char *row = smem + base + t * 256;
+                        *reinterpret_cast<f16x4 *>(row + (((g0 ^ sw) << 4) + hb)) = to_f16x4(x0);
+                        *reinterpret_cast<f16x4 *>(row + ((((g0 + 1) ^ sw) << 4) + hb)) = to_f16x4(x1);
+                    };
+                    auto widen = [](u16x8 a, f32x4 &x0, f32x4 &x1) {
+                        x0 = f32x4{bf16_bits_to_f32(a[0]), bf16_bits_to_f32(a[1]), bf16_bits_to_f32(a[2]), bf16_bits_to_f32(a[3])};
+                        x1 = f32x4{bf16_bits_to_f32(a[4]), bf16_bits_to_f32(a[5]), bf16_bits_to_f32(a[6]), bf16_bits_to_f32(a[7])};
+                    };
+                    auto rcp4 = [](f32x4 x) {
+                        return f32x4{__builtin_amdgcn_rcpf(x[0]), __builtin_amdgcn_rcpf(x[1]), __builtin_amdgcn_rcpf(x[2]),
+                                     __builtin_amdgcn_rcpf(x[3])};
+                    };
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * m + 4 * j + lrow;
-                    const int sw = ksw(t & 15);
-                    unsigned char *krow = smem + L::oK + s * L::kTile + t * 256;
-                    const u16x8 a = kr[j];
-                    *reinterpret_cast<f16x4 *>(krow + (((g0 ^ sw) << 4) + hb)) = bf4_to_h4(a[0], a[1], a[2], a[3]);
-                    *reinterpret_cast<f16x4 *>(krow + ((((g0 + 1) ^ sw) << 4) + hb)) = bf4_to_h4(a[4], a[5], a[6], a[7]);
-                }
-                fence();
-                request_rows(kr, kg, cn);
-                fence();
-                if (OUT) {
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 16 * m + 4 * j + lrow;
+                        const f32x4 E0 = ldf4(Es + t * L::kERow), E1 = ldf4(Es + t * L::kERow + 16);
+                        f32x4 x0, x1;
+                        widen(kr[j], x0, x1);
+                        put(L::oRK, t, x0, x1);
+                        put(L::oK + s * L::kTile, t, x0 * E0 * eR0, x1 * E1 * eR1);
+                        put(L::oKT + s * L::kTile, t, x0 * rcp4(E0) * eC0, x1 * rcp4(E1) * eC1);
+                    }
+                    fence();
+                    request_rows(kr, kg, cn);
+                    fence();
+                    if (OUT) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int t = 16 * m + 4 * j + lrow;
+                            const f32x4 E0 = ldf4(Es + t * L::kERow), E1 = ldf4(Es + t * L::kERow + 16);
+                            f32x4 x0, x1;
+                            widen(qr[j], x0, x1);
+                            put(L::oRQ, t, x0, x1);
+                            put(L::oQ + s * L::kTile, t, x0 * E0 * eR0, x1 * E1 * eR1);
+                        }
+                        fence();
+                        request_rows(qr, qg, cn);
+                        fence();
+                    }
+                } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int t = 16 * m + 4 * j + lrow;
                         const int sw = ksw(t & 15);
-                        unsigned char *qrow = smem + L::oQ + s * L::kTile + t * 256;
-                        const u16x8 b = qr[j];
-                        *reinterpret_cast<f16x4 *>(qrow + (((g0 ^ sw) << 4) + hb)) = bf4_to_h4(b[0], b[1], b[2], b[3]);
-                        *reinterpret_cast<f16x4 *>(qrow + ((((g0 + 1) ^ sw) << 4) + hb)) = bf4_to_h4(b[4], b[5], b[6], b[7]);
+                        unsigned char *krow = smem + L::oK + s * L::kTile + t * 256;
+                        const u16x8 a = kr[j];
+                        *reinterpret_cast<f16x4 *>(krow + (((g0 ^ sw) << 4) + hb)) = bf4_to_h4(a[0], a[1], a[2], a[3]);
+                        *reinterpret_cast<f16x4 *>(krow + ((((g0 + 1) ^ sw) << 4) + hb)) = bf4_to_h4(a[4], a[5], a[6], a[7]);
                     }
                     fence();
-                    request_rows(qr, qg, cn);
+                    request_rows(kr, kg, cn);
                     fence();
+                    if (OUT) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int t = 16 * m + 4 * j + lrow;
+                            const int sw = ksw(t & 15);
+                            unsigned char *qrow = smem + L::oQ + s * L::kTile + t * 256;
+                            const u16x8 b = qr[j];
+                            *reinterpret_cast<f16x4 *>(qrow + (((g0 ^ sw) << 4) + hb)) = bf4_to_h4(b[0], b[1], b[2], b[3]);
+                            *reinterpret_cast<f16x4 *>(qrow + ((((g0 + 1) ^ sw) << 4) + hb)) = bf4_to_h4(b[4], b[5], b[6], b[7]);
+                        }
+                        fence();
+                        request_rows(qr, qg, cn);
+                        fence();
+                    }
                 }
                 if (has_v) {
 #pragma unroll
@@ -788,6 +946,14 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     fence();
                     request_rows(vr, vg, cn);
                     fence();
+                }
+            }
+            if constexpr (KDA) {
+                // the factors of chunk cn into the other slot (its parity), from the log-decays
+                // loaded during the last interval; then those of the chunk after it requested
+                if (m == 2) {
+                    form_factors(cn, 1 - s);
+                    request_g(min(cn + 1, cb + max(n, 1) - 1));
                 }
             }
         };
@@ -891,17 +1057,104 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(egt * tq);
             }
         };
+        // P2, per-channel decay (C = 32): W0 the block (0,0), W1 (1,1), W2 (1,0), in float32 from the
+        // raw k, q tiles and the factors: block (m, m) as (k o 1/E)(k o E)^T with E relative to the
+        // tile's 8th token (every factor within e^{+-80}), block (1,0) relative to the last token b of
+        // tile 0, (k o e^{G_b - G})(k o e^{G - G_b})^T = (k o e^{G_b - G_r0} / E)(k o E e^{G_r1 - G_b})^T,
+        // whose operands are decays (<= 1). Lane (q4, li) supplies row li of both operands for k = q4:
+        // channels 4 rho .. + 3 of run rho = 4 blk + q4 over the eight runs' steps.
+        auto phase2k = [&](int s, auto wc) __attribute__((always_inline)) {
+            constexpr int W = decltype(wc)::value;
+            if constexpr (KDA && W < 3) {
+                constexpr int MM = W == 0 ? 0 : 1, NB = W == 1 ? 1 : 0;
+                const int ts = 16 * NB + li, tt = 16 * MM + li;  // A-operand token, B-operand token
+                const unsigned char *Es = smem + L::oE + s * C * L::kERow;
+                const unsigned char *EV = smem + L::oEV + s * kNVec * 512;
+                const float *gts = reinterpret_cast<const float *>(smem + L::oG + s * 20 * C);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int blk = 0; blk < 8; ++blk) {
+                    const int rho = 4 * blk + q4;
+                    const int grp = 4 * (rho >> 3) + (rho & 3), half = 8 * ((rho >> 2) & 1);
+                    const f16x4 ks = ld4(smem + L::oRK + ts * 256 + ((grp ^ ksw(ts & 15)) << 4) + half);
+                    const f16x4 kt = ld4(smem + L::oRK + tt * 256 + ((grp ^ ksw(tt & 15)) << 4) + half);
+                    f16x4 qt = {};
+                    if (OUT) qt = ld4(smem + L::oRQ + tt * 256 + ((grp ^ ksw(tt & 15)) << 4) + half);
+                    const f32x4 es = ldf4(Es + ts * L::kERow + 16 * rho);
+                    f32x4 et = ldf4(Es + tt * L::kERow + 16 * rho), fs = {1.f, 1.f, 1.f, 1.f};
+                    if constexpr (W == 2) {
+                        et *= ldf4(EV + kVecR1B * 512 + 16 * rho);
+                        fs = ldf4(EV + kVecBR0 * 512 + 16 * rho);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float a = (float)ks[e] * (__builtin_amdgcn_rcpf(es[e]) * fs[e]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, (float)kt[e] * et[e], acc, 0, 0, 0);
+                        if (OUT) accq = __builtin_amdgcn_mfma_f32_16x16x4f32(a, (float)qt[e] * et[e], accq, 0, 0, 0);
+                    }
+                }
+                // lane (q4, li), element r: s = 16 NB + 4 q4 + r, t = 16 MM + li
+                const float bt = gts[C + 16 * MM + li], sct = p.scale;
+                f32x4 a, aqv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int sidx = 4 * q4 + r;
+                    a[r] = (W == 2 || sidx < li) ? bt * acc[r] : 0.0f;
+                    aqv[r] = (W == 2 || sidx <= li) ? sct * accq[r] : 0.0f;
+                }
+                if (OUT) {
+                    unsigned char *aqb = smem + L::oA + s * L::kFr * 1024 + lane * 16;
+                    *reinterpret_cast<f16x4 *>(aqb + fblk(MM, NB / 2) * 1024 + (NB & 1) * 8) = to_f16x4(aqv);
+                    if constexpr (W == 0) *reinterpret_cast<f16x4 *>(aqb + fblk(0, 0) * 1024 + 8) = f16x4{};
+                }
+                if constexpr (W == 2) {
+                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(1, 0) * 512 + lane * 8) =
+                        to_f16x4(-a);
+                } else {
+                    // T_MM = (I + A_MM)^{-1}, as for the scalar decay (Td's scaled copy is T itself:
+                    // the update's decay is in its k tile)
+                    float *at = reinterpret_cast<float *>(smem + L::oAt) + MM * 16 * 20;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) at[(4 * q4 + r) * 20 + li] = -a[r];
+                    float nrow[16];
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) nrow[k] = at[k * 20 + li];
+                    f32x4 tq;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tq[e] = 4 * q4 + e == li ? 1.0f : 0.0f;
+                    inv_rows(tq, nrow);
+                    unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + MM * 1024 + lane * 8;
+                    *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
+                    *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(tq);
+                }
+            }
+        };
         auto phase2 = [&](int s) __attribute__((always_inline)) {
-            if (m == 0) phase2w(s, IC<0>{});
-            else if (m == 1) phase2w(s, IC<1>{});
-            else if (m == 2) phase2w(s, IC<2>{});
-            else phase2w(s, IC<3>{});
+            if constexpr (KDA) {
+                if (m == 0) phase2k(s, IC<0>{});
+                else if (m == 1) phase2k(s, IC<1>{});
+                else if (m == 2) phase2k(s, IC<2>{});
+            } else {
+                if (m == 0) phase2w(s, IC<0>{});
+                else if (m == 1) phase2w(s, IC<1>{});
+                else if (m == 2) phase2w(s, IC<2>{});
+                else phase2w(s, IC<3>{});
+            }
         };
 
         // prologue: chunk 0 of the segment into slot 0. Every load is issued and every P1 runs, the
         // chunk indices clamped to the segment (a clamped P1 fills the slot no one reads next),
         // so that the loop carries no register whose load is optional.
         const int clast = cb + max(n, 1) - 1;
+        if constexpr (KDA) {
+            // the first chunk's factors before its rows are converted
+            if (m == 2) {
+                request_g(cb);
+                form_factors(cb, 0);
+                request_g(min(cb + 1, clast));
+            }
+            lds_barrier();
+        }
         request_gate(cb);
         issue(cb);
         phase1(cb, min(cb + 1, clast), IC<0>{});
@@ -1010,28 +1263,28 @@ __global__ __launch_bounds__(256) void gdn_state_copy_kernel(PrefillParams p, in
     store_state4(p.final_state, i, x, p.final_f16);
 }
 
-template <int C, bool OUT, int NORM = 0>
+template <int C, bool OUT, int NORM = 0, bool KDA = false>
 hipError_t launch_pass(const SegParams &sp, int64_t nblocks, hipStream_t stream) {
-    const size_t bytes = SegSmem<C, OUT, (NORM > 0)>::kBytes;
+    const size_t bytes = SegSmem<C, OUT, (NORM > 0), KDA>::kBytes;
     static bool attr_set = false;  // the attribute is a property of the function: set once
     if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_seg_pass_kernel<C, OUT, NORM>),
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gdn_seg_pass_kernel<C, OUT, NORM, KDA>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
         if (err != hipSuccess) return err;
         attr_set = true;
     }
     if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gdn_seg_pass_kernel<C, OUT, NORM>), dim3((unsigned)nblocks), dim3(kSegThreads), bytes, stream,
-                       sp);
+    hipLaunchKernelGGL((gdn_seg_pass_kernel<C, OUT, NORM, KDA>), dim3((unsigned)nblocks), dim3(kSegThreads), bytes,
+                       stream, sp);
     return hipGetLastError();
 }
 
-template <int C>
+template <int C, bool KDA = false>
 hipError_t launch_seg_c(const SegParams &sp, hipStream_t stream) {
     const int64_t pairs = (int64_t)sp.p.B * sp.p.Hv;
     hipError_t err = hipSuccess;
     if (sp.P > 1) {
-        err = launch_pass<C, false>(sp, pairs * (2 * sp.P - 3), stream);
+        err = launch_pass<C, false, 0, KDA>(sp, pairs * (2 * sp.P - 3), stream);
         if (err != hipSuccess) return err;
         if (sp.P > 2) {
             static bool attr_set = false;
@@ -1046,9 +1299,13 @@ hipError_t launch_seg_c(const SegParams &sp, hipStream_t stream) {
             if (err != hipSuccess) return err;
         }
     }
-    if (!sp.p.norm_w) return launch_pass<C, true>(sp, pairs * sp.P, stream);
-    return sp.p.norm_gate ? launch_pass<C, true, 2>(sp, pairs * sp.P, stream)
-                          : launch_pass<C, true, 1>(sp, pairs * sp.P, stream);
+    if constexpr (KDA) {
+        return launch_pass<C, true, 0, true>(sp, pairs * sp.P, stream);
+    } else {
+        if (!sp.p.norm_w) return launch_pass<C, true>(sp, pairs * sp.P, stream);
+        return sp.p.norm_gate ? launch_pass<C, true, 2>(sp, pairs * sp.P, stream)
+                              : launch_pass<C, true, 1>(sp, pairs * sp.P, stream);
+    }
 }
 
 }  // namespace
@@ -1070,7 +1327,7 @@ int seg_count(int64_t B, int64_t Hv, int64_t T, int chunk, size_t workspace_byte
     return (int)((nc + per - 1) / per);
 }
 
-hipError_t launch_prefill_seg(const PrefillParams &p, int chunk, int P, void *ws, hipStream_t stream) {
+hipError_t launch_prefill_seg(const PrefillParams &p, int chunk, int P, void *ws, hipStream_t stream, bool kda) {
     if (p.D != kD) return hipErrorInvalidValue;
     if (p.T == 0) {
         if (!p.final_state) return hipSuccess;
@@ -1089,6 +1346,7 @@ hipError_t launch_prefill_seg(const PrefillParams &p, int chunk, int P, void *ws
     sp.ws_start = w;
     sp.ws_n = w + pairs * P * kD * kD;
     sp.ws_m = w + 2 * pairs * P * kD * kD;
+    if (kda) return chunk == 32 ? launch_seg_c<32, true>(sp, stream) : hipErrorInvalidValue;
     switch (chunk) {
         case 32: return launch_seg_c<32>(sp, stream);
         case 64: return launch_seg_c<64>(sp, stream);

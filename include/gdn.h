@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum {
     GDN_OK = 0,
@@ -289,15 +289,23 @@ gdn_status gdn_decode(const gdn_shape *shape, const void *q, const void *k, cons
  * is the gated delta rule with its scalar decay made diagonal over the key channels (with
  * every channel of g_t equal it is gdn_prefill / gdn_decode). Layouts as gdn_prefill and
  * gdn_decode except g:
- *   gdn_kda_prefill  g [B][Hv][T][dk] float32, 16-byte aligned; no workspace, shape->chunk
- *                    ignored (the prefill runs token by token)
+ *   gdn_kda_prefill  g [B][Hv][T][dk] float32, 16-byte aligned. bfloat16 q/k/v with chunk
+ *                    32 or 64: the chunked (WY) form in 32-token chunks on MFMA, segment-
+ *                    parallel within the workspace passed (as gdn_prefill: query
+ *                    gdn_prefill_workspace_bytes and gdn_prefill_segments with the same shape
+ *                    and chunk 32; any size, NULL included, is valid). It takes every log-decay
+ *                    below -10 as -10 (a step keeping less than e^-10 = 4.5e-5 of a state
+ *                    channel keeps that much of it), which bounds the factors of its intra-
+ *                    chunk products within e^(+-80). float32 q/k/v, or chunk 16: token by
+ *                    token, exact for any decay, no workspace used.
  *   gdn_kda_decode   g [B][Hv][dk] float32, 16-byte aligned
  * Supported: dk = dv = 128 for the prefill (32, 64 or 128 for decode), bfloat16 or float32
  * q/k/v, both state and output storage types.
  */
 gdn_status gdn_kda_prefill(const gdn_shape *shape, const void *q, const void *k, const void *v,
-                           const float *g, const float *beta, const void *initial_state, void *o,
-                           void *final_state, void *stream);
+                           const float *g, const float *beta, const void *initial_state,
+                           void *o, void *final_state, void *workspace, size_t workspace_bytes,
+                           void *stream);
 gdn_status gdn_kda_decode(const gdn_shape *shape, const void *q, const void *k, const void *v,
                           const float *g, const float *beta, void *state, void *o, void *stream);
 

@@ -143,3 +143,127 @@ def segmented_prefill(q, k, v, g, beta, s0, scale, chunk, P, head_map=0):
                 S = run(starts[b, h, p], *bounds[p], out=True)
             S_out[b, h] = S
     return o, S_out, starts
+
+
+# ---- per-channel decay (KDA): S_t = S_{t-1} diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+#
+# With G [C][dk] the per-channel prefix of g inside a chunk and u_t = beta_t (v_t - S_{t-1}
+# diag(alpha_t) k_t), S_t = S diag(e^{G_t}) + sum_{s<=t} u_s (k_s o e^{G_t - G_s})^T, so
+# (I + A) U = R with
+#   A[t, s]   = beta_t sum_c k_tc k_sc e^{G_tc - G_sc}          (s < t)
+#   R         = diag(beta) (V - (K o e^G) S^T)
+#   O         = scale (Q o e^G) S^T + A_qk U,  A_qk[t, s] = scale sum_c q_tc k_sc e^{G_tc - G_sc} (s <= t)
+#   S        <- S diag(e^{G_C}) + U^T (K o e^{G_C - G}).
+# The decays inside A and A_qk differ per channel, so they cannot be a mask on K K^T; the kernel
+# forms them from scaled operands (kda_blocks_factored), which needs every factor in range.
+
+KDA_G_MIN = -10.0  # the chunked form takes log-decays below this as this (see kda_blocks_factored)
+KDA_TILE = 16
+
+
+def kda_blocks_exact(Q, K, G, bc, scale):
+    """A (strict lower, with beta) and A_qk (lower incl., with scale) from the pairwise decays."""
+    C = K.shape[0]
+    A = np.zeros((C, C))
+    Aqk = np.zeros((C, C))
+    for t in range(C):
+        for s in range(t + 1):
+            f = np.exp(G[t] - G[s])
+            if s < t:
+                A[t, s] = bc[t] * np.dot(K[t] * f, K[s])
+            Aqk[t, s] = scale * np.dot(Q[t] * f, K[s])
+    return A, Aqk
+
+
+def kda_blocks_factored(Q, K, G, bc, scale, tile=KDA_TILE):
+    """The same blocks as 16 x 16 tiles of products of scaled operands, as the kernel forms them:
+
+    * block (m, j), j < m: reference b = the last token of tile m - 1; left k_t o e^{G_t - G_b}
+      (t in tile m, a decay, <= 1), right k_s o e^{G_b - G_s} (s <= b, <= 1): both fit float16;
+    * block (m, m): reference r = token 7 of the tile; left k_t o e^{G_t - G_r}, right
+      k_s o e^{G_r - G_s}: factors between e^{-8 |g|max} and e^{8 |g|max}, inside float32 range
+      (e^{+-80}) when every log-decay is >= KDA_G_MIN = -10; formed in float32.
+    Returns (A, A_qk, the largest |exponent| used in a diagonal tile)."""
+    C, dk = K.shape
+    A = np.zeros((C, C))
+    Aqk = np.zeros((C, C))
+    big = 0.0
+    for m in range(C // tile):
+        tm = slice(tile * m, tile * (m + 1))
+        r = tile * m + tile // 2 - 1
+        e_l, e_r = G[tm] - G[r], G[r] - G[tm]
+        big = max(big, float(np.max(np.abs(e_l))))
+        L, Lq, Rt = K[tm] * np.exp(e_l), Q[tm] * np.exp(e_l), K[tm] * np.exp(e_r)
+        A[tm, tm] = np.tril(bc[tm, None] * (L @ Rt.T), -1)
+        Aqk[tm, tm] = np.tril(scale * (Lq @ Rt.T))
+        if m > 0:
+            b = tile * m - 1
+            Lo, Loq = K[tm] * np.exp(G[tm] - G[b]), Q[tm] * np.exp(G[tm] - G[b])
+            Ro = K[:tile * m] * np.exp(G[b] - G[:tile * m])
+            A[tm, :tile * m] = bc[tm, None] * (Lo @ Ro.T)
+            Aqk[tm, :tile * m] = scale * (Loq @ Ro.T)
+    return A, Aqk, big
+
+
+def kda_chunk_step(S, Q, K, V, gc, bc, scale, factored=False):
+    """One chunk of the per-channel-decay WY form (gc [C][dk]); returns (O, S at the chunk end).
+    factored: the blocks as the kernel forms them (chunk a multiple of KDA_TILE)."""
+    G = np.cumsum(gc, axis=0)
+    if factored:
+        A, Aqk, _ = kda_blocks_factored(Q, K, G, bc, scale)
+    else:
+        A, Aqk = kda_blocks_exact(Q, K, G, bc, scale)
+    Tm = inverse_unit_lower(-A)
+    R = bc[:, None] * (V - (K * np.exp(G)) @ S.T)
+    U = Tm @ R
+    O = scale * (Q * np.exp(G)) @ S.T + Aqk @ U
+    S = S * np.exp(G[-1])[None, :] + U.T @ (K * np.exp(G[-1] - G))
+    return O, S
+
+
+def _kda_chunk(x, b, h, kh, t0, C):
+    q, k, v, g, beta = x
+    T, dk = q.shape[2], q.shape[3]
+    n = max(0, min(C, T - t0))
+    Q, K, V, _, bc, _ = _chunk((q, k, v, np.zeros(beta.shape), beta), b, h, kh, t0, C)
+    gc = np.zeros((C, dk))
+    gc[:n] = g[b, h, t0:t0 + n]
+    return Q, K, V, gc, bc, n
+
+
+def kda_chunked_prefill(q, k, v, g, beta, s0, scale, chunk, head_map=0, factored=False, clamp=False, P=1):
+    """Chunked per-channel-decay prefill in float64 (g [B][Hv][T][dk]); clamp: log-decays below
+    KDA_G_MIN taken as KDA_G_MIN; P > 1: run as P segments through their affine maps, as the
+    segmented prefill does. Returns (o, s_final)."""
+    B, Hk, T, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[3]
+    C = chunk
+    g = np.maximum(g, KDA_G_MIN) if clamp else g
+    x = (q, k, v, g, beta)
+    bounds = segment_bounds(T, C, P)
+    o = np.zeros((B, Hv, T, dv))
+    S_out = np.zeros((B, Hv, dv, dk))
+    for b in range(B):
+        for h in range(Hv):
+            kh = h % Hk if head_map == 0 else h // (Hv // Hk)
+            S0 = np.zeros((dv, dk)) if s0 is None else np.array(s0[b, h], dtype=np.float64)
+
+            def run(S, c0, c1, with_v=True, out=False):
+                for c in range(c0, c1):
+                    Q, K, V, gc, bc, n = _kda_chunk(x, b, h, kh, c * C, C)
+                    O, S = kda_chunk_step(S, Q, K, V if with_v else np.zeros_like(V), gc, bc, scale, factored)
+                    if out:
+                        o[b, h, c * C:c * C + n] = O[:n]
+                return S
+
+            starts = [S0]
+            if P > 1:
+                starts.append(run(S0, *bounds[0]))
+            for p in range(1, P - 1):
+                N = run(np.zeros((dv, dk)), *bounds[p])
+                M = run(np.eye(dk), *bounds[p], with_v=False)
+                starts.append(starts[p] @ M + N)
+            for p in range(P):
+                S = run(starts[p], *bounds[p], out=True)
+            S_out[b, h] = S
+    return o, S_out

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib, bnd):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn_abi_version() == 6
+    assert lib.gdn_abi_version() == 7
     assert lib.gdn_status_string(0) == b"ok"
     assert lib.gdn_status_string(1) == b"invalid argument"
     assert lib.gdn_status_string(2) == b"unsupported configuration"
@@ -382,11 +382,20 @@ def test_kda_rejects(lib, bnd):
     a = ADDR
     shape = _shape(bnd, seq_len=10)
     call = lambda sh, **o: lib.gdn_kda_prefill(ctypes.byref(sh), a["q"], a["k"], a["v"], o.get("g", a["g"]), a["beta"],
-                                                a["s0"], o.get("o", a["o"]), a["sf"], None)
+                                                a["s0"], o.get("o", a["o"]), a["sf"], o.get("ws"), o.get("nbytes", 0),
+                                                None)
     assert call(_shape(bnd, seq_len=10, head_dim=64)) == 2 and "head_dim" in _err(lib)
     assert call(shape, g=a["g"] + 4) == 1 and "aligned" in _err(lib)  # per-channel g: 16-byte aligned
     assert call(shape, g=None) == 1 and "g is NULL" in _err(lib)
     assert call(shape, o=a["g"] + 4096) == 1 and "o overlaps g" in _err(lib)
+    # the chunked bf16 form (chunk 32 or 64) splits into segments within the workspace like
+    # gdn_prefill: two 32-token chunks of four value heads take two segments
+    two = _shape(bnd, seq_len=64, chunk=32)
+    need = lib.gdn_prefill_workspace_bytes(ctypes.byref(two))
+    assert need == _ws_bytes(1, 4, 2)
+    assert call(two, ws=9 * GB + 8, nbytes=need) == 1 and "workspace is not 16-byte aligned" in _err(lib)
+    assert call(_shape(bnd, seq_len=64, chunk=64), ws=9 * GB + 8, nbytes=need) == 1 and "16-byte" in _err(lib)
+    assert call(two, ws=a["v"], nbytes=need) == 1 and "overlaps" in _err(lib)
     dec = lambda sh, **o: lib.gdn_kda_decode(ctypes.byref(sh), a["q"], a["k"], a["v"], o.get("g", a["g"]), a["beta"],
                                              a["s0"], o.get("o", a["o"]), None)
     assert dec(_shape(bnd, seq_len=2)) == 1 and "seq_len" in _err(lib)

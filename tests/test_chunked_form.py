@@ -76,3 +76,56 @@ def test_segment_map_of_identity_is_transition(oracle_lib):
         Q, K, V, gc, bc, n = chunked_model._chunk((q, k, v, g, beta), 0, 0, 0, t0, 16)
         _, S = chunked_model.chunk_step(S, Q, K, np.zeros_like(V), gc, bc, 0.5)
     assert _rel(S, M_dense) < 1e-12
+
+
+# ---- per-channel decay (KDA)
+
+def _kda_inputs(rng, B, Hk, Hv, T, d, mult=1.0):
+    q, k, v, _, beta, S0 = _rand_inputs(rng, B, Hk, Hv, T, d)
+    g = -np.log1p(np.exp(rng.standard_normal((B, Hv, T, d)))) * mult
+    return q, k, v, g.astype(np.float32), beta, S0
+
+
+@pytest.mark.parametrize("chunk,factored", [(4, False), (16, False), (32, False), (16, True), (32, True), (64, True)])
+def test_kda_chunked_equals_sequential(oracle_lib, chunk, factored):
+    """The per-channel-decay WY form, with the blocks from pairwise decays or from the kernel's
+    scaled tiles (references at tile boundaries and mid-tile), equals the sequential oracle."""
+    rng = np.random.default_rng(200 + chunk)
+    q, k, v, g, beta, S0 = _kda_inputs(rng, 2, 2, 4, 150, 16)  # ragged tail
+    o_ref, S_ref = oracle_lib.kda_prefill(q, k, v, g, beta, S0, scale=0.25, head_map=1)
+    o, S = chunked_model.kda_chunked_prefill(q, k, v, g, beta, S0, 0.25, chunk, head_map=1, factored=factored)
+    assert _rel(o, o_ref) < 1e-12 and _rel(S, S_ref) < 1e-12
+
+
+def test_kda_segmented_equals_sequential(oracle_lib):
+    rng = np.random.default_rng(210)
+    q, k, v, g, beta, S0 = _kda_inputs(rng, 1, 2, 4, 300, 16)
+    o_ref, S_ref = oracle_lib.kda_prefill(q, k, v, g, beta, S0, scale=0.3)
+    for P in (2, 3, 5):
+        o, S = chunked_model.kda_chunked_prefill(q, k, v, g, beta, S0, 0.3, 32, factored=True, P=P)
+        assert _rel(o, o_ref) < 1e-11 and _rel(S, S_ref) < 1e-11, P
+
+
+def test_kda_factor_range():
+    """With every log-decay >= KDA_G_MIN the diagonal tiles' factors stay within e^{+-80}
+    (float32 range with margin); without the clamp a strong decay leaves it."""
+    rng = np.random.default_rng(211)
+    K = rng.standard_normal((32, 16)); Q = rng.standard_normal((32, 16)); bc = rng.random(32)
+    g = -np.abs(rng.standard_normal((32, 16))) * 30.0  # up to ~-100 per step
+    g[0, 0] = -1000.0
+    _, _, big = chunked_model.kda_blocks_factored(Q, K, np.cumsum(g, axis=0), bc, 0.5)
+    assert big > 80
+    gcl = np.maximum(g, chunked_model.KDA_G_MIN)
+    _, _, big = chunked_model.kda_blocks_factored(Q, K, np.cumsum(gcl, axis=0), bc, 0.5)
+    assert big <= 8 * -chunked_model.KDA_G_MIN
+
+
+def test_kda_clamp_is_within_bound(oracle_lib):
+    """Strong decay (g x 10, steps below -10 common): the clamped chunked form stays within
+    e^{-10} of the state's size from the exact recurrence, far inside the 2e-3 bar."""
+    rng = np.random.default_rng(212)
+    q, k, v, g, beta, S0 = _kda_inputs(rng, 1, 1, 2, 96, 16, mult=10.0)
+    assert (g < chunked_model.KDA_G_MIN).mean() > 0.2
+    o_ref, S_ref = oracle_lib.kda_prefill(q, k, v, g, beta, S0, scale=0.25)
+    o, S = chunked_model.kda_chunked_prefill(q, k, v, g, beta, S0, 0.25, 32, factored=True, clamp=True)
+    assert _rel(o, o_ref) < 1e-4 and _rel(S, S_ref) < 1e-4

@@ -1,5 +1,6 @@
 """GPU parity of the per-channel-decay variant (gdn_kda_prefill, gdn_kda_decode) against the
-float64 oracle's per-channel recurrence (needs an MI355X)."""
+float64 oracle's per-channel recurrence (needs an MI355X). The bf16 prefill runs the chunked form
+(chunk 32 or 64: 32-token chunks, segment-parallel) or, with chunk 16, token by token."""
 import numpy as np
 import pytest
 
@@ -30,17 +31,54 @@ def check(oracle_lib, x, g, o, sf, tol, head_map=0, pairs=None, label=""):
     assert eo <= tol and es <= tol, (label, eo, es)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-# the kernel streams 16-token blocks three ahead: one, two, three and four blocks, whole and ragged
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 32), ("bf16", 16), ("f32", 32)])
+# one, two, three and four 16-token blocks and 32-token chunks, whole and ragged
 @pytest.mark.parametrize("T", [1, 16, 37, 48, 64, 200])
 @pytest.mark.parametrize("head_map", [0, 1])
-def test_kda_prefill_small(gdn, oracle_lib, dtype, T, head_map):
+def test_kda_prefill_small(gdn, oracle_lib, dtype, chunk, T, head_map):
     x = inputs.generate(2, T, 2, 4, 128, dtype, seed=120 + T, init_state="normal")
     g = inputs.generate_channel_decay((2, 4, T, 128), seed=121 + T)
     q, k, v = qkv_dev(x)
-    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), head_map=head_map, scale=x.scale)
+    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), chunk=chunk, head_map=head_map, scale=x.scale)
     check(oracle_lib, x, g, o.cpu().numpy(), sf.cpu().numpy(), tol_for(x), head_map=head_map,
-          label=f"kda {dtype} T{T} map{head_map}")
+          label=f"kda {dtype} C{chunk} T{T} map{head_map}")
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8])
+def test_kda_chunked_segments(gdn, oracle_lib, P):
+    """The chunked form split into P segments by the workspace size (maps, combine, output)."""
+    import torch
+    B, Hk, Hv, T = 1, 2, 4, 700
+    x = inputs.generate(B, T, Hk, Hv, 128, "bf16", seed=140 + P, init_state="normal")
+    g = inputs.generate_channel_decay((B, Hv, T, 128), seed=141 + P)
+    nbytes = 3 * B * Hv * P * 128 * 128 * 4 if P > 1 else 0
+    assert gdn.prefill_segments(B, T, Hk, Hv, 128, nbytes, chunk=32) == P
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    q, k, v = qkv_dev(x)
+    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), scale=x.scale, workspace=ws)
+    check(oracle_lib, x, g, o.cpu().numpy(), sf.cpu().numpy(), TOL_BF16, label=f"kda chunked P{P}")
+
+
+@pytest.mark.parametrize("mult", [3.0, 10.0])
+def test_kda_chunked_strong_decay(gdn, oracle_lib, mult):
+    """Per-channel decays three and ten times the workload's: at x10 a fifth of the steps fall
+    below -10, which the chunked form takes as -10 (a difference below e^-10 of the state)."""
+    x = inputs.generate(1, 200, 2, 4, 128, "bf16", seed=150, init_state="normal")
+    g = inputs.generate_channel_decay((1, 4, 200, 128), seed=151, factor=mult)
+    q, k, v = qkv_dev(x)
+    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), scale=x.scale)
+    check(oracle_lib, x, g, o.cpu().numpy(), sf.cpu().numpy(), TOL_BF16, label=f"kda chunked decay x{mult}")
+
+
+def test_kda_chunk_64_runs_chunked(gdn):
+    """chunk 64 is served by the 32-token chunked form: bit-equal to chunk 32."""
+    import torch
+    x = inputs.generate(1, 150, 2, 4, 128, "bf16", seed=152, init_state="normal")
+    g = dev(inputs.generate_channel_decay((1, 4, 150, 128), seed=153))
+    q, k, v = qkv_dev(x)
+    o32, s32 = gdn.kda_prefill(q, k, v, g, dev(x.beta), dev(x.s0), chunk=32, scale=x.scale)
+    o64, s64 = gdn.kda_prefill(q, k, v, g, dev(x.beta), dev(x.s0), chunk=64, scale=x.scale)
+    assert torch.equal(o32, o64) and torch.equal(s32, s64)
 
 
 def test_kda_prefill_empty(gdn):
@@ -84,7 +122,7 @@ def test_kda_prefill_equals_decode_steps(gdn):
     x = inputs.generate(2, T, 2, 4, 128, "bf16", seed=124, init_state="normal")
     g = inputs.generate_channel_decay((2, 4, T, 128), seed=125)
     q, k, v = qkv_dev(x)
-    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), scale=x.scale)
+    o, sf = gdn.kda_prefill(q, k, v, dev(g), dev(x.beta), dev(x.s0), chunk=16, scale=x.scale)  # token by token
     state = dev(x.s0)
     gd, bd = dev(g), dev(x.beta)
     for t in range(T):
