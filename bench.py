@@ -273,14 +273,21 @@ def main():
                                                   o=po16, final_state=psf), args.steps)
     p16_bytes = prefill_bytes(B, T, Hk, Hv, d, o_bytes=2)
 
-    # the per-channel-decay variant: the long prefill (token-recurrent kernel) and the batched
-    # decode step, with one log-decay per key channel (-softplus(N(0,1)) * 0.1 and * 1)
+    # the per-channel-decay variant: the long prefill (the chunked form, 32-token chunks in the
+    # segmented passes; and token by token, chunk 16) and the batched decode step, with one
+    # log-decay per key channel (-softplus(N(0,1)) * 0.1 and * 1)
     kg = torch.from_numpy(inputs.generate_channel_decay((B, Hv, T, d), seed=pw.seed + 300, factor=0.1)).to(dev)
-    binding.kda_prefill(pq, pk, pv, kg, pb, None, scale=px.scale, o=po, final_state=psf)
-    kda_p_ms = time_batch(lambda i: binding.kda_prefill(pq, pk, pv, kg, pb, None, scale=px.scale, o=po,
-                                                        final_state=psf), max(1, args.steps // 10))
+    kws = torch.empty(binding.prefill_workspace_bytes(B, T, Hk, Hv, d, chunk=32), dtype=torch.uint8, device=dev)
+    for _ in range(max(1, args.warmup)):
+        binding.kda_prefill(pq, pk, pv, kg, pb, None, chunk=32, scale=px.scale, o=po, final_state=psf, workspace=kws)
+    kda_p_ms = time_batch(lambda i: binding.kda_prefill(pq, pk, pv, kg, pb, None, chunk=32, scale=px.scale, o=po,
+                                                        final_state=psf, workspace=kws), args.steps)
+    kda_segments = binding.prefill_segments(B, T, Hk, Hv, d, kws.numel(), chunk=32)
+    binding.kda_prefill(pq, pk, pv, kg, pb, None, chunk=16, scale=px.scale, o=po, final_state=psf)
+    kda_tok_ms = time_batch(lambda i: binding.kda_prefill(pq, pk, pv, kg, pb, None, chunk=16, scale=px.scale, o=po,
+                                                          final_state=psf), max(1, args.steps // 10))
     kda_p_bytes = prefill_bytes(B, T, Hk, Hv, d) + B * Hv * T * d * 4  # + the per-channel decays
-    del kg
+    del kg, kws
     kdg = torch.from_numpy(inputs.generate_channel_decay((dB, dHv, dd), seed=dw.seed + 300)).to(dev)
     kstate = state.clone()
     binding.kda_decode(dq[0], dk[0], dv[0], kdg, db[0], kstate, scale=dx.scale, o=do)
@@ -305,6 +312,22 @@ def main():
     if not torch.isfinite(po16).all():
         raise RuntimeError("non-finite float16 outputs after the gated RMSNorm")
     del po16
+    # the same norm as an argument of the calls: fused into the segmented prefill's o store and
+    # into the decode update (B * Hv >= 256 pairs)
+    for _ in range(max(1, args.warmup)):
+        binding.prefill(pq, pk, pv, pg, pb, None, chunk=pw.chunk, scale=px.scale, o=po, final_state=psf,
+                        norm_weight=nweight, norm_gate=ngate)
+    pnorm_ms = time_batch(lambda i: binding.prefill(pq, pk, pv, pg, pb, None, chunk=pw.chunk, scale=px.scale, o=po,
+                                                    final_state=psf, norm_weight=nweight, norm_gate=ngate), args.steps)
+    dnrm = inputs.generate_norm(do.shape, "bf16", seed=dw.seed + 100)
+    dgate, dweight = bf(dnrm.gate_bits), torch.from_numpy(dnrm.weight).to(dev)
+    dnstate = state.clone()
+    binding.decode(dq[0], dk[0], dv[0], dg[0], db[0], dnstate, scale=dx.scale, o=do, norm_weight=dweight,
+                   norm_gate=dgate)
+    dnorm_ms = time_batch(lambda i: binding.decode(dq[i % nsteps_dec], dk[i % nsteps_dec], dv[i % nsteps_dec],
+                                                   dg[i % nsteps_dec], db[i % nsteps_dec], dnstate, scale=dx.scale,
+                                                   o=do, norm_weight=dweight, norm_gate=dgate), args.steps)
+    del dnstate
     if not torch.isfinite(po).all():
         raise RuntimeError("non-finite outputs after the gated RMSNorm")
 
@@ -442,9 +465,11 @@ def main():
             "traffic": measured_prefill_traffic("traffic_bytes_per_launch_f16_o"),
         },
         "kda": {
-            "what": "per-channel decay (one log-decay per key channel): long prefill, token-recurrent "
-                    "kernel; batched decode step",
-            "prefill_kernel": "gdn_kda_prefill_kernel<bf16>",
+            "what": "per-channel decay (one log-decay per key channel): long prefill, chunked form "
+                    "(32-token chunks, segmented passes), and token by token; batched decode step",
+            "prefill_kernel": "gdn_seg_pass_kernel<32, map / output, per-channel decay> + gdn_seg_combine_kernel",
+            "prefill_segments": kda_segments,
+            "prefill_token_by_token_ms": kda_tok_ms,
             "prefill_ms": kda_p_ms,
             "prefill_tokens_per_s": tokens / (kda_p_ms * 1e-3),
             "prefill_achieved": kda_p_bytes / (kda_p_ms * 1e-3) / 1e9,
@@ -472,6 +497,15 @@ def main():
                 "achieved": norm16_bytes / (norm16_ms * 1e-3) / 1e9,
                 "frac": norm16_bytes / (norm16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 "algorithmic_bytes_per_launch": norm16_bytes,
+            },
+            "fused": {
+                "what": "the norm as an argument of the calls: gdn_prefill (long workload, fused into the "
+                        "segmented o store) and gdn_decode (B = 256, fused into the update)",
+                "prefill_ms": pnorm_ms,
+                "prefill_ms_without_norm": p_avg,
+                "prefill_then_separate_norm_ms": p_avg + norm_ms,
+                "decode_ms": dnorm_ms,
+                "decode_ms_without_norm": d_avg,
             },
         },
         "qkv_prologue": {
