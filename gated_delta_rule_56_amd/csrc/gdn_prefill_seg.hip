@@ -1057,63 +1057,79 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(egt * tq);
             }
         };
-        // P2, per-channel decay (C = 32): W0 the block (0,0), W1 (1,1), W2 (1,0), in float32 from the
-        // raw k, q tiles and the factors: block (m, m) as (k o 1/E)(k o E)^T with E relative to the
-        // tile's 8th token (every factor within e^{+-80}), block (1,0) relative to the last token b of
-        // tile 0, (k o e^{G_b - G})(k o e^{G - G_b})^T = (k o e^{G_b - G_r0} / E)(k o E e^{G_r1 - G_b})^T,
-        // whose operands are decays (<= 1). Lane (q4, li) supplies row li of both operands for k = q4:
-        // channels 4 rho .. + 3 of run rho = 4 blk + q4 over the eight runs' steps.
-        auto phase2k = [&](int s, auto wc) __attribute__((always_inline)) {
-            constexpr int W = decltype(wc)::value;
-            if constexpr (KDA && W < 3) {
-                constexpr int MM = W == 0 ? 0 : 1, NB = W == 1 ? 1 : 0;
-                const int ts = 16 * NB + li, tt = 16 * MM + li;  // A-operand token, B-operand token
-                const unsigned char *Es = smem + L::oE + s * C * L::kERow;
-                const unsigned char *EV = smem + L::oEV + s * kNVec * 512;
-                const float *gts = reinterpret_cast<const float *>(smem + L::oG + s * 20 * C);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
+        // P2, per-channel decay (C = 32). The diagonal blocks (m, m) in float32 as (k o 1/E)(k o E)^T
+        // with E relative to the tile's 8th token (every factor within e^{+-80}); lane (q4, li)
+        // supplies row li of both operands for k = q4: channels 4 rho .. + 3 of run rho = 4 blk +
+        // q4 over the eight runs' steps. The block (1,0) relative to the last token b of tile 0,
+        // (k o e^{G_b - G_r0} / E)(k o E e^{G_r1 - G_b})^T, whose operands are decays (<= 1): in fp16,
+        // the same runs as 16 x 16 x 16 steps. Work: W0 A(0,0) and its inverse,
+        // W1 A(1,1) and its inverse, W2 (which holds the next log-decays) A_qk(0,0), W3 A(1,0),
+        // A_qk(1,0) and A_qk(1,1).
+        auto kda_diag = [&](int s, int mm, bool qside) __attribute__((always_inline)) {
+            const int tok = 16 * mm + li;
+            const unsigned char *Es = smem + L::oE + s * C * L::kERow + tok * L::kERow;
+            const unsigned char *rk = smem + L::oRK + tok * 256;
+            const unsigned char *rb = smem + (qside ? L::oRQ : L::oRK) + tok * 256;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int blk = 0; blk < 8; ++blk) {
-                    const int rho = 4 * blk + q4;
-                    const int grp = 4 * (rho >> 3) + (rho & 3), half = 8 * ((rho >> 2) & 1);
-                    const f16x4 ks = ld4(smem + L::oRK + ts * 256 + ((grp ^ ksw(ts & 15)) << 4) + half);
-                    const f16x4 kt = ld4(smem + L::oRK + tt * 256 + ((grp ^ ksw(tt & 15)) << 4) + half);
-                    f16x4 qt = {};
-                    if (OUT) qt = ld4(smem + L::oRQ + tt * 256 + ((grp ^ ksw(tt & 15)) << 4) + half);
-                    const f32x4 es = ldf4(Es + ts * L::kERow + 16 * rho);
-                    f32x4 et = ldf4(Es + tt * L::kERow + 16 * rho), fs = {1.f, 1.f, 1.f, 1.f};
-                    if constexpr (W == 2) {
-                        et *= ldf4(EV + kVecR1B * 512 + 16 * rho);
-                        fs = ldf4(EV + kVecBR0 * 512 + 16 * rho);
-                    }
+            for (int blk = 0; blk < 8; ++blk) {
+                const int rho = 4 * blk + q4;
+                const int off = ((((4 * (rho >> 3) + (rho & 3)) ^ ksw(tok & 15))) << 4) + 8 * ((rho >> 2) & 1);
+                const f16x4 ks = ld4(rk + off), kt = ld4(rb + off);
+                const f32x4 e = ldf4(Es + 16 * rho);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float a = (float)ks[e] * (__builtin_amdgcn_rcpf(es[e]) * fs[e]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, (float)kt[e] * et[e], acc, 0, 0, 0);
-                        if (OUT) accq = __builtin_amdgcn_mfma_f32_16x16x4f32(a, (float)qt[e] * et[e], accq, 0, 0, 0);
-                    }
-                }
-                // lane (q4, li), element r: s = 16 NB + 4 q4 + r, t = 16 MM + li
-                const float bt = gts[C + 16 * MM + li], sct = p.scale;
-                f32x4 a, aqv;
+                for (int r = 0; r < 4; ++r)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32((float)ks[r] * __builtin_amdgcn_rcpf(e[r]), (float)kt[r] * e[r],
+                                                            acc, 0, 0, 0);
+                if ((blk & 1) == 1) fence();  // two runs' operands live at a time
+            }
+            return acc;  // lane (q4, li), element r: s = 16 mm + 4 q4 + r, t = 16 mm + li
+        };
+        auto kda_off = [&](int s, f32x4 &acc, f32x4 &accq) __attribute__((always_inline)) {
+            const int tsk = li, ttk = 16 + li;
+            const unsigned char *Es = smem + L::oE + s * C * L::kERow;
+            const unsigned char *EV = smem + L::oEV + s * kNVec * 512;
+            const unsigned char *rks = smem + L::oRK + tsk * 256, *rkt = smem + L::oRK + ttk * 256;
+            const unsigned char *rqt = smem + L::oRQ + ttk * 256;
+            acc = accq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) {
+                const int rho = 4 * blk + q4;
+                const int grp = 4 * (rho >> 3) + (rho & 3), half = 8 * ((rho >> 2) & 1);
+                const f16x4 ks = ld4(rks + ((grp ^ ksw(tsk & 15)) << 4) + half);
+                const f16x4 kt = ld4(rkt + ((grp ^ ksw(ttk & 15)) << 4) + half);
+                f16x4 qt = {};
+                if (OUT) qt = ld4(rqt + ((grp ^ ksw(ttk & 15)) << 4) + half);
+                const f32x4 es = ldf4(Es + tsk * L::kERow + 16 * rho), et = ldf4(Es + ttk * L::kERow + 16 * rho);
+                const f32x4 fb = ldf4(EV + kVecBR0 * 512 + 16 * rho), fr = ldf4(EV + kVecR1B * 512 + 16 * rho);
+                f16x4 a, b, bq;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int sidx = 4 * q4 + r;
-                    a[r] = (W == 2 || sidx < li) ? bt * acc[r] : 0.0f;
-                    aqv[r] = (W == 2 || sidx <= li) ? sct * accq[r] : 0.0f;
+                    a[r] = (_Float16)((float)ks[r] * (__builtin_amdgcn_rcpf(es[r]) * fb[r]));
+                    const float l = et[r] * fr[r];
+                    b[r] = (_Float16)((float)kt[r] * l);
+                    if (OUT) bq[r] = (_Float16)((float)qt[r] * l);
                 }
-                if (OUT) {
-                    unsigned char *aqb = smem + L::oA + s * L::kFr * 1024 + lane * 16;
-                    *reinterpret_cast<f16x4 *>(aqb + fblk(MM, NB / 2) * 1024 + (NB & 1) * 8) = to_f16x4(aqv);
-                    if constexpr (W == 0) *reinterpret_cast<f16x4 *>(aqb + fblk(0, 0) * 1024 + 8) = f16x4{};
-                }
-                if constexpr (W == 2) {
-                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(1, 0) * 512 + lane * 8) =
-                        to_f16x4(-a);
-                } else {
-                    // T_MM = (I + A_MM)^{-1}, as for the scalar decay (Td's scaled copy is T itself:
-                    // the update's decay is in its k tile)
-                    float *at = reinterpret_cast<float *>(smem + L::oAt) + MM * 16 * 20;
+                acc = mfma16x16x16(a, b, acc);
+                if (OUT) accq = mfma16x16x16(a, bq, accq);
+                if ((blk & 1) == 1) fence();  // two runs' operands live at a time
+            }  // lane (q4, li), element r: s = 4 q4 + r, t = 16 + li
+        };
+        auto phase2k = [&](int s, auto wc) __attribute__((always_inline)) {
+            constexpr int W = decltype(wc)::value;
+            if constexpr (KDA) {
+                const float *gts = reinterpret_cast<const float *>(smem + L::oG + s * 20 * C);
+                const float sct = p.scale;
+                unsigned char *aqb = smem + L::oA + s * L::kFr * 1024 + lane * 16;
+                if constexpr (W < 2) {
+                    // A(W, W) (strict lower, with beta), then T_WW = (I + A_WW)^{-1} as for the scalar
+                    // decay (Td's scaled copy is T itself: the update's decay is in its k tile)
+                    const f32x4 acc = kda_diag(s, W, false);
+                    const float bt = gts[C + 16 * W + li];
+                    f32x4 a;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a[r] = 4 * q4 + r < li ? bt * acc[r] : 0.0f;
+                    float *at = reinterpret_cast<float *>(smem + L::oAt) + W * 16 * 20;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) at[(4 * q4 + r) * 20 + li] = -a[r];
                     float nrow[16];
@@ -1123,9 +1139,31 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
 #pragma unroll
                     for (int e = 0; e < 4; ++e) tq[e] = 4 * q4 + e == li ? 1.0f : 0.0f;
                     inv_rows(tq, nrow);
-                    unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + MM * 1024 + lane * 8;
+                    unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + W * 1024 + lane * 8;
                     *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
                     *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(tq);
+                } else if constexpr (W == 3) {
+                    f32x4 acc, accq;
+                    kda_off(s, acc, accq);
+                    const float bt = gts[C + 16 + li];
+                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(1, 0) * 512 + lane * 8) =
+                        to_f16x4(-(bt * acc));
+                    if (OUT) {
+                        *reinterpret_cast<f16x4 *>(aqb + fblk(1, 0) * 1024) = to_f16x4(sct * accq);
+                        const f32x4 dq = kda_diag(s, 1, true);
+                        f32x4 aq;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) aq[r] = 4 * q4 + r <= li ? sct * dq[r] : 0.0f;
+                        *reinterpret_cast<f16x4 *>(aqb + fblk(1, 0) * 1024 + 8) = to_f16x4(aq);
+                    }
+                } else if (OUT) {
+                    // W2: A_qk(0,0) (lower incl., with scale); the fragment's other half is zero
+                    const f32x4 dq = kda_diag(s, 0, true);
+                    f32x4 aq;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) aq[r] = 4 * q4 + r <= li ? sct * dq[r] : 0.0f;
+                    *reinterpret_cast<f16x4 *>(aqb + fblk(0, 0) * 1024) = to_f16x4(aq);
+                    *reinterpret_cast<f16x4 *>(aqb + fblk(0, 0) * 1024 + 8) = f16x4{};
                 }
             }
         };
@@ -1134,6 +1172,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 if (m == 0) phase2k(s, IC<0>{});
                 else if (m == 1) phase2k(s, IC<1>{});
                 else if (m == 2) phase2k(s, IC<2>{});
+                else phase2k(s, IC<3>{});
             } else {
                 if (m == 0) phase2w(s, IC<0>{});
                 else if (m == 1) phase2w(s, IC<1>{});
