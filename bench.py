@@ -234,6 +234,20 @@ def main():
                                                  dg[i % nsteps_dec], db[i % nsteps_dec], dstate16,
                                                  scale=dx.scale, o=do), args.steps)
     d16_bytes = decode_bytes(dB, dHk, dHv, dd, state_bytes=2)
+    if not torch.isfinite(dstate16).all():
+        raise RuntimeError("non-finite float16 state")
+    del dstate16
+
+    # the same on a bfloat16 copy (float32 arithmetic, the state stored in bfloat16)
+    dstatebf = state.to(torch.bfloat16)
+    for s in range(max(1, args.warmup)):
+        binding.decode(dq[s], dk[s], dv[s], dg[s], db[s], dstatebf, scale=dx.scale, o=do)
+    dbf_ms = time_batch(lambda i: binding.decode(dq[i % nsteps_dec], dk[i % nsteps_dec], dv[i % nsteps_dec],
+                                                 dg[i % nsteps_dec], db[i % nsteps_dec], dstatebf,
+                                                 scale=dx.scale, o=do), args.steps)
+    if not torch.isfinite(dstatebf.float()).all():
+        raise RuntimeError("non-finite bfloat16 state")
+    del dstatebf
 
     # one sequence (B = 1): a step moves 4.2 MB, so launch overhead decides; the decode sequence
     # back to back as eager calls, and captured in one HIP graph
@@ -261,9 +275,6 @@ def main():
         raise RuntimeError("non-finite state after the single-sequence decode")
     b1_bytes = decode_bytes(1, dHk, dHv, dd)
     del g1, s1, o1
-    if not torch.isfinite(dstate16).all():
-        raise RuntimeError("non-finite float16 state")
-    del dstate16
 
     # the same prefill writing float16 o, and the epilogue on those rows (generated below)
     po16 = torch.empty(po.shape, dtype=torch.float16, device=dev)
@@ -436,6 +447,15 @@ def main():
                 "frac": d16_bytes / (d16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 "algorithmic_bytes_per_launch": d16_bytes,
                 "sequence_updates_per_s": dB / (d16_ms * 1e-3),
+            },
+            "bf16_state": {
+                "what": "the same step with the state stored in bfloat16 (268 MB), float32 arithmetic",
+                "kernel": "gdn_decode_kernel<128, bf16, bf16 state>",
+                "avg_launch_ms": dbf_ms,
+                "achieved": d16_bytes / (dbf_ms * 1e-3) / 1e9,
+                "frac": d16_bytes / (dbf_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "algorithmic_bytes_per_launch": d16_bytes,
+                "sequence_updates_per_s": dB / (dbf_ms * 1e-3),
             },
             "single_sequence": {
                 "what": f"B = 1, {nsteps_dec} consecutive in-place steps, per step: eager calls back to back, "

@@ -19,12 +19,12 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
 GDN_HEADS_TILED, GDN_HEADS_GROUPED = 0, 1
-GDN_STATE_F32, GDN_STATE_F16 = 0, 1
+GDN_STATE_F32, GDN_STATE_F16, GDN_STATE_BF16 = 0, 1, 2
 GDN_OUT_F32, GDN_OUT_F16 = 0, 1
 ABI_VERSION = 7
 # GDN_STATIC_SCRATCH_BYTES: the largest workspace_bytes of gdn_prefill_static
 STATIC_SCRATCH_BYTES = 96 << 20
-_STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16}
+_STATE_DTYPES = {torch.float32: GDN_STATE_F32, torch.float16: GDN_STATE_F16, torch.bfloat16: GDN_STATE_BF16}
 _OUT_DTYPES = {torch.float32: GDN_OUT_F32, torch.float16: GDN_OUT_F16}
 
 EXPORTED_SYMBOLS = ("gdn_prefill_workspace_bytes", "gdn_prefill_segments", "gdn_prefill", "gdn_prefill_static",
@@ -181,7 +181,7 @@ def _out_tensor(o: Optional[torch.Tensor], shape, o_dtype: torch.dtype, device) 
 
 def _state_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
     if not isinstance(t, torch.Tensor) or t.dtype not in _STATE_DTYPES:
-        raise TypeError(f"{name} must be a float32 or float16 tensor")
+        raise TypeError(f"{name} must be a float32, float16 or bfloat16 tensor")
     return _dev_tensor(t, name, t.dtype)
 
 
@@ -229,7 +229,7 @@ def _prefill_marshal(q, k, v, g, beta, initial_state, chunk, head_map, scale, o,
         raise TypeError(f"state_dtype {state_dtype} differs from the state tensors' {given[0]}")
     sdt = given[0] if given else (state_dtype or torch.float32)
     if sdt not in _STATE_DTYPES or any(t != sdt for t in given):
-        raise TypeError("the states must be float32 or float16, both of the same type")
+        raise TypeError("the states must be float32, float16 or bfloat16, both of the same type")
     if initial_state is not None:
         _state_tensor(initial_state, "initial_state")
         if initial_state.shape != (B, Hv, d, d):
@@ -261,7 +261,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, 
     """gdn_prefill on torch tensors.
 
     q, k [B][Hk][T][d] and v [B][Hv][T][d] (bfloat16 or float32); g, beta [B][Hv][T] float32;
-    initial_state [B][Hv][d][d] float32 or float16, or None. Returns (o, final_state). Pass
+    initial_state [B][Hv][d][d] float32, float16 or bfloat16, or None. Returns (o, final_state). Pass
     final_state=initial_state to update a state in place. The states share one storage type:
     that of the state tensors passed, else state_dtype (default float32). o is float32, or
     float16 (o_dtype, or the type of the o passed). workspace: a uint8 device tensor of at
@@ -339,7 +339,7 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
         raise TypeError(f"state_dtype {state_dtype} differs from the state tensors' {given[0]}")
     sdt = given[0] if given else (state_dtype or torch.float32)
     if sdt not in _STATE_DTYPES or any(t != sdt for t in given):
-        raise TypeError("the states must be float32 or float16, both of the same type")
+        raise TypeError("the states must be float32, float16 or bfloat16, both of the same type")
     if initial_state is not None:
         _state_tensor(initial_state, "initial_state")
         if initial_state.shape != (B, Hv, d, d):
@@ -372,7 +372,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, b
            norm_weight: Optional[torch.Tensor] = None, norm_gate: Optional[torch.Tensor] = None,
            norm_eps: float = 1e-6, stream=None) -> torch.Tensor:
     """gdn_decode on torch tensors: q, k [B][Hk][d], v [B][Hv][d], g, beta [B][Hv],
-    state [B][Hv][d][d] float32 or float16 (updated in place). Returns o [B][Hv][d] float32 or
+    state [B][Hv][d][d] float32, float16 or bfloat16 (updated in place). Returns o [B][Hv][d] float32 or
     float16 (o_dtype, or the type of the o passed); with norm_weight (and optionally norm_gate
     [B][Hv][d]) the gated RMSNorm of every output row (gdn_norm)."""
     lib = load_library()
@@ -428,7 +428,7 @@ def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     given = [t.dtype for t in (initial_state, final_state) if t is not None]
     sdt = given[0] if given else (state_dtype or torch.float32)
     if sdt not in _STATE_DTYPES or any(t != sdt for t in given):
-        raise TypeError("the states must be float32 or float16, both of the same type")
+        raise TypeError("the states must be float32, float16 or bfloat16, both of the same type")
     if initial_state is not None:
         _state_tensor(initial_state, "initial_state")
         if initial_state.shape != (B, Hv, d, d):

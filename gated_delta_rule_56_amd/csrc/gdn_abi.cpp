@@ -54,7 +54,7 @@ gdn_status check_common(const gdn_shape *s) {
         return fail(GDN_ERR_INVALID_ARG, "unknown qkv_dtype %d", (int)s->qkv_dtype);
     if (s->head_map != GDN_HEADS_TILED && s->head_map != GDN_HEADS_GROUPED)
         return fail(GDN_ERR_INVALID_ARG, "unknown head_map %d", (int)s->head_map);
-    if (s->state_dtype != GDN_STATE_F32 && s->state_dtype != GDN_STATE_F16)
+    if (s->state_dtype != GDN_STATE_F32 && s->state_dtype != GDN_STATE_F16 && s->state_dtype != GDN_STATE_BF16)
         return fail(GDN_ERR_INVALID_ARG, "unknown state_dtype %d", (int)s->state_dtype);
     if (s->o_dtype != GDN_OUT_F32 && s->o_dtype != GDN_OUT_F16)
         return fail(GDN_ERR_INVALID_ARG, "unknown o_dtype %d", (int)s->o_dtype);
@@ -157,7 +157,7 @@ gdn_status prefill_impl(const gdn_shape *s, const void *q, const void *k, const 
     const int64_t B = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
     const int64_t esz = bf16 ? 2 : 4;
     const int64_t qk_bytes = B * Hk * T * d * esz, v_bytes = B * Hv * T * d * esz;
-    const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
+    const bool st16 = s->state_dtype != GDN_STATE_F32, o16 = s->o_dtype == GDN_OUT_F16;
     const int64_t gb_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * (o16 ? 2 : 4);
     const int64_t st_bytes = B * Hv * d * d * (st16 ? 2 : 4);
     if (T > 0) {
@@ -207,6 +207,7 @@ gdn_status prefill_impl(const gdn_shape *s, const void *q, const void *k, const 
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
     p.init_f16 = p.final_f16 = st16;
+    p.state_bf16 = s->state_dtype == GDN_STATE_BF16;
     p.o_f16 = o16;
     // the segmented path splits every sequence into as many segments as its preferred count
     // allows within the workspace the caller passes (one segment, no workspace, at the least)
@@ -301,7 +302,7 @@ gdn_status gdn_prefill_varlen(const gdn_shape *s, const int32_t *cu_seqlens, con
     if (d != 128) return fail(GDN_ERR_UNSUPPORTED, "packed sequences need head_dim 128 (got %d)", d);
     const int64_t N = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
     if ((double)Hv * T * d > 4.0e15 || N > (1 << 24)) return fail(GDN_ERR_UNSUPPORTED, "tensor sizes overflow");
-    const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
+    const bool st16 = s->state_dtype != GDN_STATE_F32, o16 = s->o_dtype == GDN_OUT_F16;
     const int64_t qk_bytes = Hk * T * d * 2, v_bytes = Hv * T * d * 2, gb_bytes = Hv * T * 4;
     const int64_t o_bytes = Hv * T * d * (o16 ? 2 : 4);
     const int64_t st_bytes = N * Hv * d * d * (st16 ? 2 : 4);
@@ -357,6 +358,7 @@ gdn_status gdn_prefill_varlen(const gdn_shape *s, const int32_t *cu_seqlens, con
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
     p.init_f16 = p.final_f16 = st16;
+    p.state_bf16 = s->state_dtype == GDN_STATE_BF16;
     p.o_f16 = o16;
     char *wsb = static_cast<char *>(workspace);
     p.seqs = reinterpret_cast<const int32_t *>(wsb + vl.seq_offset);
@@ -477,7 +479,7 @@ gdn_status decode_impl(const gdn_shape *s, const void *q, const void *k, const v
     const Range ins[] = {range("q", q, B * Hk * d * esz), range("k", k, B * Hk * d * esz),
                          range("v", v, B * Hv * d * esz), range("g", g, B * Hv * (kda ? d : 1) * 4),
                          range("beta", beta, B * Hv * 4)};
-    const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
+    const bool st16 = s->state_dtype != GDN_STATE_F32, o16 = s->o_dtype == GDN_OUT_F16;
     const Range outs[] = {range("o", o, B * Hv * d * (o16 ? 2 : 4)),
                           range("state", state, B * Hv * d * d * (st16 ? 2 : 4))};
     GDN_TRY(check_no_overlap(outs, 2, ins, 5));
@@ -499,6 +501,7 @@ gdn_status decode_impl(const gdn_shape *s, const void *q, const void *k, const v
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
     p.state_f16 = st16;
+    p.state_bf16 = s->state_dtype == GDN_STATE_BF16;
     p.o_f16 = o16;
     p.kda = kda;
     if (norm) {
@@ -535,7 +538,7 @@ gdn_status gdn_kda_prefill(const gdn_shape *s, const void *q, const void *k, con
     const int64_t B = s->batch, T = s->seq_len, Hk = s->num_k_heads, Hv = s->num_v_heads;
     if ((double)B * Hv * T * d > 4.0e15) return fail(GDN_ERR_UNSUPPORTED, "tensor sizes overflow");
     const int64_t esz = bf16 ? 2 : 4;
-    const bool st16 = s->state_dtype == GDN_STATE_F16, o16 = s->o_dtype == GDN_OUT_F16;
+    const bool st16 = s->state_dtype != GDN_STATE_F32, o16 = s->o_dtype == GDN_OUT_F16;
     const int64_t qk_bytes = B * Hk * T * d * esz, v_bytes = B * Hv * T * d * esz, g_bytes = B * Hv * T * d * 4;
     const int64_t b_bytes = B * Hv * T * 4, o_bytes = B * Hv * T * d * (o16 ? 2 : 4);
     const int64_t st_bytes = B * Hv * d * d * (st16 ? 2 : 4);
@@ -599,6 +602,7 @@ gdn_status gdn_kda_prefill(const gdn_shape *s, const void *q, const void *k, con
     p.head_map = (int32_t)s->head_map;
     p.scale = s->scale;
     p.init_f16 = p.final_f16 = st16;
+    p.state_bf16 = s->state_dtype == GDN_STATE_BF16;
     p.o_f16 = o16;
     const hipError_t err = chunked ? gdn::launch_prefill_seg(p, 32, P, workspace, static_cast<hipStream_t>(stream), true)
                                    : gdn::launch_kda_prefill(p, bf16, static_cast<hipStream_t>(stream));

@@ -19,6 +19,8 @@
 // row loads (D/4 * 16 bytes per lane for D = 128) to keep HBM busy, then
 // reduces the two dot products across the row's lanes with xor shuffles and
 // streams the updated rows back with non-temporal stores.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -57,7 +59,7 @@ __device__ __forceinline__ void load_vec(const T *p, int64_t i, float *out) {
     }
 }
 
-// N consecutive state values (float32 or float16), loaded and stored non-temporally
+// N consecutive state values (float32, float16 or bfloat16), loaded and stored non-temporally
 template <int N, typename SD>
 struct StateRow {
     typedef SD vec __attribute__((ext_vector_type(N)));
@@ -68,8 +70,10 @@ struct StateRow {
         vec v;
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            if constexpr (sizeof(SD) == 2)
-                v[e] = f16_out(y[e]);  // round to nearest even
+            if constexpr (std::is_same<SD, __bf16>::value)
+                v[e] = bf16_out(y[e]);  // round to nearest even
+            else if constexpr (sizeof(SD) == 2)
+                v[e] = f16_out(y[e]);
             else
                 v[e] = y[e];
         }
@@ -82,7 +86,7 @@ struct StateRow {
 template <int D, typename SD>
 constexpr int cols_per_lane() { return sizeof(SD) == 2 && D >= 64 ? 8 : 4; }
 
-// T: q/k/v element (float or bfloat16 bits); SD: state element (float or _Float16);
+// T: q/k/v element (float or bfloat16 bits); SD: state element (float, _Float16 or __bf16);
 // workgroups per (b, h) when the pairs alone do not fill the GPU: as many as keep every wave at
 // one full access of rows or more, at most 8
 template <int D, typename SD>
@@ -259,8 +263,12 @@ hipError_t launch_sd(const DecodeParams &p, hipStream_t stream) {
 
 template <int D, typename T>
 hipError_t launch_dt(const DecodeParams &p, hipStream_t stream) {
-    if (p.kda) return p.state_f16 ? launch_sd<D, T, _Float16, true>(p, stream) : launch_sd<D, T, float, true>(p, stream);
-    return p.state_f16 ? launch_sd<D, T, _Float16, false>(p, stream) : launch_sd<D, T, float, false>(p, stream);
+    if (p.kda) {
+        if (!p.state_f16) return launch_sd<D, T, float, true>(p, stream);
+        return p.state_bf16 ? launch_sd<D, T, __bf16, true>(p, stream) : launch_sd<D, T, _Float16, true>(p, stream);
+    }
+    if (!p.state_f16) return launch_sd<D, T, float, false>(p, stream);
+    return p.state_bf16 ? launch_sd<D, T, __bf16, false>(p, stream) : launch_sd<D, T, _Float16, false>(p, stream);
 }
 
 template <int D>

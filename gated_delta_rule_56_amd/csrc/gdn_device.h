@@ -52,6 +52,12 @@ __device__ __forceinline__ _Float16 f16_out(float x) {
     return (_Float16)x;
 }
 
+// ... and in bfloat16 (the same rounding, the same reason for the empty asm)
+__device__ __forceinline__ __bf16 bf16_out(float x) {
+    asm("" : "+v"(x));
+    return (__bf16)x;
+}
+
 // x plus the value of the lane a DPP control names (all source lanes in range)
 template <int kCtrl>
 __device__ __forceinline__ float add_dpp(float x) {
@@ -74,22 +80,31 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// 4 consecutive state values at element index i of a float32 or float16 state.
-__device__ __forceinline__ f32x4 load_state4(const void *base, int64_t i, bool f16) {
+// 4 consecutive state values at element index i of a float32 or 16-bit state (float16, or
+// bfloat16 with bf), widened to float32 ...
+__device__ __forceinline__ f32x4 load_state4(const void *base, int64_t i, bool f16, bool bf = false) {
     if (f16) {
+        if (bf) {
+            const u16x4 h = *reinterpret_cast<const u16x4 *>(static_cast<const uint16_t *>(base) + i);
+            return f32x4{bf16_bits_to_f32(h[0]), bf16_bits_to_f32(h[1]), bf16_bits_to_f32(h[2]), bf16_bits_to_f32(h[3])};
+        }
         const f16x4 h = *reinterpret_cast<const f16x4 *>(static_cast<const _Float16 *>(base) + i);
         return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
     }
     return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + i);
 }
 
-// ... and stored, float16 rounded to nearest even.
-__device__ __forceinline__ void store_state4(void *base, int64_t i, f32x4 v, bool f16) {
-    if (f16)
+// ... and stored, float16 (bfloat16 with bf) rounded to nearest even.
+__device__ __forceinline__ void store_state4(void *base, int64_t i, f32x4 v, bool f16, bool bf = false) {
+    if (f16 && bf) {
+        typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<b4 *>(static_cast<__bf16 *>(base) + i) = b4{bf16_out(v[0]), bf16_out(v[1]), bf16_out(v[2]), bf16_out(v[3])};
+    } else if (f16) {
         *reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(base) + i) =
             f16x4{f16_out(v[0]), f16_out(v[1]), f16_out(v[2]), f16_out(v[3])};
-    else
+    } else {
         *reinterpret_cast<f32x4 *>(static_cast<float *>(base) + i) = v;
+    }
 }
 
 }  // namespace gdn

@@ -22,7 +22,8 @@ struct PrefillParams {
                                // sequence and the pointers are offset to the window's start)
     int32_t head_map;          // 0 tiled (h % Hk), 1 grouped (h / (Hv/Hk))
     float scale;
-    bool init_f16 = false, final_f16 = false;  // state storage types
+    bool init_f16 = false, final_f16 = false;  // state storage types: 16-bit ...
+    bool state_bf16 = false;                   // ... in bfloat16 rather than float16
     bool o_f16 = false;                        // o stored as f16 (the chunk-32/64 bf16 path)
     // packed sequences (chunk-32/64 bf16 path): B sequences laid end to end in one token axis
     // of T tokens (q, k, v, g, beta, o as for one sequence); nullptr for the padded layout
@@ -48,6 +49,7 @@ struct DecodeParams {
     int32_t head_map;
     float scale;
     bool state_f16 = false;
+    bool state_bf16 = false;  // the 16-bit state is bfloat16 rather than float16
     bool o_f16 = false;
     bool kda = false;          // one decay per key channel
     // output norm fused into the o store (one workgroup per pair): as PrefillParams

@@ -190,8 +190,8 @@ void gdn_kda_prefill_kernel(PrefillParams p) {
     const int64_t si = ((int64_t)pair * kD + row) * kD + col;
     f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = S0;
     if (p.init_state) {
-        S0 = load_state4(p.init_state, si, p.init_f16);
-        S1 = load_state4(p.init_state, si + 64, p.init_f16);
+        S0 = load_state4(p.init_state, si, p.init_f16, p.state_bf16);
+        S1 = load_state4(p.init_state, si + 64, p.init_f16, p.state_bf16);
     }
     const int64_t obase = (int64_t)pair * p.Ts * kD + row;
 
@@ -306,8 +306,8 @@ void gdn_kda_prefill_kernel(PrefillParams p) {
         lds_barrier();
     }
     if (p.final_state) {
-        store_state4(p.final_state, si, S0, p.final_f16);
-        store_state4(p.final_state, si + 64, S1, p.final_f16);
+        store_state4(p.final_state, si, S0, p.final_f16, p.state_bf16);
+        store_state4(p.final_state, si + 64, S1, p.final_f16, p.state_bf16);
     }
 }
 

@@ -77,9 +77,10 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
     for (int e = tid; e < kRows * D; e += kF32Threads) {
         const int i = e / D, j = e % D;
         const int64_t si = sbase + (int64_t)i * D + j;
-        S[i * L::QP + j] = !p.init_state ? 0.0f
-                           : p.init_f16  ? (float)static_cast<const _Float16 *>(p.init_state)[si]
-                                         : static_cast<const float *>(p.init_state)[si];
+        S[i * L::QP + j] = !p.init_state               ? 0.0f
+                           : p.init_f16 && p.state_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t *>(p.init_state)[si])
+                           : p.init_f16                 ? (float)static_cast<const _Float16 *>(p.init_state)[si]
+                                                        : static_cast<const float *>(p.init_state)[si];
     }
 
     for (int t0 = 0; t0 < T; t0 += C) {
@@ -200,7 +201,9 @@ __global__ __launch_bounds__(kF32Threads) void gdn_prefill_f32_kernel(PrefillPar
         for (int e = tid; e < kRows * D; e += kF32Threads) {
             const int i = e / D, j = e % D;
             const int64_t si = sbase + (int64_t)i * D + j;
-            if (p.final_f16)
+            if (p.final_f16 && p.state_bf16)
+                static_cast<__bf16 *>(p.final_state)[si] = bf16_out(S[i * L::QP + j]);
+            else if (p.final_f16)
                 static_cast<_Float16 *>(p.final_state)[si] = f16_out(S[i * L::QP + j]);
             else
                 static_cast<float *>(p.final_state)[si] = S[i * L::QP + j];

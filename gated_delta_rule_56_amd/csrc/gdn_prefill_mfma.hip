@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_mfma_kernel(PrefillParam
     f32x4 S[2];
 #pragma unroll
     for (int jl = 0; jl < 2; ++jl)
-        S[jl] = p.init_state ? load_state4(p.init_state, srow + 16 * jl, p.init_f16) : f32x4{0.f, 0.f, 0.f, 0.f};
+        S[jl] = p.init_state ? load_state4(p.init_state, srow + 16 * jl, p.init_f16, p.state_bf16) : f32x4{0.f, 0.f, 0.f, 0.f};
 
     // upper-triangular tiles of A, A_qk and T stay zero for the whole sequence
     for (int e = tid; e < 3 * C * CP; e += kThreads) Ah[e] = (_Float16)0.0f;  // Ah, Aqk, Tm are contiguous
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_mfma_kernel(PrefillParam
 
     if (p.final_state) {
 #pragma unroll
-        for (int jl = 0; jl < 2; ++jl) store_state4(p.final_state, srow + 16 * jl, S[jl], p.final_f16);
+        for (int jl = 0; jl < 2; ++jl) store_state4(p.final_state, srow + 16 * jl, S[jl], p.final_f16, p.state_bf16);
     }
 }
 

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         f32x4 S[8];
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt)
-            S[jt] = p.init_state ? load_state4(p.init_state, srow + 16 * jt, p.init_f16) : f32x4{0.f, 0.f, 0.f, 0.f};
+            S[jt] = p.init_state ? load_state4(p.init_state, srow + 16 * jt, p.init_f16, p.state_bf16) : f32x4{0.f, 0.f, 0.f, 0.f};
         // fp16 copy of S in fragment order: B operand of X = K S^T, and the helpers' copy
         f16x8 sb[4];
 #pragma unroll
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_scan_kernel(PrefillParam
         });
         if (p.final_state) {
 #pragma unroll
-            for (int jt = 0; jt < 8; ++jt) store_state4(p.final_state, srow + 16 * jt, S[jt], p.final_f16);
+            for (int jt = 0; jt < 8; ++jt) store_state4(p.final_state, srow + 16 * jt, S[jt], p.final_f16, p.state_bf16);
         }
         lds_barrier();
     } else if (w == 4) {

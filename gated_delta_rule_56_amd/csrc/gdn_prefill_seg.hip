@@ -289,14 +289,14 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         float *ws_start, *ws_n, *ws_m;
         int B, T, Hk, Hv, Ts, head_map, P, seg_chunks;
         float scale;
-        bool init_f16, final_f16, o_f16;
+        bool init_f16, final_f16, o_f16, state_bf16;
         const float *norm_w;
         const uint16_t *norm_gate;
         float norm_eps;
     };
     const Args p = {sp.p.q, sp.p.k, sp.p.v, sp.p.init_state, sp.p.g, sp.p.beta, sp.p.o, sp.p.final_state,
                     sp.ws_start, sp.ws_n, sp.ws_m, sp.p.B, sp.p.T, sp.p.Hk, sp.p.Hv, sp.p.Ts, sp.p.head_map,
-                    sp.P, sp.seg_chunks, sp.p.scale, sp.p.init_f16, sp.p.final_f16, sp.p.o_f16,
+                    sp.P, sp.seg_chunks, sp.p.scale, sp.p.init_f16, sp.p.final_f16, sp.p.o_f16, sp.p.state_bf16,
                     sp.p.norm_w, static_cast<const uint16_t *>(sp.p.norm_gate), sp.p.norm_eps};
 
     // ---- workgroup -> (b, key head, unit, value head of the key head). Consecutive indices
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
 #pragma unroll
                         for (int r = 0; r < 4; ++r) x[r] = (16 * jt + 4 * q4 + r == r0 + li) ? 1.0f : 0.0f;
                     } else if (src) {
-                        x = load_state4(src, srow + 16 * jt, f16);
+                        x = load_state4(src, srow + 16 * jt, f16, p.state_bf16);
                     }
                     S[bb][jt] = x;
                 }
@@ -675,7 +675,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 const int r0 = 32 * w + 16 * bb;
                 const int64_t srow = ((int64_t)(OUT ? pair * kD : 0) + r0 + li) * kD + 4 * q4;
 #pragma unroll
-                for (int jt = 0; jt < 8; ++jt) store_state4(dst, srow + 16 * jt, S[bb][jt], f16);
+                for (int jt = 0; jt < 8; ++jt) store_state4(dst, srow + 16 * jt, S[bb][jt], f16, p.state_bf16);
             }
         }
     } else {
@@ -1298,8 +1298,8 @@ __global__ __launch_bounds__(256) void gdn_state_copy_kernel(PrefillParams p, in
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= count) return;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (p.init_state) x = load_state4(p.init_state, i, p.init_f16);
-    store_state4(p.final_state, i, x, p.final_f16);
+    if (p.init_state) x = load_state4(p.init_state, i, p.init_f16, p.state_bf16);
+    store_state4(p.final_state, i, x, p.final_f16, p.state_bf16);
 }
 
 template <int C, bool OUT, int NORM = 0, bool KDA = false>

@@ -84,16 +84,20 @@ typedef enum {
 
 /*
  * Storage type of the states (prefill initial and final state, decode state). The
- * recurrence always runs in float32; a float16 state is widened on load and rounded
- * to nearest-even float16 when written, which halves the state traffic of decode.
- * The gated delta decode and prefill tests on page "27b 935/47" hold the
+ * recurrence always runs in float32; a 16-bit state is widened on load and rounded
+ * to nearest-even float16 (or bfloat16) when written, which halves the state traffic
+ * of decode. The gated delta decode and prefill tests on page "27b 935/47" hold the
  * recurrent state in float16 (the decode test rounds its expected next state
- * back to float16). float16 covers magnitudes up to 65504: a state beyond that
- * becomes infinite.
+ * back to float16). float16 covers magnitudes up to 65504 (a state beyond that
+ * becomes infinite) with 11 significant bits; bfloat16 covers float32's range with 8
+ * (each write rounds by up to 2^-9 of a value, and a decode sequence accumulates one
+ * such rounding per step). The prefill carries its state in float32 and rounds once,
+ * at the final state.
  */
 typedef enum {
     GDN_STATE_F32 = 0,
-    GDN_STATE_F16 = 1
+    GDN_STATE_F16 = 1,
+    GDN_STATE_BF16 = 2
 } gdn_state_dtype;
 
 /*
@@ -157,7 +161,8 @@ typedef struct {
  * Supported set (GDN_ERR_UNSUPPORTED otherwise):
  *   prefill:  dk = dv in {16, 32, 64, 128}, C in {16, 32, 64}, either dtype.
  *   decode:   dk = dv in {32, 64, 128}, either dtype.
- *   float16 states and float16 o: every prefill path, decode (and the gated RMSNorm for o).
+ *   float16 / bfloat16 states and float16 o: every prefill path, decode (and the gated
+ *   RMSNorm for o).
  *   (float16 o rounds each output, at most 2^-11 of its value: within the bfloat16 path's
  *   accuracy, beyond the float32 path's.)
  * Paths: bfloat16 with dk = 128 and C in {32, 64} runs the segmented MFMA prefill (below);

@@ -99,7 +99,7 @@ def _err(lib):
     ("head_dim", 96, 2, "head_dim"),
     ("qkv_dtype", 7, 1, "qkv_dtype"),
     ("head_map", 2, 1, "head_map"),
-    ("state_dtype", 2, 1, "state_dtype"),
+    ("state_dtype", 3, 1, "state_dtype"),
     ("o_dtype", 2, 1, "o_dtype"),
     ("scale", float("nan"), 1, "scale"),
     ("scale", float("inf"), 1, "scale"),
@@ -154,6 +154,10 @@ def test_state_bytes_follow_state_dtype(lib, bnd):
     assert _prefill(lib, f16, sf=ADDR["s0"] + st16 - 16) == 1 and "partially overlaps" in _err(lib)
     assert _decode(lib, _shape(bnd, seq_len=1, state_dtype=bnd.GDN_STATE_F16), o=ADDR["s0"] + st16 - 16) == 1
     assert "o overlaps state" in _err(lib)
+    # bfloat16 states are 16-bit too
+    bf = _seg_shape(bnd, state_dtype=bnd.GDN_STATE_BF16)
+    assert _passes_until_workspace(lib, bf, sf=ADDR["s0"] + st16)
+    assert _prefill(lib, bf, sf=ADDR["s0"] + st16 - 16) == 1 and "partially overlaps" in _err(lib)
 
 
 def test_decode_rejects(lib, bnd):
