@@ -495,6 +495,7 @@ def main():
             "prefill_achieved": kda_p_bytes / (kda_p_ms * 1e-3) / 1e9,
             "prefill_frac": kda_p_bytes / (kda_p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "prefill_algorithmic_bytes": kda_p_bytes,
+            "prefill_traffic": measured_prefill_traffic("traffic_bytes_per_launch_kda"),
             "decode_kernel": "gdn_decode_kernel<128, bf16, f32 state, per-channel decay>",
             "decode_ms": kda_d_ms,
             "decode_achieved": kda_d_bytes / (kda_d_ms * 1e-3) / 1e9,
