@@ -492,10 +492,8 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             float gam[NT];
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-                if (has_v) {
-                    vraw[0][m] = ld_tr_raw(Vt + va[0] + m * 4096);
-                    vraw[1][m] = ld_tr_raw(Vt + va[1] + m * 4096);
-                }
+                vraw[0][m] = ld_tr_raw(Vt + va[0] + m * 4096);
+                vraw[1][m] = ld_tr_raw(Vt + va[1] + m * 4096);
                 bt[m] = ldf4(gt + 4 * C + 64 * m + 16 * q4);
                 bg[m] = ldf4(gt + 12 * C + 64 * m + 16 * q4);
                 tdf[m] = ld4(td + m * 1024);
@@ -510,11 +508,9 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             for (int m = 0; m < NT; ++m)
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb) {
-                    f32x4 vv = {0.f, 0.f, 0.f, 0.f};
-                    if (has_v) {
+                    f32x4 vv;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) vv[r] = bf16_bits_to_f32((uint16_t)vraw[bb][m][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) vv[r] = bf16_bits_to_f32((uint16_t)vraw[bb][m][r]);
                     R[bb][m] = bt[m] * vv - bg[m] * X[bb][m];
                 }
             if constexpr (OUT) {
@@ -1193,6 +1189,15 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 request_g(min(cb + 1, clast));
             }
             lds_barrier();
+        }
+        // the identity rows have v = 0: both v slots hold zeros, written once, and the row waves
+        // read them like any values (one code path for every role, no per-chunk branch)
+        if (!has_v && tile) {
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<u16x8 *>(smem + L::oV + sl * L::kTile + (16 * m + 4 * j + lrow) * 256 + 16 * lp) = u16x8{};
         }
         request_gate(cb);
         issue(cb);
