@@ -967,18 +967,17 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 const unsigned char *Kt = smem + L::oK + s * L::kTile;
                 const unsigned char *Qt = smem + L::oQ + s * L::kTile;
                 const float *gts = reinterpret_cast<const float *>(smem + L::oG + s * 20 * C);
-                // every fragment first: lane (q4, li) reads row 16 x + li, group 4 kb + q4
+                // fragments, the diagonal tile's first: lane (q4, li) reads row 16 x + li, group
+                // 4 kb + q4 (the diagonal tile's two operands are one fragment)
                 f16x8 ka[nT][4], bk[nT][4], bq[nT][4];
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
+                auto frag = [&](int j, int kb) __attribute__((always_inline)) {
                     const int off = li * 256 + (((4 * kb + q4) ^ ksw(li)) << 4);
+                    ka[j][kb] = ld8(Kt + off + NTs[j] * 4096);
+                    bk[j][kb] = ld8(Kt + off + MMs[j] * 4096);
+                    if (OUT) bq[j][kb] = ld8(Qt + off + MMs[j] * 4096);
+                };
 #pragma unroll
-                    for (int j = 0; j < nT; ++j) {
-                        ka[j][kb] = ld8(Kt + off + NTs[j] * 4096);
-                        bk[j][kb] = ld8(Kt + off + MMs[j] * 4096);
-                        if (OUT) bq[j][kb] = ld8(Qt + off + MMs[j] * 4096);
-                    }
-                }
+                for (int kb = 0; kb < 4; ++kb) frag(0, kb);
                 float Gt[nT], btt[nT];
                 f32x4 Gs[nT];
 #pragma unroll
@@ -987,60 +986,76 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     btt[j] = gts[C + 16 * MMs[j] + li];
                     Gs[j] = *reinterpret_cast<const f32x4 *>(gts + 4 * C + 16 * NTs[j] + 4 * q4);
                 }
+#pragma unroll
+                for (int j = 1; j < nT; ++j)
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) frag(j, kb);
                 fence();
-                // raw products, lane (q4, li): t = 16 mm + li, s = 16 nt + 4 q4 + r
+                // raw products, lane (q4, li): t = 16 mm + li, s = 16 nt + 4 q4 + r; the diagonal
+                // tile's first
                 f32x4 rk[nT], rq[nT];
 #pragma unroll
                 for (int j = 0; j < nT; ++j) rk[j] = rq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                for (int j = 0; j < nT; ++j)
 #pragma unroll
-                    for (int j = 0; j < nT; ++j) {
+                    for (int kb = 0; kb < 4; ++kb) {
                         rk[j] = mfma16x16x32(ka[j][kb], bk[j][kb], rk[j]);
                         if (OUT) rq[j] = mfma16x16x32(ka[j][kb], bq[j][kb], rq[j]);
                     }
+                fence();
                 // gating; only the diagonal tile (j = 0) needs the triangular mask
                 f32x4 a[nT], aqv[nT];
                 const float sct = p.scale;
-#pragma unroll
-                for (int j = 0; j < nT; ++j) {
+                auto gate = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float gate = __expf(Gt[j] - Gs[j][r]);
+                        const float gv = __expf(Gt[j] - Gs[j][r]);
                         if (j == 0) {
                             const int sidx = 4 * q4 + r;
-                            a[j][r] = sidx < li ? btt[j] * gate * rk[j][r] : 0.0f;
-                            if (OUT) aqv[j][r] = sidx <= li ? sct * gate * rq[j][r] : 0.0f;
+                            a[j][r] = sidx < li ? btt[j] * gv * rk[j][r] : 0.0f;
+                            if (OUT) aqv[j][r] = sidx <= li ? sct * gv * rq[j][r] : 0.0f;
                         } else {
-                            a[j][r] = btt[j] * gate * rk[j][r];
-                            if (OUT) aqv[j][r] = sct * gate * rq[j][r];
+                            a[j][r] = btt[j] * gv * rk[j][r];
+                            if (OUT) aqv[j][r] = sct * gv * rq[j][r];
                         }
                     }
-                }
-                // A_qk: the tile's half of its 16-byte fragment (the block above the diagonal
-                // next to an even diagonal tile is zero)
-                if (OUT) {
-                    unsigned char *aqb = smem + L::oA + s * L::kFr * 1024 + lane * 16;
-#pragma unroll
-                    for (int j = 0; j < nT; ++j)
+                };
+                // A_qk: a tile's half of its 16-byte fragment (the block above the diagonal next to
+                // an even diagonal tile is zero)
+                unsigned char *aqb = smem + L::oA + s * L::kFr * 1024 + lane * 16;
+                auto store_aq = [&](int j) __attribute__((always_inline)) {
+                    if (OUT)
                         *reinterpret_cast<f16x4 *>(aqb + fblk(MMs[j], NTs[j] / 2) * 1024 + (NTs[j] & 1) * 8) =
                             to_f16x4(aqv[j]);
-                    if constexpr ((W & 1) == 0)
-                        *reinterpret_cast<f16x4 *>(aqb + fblk(W, W / 2) * 1024 + 8) = f16x4{};
-                }
-                // -A below the diagonal (A operands of the block substitution)
-#pragma unroll
-                for (int j = 1; j < nT; ++j)
-                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(MMs[j], NTs[j]) * 512 +
-                                               lane * 8) = to_f16x4(-a[j]);
-                // T_WW = (I + A_WW)^{-1}: lane (q4, li) builds T[li][4 q4 + e]. Its row of A_WW goes
-                // through this wave's LDS scratch (written as accumulators, read back by rows).
+                };
+                // the diagonal tile: its row of A_WW goes through this wave's LDS scratch (written as
+                // accumulators, read back by rows) for the inverse, which starts once it is back
                 float *at = reinterpret_cast<float *>(smem + L::oAt) + W * 16 * 20;
+                gate(0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) at[(4 * q4 + r) * 20 + li] = -a[0][r];  // at[s][i] = -A[i][s]
+                store_aq(0);
+                if constexpr (OUT && (W & 1) == 0) *reinterpret_cast<f16x4 *>(aqb + fblk(W, W / 2) * 1024 + 8) = f16x4{};
+                fence();
+                // the tiles below the diagonal: gated while the scratch round trip completes, stored
+                // after its reads are requested
+#pragma unroll
+                for (int j = 1; j < nT; ++j) gate(j);
+                fence();
                 float nrow[16];
 #pragma unroll
                 for (int k = 0; k < 16; ++k) nrow[k] = at[k * 20 + li];
+                fence();
+#pragma unroll
+                for (int j = 1; j < nT; ++j) {
+                    store_aq(j);
+                    // -A below the diagonal (A operands of the block substitution)
+                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(MMs[j], NTs[j]) * 512 +
+                                               lane * 8) = to_f16x4(-a[j]);
+                }
+                fence();
+                // T_WW = (I + A_WW)^{-1}: lane (q4, li) builds T[li][4 q4 + e]
                 f32x4 tq;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tq[e] = 4 * q4 + e == li ? 1.0f : 0.0f;
