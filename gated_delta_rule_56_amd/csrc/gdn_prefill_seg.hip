@@ -702,43 +702,37 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             if constexpr (!KDA) gr[sl] = gg[tg];
             br[sl] = bgp[tg];
         };
-        // per-channel decay: prep wave 6 loads the log-decays of a chunk one interval ahead (lane:
-        // channels 2 lane, 2 lane + 1, every token) and forms the chunk's factors E and channel
-        // vectors into slot sl (the chunk's parity): the inclusive prefix G over the chunk's
-        // tokens (log-decays below kKdaGMin taken as kKdaGMin, tokens past the end as 0), then
+        // per-channel decay: prep waves 6 and 7 load the log-decays of a chunk one interval ahead
+        // (lane: channel 64 (m - 2) + lane, every token) and form the chunk's factors E and channel
+        // vectors into slot sl (the chunk's parity): the inclusive prefix G over the chunk's tokens
+        // (log-decays below kKdaGMin taken as kKdaGMin, tokens past the end as 0), then
         // E[t] = e^{G_t - G_r} with r = token 7 of t's tile, and the channel vectors kVec*
-        f32x2 gq[KDA ? C : 1];
-        const float *gch = KDA ? p.g + vtok * kD + 2 * lane : nullptr;
+        float gq[KDA ? C : 1];
+        const int fch = 64 * (m - 2) + lane;  // the factor waves' channel
+        const float *gch = KDA ? p.g + vtok * kD + fch : nullptr;
         auto request_g = [&](int c) __attribute__((always_inline)) {
             if constexpr (KDA) {
 #pragma unroll
-                for (int t = 0; t < C; ++t)
-                    gq[t] = *reinterpret_cast<const f32x2 *>(gch + (int64_t)min(c * C + t, T - 1) * kD);
+                for (int t = 0; t < C; ++t) gq[t] = gch[(int64_t)min(c * C + t, T - 1) * kD];
             }
         };
         auto form_factors = [&](int c, int sl) __attribute__((always_inline)) {
             if constexpr (KDA) {
                 const int t0 = c * C;
-                f32x2 G = {0.f, 0.f};
+                float G = 0.f;
 #pragma unroll
                 for (int t = 0; t < C; ++t) {
-                    const f32x2 x = gq[t];
                     const bool live = t0 + t < T;
-                    G[0] += live ? fmaxf(x[0], kKdaGMin) : 0.f;
-                    G[1] += live ? fmaxf(x[1], kKdaGMin) : 0.f;
+                    G += live ? fmaxf(gq[t], kKdaGMin) : 0.f;
                     gq[t] = G;
                 }
-                const f32x2 r0 = gq[7], r1 = gq[23], bd = gq[15], cl = gq[C - 1];
-                unsigned char *Es = smem + L::oE + sl * C * L::kERow + 8 * lane;
+                const float r0 = gq[7], r1 = gq[23], bd = gq[15], cl = gq[C - 1];
+                unsigned char *Es = smem + L::oE + sl * C * L::kERow + 4 * fch;
 #pragma unroll
-                for (int t = 0; t < C; ++t) {
-                    const f32x2 r = t < 16 ? r0 : r1;
-                    *reinterpret_cast<f32x2 *>(Es + t * L::kERow) = f32x2{__expf(gq[t][0] - r[0]), __expf(gq[t][1] - r[1])};
-                }
-                unsigned char *EV = smem + L::oEV + sl * kNVec * 512 + 8 * lane;
-                auto put = [&](int v, f32x2 x) {
-                    *reinterpret_cast<f32x2 *>(EV + v * 512) = f32x2{__expf(x[0]), __expf(x[1])};
-                };
+                for (int t = 0; t < C; ++t)
+                    *reinterpret_cast<float *>(Es + t * L::kERow) = __expf(gq[t] - (t < 16 ? r0 : r1));
+                unsigned char *EV = smem + L::oEV + sl * kNVec * 512 + 4 * fch;
+                auto put = [&](int v, float x) { *reinterpret_cast<float *>(EV + v * 512) = __expf(x); };
                 put(kVecR0, r0);
                 put(kVecR1, r1);
                 put(kVecCR0, cl - r0);
@@ -947,7 +941,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             if constexpr (KDA) {
                 // the factors of chunk cn into the other slot (its parity), from the log-decays
                 // loaded during the last interval; then those of the chunk after it requested
-                if (m == 2) {
+                if (m >= 2) {
                     form_factors(cn, 1 - s);
                     request_g(min(cn + 1, cb + max(n, 1) - 1));
                 }
@@ -1198,7 +1192,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         const int clast = cb + max(n, 1) - 1;
         if constexpr (KDA) {
             // the first chunk's factors before its rows are converted
-            if (m == 2) {
+            if (m >= 2) {
                 request_g(cb);
                 form_factors(cb, 0);
                 request_g(min(cb + 1, clast));
