@@ -483,6 +483,9 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 fence();
             }
             lds_barrier();  // b1: the prep waves' rows of chunk i + 1 are in place
+            // issue priority to the waves on the critical path: in the output pass, the row waves
+            // from here to the end of the interval (the preparation waves before b1)
+            if constexpr (OUT) __builtin_amdgcn_s_setprio(2);
             // ---- operands of the rest of the chunk, requested together: v (transposed), the
             // gate vectors, the diagonal inverses and -A blocks, the A_qk fragments
             s16x4 vraw[2][NT];
@@ -635,6 +638,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) sb[bb][kb] = pack8(S[bb][2 * kb], S[bb][2 * kb + 1]);
+            if constexpr (OUT) __builtin_amdgcn_s_setprio(0);
             lds_barrier();  // b2: chunk i + 1 is prepared
         };
         for (int i = 0; i < n; i += 2) {
@@ -677,6 +681,9 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
     } else {
         // ================================================================ prep waves
         const int m = __builtin_amdgcn_readfirstlane(w - 4);  // token tile of this wave
+        // issue priority to the waves on the critical path: the preparation waves in the map
+        // pass, and before b1 in the output pass (the row waves raise theirs above it after b1)
+        __builtin_amdgcn_s_setprio(OUT ? 1 : 2);
         const bool tile = m < NT;
         const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ktok * kD;
         const uint16_t *qg = static_cast<const uint16_t *>(p.q) + ktok * kD;
