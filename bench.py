@@ -284,6 +284,13 @@ def main():
                                                   o=po16, final_state=psf), args.steps)
     p16_bytes = prefill_bytes(B, T, Hk, Hv, d, o_bytes=2)
 
+    # the same prefill at the other chunk lengths (the segmented passes at C = 32 and C = 16)
+    chunk_ms = {}
+    for ch in (32, 16):
+        binding.prefill(pq, pk, pv, pg, pb, None, chunk=ch, scale=px.scale, o=po, final_state=psf)
+        chunk_ms[ch] = time_batch(lambda i: binding.prefill(pq, pk, pv, pg, pb, None, chunk=ch, scale=px.scale,
+                                                            o=po, final_state=psf), max(1, args.steps // 4))
+
     # the per-channel-decay variant: the long prefill (the chunked form, 32-token chunks in the
     # segmented passes; and token by token, chunk 16) and the batched decode step, with one
     # log-decay per key channel (-softplus(N(0,1)) * 0.1 and * 1)
@@ -483,6 +490,11 @@ def main():
             "frac": p16_bytes / (p16_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": p16_bytes,
             "traffic": measured_prefill_traffic("traffic_bytes_per_launch_f16_o"),
+        },
+        "prefill_chunk_lengths": {
+            "what": "the same prefill call (float32 o) at chunk 32 and chunk 16",
+            "avg_launch_ms": {str(ch): ms for ch, ms in chunk_ms.items()},
+            "tokens_per_s": {str(ch): tokens / (ms * 1e-3) for ch, ms in chunk_ms.items()},
         },
         "kda": {
             "what": "per-channel decay (one log-decay per key channel): long prefill, chunked form "

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_abi.cpp", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_prefill_mfma.hip",
+SOURCES = ["gdn_abi.cpp", "gdn_decode.hip", "gdn_prefill_f32.hip",
            "gdn_prefill_chunk.hip", "gdn_prefill_scan.hip", "gdn_norm.hip",
            "gdn_prologue.hip", "gdn_varlen.hip", "gdn_kda.hip", "gdn_prefill_seg.hip", "gdn_static.hip"]
 

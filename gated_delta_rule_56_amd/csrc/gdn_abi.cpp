@@ -117,9 +117,10 @@ const char *gdn_status_string(gdn_status st) {
 
 const char *gdn_last_error(void) { return g_last_error; }
 
-// the segmented MFMA path: bfloat16 q/k/v, head_dim 128, chunk 32 or 64
+// the segmented MFMA path: bfloat16 q/k/v, head_dim 128 (every chunk length)
 static bool segmented_path(const gdn_shape *s) {
-    return s->qkv_dtype == GDN_DTYPE_BF16 && s->head_dim_k == 128 && (s->chunk == 32 || s->chunk == 64);
+    return s->qkv_dtype == GDN_DTYPE_BF16 && s->head_dim_k == 128 &&
+           (s->chunk == 16 || s->chunk == 32 || s->chunk == 64);
 }
 
 size_t gdn_prefill_workspace_bytes(const gdn_shape *s) {
@@ -242,10 +243,7 @@ gdn_status prefill_impl(const gdn_shape *s, const void *q, const void *k, const 
         }
         err = gdn::launch_prefill_seg(p, s->chunk, P, workspace, st);
     } else {
-        if (bf16 && d == 128)
-            err = gdn::launch_prefill_mfma(p, s->chunk, st);  // chunk 16
-        else
-            err = gdn::launch_prefill_f32(p, s->chunk, bf16, st);
+        err = gdn::launch_prefill_f32(p, s->chunk, bf16, st);  // float32 q/k/v, or bf16 below d = 128
         if (err == hipSuccess && norm && T > 0) {  // the norm as one more pass over o
             gdn::NormParams np;
             np.o = o;

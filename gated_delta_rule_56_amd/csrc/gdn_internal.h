@@ -58,8 +58,6 @@ struct DecodeParams {
     float norm_eps = 0.0f;
 };
 
-// bf16 q/k/v, D = 128, chunk 16: single fused chunked WY kernel on fp16 MFMA.
-hipError_t launch_prefill_mfma(const PrefillParams &p, int chunk, hipStream_t stream);
 // Packed sequences (bf16 q/k/v, D = 128, chunk in {32, 64}): chunk-parallel kernel (T and
 // A_qk per chunk into the workspace), then the sequential state pass reading them.
 hipError_t launch_chunk_prep(const PrefillParams &p, int chunk, void *ws, hipStream_t stream);

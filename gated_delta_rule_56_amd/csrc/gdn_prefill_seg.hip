@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             // ---- O^T = scale Y^T diag(gamma) + U^T A_qk^T; lane: token 16 m + li,
             // columns r0 + 4 q4 .. + 3
             if constexpr (OUT) {
-                f16x8 ua[2][KBC];
+                f16x8 ua[2][KBC > 0 ? KBC : 1];
 #pragma unroll
                 for (int kb = 0; kb < KBC; ++kb) {
                     ua[0][kb] = cat(uh[0][2 * kb], uh[0][2 * kb + 1]);
@@ -556,10 +556,17 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 for (int m = 0; m < NT; ++m) {
                     const float gs = gam[m] * p.scale;
                     f32x4 O0 = gs * Y[0][m], O1 = gs * Y[1][m];
+                    if constexpr (C == 16) {
+                        // one 16-token tile: the A_qk block is the fragment's first half
+                        const f16x4 aq0 = __builtin_shufflevector(aqf[0], aqf[0], 0, 1, 2, 3);
+                        O0 = mfma16x16x16(uh[0][0], aq0, O0);
+                        O1 = mfma16x16x16(uh[1][0], aq0, O1);
+                    } else {
 #pragma unroll
-                    for (int kb = 0; kb <= m / 2; ++kb) {
-                        O0 = mfma16x16x32(ua[0][kb], aqf[fblk(m, kb)], O0);
-                        O1 = mfma16x16x32(ua[1][kb], aqf[fblk(m, kb)], O1);
+                        for (int kb = 0; kb <= m / 2; ++kb) {
+                            O0 = mfma16x16x32(ua[0][kb], aqf[fblk(m, kb)], O0);
+                            O1 = mfma16x16x32(ua[1][kb], aqf[fblk(m, kb)], O1);
+                        }
                     }
                     const int t = 16 * m + li;
                     if constexpr (NORM > 0) {
@@ -589,7 +596,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 }
             }
             // ---- S <- gamma_C S + K^T (diag(exp(G_C - G)) U), k block by k block of tokens
-            f16x8 ub[2][KBC];
+            f16x8 ub[2][KBC > 0 ? KBC : 1];
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) {
                 ub[0][kb] = cat(ue[0][2 * kb], ue[0][2 * kb + 1]);
@@ -614,9 +621,24 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     S[1][jt] *= gC;
                 }
             }
-            f16x8 kt[2][8];
+            if constexpr (C == 16) {
+                // one 16-token tile: 16 x 16 x 16 steps over its tokens
+                f16x4 kt4[8];
 #pragma unroll
-            for (int jt = 0; jt < 8; ++jt) kt[0][jt] = cat(ld_tr(Ku + ta[jt]), ld_tr(Ku + ta[jt] + 4096));
+                for (int jt = 0; jt < 8; ++jt) kt4[jt] = ld_tr(Ku + ta[jt]);
+                fence();
+#pragma unroll
+                for (int jt = 0; jt < 8; ++jt) {
+                    S[0][jt] = mfma16x16x16(kt4[jt], ue[0][0], S[0][jt]);
+                    S[1][jt] = mfma16x16x16(kt4[jt], ue[1][0], S[1][jt]);
+                }
+                fence();
+            }
+            f16x8 kt[2][8];
+            if constexpr (C > 16) {
+#pragma unroll
+                for (int jt = 0; jt < 8; ++jt) kt[0][jt] = cat(ld_tr(Ku + ta[jt]), ld_tr(Ku + ta[jt] + 4096));
+            }
 #pragma unroll
             for (int kb = 0; kb < KBC; ++kb) {
                 const int cur = kb & 1, nxt = cur ^ 1;
@@ -958,10 +980,11 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         // A_qk of chunk slot s. A tile (mm, nt) is the 16 x 16 block of rows 16 mm .. and columns
         // 16 nt .. (nt <= mm) from K K^T and Q K^T; prep wave W forms its diagonal tile (W, W),
         // whose inverse it builds, and off-diagonal tiles chosen so that no wave forms more than
-        // three (C = 64: W0 (3,0) (3,1), W1 (1,0) (2,0), W2 (2,1), W3 (3,2); C = 32: W1 (1,0)).
+        // three (C = 64: W0 (3,0) (3,1), W1 (1,0) (2,0), W2 (2,1), W3 (3,2); C = 32: W1 (1,0); C = 16:
+        // W0 its diagonal tile only).
         auto phase2w = [&](int s, auto wc) __attribute__((always_inline)) {
             constexpr int W = decltype(wc)::value;
-            constexpr int nT = C == 64 ? (W < 2 ? 3 : 2) : (W == 0 ? 1 : W == 1 ? 2 : 0);
+            constexpr int nT = C == 64 ? (W < 2 ? 3 : 2) : C == 32 ? (W == 0 ? 1 : W == 1 ? 2 : 0) : (W == 0 ? 1 : 0);
             constexpr int MMs[3] = {W, C == 64 ? (W == 0 ? 3 : W == 1 ? 1 : W) : W, C == 64 ? (W == 0 ? 3 : 2) : 0};
             constexpr int NTs[3] = {W, C == 64 ? (W == 0 ? 0 : W == 1 ? 0 : W - 1) : 0, C == 64 ? (W == 0 ? 1 : 0) : 0};
             if constexpr (nT > 0) {
@@ -1408,6 +1431,7 @@ hipError_t launch_prefill_seg(const PrefillParams &p, int chunk, int P, void *ws
     sp.ws_m = w + 2 * pairs * P * kD * kD;
     if (kda) return chunk == 32 ? launch_seg_c<32, true>(sp, stream) : hipErrorInvalidValue;
     switch (chunk) {
+        case 16: return launch_seg_c<16>(sp, stream);
         case 32: return launch_seg_c<32>(sp, stream);
         case 64: return launch_seg_c<64>(sp, stream);
         default: return hipErrorInvalidValue;

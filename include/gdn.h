@@ -144,7 +144,7 @@ typedef struct {
  *           NULL for no gate factor; 16-byte aligned
  *   eps     finite, >= 0
  * weight and gate must not overlap any output. Fused into the output store of the segmented
- * bf16 prefill (dk = 128, C in {32, 64}) and of decode when B * Hv >= 256 (a workgroup then
+ * bf16 prefill (dk = 128, every C) and of decode when B * Hv >= 256 (a workgroup then
  * owns whole output rows); the other paths apply it as one more pass over o after the scan.
  * In the segmented prefill a row passes through float16 twice: before the norm, each group of
  * 8 values scaled by a power of two taken from its own sum of squares (so one rounding to 11
@@ -165,12 +165,11 @@ typedef struct {
  *   RMSNorm for o).
  *   (float16 o rounds each output, at most 2^-11 of its value: within the bfloat16 path's
  *   accuracy, beyond the float32 path's.)
- * Paths: bfloat16 with dk = 128 and C in {32, 64} runs the segmented MFMA prefill (below);
- * bfloat16 with dk = 128 and C = 16 one fused MFMA kernel that redoes the chunk products in
- * every block of 16 state rows (about ten times slower on long sequences); float32 q/k/v,
- * and bfloat16 with dk < 128, a float32 VALU kernel.
+ * Paths: bfloat16 with dk = 128 runs the segmented MFMA prefill (below; C = 16 about 1.3 times
+ * the time of C = 64 on long sequences, C = 32 about 1.2 times); float32 q/k/v, and bfloat16
+ * with dk < 128, a float32 VALU kernel.
  *
- * Segmented prefill (bfloat16, dk = 128, C in {32, 64}): the chunks of each sequence are cut
+ * Segmented prefill (bfloat16, dk = 128, C in {16, 32, 64}): the chunks of each sequence are cut
  * into P segments of equal chunk counts that run in parallel: a map pass computes, per
  * segment, the end state of segment 0 and the affine map S -> S M + N of each later segment
  * (the chunk update is affine in the start state), a combine chains the maps into every

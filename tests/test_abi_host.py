@@ -246,8 +246,9 @@ def test_workspace_query(lib, bnd):
     assert q(big) == _ws_bytes(1, 32, 8) == 50331648
     # a batch that fills the GPU by itself needs no segments
     assert q(_shape(bnd, batch=8, seq_len=32768, num_k_heads=16, num_v_heads=32)) == 0
+    # chunk 16 segments like 32 and 64 (its chunk count is higher, the preferred segment count the same)
+    assert q(_shape(bnd, seq_len=4096, chunk=16)) == q(_shape(bnd, seq_len=4096, chunk=32)) > 0
     # paths that do not segment, invalid shapes
-    assert q(_shape(bnd, seq_len=4096, chunk=16)) == 0
     assert q(_shape(bnd, seq_len=4096, qkv_dtype=bnd.GDN_DTYPE_F32)) == 0
     assert q(_shape(bnd, seq_len=4096, head_dim=64)) == 0
     assert q(_shape(bnd, batch=0)) == 0
@@ -264,7 +265,9 @@ def test_segments_follow_workspace(lib, bnd):
     assert seg(_ws_bytes(1, 32, 3)) == 3
     assert seg(_ws_bytes(1, 32, 2) - 1) == 1
     assert seg(0) == 1
-    assert lib.gdn_prefill_segments(ctypes.byref(_shape(bnd, seq_len=4096, chunk=16)), 1 << 30) == 1
+    assert lib.gdn_prefill_segments(ctypes.byref(_shape(bnd, seq_len=4096, chunk=16)), 1 << 30) == \
+        lib.gdn_prefill_segments(ctypes.byref(_shape(bnd, seq_len=4096, chunk=32)), 1 << 30) > 1
+    assert lib.gdn_prefill_segments(ctypes.byref(_shape(bnd, seq_len=4096, qkv_dtype=bnd.GDN_DTYPE_F32)), 1 << 30) == 1
     assert lib.gdn_prefill_segments(ctypes.byref(_shape(bnd, batch=0)), 1 << 30) == 0
     short = _shape(bnd, seq_len=65, chunk=32)  # 3 chunks: at most 3 segments
     assert lib.gdn_prefill_segments(ctypes.byref(short), 1 << 40) == 3
