@@ -1,4 +1,4 @@
-"""GPU parity of the segmented bfloat16 prefill (head_dim 128, chunk 32 and 64) against the
+"""GPU parity of the segmented bfloat16 prefill (head_dim 128, chunk 16, 32 and 64) against the
 float64 oracle, over the segment counts the workspace size selects: one segment (no
 workspace), two, several, and one per chunk; ragged tails, both head maps, in-place and
 float16 storage (needs an MI355X).
@@ -68,6 +68,10 @@ def check(oracle_lib, x, o, sf, head_map=0, init=True, tol=TOL_BF16, label=""):
     (1000, 32, 5, True),
     (1000, 64, 16, True),   # the preferred count for 4 value heads: one chunk per segment
     (4100, 64, 8, True),
+    (40, 16, 1, True),      # chunk 16: one tile per chunk, ragged tail
+    (40, 16, 3, True),      # one chunk per segment
+    (300, 16, 4, True),
+    (1000, 16, 16, True),
 ])
 def test_segment_counts(gdn, oracle_lib, T, chunk, P, init):
     x = inputs.generate(1, T, 2, 4, 128, "bf16", seed=T + chunk + P, init_state="normal")
@@ -76,7 +80,7 @@ def test_segment_counts(gdn, oracle_lib, T, chunk, P, init):
 
 
 @pytest.mark.parametrize("T", [1, 15, 33])
-@pytest.mark.parametrize("chunk", [32, 64])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_short_sequences(gdn, oracle_lib, T, chunk):
     """Fewer tokens than a chunk (or just over one): the whole sequence is a masked tail."""
     x = inputs.generate(2, T, 2, 4, 128, "bf16", seed=40 + T, init_state="normal")
