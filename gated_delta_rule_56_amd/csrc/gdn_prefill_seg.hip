@@ -482,29 +482,51 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 }
                 fence();
             }
-            lds_barrier();  // b1: the prep waves' rows of chunk i + 1 are in place
-            // issue priority to the waves on the critical path: in the output pass, the row waves
-            // from here to the end of the interval (the preparation waves before b1)
-            if constexpr (OUT) __builtin_amdgcn_s_setprio(2);
-            // ---- operands of the rest of the chunk, requested together: v (transposed), the
-            // gate vectors, the diagonal inverses and -A blocks, the A_qk fragments
+            // ---- operands of the rest of the chunk: v (transposed), the gate vectors, the diagonal
+            // inverses and -A blocks, the A_qk fragments. They are this chunk's slot, complete since
+            // the last b2, so where the registers allow (all but the 64-token output pass) they are
+            // requested before b1, to arrive while the preparation waves finish and ahead of their
+            // post-b1 traffic
+            constexpr bool kEarly = !OUT || C < 64;
             s16x4 vraw[2][NT];
             f32x4 bt[NT], bg[NT];
             f16x4 tdf[NT], tef[NT], naf[L::kNA > 0 ? L::kNA : 1];
             f16x8 aqf[L::kFr];
             float gam[NT];
+            auto request_rest = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int m = 0; m < NT; ++m) {
-                vraw[0][m] = ld_tr_raw(Vt + va[0] + m * 4096);
-                vraw[1][m] = ld_tr_raw(Vt + va[1] + m * 4096);
-                bt[m] = ldf4(gt + 4 * C + 64 * m + 16 * q4);
-                bg[m] = ldf4(gt + 12 * C + 64 * m + 16 * q4);
-                tdf[m] = ld4(td + m * 1024);
-                tef[m] = ld4(td + m * 1024 + 512);
+                for (int m = 0; m < NT; ++m) {
+                    vraw[0][m] = ld_tr_raw(Vt + va[0] + m * 4096);
+                    vraw[1][m] = ld_tr_raw(Vt + va[1] + m * 4096);
+                    bt[m] = ldf4(gt + 4 * C + 64 * m + 16 * q4);
+                    bg[m] = ldf4(gt + 12 * C + 64 * m + 16 * q4);
+                    tdf[m] = ld4(td + m * 1024);
+                    tef[m] = ld4(td + m * 1024 + 512);
+                }
+#pragma unroll
+                for (int e = 0; e < L::kNA; ++e) naf[e] = ld4(na + e * 512);
+            };
+            auto request_aq = [&]() __attribute__((always_inline)) {
+                if constexpr (OUT) {
+#pragma unroll
+                    for (int f = 0; f < L::kFr; ++f) aqf[f] = ld8(aq + f * 1024);
+#pragma unroll
+                    for (int m = 0; m < NT; ++m) gam[m] = *reinterpret_cast<const float *>(gt + 4 * (16 * m + li));
+                }
+            };
+            if constexpr (kEarly) {
+                request_rest();
+                request_aq();
+                fence();
             }
-#pragma unroll
-            for (int e = 0; e < L::kNA; ++e) naf[e] = ld4(na + e * 512);
-            fence();
+            lds_barrier();  // b1: the prep waves' rows of chunk i + 1 are in place
+            // issue priority to the waves on the critical path: in the output pass, the row waves
+            // from here to the end of the interval (the preparation waves before b1)
+            if constexpr (OUT) __builtin_amdgcn_s_setprio(2);
+            if constexpr (!kEarly) {
+                request_rest();
+                fence();
+            }
             // R = beta V - beta gamma X  (v: tokens 16 m + 4 q4 + r, column r0 + li)
             f32x4 R[2][NT];
 #pragma unroll
@@ -516,12 +538,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     for (int r = 0; r < 4; ++r) vv[r] = bf16_bits_to_f32((uint16_t)vraw[bb][m][r]);
                     R[bb][m] = bt[m] * vv - bg[m] * X[bb][m];
                 }
-            if constexpr (OUT) {
-#pragma unroll
-                for (int f = 0; f < L::kFr; ++f) aqf[f] = ld8(aq + f * 1024);
-#pragma unroll
-                for (int m = 0; m < NT; ++m) gam[m] = *reinterpret_cast<const float *>(gt + 4 * (16 * m + li));
-            }
+            if constexpr (!kEarly) request_aq();  // after R, as its registers free
             fence();
             // ---- U_m = T_mm (R_m - sum_{j<m} A_mj U_j), the two row blocks interleaved, and the
             // update's values diag(exp(G_C - G)) U_m from the scaled inverse
