@@ -147,6 +147,12 @@ __device__ __forceinline__ s16x4 ld_tr_raw(const unsigned char *p) {
 __device__ __forceinline__ f16x4 ld_tr(const unsigned char *p) { return __builtin_bit_cast(f16x4, ld_tr_raw(p)); }
 
 // Workgroup barrier for LDS traffic only: outstanding global loads stay in flight.
+// The gate vectors of a chunk into its LDS slot, lane = token: G = inclusive prefix of g over
+// the chunk, gamma = e^G, beta, e^{G_C - G}, beta gamma, G ([5][C] float32). Tokens past the
+// end come in with g = beta = 0.
+template <int C>
+__device__ __forceinline__ void form_gates(unsigned char *slot, float gv, float bv, int lane);
+
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // keeps the compiler from moving instructions across this point (so that a batch of LDS
@@ -273,12 +279,30 @@ __device__ __forceinline__ float stage_unscale(float ss) {
     return __uint_as_float((uint32_t)(127 - 14 + h) << 23);
 }
 
+template <int C>
+__device__ __forceinline__ void form_gates(unsigned char *slot, float gv, float bv, int lane) {
+    const float G = wave_prefix_sum(gv);
+    const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), C - 1));
+    if (lane < C) {
+        float *gts = reinterpret_cast<float *>(slot);
+        const float gam = __expf(G);
+        gts[lane] = gam;
+        gts[C + lane] = bv;
+        gts[2 * C + lane] = __expf(gC - G);
+        gts[3 * C + lane] = bv * gam;
+        gts[4 * C + lane] = G;
+    }
+}
+
 // NORM: 0 no output norm, 1 the norm without a gate, 2 with a gate. KDA: one log-decay per key
 // channel (g [B][Hv][T][dk]), C = 32.
 template <int C, bool OUT, int NORM = 0, bool KDA = false>
 __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams sp) {
     using L = SegSmem<C, OUT, (NORM > 0), KDA>;
     constexpr int NT = L::NT, KBC = L::KBC;
+    // in the map pass (no global stores in the loop) row wave 0, idle after its X products until
+    // b1, forms the next chunk's gate vectors in place of the first preparation wave
+    constexpr bool kRowScan = !OUT && !KDA;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // every argument into a scalar local: a reference to the argument structure would make
     // the compiler copy it to scratch memory
@@ -432,6 +456,26 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             }
         };
 
+        // map pass: row wave 0 forms every chunk's gate vectors (kRowScan), the first one's here,
+        // each later one's in the interval before its chunk, from g and beta loaded an interval
+        // ahead
+        float rg = 0.f, rb = 0.f;
+        const int rclast = cb + max(n, 1) - 1;
+        const bool scan_wave = kRowScan && __builtin_amdgcn_readfirstlane(w) == 0;
+        auto request_gates = [&](int c) __attribute__((always_inline)) {
+            const int tg = min(c * C + lane, T - 1);
+            rg = p.g[vtok + tg];
+            rb = p.beta[vtok + tg];
+        };
+        auto scan_gates = [&](int c, int sl) __attribute__((always_inline)) {
+            const bool gl = lane < C && c * C + lane < T;  // tokens past the end: g = beta = 0
+            form_gates<C>(smem + L::oG + sl * 20 * C, gl ? rg : 0.f, gl ? rb : 0.f, lane);
+        };
+        if (scan_wave) {
+            request_gates(cb);
+            scan_gates(cb, 0);
+            request_gates(min(cb + 1, rclast));
+        }
         lds_barrier();
         lds_barrier();
         if constexpr (KDA) lds_barrier();  // the preparation waves' first factors
@@ -481,6 +525,12 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     }
                 }
                 fence();
+            }
+            // the next chunk's gate vectors into the other slot (read by the preparation waves after
+            // b1), then the g and beta of the chunk after it requested
+            if (scan_wave) {
+                scan_gates(min(cb + i + 1, rclast), 1 - s);
+                request_gates(min(cb + i + 2, rclast));
             }
             // ---- operands of the rest of the chunk: v (transposed), the gate vectors, the diagonal
             // inverses and -A blocks, the A_qk fragments. They are this chunk's slot, complete since
@@ -741,6 +791,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         const int lrow = lane >> 4, lp = lane & 15;
         // requests of chunk c (absolute): g and beta, the rows of one tensor
         auto request_gb = [&](int c, auto slc) __attribute__((always_inline)) {
+            if constexpr (kRowScan) return;  // row wave 0 loads and scans them
             constexpr int sl = decltype(slc)::value;
             // every prep wave loads them (only wave 4 uses them): unconditional loads keep the
             // wait counts before their use exact
@@ -850,8 +901,9 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 }
             }
         };
-        // P1: wave 4 forms the gate vectors of chunk c; tile m's rows of chunk c into slot s (waits
-        // for their loads), each tensor's rows of chunk cn requested right after
+        // P1: wave 4 forms the gate vectors of chunk c (in the map pass row wave 0 does); tile m's
+        // rows of chunk c into slot s (waits for their loads), each tensor's rows of chunk cn
+        // requested right after
         auto phase1 = [&](int c, int cn, auto sc) __attribute__((always_inline)) {
             constexpr int s = decltype(sc)::value;
             const int t0 = c * C;
@@ -868,21 +920,10 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     gts[3 * C + lane] = bv;
                     gts[4 * C + lane] = 0.0f;
                 }
-            } else if (m == 0) {
-                // G = inclusive prefix sum of g over the chunk; tokens past the end have g = beta = 0
+            } else if (!kRowScan && m == 0) {
+                // tokens past the end have g = beta = 0
                 const bool gl = lane < C && t0 + lane < T;
-                const float gv = gl ? gr[s] : 0.f, bv = gl ? br[s] : 0.f;
-                const float G = wave_prefix_sum(gv);
-                const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), C - 1));
-                if (lane < C) {
-                    float *gts = reinterpret_cast<float *>(smem + L::oG + s * 20 * C);
-                    const float gam = __expf(G);
-                    gts[lane] = gam;
-                    gts[C + lane] = bv;
-                    gts[2 * C + lane] = __expf(gC - G);
-                    gts[3 * C + lane] = bv * gam;
-                    gts[4 * C + lane] = G;
-                }
+                form_gates<C>(smem + L::oG + s * 20 * C, gl ? gr[s] : 0.f, gl ? br[s] : 0.f, lane);
             }
             request_gb(cn, IC<1 - s>{});  // after the scan: its wait then covers only older requests
             fence();
