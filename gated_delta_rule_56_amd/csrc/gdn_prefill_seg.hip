@@ -1324,27 +1324,37 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
     }
 }
 
-// S_{p+1} = S_p M_p + N_p for p = 1 .. P-2, one workgroup per (pair, block of 16 rows), fp32.
-// Thread (r, cg) owns row r of the block, columns 8 cg .. 8 cg + 7. M_p goes through LDS; the
-// next map and the next N rows are loaded into registers while the current product runs, so
-// that only the chain of S (LDS and arithmetic) is sequential.
+// S_{p+1} = S_p M_p + N_p for p = 1 .. P-2, one workgroup per (pair, block of 16 rows), fp32,
+// the 16 x 128 x 128 product on float32 MFMAs. M_p goes through LDS; the next map and the next
+// N values are loaded into registers while the current product runs, so that only the chain of
+// S (LDS and matrix core) is sequential.
+constexpr int kCombineMRow = kD + 16;  // 144 floats: four map rows 16 banks apart
+
 __global__ __launch_bounds__(256) void gdn_seg_combine_kernel(SegParams sp) {
     extern __shared__ __attribute__((aligned(16))) unsigned char csmem[];
+    // srow: this block's 16 rows of the running start state; mt: the map M_seg, rows padded to
+    // 144 floats so that the operand reads below meet 64 distinct banks
     float(*srow)[kD + 4] = reinterpret_cast<float(*)[kD + 4]>(csmem);
-    float(*mt)[kD] = reinterpret_cast<float(*)[kD]>(csmem + 16 * (kD + 4) * 4);
+    float(*mt)[kCombineMRow] = reinterpret_cast<float(*)[kCombineMRow]>(csmem + 16 * (kD + 4) * 4);
     // workgroups go round-robin over the 8 XCDs: the 8 row blocks of a pair share one XCD (and
     // its L2 for the maps they all read) when the grid is a multiple of 64
     const int nb = gridDim.x;
     const int lin = (nb & 63) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     const int pair = lin >> 3, rb = lin & 7;
     const int tid = threadIdx.x, r = tid >> 4, cg = tid & 15;
+    const int lane = tid & 63, w = tid >> 6, li = lane & 15, q4 = lane >> 4;
     const int64_t base = (int64_t)pair * sp.P;
     constexpr int kPer = kD * kD / 4 / 256;  // f32x4 of a map per thread
-    f32x4 mnext[kPer], n0, n1;
-    auto load_next = [&](int seg) {  // this thread's 8 values of N_seg (first: needed first), M_seg
-        const float *N = sp.ws_n + (base + seg) * (kD * kD) + rb * 16 * kD + r * kD + 8 * cg;
-        n0 = *reinterpret_cast<const f32x4 *>(N);
-        n1 = *reinterpret_cast<const f32x4 *>(N + 4);
+    // the products on float32 MFMAs (16 x 16 x 4): wave w owns the 16-column tiles 2 w and
+    // 2 w + 1; lane (q4, li) holds rows 4 q4 + e, column 16 jt + li of the new state, with N
+    // there as the products' start
+    f32x4 mnext[kPer], nnext[2];
+    auto load_next = [&](int seg) {  // N_seg at this lane's output places (first: needed first), M_seg
+        const float *N = sp.ws_n + (base + seg) * (kD * kD) + (rb * 16 + 4 * q4) * kD + li;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nnext[t][e] = N[e * kD + 16 * (2 * w + t)];
         const f32x4 *M = reinterpret_cast<const f32x4 *>(sp.ws_m + (base + seg) * (kD * kD));
 #pragma unroll
         for (int j = 0; j < kPer; ++j) mnext[j] = M[tid + 256 * j];
@@ -1356,44 +1366,37 @@ __global__ __launch_bounds__(256) void gdn_seg_combine_kernel(SegParams sp) {
     *reinterpret_cast<f32x4 *>(&srow[r][8 * cg]) = x0;
     *reinterpret_cast<f32x4 *>(&srow[r][8 * cg + 4]) = x1;
     for (int seg = 1; seg + 1 < sp.P; ++seg) {
-        float *Sn = sp.ws_start + (base + seg + 1) * (kD * kD) + rb * 16 * kD;
+        float *Sn = sp.ws_start + (base + seg + 1) * (kD * kD) + (rb * 16 + 4 * q4) * kD + li;
         __syncthreads();  // srow written; earlier reads of mt done
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) reinterpret_cast<f32x4 *>(&mt[0][0])[tid + 256 * j] = mnext[j];
-        const f32x4 c0 = n0, c1 = n1;
+        for (int j = 0; j < kPer; ++j) {
+            const int f = tid + 256 * j;  // f32x4 index of the map: row f / 32, columns 4 (f % 32) ..
+            *reinterpret_cast<f32x4 *>(&mt[f >> 5][4 * (f & 31)]) = mnext[j];
+        }
+        f32x4 acc[2] = {nnext[0], nnext[1]};
         if (seg + 2 < sp.P) load_next(seg + 1);
         __syncthreads();
-        // eight rows of the map per group, read into their own registers before they are used
-        // (with one buffer reused, every read would wait out the LDS latency)
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < kD; k0 += 8) {
-            const f32x4 sa = *reinterpret_cast<const f32x4 *>(&srow[r][k0]);
-            const f32x4 sb = *reinterpret_cast<const f32x4 *>(&srow[r][k0 + 4]);
-            f32x4 m0[8], m1[8];
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                m0[kk] = *reinterpret_cast<const f32x4 *>(&mt[k0 + kk][8 * cg]);
-                m1[kk] = *reinterpret_cast<const f32x4 *>(&mt[k0 + kk][8 * cg + 4]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const float sv = kk < 4 ? sa[kk] : sb[kk - 4];
-                a0 += sv * m0[kk];
-                a1 += sv * m1[kk];
-            }
+        // S_new = S M + N: A = S (row li, k = 4 s + q4), B = M (row k, column 16 jt + li)
+#pragma unroll 8
+        for (int s = 0; s < kD / 4; ++s) {
+            const float a = srow[li][4 * s + q4];
+            const float *mrow = &mt[4 * s + q4][li];
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, mrow[32 * w], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, mrow[32 * w + 16], acc[1], 0, 0, 0);
         }
-        a0 += c0;
-        a1 += c1;
-        *reinterpret_cast<f32x4 *>(Sn + r * kD + 8 * cg) = a0;
-        *reinterpret_cast<f32x4 *>(Sn + r * kD + 8 * cg + 4) = a1;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sn[e * kD + 16 * (2 * w + t)] = acc[t][e];
         __syncthreads();  // every read of srow done
-        *reinterpret_cast<f32x4 *>(&srow[r][8 * cg]) = a0;
-        *reinterpret_cast<f32x4 *>(&srow[r][8 * cg + 4]) = a1;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) srow[4 * q4 + e][16 * (2 * w + t) + li] = acc[t][e];
     }
 }
 
-constexpr size_t kCombineLds = 16 * (kD + 4) * 4 + kD * kD * 4;
+constexpr size_t kCombineLds = 16 * (kD + 4) * 4 + kD * kCombineMRow * 4;
 
 // T = 0: the final state is the initial state (converted to its storage type), or zero.
 __global__ __launch_bounds__(256) void gdn_state_copy_kernel(PrefillParams p, int64_t count) {

@@ -79,6 +79,17 @@ def test_segment_counts(gdn, oracle_lib, T, chunk, P, init):
     check(oracle_lib, x, o, sf, init=init, label=f"T{T} C{chunk} P{P} init{init}")
 
 
+@pytest.mark.parametrize("T,chunk,P", [(1000, 64, 16), (4100, 64, 8), (1000, 32, 5), (1000, 16, 16)])
+def test_segment_counts_slow_decay(gdn, oracle_lib, T, chunk, P):
+    """Gates near one: the state that enters a segment still counts at its end, so the chain
+    S_{p+1} = S_p M_p + N_p carries a full-rank share of the result through every segment."""
+    x = inputs.generate(1, T, 2, 4, 128, "bf16", seed=7 * T + chunk + P, init_state="normal", decay_mult=0.002)
+    seg = T / P
+    assert np.exp(x.g.astype(np.float64)[..., :int(seg)].sum(axis=-1)).min() > 0.05  # a segment keeps > 5%
+    o, sf = run(gdn, x, chunk, P)
+    check(oracle_lib, x, o, sf, label=f"slow decay T{T} C{chunk} P{P}")
+
+
 @pytest.mark.parametrize("T", [1, 15, 33])
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_short_sequences(gdn, oracle_lib, T, chunk):
