@@ -391,7 +391,8 @@ def main():
     counted_flops = measured_prefill_mfma_flops()  # rocprofv3 MFMA op counters, when current
     segments = binding.prefill_segments(B, T, Hk, Hv, d, binding.prefill_workspace_bytes(B, T, Hk, Hv, d, chunk=pw.chunk),
                                         chunk=pw.chunk)
-    map_wgs = B * Hv * (2 * segments - 3) if segments > 1 else 0
+    # map pass: one 12-wave workgroup per (pair, segment) but the last, at 32-token chunks
+    map_wgs = B * Hv * (segments - 1)
 
     result = {
         "metric": "GDN prefill tokens/s (Hv=32,d=128,T=32k) + MFMA util; decode HBM GB/s",
@@ -415,7 +416,7 @@ def main():
                        "state_bytes": dB * dHv * dd * dd * 4},
         },
         "roofline": {
-            "kernel": (f"gdn_prefill call, {segments} segments: gdn_seg_pass_kernel<64, false> (map pass, "
+            "kernel": (f"gdn_prefill call, {segments} segments: gdn_seg_pass_kernel<32, false> (map pass, "
                        f"{map_wgs} workgroups) + gdn_seg_combine_kernel + gdn_seg_pass_kernel<64, true> "
                        f"(output pass, {B * Hv * segments} workgroups)"),
             "bound": "mfma",

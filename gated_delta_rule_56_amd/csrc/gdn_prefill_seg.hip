@@ -25,19 +25,23 @@
 // identity row is a state row; rows never mix). Three launches:
 //   1. map pass (OUT = false): segment 0 from the initial state (its end is the
 //      true start of segment 1), and for segments 1 .. P-2 both N_p (role 0) and
-//      M_p (role 1);
+//      M_p (role 1). With scalar decay one workgroup per (pair, segment) holds both
+//      row sets over one shared chunk preparation, at 32-token chunks (16 at chunk
+//      16; the 64-token call's segments are whole 32-token chunks too);
 //   2. combine: S_{p+1} = S_p M_p + N_p, sequential over the segments, in fp32;
 //   3. output pass (OUT = true): every segment from its true start, writing o and,
 //      in the last segment, the final state.
 // With P = 1 only the output pass runs.
 //
-// Workgroup of 8 waves (wave i on SIMD i % 4), two barriers per chunk:
+// Workgroup of 8 waves (wave i on SIMD i % 4), two barriers per chunk (the scalar-decay
+// map pass: 12 waves, row waves 0-3 for the zero-start rows, 4-7 for the identity
+// rows, preparation waves 8-11):
 //   waves 0-3, "row waves": state rows 32 w .. 32 w + 31 as two 16-row MFMA blocks
 //     held in registers for the whole segment; per chunk X and (OUT) Y = S Q^T before
 //     the first barrier, then R, U, O^T and the update. Every operand of chunk i is in
 //     LDS slot i & 1 when the chunk starts; LDS operands are requested in batches one
 //     batch ahead of the MFMAs that use them.
-//   waves 4-7, "prep waves", token tile m = w - 4: prepare chunk i + 1 into slot
+//   waves 4-7 (8-11), "prep waves", token tile m: prepare chunk i + 1 into slot
 //     (i + 1) & 1 during chunk i. Before the first barrier (P1) each converts its
 //     16 raw bf16 k and q rows (loaded one chunk earlier into registers) to the fp16
 //     tiles and stores its v rows, wave 4 also forms the gate vectors, and each
@@ -60,7 +64,11 @@ namespace gdn {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kSegThreads = 512;
+// threads of a segment-pass workgroup: 4 row waves and 4 preparation waves, or in the scalar-decay
+// map pass 8 row waves (the zero-start rows and the identity rows of one segment) and 4
+// preparation waves
+template <bool OUT, bool KDA>
+__host__ __device__ constexpr int seg_threads() { return (!OUT && !KDA ? 12 : 8) * 64; }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -115,7 +123,9 @@ struct SegSmem {
     // so that the 8-byte accesses of 32 lanes (16 tokens, two column groups) meet all 64 banks;
     // the partial sums of squares [C][20] f32 (16 used: 4 row waves x 4 lanes of 8 columns);
     // the norm weight [128] f32
-    static constexpr size_t oNO = oEC + (KDA ? 2 * 512 : 0);
+    // the merged map pass (scalar decay): a zero v tile read by the identity rows
+    static constexpr size_t oZV = oEC + (KDA ? 2 * 512 : 0);
+    static constexpr size_t oNO = oZV + (!OUT && !KDA ? kTile : 0);
     static constexpr size_t oNP = oNO + (NORM ? (size_t)C * 272 : 0);
     static constexpr size_t oNW = oNP + (NORM ? (size_t)C * 80 : 0);
     static constexpr size_t kBytes = oNW + (NORM ? 512 : 0);
@@ -123,7 +133,7 @@ struct SegSmem {
     static_assert(!KDA || (C == 32 && !NORM), "the per-channel decay runs at C = 32, without the norm");
     static_assert(oQ % 16 == 0 && oV % 16 == 0 && oA % 16 == 0 && oNA % 16 == 0 && oTd % 16 == 0 &&
                       oG % 16 == 0 && oAt % 16 == 0 && oKT % 16 == 0 && oRK % 16 == 0 && oRQ % 16 == 0 &&
-                      oE % 16 == 0 && oEV % 16 == 0 && oEC % 16 == 0 && oNO % 16 == 0 && oNP % 16 == 0 &&
+                      oE % 16 == 0 && oEV % 16 == 0 && oEC % 16 == 0 && oZV % 16 == 0 && oNO % 16 == 0 && oNP % 16 == 0 &&
                       oNW % 16 == 0,
                   "alignment");
     static_assert(kBytes <= 160 * 1024, "LDS");
@@ -297,9 +307,16 @@ __device__ __forceinline__ void form_gates(unsigned char *slot, float gv, float 
 // NORM: 0 no output norm, 1 the norm without a gate, 2 with a gate. KDA: one log-decay per key
 // channel (g [B][Hv][T][dk]), C = 32.
 template <int C, bool OUT, int NORM = 0, bool KDA = false>
-__global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams sp) {
+__global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_kernel(SegParams sp) {
     using L = SegSmem<C, OUT, (NORM > 0), KDA>;
     constexpr int NT = L::NT, KBC = L::KBC;
+    // scalar-decay map pass: one workgroup per (pair, segment) runs both the zero-start rows
+    // (waves 0-3, with v) and the identity rows (waves 4-7, v = 0) on one shared chunk
+    // preparation (waves 8-11)
+    constexpr bool kMerge = !OUT && !KDA;
+    constexpr int kRowW = kMerge ? 8 : 4;
+    // three waves per SIMD leave each 168 VGPRs: the merged map pass runs 32- and 16-token chunks
+    static_assert(!kMerge || C <= 32, "the merged map pass runs at C <= 32");
     // in the map pass (no global stores in the loop) row wave 0, idle after its X products until
     // b1, forms the next chunk's gate vectors in place of the first preparation wave
     constexpr bool kRowScan = !OUT && !KDA;
@@ -331,11 +348,16 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
     const int ratio = p.Hv / p.Hk;
     const int jj = lin % ratio;
     int rest = lin / ratio;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int seg, role;  // role 0: state rows (from the start state, with v); 1: identity rows, v = 0
     if (OUT) {
         seg = rest % p.P;
         rest /= p.P;
         role = 0;
+    } else if (kMerge) {
+        seg = rest % (p.P - 1);
+        rest /= p.P - 1;
+        role = (w >> 2) == 1 ? 1 : 0;  // the preparation waves load v: role 0
     } else {
         const int units = 2 * p.P - 3;
         const int u = rest % units;
@@ -356,12 +378,13 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
     const int64_t vtok = (int64_t)pair * p.Ts;                // first token row of v, g, beta, o
     const int64_t wsi = ((int64_t)pair * p.P + seg) * (kD * kD);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int li = lane & 15, q4 = lane >> 4;
 
-    if (w < 4) {
+    if (w < kRowW) {
         // ================================================================ row waves
-        // S[bb][jt][r] = state[r0 + li][16 jt + 4 q4 + r], r0 = 32 w + 16 bb
+        const int wr = w & 3;  // row block of this wave
+        // S[bb][jt][r] = state[r0 + li][16 jt + 4 q4 + r], r0 = 32 wr + 16 bb
         f32x4 S[2][8];
         {
             // start state: the output pass reads the float32 copies in the workspace when the
@@ -379,7 +402,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
-                const int r0 = 32 * w + 16 * bb;
+                const int r0 = 32 * wr + 16 * bb;
                 const int64_t srow = ws_layout ? (int64_t)(r0 + li) * kD + 4 * q4
                                                : ((int64_t)pair * kD + r0 + li) * kD + 4 * q4;
 #pragma unroll
@@ -400,7 +423,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         if (!OUT && role == 0 && seg == 0 && p.init_state) {
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
-                const int64_t wrow = (int64_t)(32 * w + 16 * bb + li) * kD + 4 * q4;
+                const int64_t wrow = (int64_t)(32 * wr + 16 * bb + li) * kD + 4 * q4;
 #pragma unroll
                 for (int jt = 0; jt < 8; ++jt)
                     *reinterpret_cast<f32x4 *>(p.ws_start + wsi + wrow + 16 * jt) = S[bb][jt];
@@ -411,6 +434,16 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) sb[bb][kb] = pack8(S[bb][2 * kb], S[bb][2 * kb + 1]);
+        // the identity rows read v = 0 from a zero tile, written once (visible after the setup
+        // barriers); the zero-start rows read the preparation waves' v tiles
+        if constexpr (kMerge) {
+            if (role == 1) {
+                for (int o = (tid - 256) * 16; o < (int)L::kTile; o += 256 * 16)
+                    *reinterpret_cast<u16x8 *>(smem + L::oZV + o) = u16x8{};
+            }
+        }
+        const int voff = (kMerge && role == 1) ? (int)L::oZV : (int)L::oV;
+        const int vstep = (kMerge && role == 1) ? 0 : (int)L::kTile;
 
         // per-lane LDS offsets (slot, tile and block offsets are immediates)
         int xo[4];  // k / q tile: row li, group 4 kb + q4
@@ -430,7 +463,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             const int rt = 4 * q4 + (li >> 2);
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
-                const int c = 32 * w + 16 * bb + 4 * (li & 3);
+                const int c = 32 * wr + 16 * bb + 4 * (li & 3);
                 va[bb] = rt * 256 + (((c >> 3) ^ ksw(rt)) << 4) + (c & 7) * 2;
             }
         }
@@ -446,7 +479,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         }
         auto store_normed = [&](const unsigned char *xo, int64_t tok) __attribute__((always_inline)) {
             const f16x4 y0 = ld4(xo), y1 = ld4(xo + 32);
-            const int64_t row = (vtok + tok) * kD + 32 * w + 4 * q4;
+            const int64_t row = (vtok + tok) * kD + 32 * wr + 4 * q4;
             if (p.o_f16) {
                 *reinterpret_cast<f16x4 *>(o_f16 + row) = y0;
                 *reinterpret_cast<f16x4 *>(o_f16 + row + 16) = y1;
@@ -484,7 +517,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
             constexpr int s = decltype(sl)::value;
             const unsigned char *Kt = smem + L::oK + s * L::kTile;
             const unsigned char *Qt = smem + L::oQ + s * L::kTile;
-            const unsigned char *Vt = smem + L::oV + s * L::kTile;
+            const unsigned char *Vt = smem + voff + s * vstep;
             const unsigned char *gt = smem + L::oG + s * 20 * C;  // gate vectors of this chunk
             const unsigned char *na = smem + L::oNA + s * L::kNA * 512 + lane * 8;
             const unsigned char *td = smem + L::oTd + s * 2 * NT * 512 + lane * 8;
@@ -637,19 +670,19 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                     }
                     const int t = 16 * m + li;
                     if constexpr (NORM > 0) {
-                        unsigned char *xo = smem + L::oNO + t * 272 + 2 * (32 * w + 4 * q4);
+                        unsigned char *xo = smem + L::oNO + t * 272 + 2 * (32 * wr + 4 * q4);
                         if (i > 0) store_normed(xo, (int64_t)(c - 1) * C + t);  // chunk c - 1: all C rows
                         // stage for the prep waves' norm (next interval): this lane's 8 columns
                         // in fp16, scaled, and their sum of squares in fp32
                         float ss = 0.0f;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) ss += O0[e] * O0[e] + O1[e] * O1[e];
-                        *reinterpret_cast<float *>(smem + L::oNP + t * 80 + 4 * (4 * w + q4)) = ss;
+                        *reinterpret_cast<float *>(smem + L::oNP + t * 80 + 4 * (4 * wr + q4)) = ss;
                         const float sc = stage_scale(ss);
                         *reinterpret_cast<f16x4 *>(xo) = to_f16x4(O0 * sc);
                         *reinterpret_cast<f16x4 *>(xo + 32) = to_f16x4(O1 * sc);
                     } else if (t < ntok) {
-                        const int64_t row = (vtok + (int64_t)c * C + t) * kD + 32 * w + 4 * q4;
+                        const int64_t row = (vtok + (int64_t)c * C + t) * kD + 32 * wr + 4 * q4;
                         if (p.o_f16) {
                             *reinterpret_cast<f16x4 *>(o_f16 + row) =
                                 f16x4{f16_out(O0[0]), f16_out(O0[1]), f16_out(O0[2]), f16_out(O0[3])};
@@ -742,7 +775,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
 #pragma unroll
                 for (int m = 0; m < NT; ++m) {
                     const int t = 16 * m + li;
-                    if (t < ntok) store_normed(smem + L::oNO + t * 272 + 2 * (32 * w + 4 * q4), (int64_t)c * C + t);
+                    if (t < ntok) store_normed(smem + L::oNO + t * 272 + 2 * (32 * wr + 4 * q4), (int64_t)c * C + t);
                 }
             }
         }
@@ -756,12 +789,14 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
                 f16 = p.final_f16;
             }
         } else {
-            dst = role == 1 ? p.ws_m + wsi : seg == 0 ? p.ws_start + wsi + kD * kD : p.ws_n + wsi;
+            // (the merged map pass's identity rows of segment 0 are not needed)
+            if (!(kMerge && seg == 0 && role == 1))
+                dst = role == 1 ? p.ws_m + wsi : seg == 0 ? p.ws_start + wsi + kD * kD : p.ws_n + wsi;
         }
         if (dst) {
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
-                const int r0 = 32 * w + 16 * bb;
+                const int r0 = 32 * wr + 16 * bb;
                 const int64_t srow = ((int64_t)(OUT ? pair * kD : 0) + r0 + li) * kD + 4 * q4;
 #pragma unroll
                 for (int jt = 0; jt < 8; ++jt) store_state4(dst, srow + 16 * jt, S[bb][jt], f16, p.state_bf16);
@@ -769,7 +804,7 @@ __global__ __launch_bounds__(kSegThreads, 1) void gdn_seg_pass_kernel(SegParams 
         }
     } else {
         // ================================================================ prep waves
-        const int m = __builtin_amdgcn_readfirstlane(w - 4);  // token tile of this wave
+        const int m = w - kRowW;  // token tile of this wave
         // issue priority to the waves on the critical path: the preparation waves in the map
         // pass, and before b1 in the output pass (the row waves raise theirs above it after b1)
         __builtin_amdgcn_s_setprio(OUT ? 1 : 2);
@@ -1418,7 +1453,7 @@ hipError_t launch_pass(const SegParams &sp, int64_t nblocks, hipStream_t stream)
         attr_set = true;
     }
     if (nblocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gdn_seg_pass_kernel<C, OUT, NORM, KDA>), dim3((unsigned)nblocks), dim3(kSegThreads), bytes,
+    hipLaunchKernelGGL((gdn_seg_pass_kernel<C, OUT, NORM, KDA>), dim3((unsigned)nblocks), dim3(seg_threads<OUT, KDA>()), bytes,
                        stream, sp);
     return hipGetLastError();
 }
@@ -1428,7 +1463,14 @@ hipError_t launch_seg_c(const SegParams &sp, hipStream_t stream) {
     const int64_t pairs = (int64_t)sp.p.B * sp.p.Hv;
     hipError_t err = hipSuccess;
     if (sp.P > 1) {
-        err = launch_pass<C, false, 0, KDA>(sp, pairs * (2 * sp.P - 3), stream);
+        // map pass: per pair, segment 0 and each later segment but the last (the per-channel
+        // decay: the zero-start and the identity rows of a segment in workgroups of their own)
+        // the 64-token call's map pass runs 32-token chunks (twice as many per segment: the same
+        // segment boundaries), where the merged workgroup's registers fit without spills
+        constexpr int CM = C == 64 ? 32 : C;
+        SegParams spm = sp;
+        spm.seg_chunks = sp.seg_chunks * (C / CM);
+        err = launch_pass<CM, false, 0, KDA>(spm, pairs * (KDA ? 2 * sp.P - 3 : sp.P - 1), stream);
         if (err != hipSuccess) return err;
         if (sp.P > 2) {
             static bool attr_set = false;
