@@ -25,16 +25,16 @@
 // identity row is a state row; rows never mix). Three launches:
 //   1. map pass (OUT = false): segment 0 from the initial state (its end is the
 //      true start of segment 1), and for segments 1 .. P-2 both N_p (role 0) and
-//      M_p (role 1). With scalar decay one workgroup per (pair, segment) holds both
-//      row sets over one shared chunk preparation, at 32-token chunks (16 at chunk
-//      16; the 64-token call's segments are whole 32-token chunks too);
+//      M_p (role 1). One workgroup per (pair, segment) holds both row sets over
+//      one shared chunk preparation, at 32-token chunks (16 at chunk 16; the
+//      64-token call's segments are whole 32-token chunks too);
 //   2. combine: S_{p+1} = S_p M_p + N_p, sequential over the segments, in fp32;
 //   3. output pass (OUT = true): every segment from its true start, writing o and,
 //      in the last segment, the final state.
 // With P = 1 only the output pass runs.
 //
-// Workgroup of 8 waves (wave i on SIMD i % 4), two barriers per chunk (the scalar-decay
-// map pass: 12 waves, row waves 0-3 for the zero-start rows, 4-7 for the identity
+// Workgroup of 8 waves (wave i on SIMD i % 4), two barriers per chunk (the map pass:
+// 12 waves, row waves 0-3 for the zero-start rows, 4-7 for the identity
 // rows, preparation waves 8-11):
 //   waves 0-3, "row waves": state rows 32 w .. 32 w + 31 as two 16-row MFMA blocks
 //     held in registers for the whole segment; per chunk X and (OUT) Y = S Q^T before
@@ -64,11 +64,11 @@ namespace gdn {
 namespace {
 
 constexpr int kD = 128;
-// threads of a segment-pass workgroup: 4 row waves and 4 preparation waves, or in the scalar-decay
-// map pass 8 row waves (the zero-start rows and the identity rows of one segment) and 4
+// threads of a segment-pass workgroup: 4 row waves and 4 preparation waves, or in the map pass
+// 8 row waves (the zero-start rows and the identity rows of one segment) and 4
 // preparation waves
 template <bool OUT, bool KDA>
-__host__ __device__ constexpr int seg_threads() { return (!OUT && !KDA ? 12 : 8) * 64; }
+__host__ __device__ constexpr int seg_threads() { return (!OUT ? 12 : 8) * 64; }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -123,9 +123,9 @@ struct SegSmem {
     // so that the 8-byte accesses of 32 lanes (16 tokens, two column groups) meet all 64 banks;
     // the partial sums of squares [C][20] f32 (16 used: 4 row waves x 4 lanes of 8 columns);
     // the norm weight [128] f32
-    // the merged map pass (scalar decay): a zero v tile read by the identity rows
+    // the map pass: a zero v tile read by the identity rows
     static constexpr size_t oZV = oEC + (KDA ? 2 * 512 : 0);
-    static constexpr size_t oNO = oZV + (!OUT && !KDA ? kTile : 0);
+    static constexpr size_t oNO = oZV + (!OUT ? kTile : 0);
     static constexpr size_t oNP = oNO + (NORM ? (size_t)C * 272 : 0);
     static constexpr size_t oNW = oNP + (NORM ? (size_t)C * 80 : 0);
     static constexpr size_t kBytes = oNW + (NORM ? 512 : 0);
@@ -310,10 +310,10 @@ template <int C, bool OUT, int NORM = 0, bool KDA = false>
 __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_kernel(SegParams sp) {
     using L = SegSmem<C, OUT, (NORM > 0), KDA>;
     constexpr int NT = L::NT, KBC = L::KBC;
-    // scalar-decay map pass: one workgroup per (pair, segment) runs both the zero-start rows
+    // map pass: one workgroup per (pair, segment) runs both the zero-start rows
     // (waves 0-3, with v) and the identity rows (waves 4-7, v = 0) on one shared chunk
     // preparation (waves 8-11)
-    constexpr bool kMerge = !OUT && !KDA;
+    constexpr bool kMerge = !OUT;
     constexpr int kRowW = kMerge ? 8 : 4;
     // three waves per SIMD leave each 168 VGPRs: the merged map pass runs 32- and 16-token chunks
     static_assert(!kMerge || C <= 32, "the merged map pass runs at C <= 32");
@@ -349,26 +349,15 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
     const int jj = lin % ratio;
     int rest = lin / ratio;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int seg, role;  // role 0: state rows (from the start state, with v); 1: identity rows, v = 0
-    if (OUT) {
-        seg = rest % p.P;
-        rest /= p.P;
-        role = 0;
-    } else if (kMerge) {
-        seg = rest % (p.P - 1);
-        rest /= p.P - 1;
-        role = (w >> 2) == 1 ? 1 : 0;  // the preparation waves load v: role 0
-    } else {
-        const int units = 2 * p.P - 3;
-        const int u = rest % units;
-        rest /= units;
-        seg = u == 0 ? 0 : 1 + (u - 1) / 2;
-        role = u == 0 ? 0 : (u - 1) % 2;
-    }
+    // segments: all P in the output pass, all but the last in the map pass
+    const int nseg = OUT ? p.P : p.P - 1;
+    const int seg = rest % nseg;
+    rest /= nseg;
+    // role of a row wave: 0 state rows (from the start state, with v), 1 identity rows (v = 0)
+    const int role = (kMerge && (w >> 2) == 1) ? 1 : 0;
     const int kh = rest % p.Hk, b = rest / p.Hk;
     const int h = p.head_map == 0 ? kh + jj * p.Hk : kh * ratio + jj;
     const int pair = b * p.Hv + h;
-    const bool has_v = role == 0;
 
     const int T = p.T;
     const int NC = (T + C - 1) / C;
@@ -884,7 +873,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             if (tile) {
                 request_rows(kr, kg, c);
                 if (OUT) request_rows(qr, qg, c);
-                if (has_v) request_rows(vr, vg, c);
+                request_rows(vr, vg, c);
             }
         };
         // output norm (NORM): the row waves stage chunk c's o rows between b1 and b2 of its
@@ -1049,7 +1038,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                         fence();
                     }
                 }
-                if (has_v) {
+                {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int t = 16 * m + 4 * j + lrow;
@@ -1322,15 +1311,6 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             }
             lds_barrier();
         }
-        // the identity rows have v = 0: both v slots hold zeros, written once, and the row waves
-        // read them like any values (one code path for every role, no per-chunk branch)
-        if (!has_v && tile) {
-#pragma unroll
-            for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<u16x8 *>(smem + L::oV + sl * L::kTile + (16 * m + 4 * j + lrow) * 256 + 16 * lp) = u16x8{};
-        }
         request_gate(cb);
         issue(cb);
         phase1(cb, min(cb + 1, clast), IC<0>{});
@@ -1463,14 +1443,13 @@ hipError_t launch_seg_c(const SegParams &sp, hipStream_t stream) {
     const int64_t pairs = (int64_t)sp.p.B * sp.p.Hv;
     hipError_t err = hipSuccess;
     if (sp.P > 1) {
-        // map pass: per pair, segment 0 and each later segment but the last (the per-channel
-        // decay: the zero-start and the identity rows of a segment in workgroups of their own)
-        // the 64-token call's map pass runs 32-token chunks (twice as many per segment: the same
-        // segment boundaries), where the merged workgroup's registers fit without spills
+        // map pass: one workgroup per pair and segment but the last. The 64-token call's map pass
+        // runs 32-token chunks (twice as many per segment: the same segment boundaries), where the
+        // merged workgroup's registers fit without spills
         constexpr int CM = C == 64 ? 32 : C;
         SegParams spm = sp;
         spm.seg_chunks = sp.seg_chunks * (C / CM);
-        err = launch_pass<CM, false, 0, KDA>(spm, pairs * (KDA ? 2 * sp.P - 3 : sp.P - 1), stream);
+        err = launch_pass<CM, false, 0, KDA>(spm, pairs * (sp.P - 1), stream);
         if (err != hipSuccess) return err;
         if (sp.P > 2) {
             static bool attr_set = false;
