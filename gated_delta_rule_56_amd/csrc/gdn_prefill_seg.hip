@@ -594,7 +594,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             lds_barrier();  // b1: the prep waves' rows of chunk i + 1 are in place
             // issue priority to the waves on the critical path: in the output pass, the row waves
             // from here to the end of the interval (the preparation waves before b1)
-            if constexpr (OUT) __builtin_amdgcn_s_setprio(2);
+            if constexpr (OUT && !KDA) __builtin_amdgcn_s_setprio(2);
             if constexpr (!kEarly) {
                 request_rest();
                 fence();
@@ -749,7 +749,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) sb[bb][kb] = pack8(S[bb][2 * kb], S[bb][2 * kb + 1]);
-            if constexpr (OUT) __builtin_amdgcn_s_setprio(0);
+            if constexpr (OUT && !KDA) __builtin_amdgcn_s_setprio(0);
             lds_barrier();  // b2: chunk i + 1 is prepared
         };
         for (int i = 0; i < n; i += 2) {
@@ -796,7 +796,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
         const int m = w - kRowW;  // token tile of this wave
         // issue priority to the waves on the critical path: the preparation waves in the map
         // pass, and before b1 in the output pass (the row waves raise theirs above it after b1)
-        __builtin_amdgcn_s_setprio(OUT ? 1 : 2);
+        __builtin_amdgcn_s_setprio(OUT && !KDA ? 1 : 2);
         const bool tile = m < NT;
         const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ktok * kD;
         const uint16_t *qg = static_cast<const uint16_t *>(p.q) + ktok * kD;
@@ -1180,8 +1180,8 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
         // q4 over the eight runs' steps. The block (1,0) relative to the last token b of tile 0,
         // (k o e^{G_b - G_r0} / E)(k o E e^{G_r1 - G_b})^T, whose operands are decays (<= 1): in fp16,
         // the same runs as 16 x 16 x 16 steps. Work: W0 A(0,0) and its inverse,
-        // W1 A(1,1) and its inverse, W2 (which holds the next log-decays) A_qk(0,0), W3 A(1,0),
-        // A_qk(1,0) and A_qk(1,1).
+        // W1 A(1,1) and its inverse, W2 (which holds the next log-decays) A_qk(0,0) and A_qk(1,0),
+        // W3 A(1,0) and A_qk(1,1).
         auto kda_diag = [&](int s, int mm, bool qside) __attribute__((always_inline)) {
             const int tok = 16 * mm + li;
             const unsigned char *Es = smem + L::oE + s * C * L::kERow + tok * L::kERow;
@@ -1202,35 +1202,33 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             }
             return acc;  // lane (q4, li), element r: s = 16 mm + 4 q4 + r, t = 16 mm + li
         };
-        auto kda_off = [&](int s, f32x4 &acc, f32x4 &accq) __attribute__((always_inline)) {
+        // the block (1,0) of A (QS = false: k of tile 1) or of A_qk (QS = true: q of tile 1)
+        auto kda_off = [&](int s, auto qs) __attribute__((always_inline)) {
+            constexpr bool QS = decltype(qs)::value;
             const int tsk = li, ttk = 16 + li;
             const unsigned char *Es = smem + L::oE + s * C * L::kERow;
             const unsigned char *EV = smem + L::oEV + s * kNVec * 512;
-            const unsigned char *rks = smem + L::oRK + tsk * 256, *rkt = smem + L::oRK + ttk * 256;
-            const unsigned char *rqt = smem + L::oRQ + ttk * 256;
-            acc = accq = f32x4{0.f, 0.f, 0.f, 0.f};
+            const unsigned char *rks = smem + L::oRK + tsk * 256;
+            const unsigned char *rbt = smem + (QS ? L::oRQ : L::oRK) + ttk * 256;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int blk = 0; blk < 8; ++blk) {
                 const int rho = 4 * blk + q4;
                 const int grp = 4 * (rho >> 3) + (rho & 3), half = 8 * ((rho >> 2) & 1);
                 const f16x4 ks = ld4(rks + ((grp ^ ksw(tsk & 15)) << 4) + half);
-                const f16x4 kt = ld4(rkt + ((grp ^ ksw(ttk & 15)) << 4) + half);
-                f16x4 qt = {};
-                if (OUT) qt = ld4(rqt + ((grp ^ ksw(ttk & 15)) << 4) + half);
+                const f16x4 kt = ld4(rbt + ((grp ^ ksw(ttk & 15)) << 4) + half);
                 const f32x4 es = ldf4(Es + tsk * L::kERow + 16 * rho), et = ldf4(Es + ttk * L::kERow + 16 * rho);
                 const f32x4 fb = ldf4(EV + kVecBR0 * 512 + 16 * rho), fr = ldf4(EV + kVecR1B * 512 + 16 * rho);
-                f16x4 a, b, bq;
+                f16x4 a, b;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     a[r] = (_Float16)((float)ks[r] * (__builtin_amdgcn_rcpf(es[r]) * fb[r]));
-                    const float l = et[r] * fr[r];
-                    b[r] = (_Float16)((float)kt[r] * l);
-                    if (OUT) bq[r] = (_Float16)((float)qt[r] * l);
+                    b[r] = (_Float16)((float)kt[r] * (et[r] * fr[r]));
                 }
                 acc = mfma16x16x16(a, b, acc);
-                if (OUT) accq = mfma16x16x16(a, bq, accq);
                 if ((blk & 1) == 1) fence();  // two runs' operands live at a time
-            }  // lane (q4, li), element r: s = 4 q4 + r, t = 16 + li
+            }
+            return acc;  // lane (q4, li), element r: s = 4 q4 + r, t = 16 + li
         };
         auto phase2k = [&](int s, auto wc) __attribute__((always_inline)) {
             constexpr int W = decltype(wc)::value;
@@ -1260,13 +1258,11 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                     *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
                     *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(tq);
                 } else if constexpr (W == 3) {
-                    f32x4 acc, accq;
-                    kda_off(s, acc, accq);
+                    const f32x4 acc = kda_off(s, IC<0>{});
                     const float bt = gts[C + 16 + li];
                     *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(1, 0) * 512 + lane * 8) =
                         to_f16x4(-(bt * acc));
                     if (OUT) {
-                        *reinterpret_cast<f16x4 *>(aqb + fblk(1, 0) * 1024) = to_f16x4(sct * accq);
                         const f32x4 dq = kda_diag(s, 1, true);
                         f32x4 aq;
 #pragma unroll
@@ -1281,6 +1277,8 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                     for (int r = 0; r < 4; ++r) aq[r] = 4 * q4 + r <= li ? sct * dq[r] : 0.0f;
                     *reinterpret_cast<f16x4 *>(aqb + fblk(0, 0) * 1024) = to_f16x4(aq);
                     *reinterpret_cast<f16x4 *>(aqb + fblk(0, 0) * 1024 + 8) = f16x4{};
+                    // and A_qk(1,0), the first half of the fragment whose second half W3 writes
+                    *reinterpret_cast<f16x4 *>(aqb + fblk(1, 0) * 1024) = to_f16x4(sct * kda_off(s, IC<1>{}));
                 }
             }
         };
