@@ -44,10 +44,12 @@
 //   waves 4-7 (8-11), "prep waves", token tile m: prepare chunk i + 1 into slot
 //     (i + 1) & 1 during chunk i. Before the first barrier (P1) each converts its
 //     16 raw bf16 k and q rows (loaded one chunk earlier into registers) to the fp16
-//     tiles and stores its v rows, wave 4 also forms the gate vectors, and each
+//     tiles and stores its v rows, one prep wave also forms the gate vectors (the
+//     fourth when the chunk has fewer than four tiles, so one with none), and each
 //     issues the loads of chunk i + 2; after it (P2) each forms K K^T and Q K^T of
 //     its tile against the tiles at or before it on MFMA, the gated blocks of A
-//     and A_qk, and the inverse of its diagonal block row by row. No prep wave
+//     and A_qk, and the inverse of its diagonal block row by row (at 32-token
+//     chunks the third prep wave takes the tile below the diagonal). No prep wave
 //     waits for another.
 //
 // LDS tiles of k and q: row-major 256-byte token rows, each 32-column block in
@@ -317,9 +319,9 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
     constexpr int kRowW = kMerge ? 8 : 4;
     // three waves per SIMD leave each 168 VGPRs: the merged map pass runs 32- and 16-token chunks
     static_assert(!kMerge || C <= 32, "the merged map pass runs at C <= 32");
-    // in the map pass (no global stores in the loop) row wave 0, idle after its X products until
-    // b1, forms the next chunk's gate vectors in place of the first preparation wave
-    constexpr bool kRowScan = !OUT && !KDA;
+    // the preparation wave that forms the gate vectors: one without a tile of its own when the
+    // chunk has fewer than four 16-token tiles
+    constexpr int kScanW = L::NT < 4 ? 3 : 0;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     // every argument into a scalar local: a reference to the argument structure would make
     // the compiler copy it to scratch memory
@@ -478,26 +480,6 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             }
         };
 
-        // map pass: row wave 0 forms every chunk's gate vectors (kRowScan), the first one's here,
-        // each later one's in the interval before its chunk, from g and beta loaded an interval
-        // ahead
-        float rg = 0.f, rb = 0.f;
-        const int rclast = cb + max(n, 1) - 1;
-        const bool scan_wave = kRowScan && __builtin_amdgcn_readfirstlane(w) == 0;
-        auto request_gates = [&](int c) __attribute__((always_inline)) {
-            const int tg = min(c * C + lane, T - 1);
-            rg = p.g[vtok + tg];
-            rb = p.beta[vtok + tg];
-        };
-        auto scan_gates = [&](int c, int sl) __attribute__((always_inline)) {
-            const bool gl = lane < C && c * C + lane < T;  // tokens past the end: g = beta = 0
-            form_gates<C>(smem + L::oG + sl * 20 * C, gl ? rg : 0.f, gl ? rb : 0.f, lane);
-        };
-        if (scan_wave) {
-            request_gates(cb);
-            scan_gates(cb, 0);
-            request_gates(min(cb + 1, rclast));
-        }
         lds_barrier();
         lds_barrier();
         if constexpr (KDA) lds_barrier();  // the preparation waves' first factors
@@ -547,12 +529,6 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                     }
                 }
                 fence();
-            }
-            // the next chunk's gate vectors into the other slot (read by the preparation waves after
-            // b1), then the g and beta of the chunk after it requested
-            if (scan_wave) {
-                scan_gates(min(cb + i + 1, rclast), 1 - s);
-                request_gates(min(cb + i + 2, rclast));
             }
             // ---- operands of the rest of the chunk: v (transposed), the gate vectors, the diagonal
             // inverses and -A blocks, the A_qk fragments. They are this chunk's slot, complete since
@@ -806,7 +782,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
 
         // raw rows of tile m of one chunk: register j of lane l holds columns 8 (l % 16) + 0..7 of
         // token 16 m + 4 j + l / 16 (of k, q and v), so that each load instruction reads four whole
-        // rows, 1 KB in eight 128-byte lines; wave 4 also holds g and beta of the chunk's token
+        // rows, 1 KB in eight 128-byte lines; the gate wave also holds g and beta of the chunk's token
         // slots (lane = slot; one pair per ring slot). Each tensor's values of the next chunk are
         // requested as soon as those of this chunk have been used (g and beta at the start of
         // P1), about one interval ahead of their use.
@@ -815,9 +791,8 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
         const int lrow = lane >> 4, lp = lane & 15;
         // requests of chunk c (absolute): g and beta, the rows of one tensor
         auto request_gb = [&](int c, auto slc) __attribute__((always_inline)) {
-            if constexpr (kRowScan) return;  // row wave 0 loads and scans them
             constexpr int sl = decltype(slc)::value;
-            // every prep wave loads them (only wave 4 uses them): unconditional loads keep the
+            // every prep wave loads them (only the gate wave uses them): unconditional loads keep the
             // wait counts before their use exact
             const int tg = min(c * C + lane, T - 1);
             if constexpr (!KDA) gr[sl] = gg[tg];
@@ -925,7 +900,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                 }
             }
         };
-        // P1: wave 4 forms the gate vectors of chunk c (in the map pass row wave 0 does); tile m's
+        // P1: prep wave kScanW forms the gate vectors of chunk c; tile m's
         // rows of chunk c into slot s (waits for their loads), each tensor's rows of chunk cn
         // requested right after
         auto phase1 = [&](int c, int cn, auto sc) __attribute__((always_inline)) {
@@ -944,7 +919,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                     gts[3 * C + lane] = bv;
                     gts[4 * C + lane] = 0.0f;
                 }
-            } else if (!kRowScan && m == 0) {
+            } else if (m == kScanW) {
                 // tokens past the end have g = beta = 0
                 const bool gl = lane < C && t0 + lane < T;
                 form_gates<C>(smem + L::oG + s * 20 * C, gl ? gr[s] : 0.f, gl ? br[s] : 0.f, lane);
@@ -1066,9 +1041,11 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
         // W0 its diagonal tile only).
         auto phase2w = [&](int s, auto wc) __attribute__((always_inline)) {
             constexpr int W = decltype(wc)::value;
-            constexpr int nT = C == 64 ? (W < 2 ? 3 : 2) : C == 32 ? (W == 0 ? 1 : W == 1 ? 2 : 0) : (W == 0 ? 1 : 0);
-            constexpr int MMs[3] = {W, C == 64 ? (W == 0 ? 3 : W == 1 ? 1 : W) : W, C == 64 ? (W == 0 ? 3 : 2) : 0};
-            constexpr int NTs[3] = {W, C == 64 ? (W == 0 ? 0 : W == 1 ? 0 : W - 1) : 0, C == 64 ? (W == 0 ? 1 : 0) : 0};
+            // C = 32: W0 and W1 the diagonal tiles and their inverses, W2 the tile (1,0) below them
+            constexpr bool kDiag = !(C == 32 && W == 2);
+            constexpr int nT = C == 64 ? (W < 2 ? 3 : 2) : C == 32 ? (W < 3 ? 1 : 0) : (W == 0 ? 1 : 0);
+            constexpr int MMs[3] = {kDiag ? W : 1, C == 64 ? (W == 0 ? 3 : W == 1 ? 1 : W) : W, C == 64 ? (W == 0 ? 3 : 2) : 0};
+            constexpr int NTs[3] = {kDiag ? W : 0, C == 64 ? (W == 0 ? 0 : W == 1 ? 0 : W - 1) : 0, C == 64 ? (W == 0 ? 1 : 0) : 0};
             if constexpr (nT > 0) {
                 const unsigned char *Kt = smem + L::oK + s * L::kTile;
                 const unsigned char *Qt = smem + L::oQ + s * L::kTile;
@@ -1117,7 +1094,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float gv = __expf(Gt[j] - Gs[j][r]);
-                        if (j == 0) {
+                        if (j == 0 && kDiag) {
                             const int sidx = 4 * q4 + r;
                             a[j][r] = sidx < li ? btt[j] * gv * rk[j][r] : 0.0f;
                             if (OUT) aqv[j][r] = sidx <= li ? sct * gv * rq[j][r] : 0.0f;
@@ -1137,41 +1114,48 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                 };
                 // the diagonal tile: its row of A_WW goes through this wave's LDS scratch (written as
                 // accumulators, read back by rows) for the inverse, which starts once it is back
-                float *at = reinterpret_cast<float *>(smem + L::oAt) + W * 16 * 20;
                 gate(0);
+                if constexpr (!kDiag) {
+                    // a tile below the diagonal alone: A_qk and -A
+                    store_aq(0);
+                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(MMs[0], NTs[0]) * 512 + lane * 8) =
+                        to_f16x4(-a[0]);
+                } else {
+                    float *at = reinterpret_cast<float *>(smem + L::oAt) + W * 16 * 20;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) at[(4 * q4 + r) * 20 + li] = -a[0][r];  // at[s][i] = -A[i][s]
-                store_aq(0);
-                if constexpr (OUT && (W & 1) == 0) *reinterpret_cast<f16x4 *>(aqb + fblk(W, W / 2) * 1024 + 8) = f16x4{};
-                fence();
-                // the tiles below the diagonal: gated while the scratch round trip completes, stored
-                // after its reads are requested
+                    for (int r = 0; r < 4; ++r) at[(4 * q4 + r) * 20 + li] = -a[0][r];  // at[s][i] = -A[i][s]
+                    store_aq(0);
+                    if constexpr (OUT && (W & 1) == 0) *reinterpret_cast<f16x4 *>(aqb + fblk(W, W / 2) * 1024 + 8) = f16x4{};
+                    fence();
+                    // the tiles below the diagonal: gated while the scratch round trip completes, stored
+                    // after its reads are requested
 #pragma unroll
-                for (int j = 1; j < nT; ++j) gate(j);
-                fence();
-                float nrow[16];
+                    for (int j = 1; j < nT; ++j) gate(j);
+                    fence();
+                    float nrow[16];
 #pragma unroll
-                for (int k = 0; k < 16; ++k) nrow[k] = at[k * 20 + li];
-                fence();
+                    for (int k = 0; k < 16; ++k) nrow[k] = at[k * 20 + li];
+                    fence();
 #pragma unroll
-                for (int j = 1; j < nT; ++j) {
-                    store_aq(j);
-                    // -A below the diagonal (A operands of the block substitution)
-                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(MMs[j], NTs[j]) * 512 +
-                                               lane * 8) = to_f16x4(-a[j]);
+                    for (int j = 1; j < nT; ++j) {
+                        store_aq(j);
+                        // -A below the diagonal (A operands of the block substitution)
+                        *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(MMs[j], NTs[j]) * 512 +
+                                                   lane * 8) = to_f16x4(-a[j]);
+                    }
+                    fence();
+                    // T_WW = (I + A_WW)^{-1}: lane (q4, li) builds T[li][4 q4 + e]
+                    f32x4 tq;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) tq[e] = 4 * q4 + e == li ? 1.0f : 0.0f;
+                    inv_rows(tq, nrow);
+                    // T_WW and diag(exp(G_C - G)) T_WW (row li scaled): the latter gives the scaled
+                    // values of the state update straight from the substitution
+                    const float egt = gts[2 * C + 16 * W + li];
+                    unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + W * 1024 + lane * 8;
+                    *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
+                    *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(egt * tq);
                 }
-                fence();
-                // T_WW = (I + A_WW)^{-1}: lane (q4, li) builds T[li][4 q4 + e]
-                f32x4 tq;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tq[e] = 4 * q4 + e == li ? 1.0f : 0.0f;
-                inv_rows(tq, nrow);
-                // T_WW and diag(exp(G_C - G)) T_WW (row li scaled): the latter gives the scaled
-                // values of the state update straight from the substitution
-                const float egt = gts[2 * C + 16 * W + li];
-                unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + W * 1024 + lane * 8;
-                *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
-                *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(egt * tq);
             }
         };
         // P2, per-channel decay (C = 32). The diagonal blocks (m, m) in float32 as (k o 1/E)(k o E)^T
