@@ -165,15 +165,16 @@ typedef struct {
  *   RMSNorm for o).
  *   (float16 o rounds each output, at most 2^-11 of its value: within the bfloat16 path's
  *   accuracy, beyond the float32 path's.)
- * Paths: bfloat16 with dk = 128 runs the segmented MFMA prefill (below; C = 16 about 1.3 times
- * the time of C = 64 on long sequences, C = 32 about 1.2 times); float32 q/k/v, and bfloat16
+ * Paths: bfloat16 with dk = 128 runs the segmented MFMA prefill (below; C = 16 about 1.4 times
+ * the time of C = 64 on long sequences, C = 32 about the same); float32 q/k/v, and bfloat16
  * with dk < 128, a float32 VALU kernel.
  *
  * Segmented prefill (bfloat16, dk = 128, C in {16, 32, 64}): the chunks of each sequence are cut
  * into P segments of equal chunk counts that run in parallel: a map pass computes, per
  * segment, the end state of segment 0 and the affine map S -> S M + N of each later segment
  * (the chunk update is affine in the start state), a combine chains the maps into every
- * segment's start state, and an output pass runs every segment from its start. P is as
+ * segment's start state, and an output pass runs every segment from its start (at C = 64 the
+ * map pass runs 32-token chunks: results differ from an all-64 run by rounding only). P is as
  * large as needed to give each of the GPU's 256 CUs a workgroup in the output pass
  * (ceil(256 / (B Hv)), at most the chunk count and 64), reduced until its workspace fits the
  * workspace_bytes the caller passes: 3 * B * Hv * P * dk * dk * 4 bytes for P > 1, nothing
