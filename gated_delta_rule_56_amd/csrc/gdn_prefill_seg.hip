@@ -1327,7 +1327,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
 // S (LDS and matrix core) is sequential.
 constexpr int kCombineMRow = kD + 16;  // 144 floats: four map rows 16 banks apart
 
-__global__ __launch_bounds__(256) void gdn_seg_combine_kernel(SegParams sp) {
+__global__ __launch_bounds__(512) void gdn_seg_combine_kernel(SegParams sp) {
     extern __shared__ __attribute__((aligned(16))) unsigned char csmem[];
     // srow: this block's 16 rows of the running start state; mt: the map M_seg, rows padded to
     // 144 floats so that the operand reads below meet 64 distinct banks
@@ -1338,58 +1338,46 @@ __global__ __launch_bounds__(256) void gdn_seg_combine_kernel(SegParams sp) {
     const int nb = gridDim.x;
     const int lin = (nb & 63) == 0 ? (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     const int pair = lin >> 3, rb = lin & 7;
-    const int tid = threadIdx.x, r = tid >> 4, cg = tid & 15;
+    const int tid = threadIdx.x, r = tid >> 5, c4 = tid & 31;
     const int lane = tid & 63, w = tid >> 6, li = lane & 15, q4 = lane >> 4;
     const int64_t base = (int64_t)pair * sp.P;
-    constexpr int kPer = kD * kD / 4 / 256;  // f32x4 of a map per thread
-    // the products on float32 MFMAs (16 x 16 x 4): wave w owns the 16-column tiles 2 w and
-    // 2 w + 1; lane (q4, li) holds rows 4 q4 + e, column 16 jt + li of the new state, with N
-    // there as the products' start
-    f32x4 mnext[kPer], nnext[2];
+    constexpr int kPer = kD * kD / 4 / 512;  // f32x4 of a map per thread
+    // the products on float32 MFMAs (16 x 16 x 4): wave w owns the 16-column tile w; lane
+    // (q4, li) holds rows 4 q4 + e, column 16 w + li of the new state, with N there as the
+    // products' start
+    f32x4 mnext[kPer], nnext;
     auto load_next = [&](int seg) {  // N_seg at this lane's output places (first: needed first), M_seg
-        const float *N = sp.ws_n + (base + seg) * (kD * kD) + (rb * 16 + 4 * q4) * kD + li;
+        const float *N = sp.ws_n + (base + seg) * (kD * kD) + (rb * 16 + 4 * q4) * kD + 16 * w + li;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) nnext[t][e] = N[e * kD + 16 * (2 * w + t)];
+        for (int e = 0; e < 4; ++e) nnext[e] = N[e * kD];
         const f32x4 *M = reinterpret_cast<const f32x4 *>(sp.ws_m + (base + seg) * (kD * kD));
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) mnext[j] = M[tid + 256 * j];
+        for (int j = 0; j < kPer; ++j) mnext[j] = M[tid + 512 * j];
     };
     // S_1's rows of this block and the first map requested together
-    const float *s1 = sp.ws_start + (base + 1) * (kD * kD) + rb * 16 * kD + r * kD + 8 * cg;
-    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(s1), x1 = *reinterpret_cast<const f32x4 *>(s1 + 4);
+    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(sp.ws_start + (base + 1) * (kD * kD) + (rb * 16 + r) * kD + 4 * c4);
     load_next(1);
-    *reinterpret_cast<f32x4 *>(&srow[r][8 * cg]) = x0;
-    *reinterpret_cast<f32x4 *>(&srow[r][8 * cg + 4]) = x1;
+    *reinterpret_cast<f32x4 *>(&srow[r][4 * c4]) = x0;
     for (int seg = 1; seg + 1 < sp.P; ++seg) {
-        float *Sn = sp.ws_start + (base + seg + 1) * (kD * kD) + (rb * 16 + 4 * q4) * kD + li;
+        float *Sn = sp.ws_start + (base + seg + 1) * (kD * kD) + (rb * 16 + 4 * q4) * kD + 16 * w + li;
         __syncthreads();  // srow written; earlier reads of mt done
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int f = tid + 256 * j;  // f32x4 index of the map: row f / 32, columns 4 (f % 32) ..
+            const int f = tid + 512 * j;  // f32x4 index of the map: row f / 32, columns 4 (f % 32) ..
             *reinterpret_cast<f32x4 *>(&mt[f >> 5][4 * (f & 31)]) = mnext[j];
         }
-        f32x4 acc[2] = {nnext[0], nnext[1]};
+        f32x4 acc = nnext;
         if (seg + 2 < sp.P) load_next(seg + 1);
         __syncthreads();
-        // S_new = S M + N: A = S (row li, k = 4 s + q4), B = M (row k, column 16 jt + li)
+        // S_new = S M + N: A = S (row li, k = 4 s + q4), B = M (row k, column 16 w + li)
 #pragma unroll 8
-        for (int s = 0; s < kD / 4; ++s) {
-            const float a = srow[li][4 * s + q4];
-            const float *mrow = &mt[4 * s + q4][li];
-            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, mrow[32 * w], acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, mrow[32 * w + 16], acc[1], 0, 0, 0);
-        }
+        for (int s = 0; s < kD / 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(srow[li][4 * s + q4], mt[4 * s + q4][16 * w + li], acc, 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Sn[e * kD + 16 * (2 * w + t)] = acc[t][e];
+        for (int e = 0; e < 4; ++e) Sn[e * kD] = acc[e];
         __syncthreads();  // every read of srow done
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) srow[4 * q4 + e][16 * (2 * w + t) + li] = acc[t][e];
+        for (int e = 0; e < 4; ++e) srow[4 * q4 + e][16 * w + li] = acc[e];
     }
 }
 
@@ -1441,7 +1429,7 @@ hipError_t launch_seg_c(const SegParams &sp, hipStream_t stream) {
                 if (err != hipSuccess) return err;
                 attr_set = true;
             }
-            hipLaunchKernelGGL(gdn_seg_combine_kernel, dim3((unsigned)(pairs * 8)), dim3(256), kCombineLds, stream, sp);
+            hipLaunchKernelGGL(gdn_seg_combine_kernel, dim3((unsigned)(pairs * 8)), dim3(512), kCombineLds, stream, sp);
             err = hipGetLastError();
             if (err != hipSuccess) return err;
         }
