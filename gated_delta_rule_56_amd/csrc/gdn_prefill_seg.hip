@@ -774,6 +774,11 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
         // pass, and before b1 in the output pass (the row waves raise theirs above it after b1)
         __builtin_amdgcn_s_setprio(OUT && !KDA ? 1 : 2);
         const bool tile = m < NT;
+        // the map pass at two tiles per chunk: the v rows of tile m - 2 go to waves 2 and 3, which
+        // have no k tile of their own
+        constexpr bool kVSplit = !OUT && !KDA && NT == 2;
+        const int vm = kVSplit ? m - 2 : m;
+        const bool vtile = kVSplit ? m >= 2 : tile;
         const uint16_t *kg = static_cast<const uint16_t *>(p.k) + ktok * kD;
         const uint16_t *qg = static_cast<const uint16_t *>(p.q) + ktok * kD;
         const uint16_t *vg = static_cast<const uint16_t *>(p.v) + vtok * kD;
@@ -838,17 +843,20 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                 put(kVecC, cl);
             }
         };
-        auto request_rows = [&](u16x8 (&r)[4], const uint16_t *src, int c) __attribute__((always_inline)) {
+        auto request_rows = [&](u16x8 (&r)[4], const uint16_t *src, int c, int tm) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                r[j] = *reinterpret_cast<const u16x8 *>(src + (int64_t)min(c * C + 16 * m + 4 * j + lrow, T - 1) * kD + 8 * lp);
+                r[j] = *reinterpret_cast<const u16x8 *>(src + (int64_t)min(c * C + 16 * tm + 4 * j + lrow, T - 1) * kD + 8 * lp);
         };
         auto issue = [&](int c) __attribute__((always_inline)) {  // all of chunk c, into slot 0
             request_gb(c, IC<0>{});
             if (tile) {
-                request_rows(kr, kg, c);
-                if (OUT) request_rows(qr, qg, c);
-                request_rows(vr, vg, c);
+                request_rows(kr, kg, c, m);
+                if (OUT) request_rows(qr, qg, c, m);
+                if constexpr (!kVSplit) request_rows(vr, vg, c, m);
+            }
+            if constexpr (kVSplit) {
+                if (vtile) request_rows(vr, vg, c, vm);
             }
         };
         // output norm (NORM): the row waves stage chunk c's o rows between b1 and b2 of its
@@ -862,7 +870,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
         const uint16_t *gzp = NORM == 2 ? p.norm_gate + vtok * kD : nullptr;
         auto request_gate = [&](int c) __attribute__((always_inline)) {
             if constexpr (NORM == 2) {
-                if (tile) request_rows(gz, gzp, c);
+                if (tile) request_rows(gz, gzp, c, m);
             }
         };
         auto norm_rows = [&]() __attribute__((always_inline)) {
@@ -969,7 +977,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                         put(L::oKT + s * L::kTile, t, x0 * rcp4(E0) * eC0, x1 * rcp4(E1) * eC1);
                     }
                     fence();
-                    request_rows(kr, kg, cn);
+                    request_rows(kr, kg, cn, m);
                     fence();
                     if (OUT) {
 #pragma unroll
@@ -982,7 +990,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                             put(L::oQ + s * L::kTile, t, x0 * E0 * eR0, x1 * E1 * eR1);
                         }
                         fence();
-                        request_rows(qr, qg, cn);
+                        request_rows(qr, qg, cn, m);
                         fence();
                     }
                 } else {
@@ -996,7 +1004,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                         *reinterpret_cast<f16x4 *>(krow + ((((g0 + 1) ^ sw) << 4) + hb)) = bf4_to_h4(a[4], a[5], a[6], a[7]);
                     }
                     fence();
-                    request_rows(kr, kg, cn);
+                    request_rows(kr, kg, cn, m);
                     fence();
                     if (OUT) {
 #pragma unroll
@@ -1009,18 +1017,30 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                             *reinterpret_cast<f16x4 *>(qrow + ((((g0 + 1) ^ sw) << 4) + hb)) = bf4_to_h4(b[4], b[5], b[6], b[7]);
                         }
                         fence();
-                        request_rows(qr, qg, cn);
+                        request_rows(qr, qg, cn, m);
                         fence();
                     }
                 }
-                {
+                if constexpr (!kVSplit) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int t = 16 * m + 4 * j + lrow;
                         *reinterpret_cast<u16x8 *>(smem + L::oV + s * L::kTile + t * 256 + ((lp ^ ksw(t & 15)) << 4)) = vr[j];
                     }
                     fence();
-                    request_rows(vr, vg, cn);
+                    request_rows(vr, vg, cn, m);
+                    fence();
+                }
+            }
+            if constexpr (kVSplit) {
+                if (vtile) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 16 * vm + 4 * j + lrow;
+                        *reinterpret_cast<u16x8 *>(smem + L::oV + s * L::kTile + t * 256 + ((lp ^ ksw(t & 15)) << 4)) = vr[j];
+                    }
+                    fence();
+                    request_rows(vr, vg, cn, vm);
                     fence();
                 }
             }
