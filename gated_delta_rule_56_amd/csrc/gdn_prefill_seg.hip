@@ -125,8 +125,12 @@ struct SegSmem {
     // so that the 8-byte accesses of 32 lanes (16 tokens, two column groups) meet all 64 banks;
     // the partial sums of squares [C][20] f32 (16 used: 4 row waves x 4 lanes of 8 columns);
     // the norm weight [128] f32
+    // per-channel-decay output pass: the second channel half of the blocks (1,0) of -A ([2][64] x
+    // 8 B) and of A_qk ([2][64] x 16 B, the fragment's first half; the second is zero)
+    static constexpr size_t oNA2 = oEC + (KDA ? 2 * 512 : 0);
+    static constexpr size_t oAQ2 = oNA2 + (KDA && OUT ? 2 * 512 : 0);
     // the map pass: a zero v tile read by the identity rows
-    static constexpr size_t oZV = oEC + (KDA ? 2 * 512 : 0);
+    static constexpr size_t oZV = oAQ2 + (KDA && OUT ? 2 * 1024 : 0);
     static constexpr size_t oNO = oZV + (!OUT ? kTile : 0);
     static constexpr size_t oNP = oNO + (NORM ? (size_t)C * 272 : 0);
     static constexpr size_t oNW = oNP + (NORM ? (size_t)C * 80 : 0);
@@ -135,7 +139,7 @@ struct SegSmem {
     static_assert(!KDA || (C == 32 && !NORM), "the per-channel decay runs at C = 32, without the norm");
     static_assert(oQ % 16 == 0 && oV % 16 == 0 && oA % 16 == 0 && oNA % 16 == 0 && oTd % 16 == 0 &&
                       oG % 16 == 0 && oAt % 16 == 0 && oKT % 16 == 0 && oRK % 16 == 0 && oRQ % 16 == 0 &&
-                      oE % 16 == 0 && oEV % 16 == 0 && oEC % 16 == 0 && oZV % 16 == 0 && oNO % 16 == 0 && oNP % 16 == 0 &&
+                      oE % 16 == 0 && oEV % 16 == 0 && oEC % 16 == 0 && oNA2 % 16 == 0 && oAQ2 % 16 == 0 && oZV % 16 == 0 && oNO % 16 == 0 && oNP % 16 == 0 &&
                       oNW % 16 == 0,
                   "alignment");
     static_assert(kBytes <= 160 * 1024, "LDS");
@@ -541,6 +545,11 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             f16x4 tdf[NT], tef[NT], naf[L::kNA > 0 ? L::kNA : 1];
             f16x8 aqf[L::kFr];
             float gam[NT];
+            // per-channel-decay output pass: the blocks (1,0) of -A and A_qk come in two channel
+            // halves, the second added by one more product each
+            constexpr bool kSplitOff = KDA && OUT;
+            f16x4 naf2;
+            f16x8 aqf2;
             auto request_rest = [&]() __attribute__((always_inline)) {
 #pragma unroll
                 for (int m = 0; m < NT; ++m) {
@@ -553,6 +562,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                 }
 #pragma unroll
                 for (int e = 0; e < L::kNA; ++e) naf[e] = ld4(na + e * 512);
+                if constexpr (kSplitOff) naf2 = ld4(smem + L::oNA2 + s * 512 + lane * 8);
             };
             auto request_aq = [&]() __attribute__((always_inline)) {
                 if constexpr (OUT) {
@@ -560,6 +570,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                     for (int f = 0; f < L::kFr; ++f) aqf[f] = ld8(aq + f * 1024);
 #pragma unroll
                     for (int m = 0; m < NT; ++m) gam[m] = *reinterpret_cast<const float *>(gt + 4 * (16 * m + li));
+                    if constexpr (kSplitOff) aqf2 = ld8(smem + L::oAQ2 + s * 1024 + lane * 16);
                 }
             };
             if constexpr (kEarly) {
@@ -599,6 +610,12 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                     a0 = mfma16x16x16(naf[ablk(m, j)], uh[0][j], a0);
                     a1 = mfma16x16x16(naf[ablk(m, j)], uh[1][j], a1);
                 }
+                if constexpr (kSplitOff) {
+                    if (m == 1) {
+                        a0 = mfma16x16x16(naf2, uh[0][0], a0);
+                        a1 = mfma16x16x16(naf2, uh[1][0], a1);
+                    }
+                }
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                 const f16x4 h0 = to_f16x4(a0), h1 = to_f16x4(a1);
                 uh[0][m] = to_f16x4(mfma16x16x16(tdf[m], h0, z));
@@ -631,6 +648,12 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                         for (int kb = 0; kb <= m / 2; ++kb) {
                             O0 = mfma16x16x32(ua[0][kb], aqf[fblk(m, kb)], O0);
                             O1 = mfma16x16x32(ua[1][kb], aqf[fblk(m, kb)], O1);
+                        }
+                        if constexpr (kSplitOff) {
+                            if (m == 1) {
+                                O0 = mfma16x16x32(ua[0][0], aqf2, O0);
+                                O1 = mfma16x16x32(ua[1][0], aqf2, O1);
+                            }
                         }
                     }
                     const int t = 16 * m + li;
@@ -1184,8 +1207,9 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
         // q4 over the eight runs' steps. The block (1,0) relative to the last token b of tile 0,
         // (k o e^{G_b - G_r0} / E)(k o E e^{G_r1 - G_b})^T, whose operands are decays (<= 1): in fp16,
         // the same runs as 16 x 16 x 16 steps. Work: W0 A(0,0) and its inverse,
-        // W1 A(1,1) and its inverse, W2 (which holds the next log-decays) A_qk(0,0) and A_qk(1,0),
-        // W3 A(1,0) and A_qk(1,1).
+        // W1 A(1,1) and its inverse, W2 (which holds the next log-decays) A_qk(0,0), W3 A(1,0) and
+        // A_qk(1,1); in the output pass the blocks (1,0) in two channel halves: of A on W0 and W3,
+        // of A_qk on W1 and W2.
         auto kda_diag = [&](int s, int mm, bool qside) __attribute__((always_inline)) {
             const int tok = 16 * mm + li;
             const unsigned char *Es = smem + L::oE + s * C * L::kERow + tok * L::kERow;
@@ -1207,8 +1231,10 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             return acc;  // lane (q4, li), element r: s = 16 mm + 4 q4 + r, t = 16 mm + li
         };
         // the block (1,0) of A (QS = false: k of tile 1) or of A_qk (QS = true: q of tile 1)
-        auto kda_off = [&](int s, auto qs) __attribute__((always_inline)) {
+        // over channel runs blk in [B0, B1) of the eight
+        auto kda_off = [&](int s, auto qs, auto b0, auto b1) __attribute__((always_inline)) {
             constexpr bool QS = decltype(qs)::value;
+            constexpr int B0 = decltype(b0)::value, B1 = decltype(b1)::value;
             const int tsk = li, ttk = 16 + li;
             const unsigned char *Es = smem + L::oE + s * C * L::kERow;
             const unsigned char *EV = smem + L::oEV + s * kNVec * 512;
@@ -1216,7 +1242,7 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
             const unsigned char *rbt = smem + (QS ? L::oRQ : L::oRK) + ttk * 256;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int blk = 0; blk < 8; ++blk) {
+            for (int blk = B0; blk < B1; ++blk) {
                 const int rho = 4 * blk + q4;
                 const int grp = 4 * (rho >> 3) + (rho & 3), half = 8 * ((rho >> 2) & 1);
                 const f16x4 ks = ld4(rks + ((grp ^ ksw(tsk & 15)) << 4) + half);
@@ -1261,11 +1287,23 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                     unsigned char *tdb = smem + L::oTd + s * 2 * NT * 512 + W * 1024 + lane * 8;
                     *reinterpret_cast<f16x4 *>(tdb) = to_f16x4(tq);
                     *reinterpret_cast<f16x4 *>(tdb + 512) = to_f16x4(tq);
+                    if constexpr (OUT) {
+                        // the first channel half of the block (1,0): of -A on W0, of A_qk on W1
+                        if constexpr (W == 0) {
+                            const float b1 = gts[C + 16 + li];
+                            *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(1, 0) * 512 + lane * 8) =
+                                to_f16x4(-(b1 * kda_off(s, IC<0>{}, IC<0>{}, IC<4>{})));
+                        } else {
+                            *reinterpret_cast<f16x4 *>(aqb + fblk(1, 0) * 1024) =
+                                to_f16x4(sct * kda_off(s, IC<1>{}, IC<0>{}, IC<4>{}));
+                        }
+                    }
                 } else if constexpr (W == 3) {
-                    const f32x4 acc = kda_off(s, IC<0>{});
+                    // -A(1,0): all of it in the map pass, its second channel half in the output pass
+                    const f32x4 acc = OUT ? kda_off(s, IC<0>{}, IC<4>{}, IC<8>{}) : kda_off(s, IC<0>{}, IC<0>{}, IC<8>{});
                     const float bt = gts[C + 16 + li];
-                    *reinterpret_cast<f16x4 *>(smem + L::oNA + s * L::kNA * 512 + ablk(1, 0) * 512 + lane * 8) =
-                        to_f16x4(-(bt * acc));
+                    *reinterpret_cast<f16x4 *>(smem + (OUT ? L::oNA2 + s * 512 : L::oNA + s * L::kNA * 512 + ablk(1, 0) * 512) +
+                                               lane * 8) = to_f16x4(-(bt * acc));
                     if (OUT) {
                         const f32x4 dq = kda_diag(s, 1, true);
                         f32x4 aq;
@@ -1281,8 +1319,10 @@ __global__ __launch_bounds__((seg_threads<OUT, KDA>()), 1) void gdn_seg_pass_ker
                     for (int r = 0; r < 4; ++r) aq[r] = 4 * q4 + r <= li ? sct * dq[r] : 0.0f;
                     *reinterpret_cast<f16x4 *>(aqb + fblk(0, 0) * 1024) = to_f16x4(aq);
                     *reinterpret_cast<f16x4 *>(aqb + fblk(0, 0) * 1024 + 8) = f16x4{};
-                    // and A_qk(1,0), the first half of the fragment whose second half W3 writes
-                    *reinterpret_cast<f16x4 *>(aqb + fblk(1, 0) * 1024) = to_f16x4(sct * kda_off(s, IC<1>{}));
+                    // and the second channel half of A_qk(1,0), with a zero second half
+                    unsigned char *aq2 = smem + L::oAQ2 + s * 1024 + lane * 16;
+                    *reinterpret_cast<f16x4 *>(aq2) = to_f16x4(sct * kda_off(s, IC<1>{}, IC<4>{}, IC<8>{}));
+                    *reinterpret_cast<f16x4 *>(aq2 + 8) = f16x4{};
                 }
             }
         };
